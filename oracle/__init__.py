@@ -1,0 +1,324 @@
+"""CPU oracle for the NF4 quantized-codebook linear layer with a LoRA side branch.
+
+TEST INFRASTRUCTURE ONLY.  This package is imported by the test-suite, by the smoke check and by
+the CPU-baseline leg of the benchmark, and by nothing else.  It shares no code, header, table or
+constant generator with the HIP library, and it never imports it.
+
+What it computes, and where each step comes from (page: "QLoRA: Efficient Finetuning of
+Quantized LLMs" study notes, gitcode.csdn.net/6a0046f754b52172bc72e356, unless noted):
+
+* ``codebook``      -- section 3.2, eq. (4) and the asymmetric exact-zero construction;
+                       section 5.1.2, Fig. 7 text (8 values on one half, 7 on the other, plus 0).
+* ``quantize``      -- section 3.1 (flatten, blocks of B, one constant per block), eq. (1) in its
+                       absmax form, section 3.2 step 3 (absmax normalisation to [-1, 1]).
+* ``double_quant``  -- section 3.3 (mean-centred 8-bit float constants, block 256).
+* ``dequant``       -- section 3.5, eq. (6), with eq. (2) at each level; output in BF16.
+* ``forward``       -- section 3.5 eq. (5) with the scalar s of eq. (3) (section 4, LoRA).
+* ``backward``      -- section 3.5: gradients for the adapters only, through the BF16 weight.
+* ``swiglu_*``      -- not a step of the method: the gated MLP that the LLaMA-shaped workloads
+                       wrap around three such linears.
+
+The bit-exact steps (codebook, quantize, double quant, dequant, bf16 and E4M3 rounding) are plain
+C in ``nf4_oracle.c``, built with gcc ``-O2 -ffp-contract=off``.  The linear-layer algebra is
+plain float64 numpy: matrix products are library primitives, nothing is blocked or fused, and no
+intermediate is rounded.
+
+Pins (tests/test_oracle_pins.py) tie every function to something other than itself: the page's
+printed numbers, closed forms, library routines (scipy's normal quantile, torch's bf16 and
+float8_e4m3fn casts, torch autograd), exact rational brute force and finite differences.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nf4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+#: Tail probability of the codebook grid (reading of the open constant in eq. 4): the midpoint
+#: between the outermost-bin centres of a 16-value symmetric type (1 - 1/32) and of a 15-value
+#: symmetric type with a zero (1 - 1/30).
+DELTA_DEFAULT = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+BLOCK = 64          # first-level block (section 3.5: blocksize 64 for W)
+DQ_BLOCK = 256      # second-level block (section 3.3: blocksize 256)
+E4M3_MAX = 448.0
+
+
+def build(force: bool = False) -> str:
+    """Compile the C part of the oracle with gcc (no HIP involved)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            i64, i32, f64, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_float
+            sig = {
+                "oracle_norm_ppf": (f64, [f64]),
+                "oracle_codebook": (ctypes.c_int, [f64, P]),
+                "oracle_bf16_rne_vec": (None, [P, i64, P]),
+                "oracle_e4m3_encode_vec": (None, [P, i64, P]),
+                "oracle_e4m3_decode_vec": (None, [P, i64, P]),
+                "oracle_quantize": (ctypes.c_int, [P, i64, i32, P, P, P]),
+                "oracle_grouped_sum": (f64, [P, i64, i32]),
+                "oracle_double_quant": (ctypes.c_int, [P, i64, i32, P, P, P]),
+                "oracle_block_scales": (ctypes.c_int, [P, P, f32, i64, i32, P]),
+                "oracle_dequant": (ctypes.c_int, [P, P, P, f32, i64, i32, i32, P, P]),
+                "oracle_dequant_plain": (ctypes.c_int, [P, P, i64, i32, P, P]),
+                "oracle_unpack": (None, [P, i64, P]),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ------------------------------------------------------------------------------------------
+# Number formats
+# ------------------------------------------------------------------------------------------
+
+def norm_ppf(p: float) -> float:
+    """Standard normal quantile by bisection on erfc (float64)."""
+    return _load().oracle_norm_ppf(float(p))
+
+
+def bf16_rne(x) -> np.ndarray:
+    """float32 -> bfloat16 bits, nearest by value, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_bf16_rne_vec(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 code: nearest finite value, ties to even, saturating, sign kept."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_vec(_p(x), x.size, _p(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float32)
+    _load().oracle_e4m3_decode_vec(_p(c), c.size, _p(out))
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# Codebook, quantize, double quant, dequant
+# ------------------------------------------------------------------------------------------
+
+def codebook(delta: float = DELTA_DEFAULT) -> np.ndarray:
+    """The 16 NF4 values, ascending, float32 (index 7 is the exact zero)."""
+    out = np.empty(16, dtype=np.float32)
+    rc = _load().oracle_codebook(float(delta), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_codebook failed (%d)" % rc)
+    return out
+
+
+def quantize(W, cb=None, block: int = BLOCK):
+    """Level-1 quantization of the row-major flattening of ``W``.
+
+    Returns (packed uint8 [ceil(n/2)], absmax float32 [ceil(n/block)])."""
+    W = np.ascontiguousarray(W, dtype=np.float32).reshape(-1)
+    cb = codebook() if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
+    n = W.size
+    packed = np.zeros((n + 1) // 2, dtype=np.uint8)
+    absmax = np.zeros((n + block - 1) // block, dtype=np.float32)
+    rc = _load().oracle_quantize(_p(W), n, block, _p(cb), _p(packed), _p(absmax))
+    if rc != 0:
+        raise ValueError("oracle_quantize failed (%d)" % rc)
+    return packed, absmax
+
+
+def grouped_sum(v, group: int = 256) -> float:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return _load().oracle_grouped_sum(_p(v), v.size, group)
+
+
+def double_quant(absmax, dq_block: int = DQ_BLOCK):
+    """Level-2 quantization of the block constants.
+
+    Returns (codes uint8 [nb], scales float32 [ceil(nb/dq_block)], mean float32)."""
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    nb = a.size
+    codes = np.zeros(nb, dtype=np.uint8)
+    scales = np.zeros((nb + dq_block - 1) // dq_block, dtype=np.float32)
+    mean = np.zeros(1, dtype=np.float32)
+    rc = _load().oracle_double_quant(_p(a), nb, dq_block, _p(codes), _p(scales), _p(mean))
+    if rc != 0:
+        raise ValueError("oracle_double_quant failed (%d)" % rc)
+    return codes, scales, np.float32(mean[0])
+
+
+def block_scales(codes, scales, mean, dq_block: int = DQ_BLOCK) -> np.ndarray:
+    """The rebuilt first-level constants a' (inner dequant of eq. 6)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    out = np.empty(codes.size, dtype=np.float32)
+    _load().oracle_block_scales(_p(codes), _p(scales), float(mean), codes.size, dq_block, _p(out))
+    return out
+
+
+def dequant(packed, codes, scales, mean, numel: int, cb=None, block: int = BLOCK,
+            dq_block: int = DQ_BLOCK) -> np.ndarray:
+    """Eq. (6): bf16 bit patterns [numel] of the double-dequantized weight."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    cb = codebook() if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
+    out = np.empty(numel, dtype=np.uint16)
+    rc = _load().oracle_dequant(_p(packed), _p(codes), _p(scales), float(mean), numel, block,
+                                dq_block, _p(cb), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_dequant failed (%d)" % rc)
+    return out
+
+
+def dequant_plain(packed, absmax, numel: int, cb=None, block: int = BLOCK) -> np.ndarray:
+    """Eq. (2) with float32 block constants (no double quantization), bf16 bits."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    absmax = np.ascontiguousarray(absmax, dtype=np.float32)
+    cb = codebook() if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
+    out = np.empty(numel, dtype=np.uint16)
+    _load().oracle_dequant_plain(_p(packed), _p(absmax), numel, block, _p(cb), _p(out))
+    return out
+
+
+def unpack(packed, numel: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty(numel, dtype=np.uint8)
+    _load().oracle_unpack(_p(packed), numel, _p(out))
+    return out
+
+
+def quantize_dq(W, cb=None):
+    """Quantize + double-quantize a weight; returns a dict of the stored pieces."""
+    W = np.asarray(W, dtype=np.float32)
+    packed, absmax = quantize(W, cb)
+    codes, scales, mean = double_quant(absmax)
+    return {"packed": packed, "absmax": absmax, "codes": codes, "scales": scales, "mean": mean,
+            "shape": W.shape}
+
+
+def dequant_weight(q, cb=None) -> np.ndarray:
+    """bf16 bits of the weight described by ``quantize_dq``'s dict, reshaped."""
+    n = int(np.prod(q["shape"]))
+    return dequant(q["packed"], q["codes"], q["scales"], q["mean"], n, cb).reshape(q["shape"])
+
+
+# ------------------------------------------------------------------------------------------
+# QLoRA linear layer, float64 (section 3.5 eq. 5 with the s of eq. 3)
+# W is stored [N_out, K_in]; the pages' W (h x o) is its transpose, so Y = X deq(W)^T + ...
+# ------------------------------------------------------------------------------------------
+
+def _f64(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = bf16_to_f32(a)
+    return a.astype(np.float64)
+
+
+def forward(X, Wdq, L1, L2, s: float):
+    """Y = X Wdq^T + s (X L1) L2.  Returns (Y, T) in float64; T = X L1 (unscaled)."""
+    X, Wdq, L1, L2 = _f64(X), _f64(Wdq), _f64(L1), _f64(L2)
+    T = X @ L1
+    Y = X @ Wdq.T + float(s) * (T @ L2)
+    return Y, T
+
+
+def backward(dY, X, Wdq, L1, L2, s: float):
+    """Gradients of E with respect to X, L1 and L2 given dE/dY; no gradient for W (frozen).
+
+    dT = s dY L2^T;  dL2 = s (X L1)^T dY;  dL1 = X^T dT;  dX = dY Wdq + dT L1^T."""
+    dY, X, Wdq, L1, L2 = _f64(dY), _f64(X), _f64(Wdq), _f64(L1), _f64(L2)
+    s = float(s)
+    T = X @ L1
+    dT = s * (dY @ L2.T)
+    dL2 = s * (T.T @ dY)
+    dL1 = X.T @ dT
+    dX = dY @ Wdq + dT @ L1.T
+    return {"dX": dX, "dL1": dL1, "dL2": dL2, "dT": dT}
+
+
+def forward_rows(X, Wdq, L1, L2, s: float, rows):
+    """Forward for a subset of token rows only (full-size spot checks)."""
+    X = _f64(np.asarray(X)[rows])
+    Y, T = forward(X, Wdq, L1, L2, s)
+    return Y, T
+
+
+# ------------------------------------------------------------------------------------------
+# SwiGLU glue for the MLP workloads (not a step of the method)
+# ------------------------------------------------------------------------------------------
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def swiglu_fwd(g, u) -> np.ndarray:
+    """h = silu(g) * u, silu(g) = g * sigmoid(g); float64."""
+    g, u = _f64(g), _f64(u)
+    return g * _sigmoid(g) * u
+
+
+def swiglu_bwd(dh, g, u):
+    """(dg, du) for h = silu(g) * u."""
+    dh, g, u = _f64(dh), _f64(g), _f64(u)
+    sg = _sigmoid(g)
+    du = dh * g * sg
+    dg = dh * u * sg * (1.0 + g * (1.0 - sg))
+    return dg, du
+
+
+# ------------------------------------------------------------------------------------------
+# Error measures used by the parity tests
+# ------------------------------------------------------------------------------------------
+
+REL_FRO_TOL = 5e-3
+MAX_ABS_TOL = 2e-2
+
+
+def rel_fro(got, ref) -> float:
+    got, ref = _f64(got), _f64(ref)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got))
+
+
+def max_abs_ratio(got, ref) -> float:
+    got, ref = _f64(got), _f64(ref)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    err = np.max(np.abs(got - ref)) if ref.size else 0.0
+    return float(err / den) if den > 0 else float(err)
+
+
+def within_tolerance(got, ref) -> bool:
+    return rel_fro(got, ref) <= REL_FRO_TOL and max_abs_ratio(got, ref) <= MAX_ABS_TOL
