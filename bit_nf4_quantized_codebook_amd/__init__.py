@@ -1,0 +1,300 @@
+"""MI355X (gfx950) NF4 quantized-codebook linear layer with a LoRA side branch.
+
+Thin Python binding over the C ABI of ``libnf4.so`` (declared in ``include/nf4.h``).  Every
+function here only marshals arguments: tensors are passed by device pointer, the stream is the
+current torch stream, and all arithmetic runs in the library's HIP kernels.  If the library is
+not built, importing the binding raises; there is no fallback path.
+
+Names follow the C ABI:
+  nf4_build_codebook, nf4_quantize, nf4_double_quant, nf4_dequant,
+  qlora_linear_fwd, qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4.so")
+
+NF4_OK = 0
+QLORA_DX_ACCUMULATE = 1
+BLOCK = 64
+DQ_BLOCK = 256
+
+#: Symbols the C ABI exports (include/nf4.h).
+EXPORTS = (
+    "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook", "nf4_quantize",
+    "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant",
+    "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_swiglu_fwd", "qlora_swiglu_bwd",
+)
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class _WeightDesc(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("absmax_scale", ctypes.c_void_p),
+        ("absmax_mean", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("dq_block", ctypes.c_int32),
+        ("codebook", ctypes.c_float * 16),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_nf4_quantized_codebook_amd.build` "
+                          "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    i = ctypes.c_int
+    W = ctypes.POINTER(_WeightDesc)
+    sigs = {
+        "nf4_status_string": (ctypes.c_char_p, [i]),
+        "nf4_last_error": (ctypes.c_char_p, []),
+        "nf4_version": (ctypes.c_char_p, []),
+        "nf4_build_codebook": (i, [P, ctypes.c_double]),
+        "nf4_quantize": (i, [P, i64, i32, P, P, P, P]),
+        "nf4_double_quant_workspace_size": (sz, [i64, i32]),
+        "nf4_double_quant": (i, [P, i64, i32, P, P, P, P, sz, P]),
+        "nf4_dequant": (i, [W, P, P]),
+        "qlora_linear_workspace_size": (sz, [i64, i64, i64, i32]),
+        "qlora_linear_fwd": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P, sz, P]),
+        "qlora_linear_bwd": (i, [W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P,
+                                 ctypes.c_uint32, P, sz, P]),
+        "qlora_swiglu_fwd": (i, [P, P, P, i64, P]),
+        "qlora_swiglu_bwd": (i, [P, P, P, P, P, i64, P]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != NF4_OK:
+        raise NF4Error(status, where, lib.nf4_last_error().decode())
+
+
+def status_string(status: int) -> str:
+    return lib.nf4_status_string(status).decode()
+
+
+def version() -> str:
+    return lib.nf4_version().decode()
+
+
+# ------------------------------------------------------------------------------------------
+# torch plumbing (device memory and streams only)
+# ------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------------------
+# Codebook, quantize, double quant, dequant
+# ------------------------------------------------------------------------------------------
+
+def nf4_build_codebook(delta: float = 0.0) -> np.ndarray:
+    """The 16 NF4 codewords (host, float32, ascending); delta 0 selects the default."""
+    out = np.zeros(16, dtype=np.float32)
+    _check(lib.nf4_build_codebook(ctypes.c_void_p(out.ctypes.data), float(delta)), "nf4_build_codebook")
+    return out
+
+
+def nf4_quantize(W, codebook=None, block: int = BLOCK):
+    """Level-1 quantization of a float32 device tensor: returns (packed uint8, absmax float32)."""
+    torch = _torch()
+    _need(W, torch.float32, "W")
+    cb = nf4_build_codebook() if codebook is None else np.ascontiguousarray(codebook, dtype=np.float32)
+    n = W.numel()
+    packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=W.device)
+    absmax = torch.empty((n + block - 1) // block, dtype=torch.float32, device=W.device)
+    _check(lib.nf4_quantize(_ptr(W), n, block, ctypes.c_void_p(cb.ctypes.data), _ptr(packed),
+                            _ptr(absmax), _stream(W.device)), "nf4_quantize")
+    return packed, absmax
+
+
+def nf4_double_quant(absmax, dq_block: int = DQ_BLOCK, workspace=None):
+    """Level-2 quantization: returns (absmax_q uint8, absmax_scale float32, absmax_mean float32[1])."""
+    torch = _torch()
+    _need(absmax, torch.float32, "absmax")
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.uint8, device=absmax.device)
+    sc = torch.empty((nb + dq_block - 1) // dq_block, dtype=torch.float32, device=absmax.device)
+    mean = torch.empty(1, dtype=torch.float32, device=absmax.device)
+    wsb = lib.nf4_double_quant_workspace_size(nb, dq_block)
+    ws = _workspace(wsb, absmax.device, workspace)
+    _check(lib.nf4_double_quant(_ptr(absmax), nb, dq_block, _ptr(q), _ptr(sc), _ptr(mean), _ptr(ws),
+                                wsb, _stream(absmax.device)), "nf4_double_quant")
+    return q, sc, mean
+
+
+@dataclass
+class NF4Weight:
+    """A frozen NF4 weight [rows = N_out, cols = K_in] in double-quantized form (device tensors)."""
+    packed: object
+    absmax_q: object
+    absmax_scale: object
+    absmax_mean: object
+    rows: int
+    cols: int
+    codebook: np.ndarray
+    block: int = BLOCK
+    dq_block: int = DQ_BLOCK
+
+    def descriptor(self) -> _WeightDesc:
+        d = _WeightDesc()
+        d.packed = self.packed.data_ptr()
+        d.absmax_q = self.absmax_q.data_ptr()
+        d.absmax_scale = self.absmax_scale.data_ptr()
+        d.absmax_mean = self.absmax_mean.data_ptr()
+        d.rows, d.cols = int(self.rows), int(self.cols)
+        d.block, d.dq_block = int(self.block), int(self.dq_block)
+        for j in range(16):
+            d.codebook[j] = float(self.codebook[j])
+        return d
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    @classmethod
+    def from_float(cls, W, codebook=None):
+        """Quantize + double-quantize a float32 [rows, cols] device tensor."""
+        cb = nf4_build_codebook() if codebook is None else np.ascontiguousarray(codebook, dtype=np.float32)
+        packed, absmax = nf4_quantize(W.contiguous(), cb)
+        q, sc, mean = nf4_double_quant(absmax)
+        return cls(packed, q, sc, mean, W.shape[0], W.shape[1], cb)
+
+
+def nf4_dequant(w: NF4Weight):
+    """Double dequantization: bf16 [rows, cols] device tensor."""
+    torch = _torch()
+    out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=w.device)
+    d = w.descriptor()
+    _check(lib.nf4_dequant(ctypes.byref(d), _ptr(out), _stream(w.device)), "nf4_dequant")
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# Linear layer
+# ------------------------------------------------------------------------------------------
+
+def qlora_linear_workspace_size(M: int, N: int, K: int, r: int) -> int:
+    return int(lib.qlora_linear_workspace_size(M, N, K, r))
+
+
+def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True, Y=None,
+                     workspace=None):
+    """Y = X deq(W)^T + scale (X L1) L2.  Returns (Y, T) with T = X L1 (or None)."""
+    torch = _torch()
+    for t, n in ((X, "X"), (L1, "L1"), (L2, "L2")):
+        _need(t, torch.bfloat16, n)
+    M, r = X.shape[0], L1.shape[1]
+    if X.shape[1] != w.cols or L1.shape[0] != w.cols or tuple(L2.shape) != (r, w.rows):
+        raise ValueError("shape mismatch")
+    if Y is None:
+        Y = torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device)
+    T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if keep_T else None
+    wsb = qlora_linear_workspace_size(M, w.rows, w.cols, r)
+    ws = _workspace(wsb, X.device, workspace)
+    d = w.descriptor()
+    _check(lib.qlora_linear_fwd(ctypes.byref(d), _ptr(X), _ptr(L1), _ptr(L2), float(scale), M, r,
+                                _ptr(Y), _ptr(T), _ptr(ws), wsb, _stream(X.device)), "qlora_linear_fwd")
+    return Y, T
+
+
+def qlora_linear_bwd(w: NF4Weight, dY, X, L1, L2, T, scale: float, need_dX: bool = True,
+                     dX=None, accumulate: bool = False, workspace=None):
+    """Returns (dX or None, dL1, dL2) for the layer above; W is not touched."""
+    torch = _torch()
+    for t, n in ((dY, "dY"), (X, "X"), (L1, "L1"), (L2, "L2")):
+        _need(t, torch.bfloat16, n)
+    if T is not None:
+        _need(T, torch.bfloat16, "T")
+    M, r = X.shape[0], L1.shape[1]
+    if tuple(dY.shape) != (M, w.rows) or X.shape[1] != w.cols:
+        raise ValueError("shape mismatch")
+    if need_dX and dX is None:
+        dX = torch.empty((M, w.cols), dtype=torch.bfloat16, device=X.device)
+    if not need_dX:
+        dX = None
+    dL1 = torch.empty((w.cols, r), dtype=torch.bfloat16, device=X.device)
+    dL2 = torch.empty((r, w.rows), dtype=torch.bfloat16, device=X.device)
+    wsb = qlora_linear_workspace_size(M, w.rows, w.cols, r)
+    ws = _workspace(wsb, X.device, workspace)
+    d = w.descriptor()
+    flags = QLORA_DX_ACCUMULATE if accumulate else 0
+    _check(lib.qlora_linear_bwd(ctypes.byref(d), _ptr(dY), _ptr(X), _ptr(L1), _ptr(L2), _ptr(T),
+                                float(scale), M, r, _ptr(dX), _ptr(dL1), _ptr(dL2), flags, _ptr(ws),
+                                wsb, _stream(X.device)), "qlora_linear_bwd")
+    return dX, dL1, dL2
+
+
+def qlora_swiglu_fwd(g, u, h=None):
+    torch = _torch()
+    _need(g, torch.bfloat16, "g")
+    _need(u, torch.bfloat16, "u")
+    if h is None:
+        h = torch.empty_like(g)
+    _check(lib.qlora_swiglu_fwd(_ptr(g), _ptr(u), _ptr(h), g.numel(), _stream(g.device)), "qlora_swiglu_fwd")
+    return h
+
+
+def qlora_swiglu_bwd(dh, g, u):
+    torch = _torch()
+    for t, n in ((dh, "dh"), (g, "g"), (u, "u")):
+        _need(t, torch.bfloat16, n)
+    dg = torch.empty_like(g)
+    du = torch.empty_like(u)
+    _check(lib.qlora_swiglu_bwd(_ptr(dh), _ptr(g), _ptr(u), _ptr(dg), _ptr(du), g.numel(),
+                                _stream(g.device)), "qlora_swiglu_bwd")
+    return dg, du

@@ -1,0 +1,362 @@
+// C ABI of the NF4 quantized-codebook linear layer: argument validation, workspace planning and
+// launch sequencing on the caller's stream.  Declarations and contracts: include/nf4.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/nf4.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, const char *detail = nullptr) {
+    if (detail) std::snprintf(g_last_error, sizeof g_last_error, fmt, detail);
+    else std::snprintf(g_last_error, sizeof g_last_error, "%s", fmt);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+    return NF4_ERR_HIP;
+}
+
+#define NF4_CHECK_HIP(expr, where)                \
+    do {                                          \
+        hipError_t e_ = (expr);                   \
+        if (e_ != hipSuccess) return hip_fail(e_, where); \
+    } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------------------------------
+// Standard normal quantile: Halley iteration on the CDF (via erfc, tail-aware form), started from
+// the rational approximation of Abramowitz & Stegun 26.2.23.
+// ---------------------------------------------------------------------------------------------
+double upper_tail(double x) { return 0.5 * std::erfc(x / std::sqrt(2.0)); }   // Q(x) = 1 - Phi(x)
+
+double normal_quantile(double p) {
+    const double q = (p < 0.5) ? p : 1.0 - p;      // exact for p >= 0.5 (Sterbenz)
+    const double t = std::sqrt(-2.0 * std::log(q));
+    double z = t - (2.515517 + 0.802853 * t + 0.010328 * t * t) /
+                       (1.0 + 1.432788 * t + 0.189269 * t * t + 0.001308 * t * t * t);
+    // z approximates the upper-tail point: Q(z) = q, z >= 0
+    if (q == 0.5) return 0.0;
+    const double inv_sqrt_2pi = 0.39894228040143267794;
+    for (int it = 0; it < 100; ++it) {
+        const double f = upper_tail(z) - q;             // decreasing in z
+        const double dens = inv_sqrt_2pi * std::exp(-0.5 * z * z);
+        const double u = -f / dens;                      // Newton step for Q(z) = q
+        const double step = u / (1.0 + 0.5 * z * u);     // Halley correction (Q'' = z * dens)
+        const double zn = z - step;
+        if (zn == z || std::fabs(step) <= 1e-17 * std::fabs(z)) { z = zn; break; }
+        z = zn;
+    }
+    return (p < 0.5) ? -z : z;
+}
+
+// Largest float f with f <= (a + b) / 2, computed exactly (TwoSum keeps the rounding error).
+float threshold_below_midpoint(float a, float b) {
+    const double s = (double)a + (double)b;
+    const double bv = s - (double)a;
+    const double err = ((double)a - (s - bv)) + ((double)b - bv);
+    const double hs = s * 0.5, he = err * 0.5;
+    auto above = [&](float f) { return ((double)f - hs) > he; };   // f > midpoint
+    float t = (float)hs;
+    while (above(t)) t = std::nextafterf(t, -INFINITY);
+    for (;;) {
+        const float u = std::nextafterf(t, INFINITY);
+        if (!above(u)) t = u; else break;
+    }
+    return t;
+}
+
+int check_codebook(const float cb[16], int *zero_code) {
+    int z = -1;
+    for (int j = 0; j < 16; ++j) {
+        if (!std::isfinite(cb[j])) return fail(NF4_ERR_ARG, "codebook entries must be finite");
+        if (j > 0 && !(cb[j - 1] < cb[j])) return fail(NF4_ERR_ARG, "codebook must be strictly ascending");
+        if (cb[j] == 0.0f) z = j;
+    }
+    if (z < 0) return fail(NF4_ERR_ARG, "codebook must contain 0.0f");
+    *zero_code = z;
+    return NF4_OK;
+}
+
+int check_weight(const nf4_weight *w) {
+    if (!w) return fail(NF4_ERR_NULL, "weight descriptor is NULL");
+    if (!w->packed || !w->absmax_q || !w->absmax_scale || !w->absmax_mean)
+        return fail(NF4_ERR_NULL, "weight descriptor has a NULL pointer");
+    if (w->rows <= 0 || w->cols <= 0) return fail(NF4_ERR_SHAPE, "weight rows and cols must be > 0");
+    if (w->block != 64) return fail(NF4_ERR_UNSUPPORTED, "block must be 64");
+    if (w->dq_block != 256) return fail(NF4_ERR_UNSUPPORTED, "dq_block must be 256");
+    if (!aligned16(w->packed)) return fail(NF4_ERR_ALIGN, "packed weight must be 16-byte aligned");
+    int zc;
+    return check_codebook(w->codebook, &zc);
+}
+
+nf4k::WeightView view_of(const nf4_weight *w) {
+    nf4k::WeightView v;
+    v.packed = w->packed;
+    v.c2 = w->absmax_q;
+    v.c1 = w->absmax_scale;
+    v.mean = w->absmax_mean;
+    v.rows = w->rows;
+    v.cols = w->cols;
+    for (int j = 0; j < 16; ++j) v.cb[j] = w->codebook[j];
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Workspace plan of the linear layer (identical for the size query and the calls)
+// ---------------------------------------------------------------------------------------------
+constexpr int64_t kTile = 64;
+
+struct Plan {
+    int ksT, ksdT, msL2, msL1;
+    size_t off_L1t, off_L2t, off_T, off_sT, off_dT, off_P, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
+    Plan p;
+    const int64_t mt = (M + kTile - 1) / kTile, rt = (r + kTile - 1) / kTile;
+    p.ksT = nf4k::choose_split(mt * rt, (K + kTile - 1) / kTile);
+    p.ksdT = nf4k::choose_split(mt * rt, (N + kTile - 1) / kTile);
+    p.msL2 = nf4k::choose_split(rt * ((N + kTile - 1) / kTile), mt);
+    p.msL1 = nf4k::choose_split(((K + kTile - 1) / kTile) * rt, mt);
+    size_t off = 0;
+    p.off_L1t = off; off += round256((size_t)r * K * 2);
+    p.off_L2t = off; off += round256((size_t)N * r * 2);
+    p.off_T = off;   off += round256((size_t)M * r * 2);
+    p.off_sT = off;  off += round256((size_t)M * r * 2);
+    p.off_dT = off;  off += round256((size_t)M * r * 2);
+    size_t pmax = (size_t)p.ksT * M * r;
+    pmax = pmax > (size_t)p.ksdT * M * r ? pmax : (size_t)p.ksdT * M * r;
+    pmax = pmax > (size_t)p.msL2 * r * N ? pmax : (size_t)p.msL2 * r * N;
+    pmax = pmax > (size_t)p.msL1 * K * r ? pmax : (size_t)p.msL1 * K * r;
+    p.off_P = off;   off += round256(pmax * 4);
+    p.total = off;
+    return p;
+}
+
+int check_linear_args(const nf4_weight *w, int64_t M, int32_t r, float scale) {
+    int rc = check_weight(w);
+    if (rc) return rc;
+    if (M <= 0) return fail(NF4_ERR_SHAPE, "M must be >= 1");
+    if (r < 1 || r > 128) return fail(NF4_ERR_UNSUPPORTED, "r must be in [1, 128]");
+    if (r % 8) return fail(NF4_ERR_UNSUPPORTED, "r must be a multiple of 8");
+    if (w->cols % 64) return fail(NF4_ERR_UNSUPPORTED, "weight cols (K) must be a multiple of 64");
+    if (w->rows % 8) return fail(NF4_ERR_UNSUPPORTED, "weight rows (N) must be a multiple of 8");
+    if (!std::isfinite(scale)) return fail(NF4_ERR_ARG, "scale must be finite");
+    return NF4_OK;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+// T (unscaled) and/or s*T, both bf16 [M, r], from X [M, K] and L1 [K, r]
+int compute_T(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32_t r, float scale,
+              uint16_t *T_out, uint16_t *sT_out, const Plan &p, void *ws, hipStream_t s) {
+    uint16_t *L1t = ws_at<uint16_t>(ws, p.off_L1t);
+    float *P = ws_at<float>(ws, p.off_P);
+    NF4_CHECK_HIP(nf4k::launch_transpose(L1, K, r, L1t, s), "transpose L1");
+    NF4_CHECK_HIP(nf4k::launch_skinny_nt(X, L1t, P, M, r, K, p.ksT, s), "T = X L1");
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksT, M * r, 1.0f, T_out, scale, sT_out, s),
+                  "T reduce");
+    return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nf4_status_string(int status) {
+    switch (status) {
+        case NF4_OK: return "ok";
+        case NF4_ERR_NULL: return "null pointer";
+        case NF4_ERR_SHAPE: return "invalid shape";
+        case NF4_ERR_ALIGN: return "misaligned pointer";
+        case NF4_ERR_UNSUPPORTED: return "unsupported parameter";
+        case NF4_ERR_WORKSPACE: return "workspace too small";
+        case NF4_ERR_HIP: return "HIP runtime error";
+        case NF4_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char *nf4_last_error(void) { return g_last_error; }
+
+const char *nf4_version(void) { return "0.1.0"; }
+
+int nf4_build_codebook(float out_codebook[16], double delta) {
+    if (!out_codebook) return fail(NF4_ERR_NULL, "out_codebook is NULL");
+    if (delta == 0.0) delta = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+    if (!(delta > 0.5 && delta < 1.0)) return fail(NF4_ERR_ARG, "delta must be in (0.5, 1)");
+    const double zmax = normal_quantile(delta);
+    double v[16];
+    int n = 0;
+    for (int j = 7; j >= 1; --j) v[n++] = -(normal_quantile(0.5 + (delta - 0.5) * ((double)j / 7.0)) / zmax);
+    v[n++] = 0.0;
+    for (int j = 1; j <= 8; ++j) v[n++] = normal_quantile(0.5 + (delta - 0.5) * ((double)j / 8.0)) / zmax;
+    for (int j = 0; j < 16; ++j) out_codebook[j] = (float)v[j];
+    return NF4_OK;
+}
+
+int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codebook[16],
+                 uint8_t *packed, float *absmax, void *stream) {
+    if (!codebook) return fail(NF4_ERR_NULL, "codebook is NULL");
+    if (numel < 0) return fail(NF4_ERR_SHAPE, "numel must be >= 0");
+    if (block != 64) return fail(NF4_ERR_UNSUPPORTED, "block must be 64");
+    int zc;
+    int rc = check_codebook(codebook, &zc);
+    if (rc) return rc;
+    if (numel == 0) return NF4_OK;
+    if (!W || !packed || !absmax) return fail(NF4_ERR_NULL, "W, packed and absmax must be non-NULL");
+    if (!aligned16(W) || !aligned16(packed)) return fail(NF4_ERR_ALIGN, "W and packed must be 16-byte aligned");
+    float thr[15];
+    for (int j = 0; j < 15; ++j) thr[j] = threshold_below_midpoint(codebook[j], codebook[j + 1]);
+    NF4_CHECK_HIP(nf4k::launch_quantize(W, numel, thr, (uint32_t)zc, packed, absmax,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                  "quantize");
+    return NF4_OK;
+}
+
+size_t nf4_double_quant_workspace_size(int64_t nblocks, int32_t dq_block) {
+    (void)dq_block;
+    if (nblocks <= 0) return 0;
+    return nf4k::double_quant_ws(nblocks);
+}
+
+int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                     float *absmax_scale, float *absmax_mean, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (nblocks <= 0) return fail(NF4_ERR_SHAPE, "nblocks must be >= 1");
+    if (dq_block != 256) return fail(NF4_ERR_UNSUPPORTED, "dq_block must be 256");
+    if (!absmax || !absmax_q || !absmax_scale || !absmax_mean || !workspace)
+        return fail(NF4_ERR_NULL, "double quant pointers must be non-NULL");
+    if (!aligned16(absmax_q) || !aligned16(workspace))
+        return fail(NF4_ERR_ALIGN, "absmax_q and workspace must be 16-byte aligned");
+    if (workspace_bytes < nf4k::double_quant_ws(nblocks))
+        return fail(NF4_ERR_WORKSPACE, "double quant workspace too small");
+    NF4_CHECK_HIP(nf4k::launch_double_quant(absmax, nblocks, absmax_q, absmax_scale, absmax_mean,
+                                            workspace, reinterpret_cast<hipStream_t>(stream)),
+                  "double quant");
+    return NF4_OK;
+}
+
+int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
+    int rc = check_weight(w);
+    if (rc) return rc;
+    if (!out_bf16) return fail(NF4_ERR_NULL, "out_bf16 is NULL");
+    if (!aligned16(out_bf16)) return fail(NF4_ERR_ALIGN, "out_bf16 must be 16-byte aligned");
+    const int64_t numel = w->rows * w->cols;
+    if (numel % 2) return fail(NF4_ERR_SHAPE, "rows*cols must be even");
+    NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, numel,
+                                       w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
+                  "dequant");
+    return NF4_OK;
+}
+
+size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
+    if (M <= 0 || N <= 0 || K <= 0 || r <= 0) return 0;
+    return make_plan(M, N, K, r).total;
+}
+
+int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                     float scale, int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    int rc = check_linear_args(w, M, r, scale);
+    if (rc) return rc;
+    if (!X || !L1 || !L2 || !Y) return fail(NF4_ERR_NULL, "X, L1, L2 and Y must be non-NULL");
+    if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) ||
+        (T_out && !aligned16(T_out)))
+        return fail(NF4_ERR_ALIGN, "activations and adapters must be 16-byte aligned");
+    const int64_t N = w->rows, K = w->cols;
+    const Plan p = make_plan(M, N, K, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
+    uint16_t *L2t = ws_at<uint16_t>(workspace, p.off_L2t);
+    rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
+    if (rc) return rc;
+    NF4_CHECK_HIP(nf4k::launch_transpose(L2, r, N, L2t, s), "transpose L2");
+    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2t, r, M, Y, s), "fused dequant GEMM (fwd)");
+    return NF4_OK;
+}
+
+int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X, const uint16_t *L1,
+                     const uint16_t *L2, const uint16_t *T, float scale, int64_t M, int32_t r,
+                     uint16_t *dX, uint16_t *dL1, uint16_t *dL2, uint32_t flags, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    int rc = check_linear_args(w, M, r, scale);
+    if (rc) return rc;
+    if (flags & ~QLORA_DX_ACCUMULATE) return fail(NF4_ERR_ARG, "unknown flags");
+    if (!dY || !X || !L1 || !L2 || !dL1 || !dL2)
+        return fail(NF4_ERR_NULL, "dY, X, L1, L2, dL1 and dL2 must be non-NULL");
+    if (!aligned16(dY) || !aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(dL1) ||
+        !aligned16(dL2) || (T && !aligned16(T)) || (dX && !aligned16(dX)))
+        return fail(NF4_ERR_ALIGN, "activations, adapters and gradients must be 16-byte aligned");
+    const int64_t N = w->rows, K = w->cols;
+    const Plan p = make_plan(M, N, K, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float *P = ws_at<float>(workspace, p.off_P);
+    uint16_t *dT = ws_at<uint16_t>(workspace, p.off_dT);
+    const uint16_t *Tuse = T;
+    if (!Tuse) {
+        uint16_t *Tb = ws_at<uint16_t>(workspace, p.off_T);
+        rc = compute_T(X, L1, M, K, r, 1.0f, Tb, nullptr, p, workspace, s);
+        if (rc) return rc;
+        Tuse = Tb;
+    }
+    // dT = s dY L2^T  (L2 [r, N] is already the row-major transpose the product needs)
+    NF4_CHECK_HIP(nf4k::launch_skinny_nt(dY, L2, P, M, r, N, p.ksdT, s), "dT = dY L2^T");
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksdT, M * r, scale, dT, 0.0f, nullptr, s), "dT reduce");
+    // dL2 = s T^T dY
+    NF4_CHECK_HIP(nf4k::launch_skinny_tn(Tuse, dY, P, M, r, N, p.msL2, s), "dL2 = T^T dY");
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.msL2, (int64_t)r * N, scale, dL2, 0.0f, nullptr, s),
+                  "dL2 reduce");
+    // dL1 = X^T dT
+    NF4_CHECK_HIP(nf4k::launch_skinny_tn(X, dT, P, M, K, r, p.msL1, s), "dL1 = X^T dT");
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr, s),
+                  "dL1 reduce");
+    // dX = dY deq(W) + dT L1^T
+    if (dX)
+        NF4_CHECK_HIP(nf4k::launch_dqgemm_bwd(view_of(w), dY, dT, L1, r, M, dX,
+                                              (flags & QLORA_DX_ACCUMULATE) != 0, s),
+                      "fused dequant GEMM (bwd)");
+    return NF4_OK;
+}
+
+int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t n, void *stream) {
+    if (n < 0) return fail(NF4_ERR_SHAPE, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!g || !u || !h) return fail(NF4_ERR_NULL, "g, u and h must be non-NULL");
+    if (!aligned16(g) || !aligned16(u) || !aligned16(h)) return fail(NF4_ERR_ALIGN, "swiglu buffers must be 16-byte aligned");
+    NF4_CHECK_HIP(nf4k::launch_swiglu_fwd(g, u, h, n, reinterpret_cast<hipStream_t>(stream)), "swiglu fwd");
+    return NF4_OK;
+}
+
+int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,
+                     uint16_t *du, int64_t n, void *stream) {
+    if (n < 0) return fail(NF4_ERR_SHAPE, "n must be >= 0");
+    if (n == 0) return NF4_OK;
+    if (!dh || !g || !u || !dg || !du) return fail(NF4_ERR_NULL, "swiglu pointers must be non-NULL");
+    if (!aligned16(dh) || !aligned16(g) || !aligned16(u) || !aligned16(dg) || !aligned16(du))
+        return fail(NF4_ERR_ALIGN, "swiglu buffers must be 16-byte aligned");
+    NF4_CHECK_HIP(nf4k::launch_swiglu_bwd(dh, g, u, dg, du, n, reinterpret_cast<hipStream_t>(stream)),
+                  "swiglu bwd");
+    return NF4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launcher declarations shared by the kernel sources and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4k {
+
+struct WeightView {
+    const uint8_t *packed;
+    const uint8_t *c2;
+    const float *c1;
+    const float *mean;
+    int64_t rows, cols;
+    float cb[16];
+};
+
+hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], uint32_t zero_code,
+                           uint8_t *packed, float *absmax, hipStream_t stream);
+size_t double_quant_ws(int64_t nb);
+hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, float *scales,
+                               float *mean, void *ws, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const float *absmax_scale,
+                          const float *absmax_mean, int64_t numel, const float cb[16],
+                          uint16_t *out, hipStream_t stream);
+
+hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
+                             const uint16_t *L2t, int32_t r, int64_t M, uint16_t *Y,
+                             hipStream_t stream);
+hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
+                             const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
+                             bool accumulate, hipStream_t stream);
+
+int choose_split(int64_t tiles, int64_t red_steps);
+hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *Bt, float *P, int64_t M, int32_t R,
+                            int64_t Kred, int nsplit, hipStream_t stream);
+hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int64_t M, int64_t Pn,
+                            int64_t Qn, int nsplit, hipStream_t stream);
+hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
+                                  float s2, uint16_t *out2, hipStream_t stream);
+hipError_t launch_transpose(const uint16_t *in, int64_t R, int64_t C, uint16_t *out,
+                            hipStream_t stream);
+
+hipError_t launch_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t n,
+                             hipStream_t stream);
+hipError_t launch_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,
+                             uint16_t *du, int64_t n, hipStream_t stream);
+
+}  // namespace nf4k

@@ -1,0 +1,171 @@
+/*
+ * nf4.h -- C ABI of the MI355X (gfx950) NF4 quantized-codebook linear layer with a LoRA branch.
+ *
+ * Citations refer to the page "QLoRA: Efficient Finetuning of Quantized LLMs" study notes
+ * (gitcode.csdn.net/6a0046f754b52172bc72e356), by section and equation.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers point to memory on the current HIP device; host pointers are marked.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major and contiguous.
+ *   - The frozen weight W is stored [rows = N_out, cols = K_in] row-major (the pages write
+ *     W in R^{h x o}, i.e. its transpose), so the layer computes Y = X deq(W)^T + s (X L1) L2.
+ *   - Ownership: the caller owns every buffer, including the workspace (sized by the matching
+ *     *_workspace_size query).  The library never allocates, frees or synchronises device
+ *     memory and keeps no mutable global state; calls are stream-ordered on `stream`
+ *     (a hipStream_t; NULL means the default stream).
+ *   - Errors: every argument check runs before any HIP call and returns a negative status.
+ *     A failed launch returns NF4_ERR_HIP with the runtime's text in nf4_last_error().  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Device pointers that kernels read or write with 16-byte accesses must be 16-byte aligned
+ *     (NF4_ERR_ALIGN otherwise); allocator-returned pointers always are.
+ *   - Determinism: identical inputs give identical output bits, run to run (no floating-point
+ *     atomics; every reduction has a fixed order).
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    NF4_OK = 0,
+    NF4_ERR_NULL = -1,         /* a required pointer is NULL */
+    NF4_ERR_SHAPE = -2,        /* a size is negative, zero where not allowed, or inconsistent */
+    NF4_ERR_ALIGN = -3,        /* a device pointer is not 16-byte aligned */
+    NF4_ERR_UNSUPPORTED = -4,  /* a valid but unimplemented parameter (block != 64, ...) */
+    NF4_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the size query returned */
+    NF4_ERR_HIP = -6,          /* the HIP runtime reported an error; see nf4_last_error() */
+    NF4_ERR_ARG = -7           /* any other invalid argument (NaN scale, bad delta, flags) */
+};
+
+/* Text for a status code (static storage, never NULL). */
+const char *nf4_status_string(int status);
+/* Detail of the last error on the calling thread (thread-local storage, never NULL). */
+const char *nf4_last_error(void);
+
+/* Library version, "major.minor.patch" (static storage). */
+const char *nf4_version(void);
+
+/*
+ * NF4 codebook -- section 3.2, eq. (4) with the asymmetric exact-zero construction, and
+ * section 5.1.2 (Fig. 7 text: 8 values on one half, 7 on the other, plus 0).
+ * Each half of N(0,1) gets an evenly spaced probability grid from 0.5 to the tail probability
+ * `delta` (9 points on the positive half, 8 on the negative, both counting 0.5); the quantiles
+ * are divided by Phi^-1(delta), the negative half negated, merged with one 0, and rounded once
+ * to float32.
+ *   out_codebook: HOST float[16], written ascending; out[0] = -1, out[7] = 0, out[15] = +1.
+ *   delta: tail probability in (0.5, 1); pass 0 for the default 1 - (1/32 + 1/30)/2.
+ * Host-only and synchronous.  NF4_ERR_NULL, NF4_ERR_ARG on a bad delta.
+ */
+int nf4_build_codebook(float out_codebook[16], double delta);
+
+/*
+ * Level-1 block-wise quantization -- section 3.1 (flatten, n = numel/B blocks of B consecutive
+ * elements, one constant per block; eq. (1) in absmax form) and section 3.2 step 3 (absmax
+ * normalisation to [-1, 1]).
+ *   W:        device float32 [numel], the row-major flattening of the weight.
+ *   numel:    >= 0.  A short last block's absmax covers only its valid elements.
+ *   block:    must be 64 (section 3.5), else NF4_ERR_UNSUPPORTED.
+ *   codebook: HOST float[16], strictly ascending, containing 0.0f (typically from
+ *             nf4_build_codebook).  Copied into the kernel arguments.
+ *   packed:   device uint8 [ceil(numel/2)].  Element 2i in bits 0-3 of byte i, element 2i+1 in
+ *             bits 4-7; an odd tail is padded with the zero code.
+ *   absmax:   device float32 [ceil(numel/64)], the per-block max |x|.
+ * Per element: n = fp32(x / absmax) (IEEE division), code = nearest codeword, ties to the lower
+ * index; an all-zero block gets the zero code everywhere.  Inputs must be finite.
+ * W and packed must be 16-byte aligned.
+ */
+int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codebook[16],
+                 uint8_t *packed, float *absmax, void *stream);
+
+/*
+ * Level-2 (double) quantization of the block constants -- section 3.3: the constants are
+ * centred by their mean and quantized to an 8-bit float in blocks of 256.
+ *   absmax:       device float32 [nblocks] (from nf4_quantize).
+ *   dq_block:     must be 256, else NF4_ERR_UNSUPPORTED.
+ *   absmax_q:     device uint8 [nblocks], OCP FP8 E4M3 codes of (absmax - mean) / scale.
+ *   absmax_scale: device float32 [ceil(nblocks/256)], scale_j = fp32(max_j |absmax - mean| / 448),
+ *                 the multiplier that undoes the scaling (the inverse of eq. (1)'s constant).
+ *   absmax_mean:  device float32 [1], mean = fp32(S / nblocks) where S is the float64 sum taken in
+ *                 groups of 256 consecutive values, each summed in ascending order, level by level.
+ *   workspace:    device, >= nf4_double_quant_workspace_size(nblocks, dq_block) bytes.
+ * Codes: E4M3 round-to-nearest-even of clamp(fp32(y / scale_j), -448, 448), sign kept; all 0x00
+ * when scale_j == 0.
+ */
+size_t nf4_double_quant_workspace_size(int64_t nblocks, int32_t dq_block);
+int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                     float *absmax_scale, float *absmax_mean, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * One frozen NF4 weight in double-quantized form (section 3.5, eq. (5) and eq. (6)).
+ * All pointers are device pointers produced by nf4_quantize + nf4_double_quant.
+ */
+typedef struct nf4_weight {
+    const uint8_t *packed;        /* [rows*cols/2] 4-bit codes */
+    const uint8_t *absmax_q;      /* [rows*cols/block] E4M3 codes of the block constants */
+    const float *absmax_scale;    /* [ceil(nblocks/dq_block)] second-level multipliers */
+    const float *absmax_mean;     /* [1] the mean removed before the second level */
+    int64_t rows;                 /* N_out */
+    int64_t cols;                 /* K_in */
+    int32_t block;                /* 64 */
+    int32_t dq_block;             /* 256 */
+    float codebook[16];           /* the codebook used by nf4_quantize (host copy) */
+} nf4_weight;
+
+/*
+ * Double dequantization to BF16 -- section 3.5, eq. (6), with eq. (2) at each level:
+ *   a'_b = fmaf(E4M3(absmax_q[b]), absmax_scale[b / dq_block], mean)   (one rounding)
+ *   out[i] = bf16_RNE(fp32(codebook[code_i] * a'_{i / block}))
+ *   out_bf16: device uint16 [rows*cols], 16-byte aligned.  rows*cols must be even.
+ */
+int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream);
+
+/*
+ * QLoRA linear forward -- section 3.5 eq. (5) with the LoRA scalar s of eq. (3) (section 4):
+ *   T = X L1;  Y = X deq(W)^T + s T L2
+ *   X: [M, K] bf16; L1: [K, r] bf16; L2: [r, N] bf16; Y: [M, N] bf16 (N = w->rows, K = w->cols).
+ *   T_out: optional [M, r] bf16 (T = X L1, unscaled), kept for the backward pass; may be NULL.
+ *   scale: s (finite).  M >= 1, 1 <= r <= 128, K % 64 == 0.
+ *   The weight's block dequantization is fused into the matrix product; accumulation is fp32.
+ *   workspace: >= qlora_linear_workspace_size(M, N, K, r) bytes.
+ */
+size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
+int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
+                     const uint16_t *L2, float scale, int64_t M, int32_t r, uint16_t *Y,
+                     uint16_t *T_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * QLoRA linear backward -- section 3.5: only the adapters get gradients (dE/dL1, dE/dL2) and
+ * the gradient flows to X through the BF16-dequantized frozen weight; W is never written.
+ *   dT  = s dY L2^T          dL2 = s T^T dY  (T = X L1)
+ *   dL1 = X^T dT             dX  = dY deq(W) + dT L1^T
+ *   dY: [M, N] bf16; X: [M, K]; L1: [K, r]; L2: [r, N]; T: [M, r] from the forward or NULL
+ *   (then recomputed).  dX: [M, K] bf16 or NULL (not computed); dL1: [K, r]; dL2: [r, N]; all
+ *   bf16, fp32 accumulation.  flags: QLORA_DX_ACCUMULATE adds into dX instead of overwriting.
+ *   dL1 and dL2 are overwritten.  Same shape limits and workspace query as the forward.
+ */
+#define QLORA_DX_ACCUMULATE 1u
+int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
+                     const uint16_t *L1, const uint16_t *L2, const uint16_t *T, float scale,
+                     int64_t M, int32_t r, uint16_t *dX, uint16_t *dL1, uint16_t *dL2,
+                     uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * SwiGLU glue for gated MLPs built from three such linears (not a step of the method):
+ *   h = silu(g) * u, silu(g) = g * sigmoid(g);  dg = dh * u * sigmoid(g) * (1 + g (1 - sigmoid(g))),
+ *   du = dh * silu(g).  All bf16 [n], fp32 arithmetic, 16-byte aligned, n >= 0.
+ */
+int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t n, void *stream);
+int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,
+                     uint16_t *du, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H */

@@ -1,0 +1,154 @@
+"""C-ABI contract on the host: the library loads, exports what include/nf4.h declares, builds the
+same codebook as the oracle, and rejects bad arguments with the documented status before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+nf4 = pytest.importorskip("bit_nf4_quantized_codebook_amd")
+lib = nf4.lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nf4.h")
+
+OK, ENULL, ESHAPE, EALIGN, EUNSUP, EWS, EHIP, EARG = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    assert set(declared) == set(nf4.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, EWS, EHIP, EARG):
+        assert nf4.status_string(s)
+    assert nf4.status_string(12345) == "unknown status"
+    assert re.match(r"\d+\.\d+\.\d+", nf4.version())
+
+
+@pytest.mark.parametrize("delta", [0.0, oracle.DELTA_DEFAULT, 16 / 17, 1 - 1 / 34, 0.99])
+def test_codebook_bit_exact_with_oracle(delta):
+    got = nf4.nf4_build_codebook(delta)
+    ref = oracle.codebook(oracle.DELTA_DEFAULT if delta == 0.0 else delta)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_codebook_errors():
+    out = np.zeros(16, np.float32)
+    p = ctypes.c_void_p(out.ctypes.data)
+    assert lib.nf4_build_codebook(None, 0.0) == ENULL
+    assert lib.nf4_build_codebook(p, 0.3) == EARG
+    assert lib.nf4_build_codebook(p, 1.0) == EARG
+    assert b"delta" in lib.nf4_last_error()
+
+
+def _cb():
+    return nf4.nf4_build_codebook()
+
+
+def test_quantize_argument_errors():
+    cb = _cb()
+    cbp = ctypes.c_void_p(cb.ctypes.data)
+    fake = ctypes.c_void_p(0x100000)           # aligned, never dereferenced on these paths
+    mis = ctypes.c_void_p(0x100004)
+    assert lib.nf4_quantize(fake, 64, 64, None, fake, fake, None) == ENULL
+    assert lib.nf4_quantize(fake, -1, 64, cbp, fake, fake, None) == ESHAPE
+    assert lib.nf4_quantize(fake, 64, 32, cbp, fake, fake, None) == EUNSUP
+    assert lib.nf4_quantize(None, 64, 64, cbp, fake, fake, None) == ENULL
+    assert lib.nf4_quantize(mis, 64, 64, cbp, fake, fake, None) == EALIGN
+    assert lib.nf4_quantize(None, 0, 64, cbp, None, None, None) == OK       # empty input
+    bad = cb.copy()
+    bad[3], bad[4] = bad[4], bad[3]
+    assert lib.nf4_quantize(fake, 64, 64, ctypes.c_void_p(bad.ctypes.data), fake, fake, None) == EARG
+    nozero = cb.copy()
+    nozero[7] = 1e-3
+    assert lib.nf4_quantize(fake, 64, 64, ctypes.c_void_p(nozero.ctypes.data), fake, fake, None) == EARG
+
+
+def test_double_quant_argument_errors():
+    fake = ctypes.c_void_p(0x100000)
+    ws = lib.nf4_double_quant_workspace_size(1000, 256)
+    assert ws > 0
+    assert lib.nf4_double_quant(fake, 0, 256, fake, fake, fake, fake, ws, None) == ESHAPE
+    assert lib.nf4_double_quant(fake, 1000, 128, fake, fake, fake, fake, ws, None) == EUNSUP
+    assert lib.nf4_double_quant(fake, 1000, 256, None, fake, fake, fake, ws, None) == ENULL
+    assert lib.nf4_double_quant(fake, 1000, 256, fake, fake, fake, fake, ws - 1, None) == EWS
+    # workspace grows with the number of summation levels
+    assert lib.nf4_double_quant_workspace_size(3670016, 256) >= 8 * (14336 + 56 + 1)
+
+
+def _desc(rows=256, cols=256, block=64, dq_block=256, ptr=0x100000, cb=None):
+    d = nf4._WeightDesc()
+    d.packed = d.absmax_q = d.absmax_scale = d.absmax_mean = ptr
+    d.rows, d.cols, d.block, d.dq_block = rows, cols, block, dq_block
+    cb = _cb() if cb is None else cb
+    for j in range(16):
+        d.codebook[j] = float(cb[j])
+    return d
+
+
+def test_linear_argument_errors():
+    fake = ctypes.c_void_p(0x100000)
+    M, r = 8, 8
+    wsb = lib.qlora_linear_workspace_size(M, 256, 256, r)
+    assert wsb > 0
+    fwd = lambda d, **kw: lib.qlora_linear_fwd(ctypes.byref(d), kw.get("X", fake), fake, fake,
+                                                kw.get("scale", 2.0), kw.get("M", M), kw.get("r", r),
+                                                fake, None, kw.get("ws", fake), kw.get("wsb", wsb), None)
+    assert lib.qlora_linear_fwd(None, fake, fake, fake, 2.0, M, r, fake, None, fake, wsb, None) == ENULL
+    assert fwd(_desc(), M=0) == ESHAPE
+    assert fwd(_desc(), r=0) == EUNSUP
+    assert fwd(_desc(), r=129) == EUNSUP
+    assert fwd(_desc(), r=12) == EUNSUP
+    assert fwd(_desc(block=128)) == EUNSUP
+    assert fwd(_desc(dq_block=64)) == EUNSUP
+    assert fwd(_desc(cols=200)) == EUNSUP
+    assert fwd(_desc(rows=0)) == ESHAPE
+    assert fwd(_desc(), scale=float("nan")) == EARG
+    assert fwd(_desc(), X=None) == ENULL
+    assert fwd(_desc(), X=ctypes.c_void_p(0x100002)) == EALIGN
+    assert fwd(_desc(), wsb=wsb - 1) == EWS
+    assert fwd(_desc(), ws=None) == EWS
+    assert fwd(_desc(ptr=0x100008)) == EALIGN
+    # backward: unknown flags, NULL gradient outputs
+    d = _desc()
+    assert lib.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, fake, None, 2.0, M, r, fake, fake,
+                                fake, 2, fake, wsb, None) == EARG
+    assert lib.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, fake, None, 2.0, M, r, fake, None,
+                                fake, 0, fake, wsb, None) == ENULL
+    assert lib.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, fake, None, 2.0, M, r, fake, fake,
+                                fake, 0, fake, wsb - 1, None) == EWS
+
+
+def test_dequant_and_swiglu_argument_errors():
+    fake = ctypes.c_void_p(0x100000)
+    d = _desc()
+    assert lib.nf4_dequant(ctypes.byref(d), None, None) == ENULL
+    assert lib.nf4_dequant(ctypes.byref(d), ctypes.c_void_p(0x100002), None) == EALIGN
+    assert lib.nf4_dequant(None, fake, None) == ENULL
+    assert lib.qlora_swiglu_fwd(fake, fake, fake, -1, None) == ESHAPE
+    assert lib.qlora_swiglu_fwd(fake, fake, fake, 0, None) == OK
+    assert lib.qlora_swiglu_fwd(None, fake, fake, 8, None) == ENULL
+    assert lib.qlora_swiglu_bwd(fake, fake, fake, fake, ctypes.c_void_p(0x100001), 8, None) == EALIGN
+
+
+def test_workspace_sizes_cover_all_configs():
+    for M, N, K, r in [(8, 256, 256, 8), (4096, 4096, 4096, 64), (4096, 11008, 4096, 64),
+                       (4096, 4096, 11008, 64), (2048, 22016, 8192, 64), (1, 28672, 8192, 64)]:
+        ws = lib.qlora_linear_workspace_size(M, N, K, r)
+        # at least T, sT, dT and the transposed adapters
+        assert ws >= 2 * (3 * M * r + r * K + N * r)
+        assert ws < 1 << 31

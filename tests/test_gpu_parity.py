@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on identical seeded inputs.
+
+Quantization, double quantization and dequantization must match bit for bit; the linear layer's
+outputs and gradients must satisfy rel-Frobenius <= 5e-3 and max-abs <= 2e-2 * max|ref| against
+the float64 oracle.  Full-size workloads are checked on sampled rows that the oracle computes
+directly, plus the full (small) adapter gradients.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_nf4_quantized_codebook_amd as nf4  # noqa: E402
+
+DEV = torch.device("cuda:0")
+CB = nf4.nf4_build_codebook()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def d16(bits: np.ndarray):
+    """bf16 bit patterns (uint16) -> device bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def h16(t) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32(t) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def check_tol(name, got, ref):
+    rf, ma = oracle.rel_fro(got, ref), oracle.max_abs_ratio(got, ref)
+    _say(f"  {name}: rel_fro {rf:.3e}  max_abs/max|ref| {ma:.3e}")
+    assert rf <= oracle.REL_FRO_TOL, (name, rf)
+    assert ma <= oracle.MAX_ABS_TOL, (name, ma)
+
+
+# ------------------------------------------------------------------------------------------
+# Quantize / double quant / dequant: bit-exact
+# ------------------------------------------------------------------------------------------
+
+def _special_tensors():
+    out = {}
+    W = synth.normal_f32(101, (64, 256), 0.02)
+    W[3, :64] = 0.0                                # all-zero block
+    W[5, 64:128] = 0.0371                          # constant block
+    W[7, 0] = 1e4                                  # single huge outlier
+    W[9, 64:128] = synth.normal_f32(102, (64,), 1e-41)   # subnormal block
+    W[11, 128:192] = -0.0
+    out["specials"] = W.reshape(-1)
+    e = np.concatenate([np.tile(CB, 4) * np.float32(2.0 ** k) for k in (-30, -3, 0, 9)])
+    out["codebook_round_trip"] = e.astype(np.float32)
+    mids = ((CB[:-1].astype(np.float64) + CB[1:]) / 2).astype(np.float32)
+    adv = np.concatenate([mids, np.nextafter(mids, np.float32(2)), np.nextafter(mids, np.float32(-2))])
+    blk = np.resize(np.concatenate([[np.float32(1.0)], adv]), 64).astype(np.float32)
+    out["midpoints"] = np.concatenate([blk * np.float32(s) for s in (1.0, 0.37, 3e-5, 1700.0)])
+    out["ragged_odd"] = synth.normal_f32(103, (64 * 5 + 37,), 1.0)
+    out["single"] = np.array([0.5], dtype=np.float32)
+    return out
+
+
+def _quant_case(W):
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    packed, absmax = nf4.nf4_quantize(Wd, CB)
+    torch.cuda.synchronize()
+    p_ref, a_ref = oracle.quantize(W, CB)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), a_ref.view(np.uint32))
+    return absmax, a_ref
+
+
+@pytest.mark.parametrize("name", list(_special_tensors().keys()))
+def test_quantize_special_tensors_bit_exact(name):
+    _say(f"quantize special: {name}")
+    W = _special_tensors()[name]
+    absmax, a_ref = _quant_case(W)
+    q, sc, mean = nf4.nf4_double_quant(absmax)
+    c_ref, s_ref, m_ref = oracle.double_quant(a_ref)
+    assert np.array_equal(q.cpu().numpy(), c_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert mean.cpu().numpy().view(np.uint32)[0] == np.float32(m_ref).view(np.uint32)
+
+
+@pytest.mark.parametrize("wl_name", ["tiny", "llama7b_attn"])
+def test_quantize_dq_dequant_bit_exact(wl_name):
+    wl = synth.WORKLOADS[wl_name]
+    lin = wl.linears[0]
+    _say(f"quantize+dq+dequant: {wl_name} {lin.N}x{lin.K}")
+    W = synth.weight_f32(wl, lin)
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+    q = oracle.quantize_dq(W, CB)
+    assert np.array_equal(w.packed.cpu().numpy(), q["packed"])
+    assert np.array_equal(w.absmax_q.cpu().numpy(), q["codes"])
+    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), q["scales"].view(np.uint32))
+    assert w.absmax_mean.cpu().numpy()[0] == q["mean"]
+    assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(-1), oracle.dequant_weight(q, CB).reshape(-1))
+
+
+def test_gemv_weight_dequant_bit_exact_full_size():
+    """28672 x 8192 (three summation levels in the double-quant mean)."""
+    wl = synth.WORKLOADS["gemv"]
+    lin = wl.linears[0]
+    _say(f"quantize+dq+dequant: gemv {lin.N}x{lin.K}")
+    W = synth.weight_f32(wl, lin)
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+    q = oracle.quantize_dq(W, CB)
+    assert np.array_equal(w.packed.cpu().numpy(), q["packed"])
+    assert np.array_equal(w.absmax_q.cpu().numpy(), q["codes"])
+    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), q["scales"].view(np.uint32))
+    assert w.absmax_mean.cpu().numpy()[0] == q["mean"]
+    got = h16(nf4.nf4_dequant(w)).reshape(-1)
+    assert np.array_equal(got, oracle.dequant_weight(q, CB).reshape(-1))
+
+
+@pytest.mark.parametrize("nb", [1, 255, 257, 1000, 65537, 300000])
+def test_double_quant_ragged_bit_exact(nb):
+    _say(f"double quant nb={nb}")
+    a = np.abs(synth.normal_f32(110 + nb % 97, (nb,), 0.05)).astype(np.float32)
+    if nb > 600:
+        a[256:512] = 0.0371                       # a constant 256-block
+    q, sc, mean = nf4.nf4_double_quant(torch.from_numpy(a).to(DEV))
+    c_ref, s_ref, m_ref = oracle.double_quant(a)
+    assert np.array_equal(q.cpu().numpy(), c_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert mean.cpu().numpy()[0] == m_ref
+
+
+# ------------------------------------------------------------------------------------------
+# Linear layer: tolerance against the float64 oracle
+# ------------------------------------------------------------------------------------------
+
+def _make_layer(M, N, K, r, seed, w_std=0.02, zero_w=False, zero_l2=False):
+    W = np.zeros((N, K), np.float32) if zero_w else synth.normal_f32(seed, (N, K), w_std)
+    X = synth.to_bf16_bits(synth.normal_f32(seed + 1, (M, K), 1.0))
+    L1 = synth.to_bf16_bits(synth.normal_f32(seed + 2, (K, r), 1.0 / r))
+    L2 = np.zeros((r, N), np.uint16) if zero_l2 else synth.to_bf16_bits(synth.normal_f32(seed + 3, (r, N), 0.01))
+    dY = synth.to_bf16_bits(synth.normal_f32(seed + 4, (M, N), 1.0))
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+    Wd = oracle.dequant_weight(oracle.quantize_dq(W, CB), CB)
+    assert np.array_equal(h16(nf4.nf4_dequant(w)), Wd)
+    return w, Wd, X, L1, L2, dY
+
+
+SHAPES = [
+    # M, N, K, r
+    (8, 256, 256, 8),          # the tiny workload's shape
+    (300, 520, 384, 16),       # several tiles, ragged M and N
+    (17, 64, 128, 64),         # M just above the small-M range, single N tile
+    (1, 512, 256, 64),
+    (4, 256, 512, 32),
+    (16, 1024, 1024, 128),
+    (513, 264, 640, 24),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r", SHAPES)
+def test_linear_fwd_bwd_parity(M, N, K, r):
+    _say(f"linear fwd/bwd M={M} N={N} K={K} r={r}")
+    s = 16.0 / r
+    w, Wd, X, L1, L2, dY = _make_layer(M, N, K, r, seed=200 + M + N)
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    packed_before = w.packed.clone()
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    Yr, Tr = oracle.forward(X, Wd, L1, L2, s)
+    g = oracle.backward(dY, X, Wd, L1, L2, s)
+    check_tol("Y", f32(Y), Yr)
+    check_tol("T", f32(T), Tr)
+    check_tol("dX", f32(dX), g["dX"])
+    check_tol("dL1", f32(dL1), g["dL1"])
+    check_tol("dL2", f32(dL2), g["dL2"])
+    assert torch.equal(w.packed, packed_before)          # the frozen weight is never written
+    # T recomputed inside the backward gives the same bits
+    dX2, dL12, dL22 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, None, s)
+    assert torch.equal(dX2, dX) and torch.equal(dL12, dL1) and torch.equal(dL22, dL2)
+    # no dX requested
+    n, dL13, _ = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s, need_dX=False)
+    assert n is None and torch.equal(dL13, dL1)
+    # accumulate into an existing dX
+    base = d16(synth.to_bf16_bits(synth.normal_f32(7, (M, K), 1.0)))
+    acc = base.clone()
+    nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s, dX=acc, accumulate=True)
+    torch.cuda.synchronize()
+    check_tol("dX+=", f32(acc), g["dX"] + f32(base))
+
+
+@pytest.mark.parametrize("M,N,K,r", [(64, 256, 256, 8), (40, 520, 384, 16)])
+def test_lora_branch_alone(M, N, K, r):
+    """W = 0 exactly: Y and dX are the pure LoRA terms (the branch is checked on its own)."""
+    _say(f"lora branch alone M={M} N={N} K={K} r={r}")
+    s = 2.0
+    w, Wd, X, L1, L2, dY = _make_layer(M, N, K, r, seed=300 + M, zero_w=True)
+    assert np.all(oracle.bf16_to_f32(Wd) == 0)
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    Yr, _ = oracle.forward(X, Wd, L1, L2, s)
+    g = oracle.backward(dY, X, Wd, L1, L2, s)
+    check_tol("Y(lora)", f32(Y), Yr)
+    check_tol("dX(lora)", f32(dX), g["dX"])
+
+
+def test_base_branch_alone():
+    """L2 = 0: Y is the dequantized product alone."""
+    M, N, K, r = 96, 512, 512, 16
+    _say("base branch alone")
+    w, Wd, X, L1, L2, dY = _make_layer(M, N, K, r, seed=400, zero_l2=True)
+    Y, _ = nf4.qlora_linear_fwd(w, d16(X), d16(L1), d16(L2), 1.0)
+    torch.cuda.synchronize()
+    ref = oracle.bf16_to_f32(X).astype(np.float64) @ oracle.bf16_to_f32(Wd).astype(np.float64).T
+    check_tol("Y(base)", f32(Y), ref)
+
+
+def test_full_size_attention_projection_sampled():
+    """LLaMA-7B attention projection at full size, the bench's launch configuration."""
+    wl = synth.WORKLOADS["llama7b_attn"]
+    lin = wl.linears[0]
+    M, N, K, r, s = wl.M, lin.N, lin.K, wl.r, wl.scale
+    _say(f"full size {wl.name}: M={M} N={N} K={K} r={r}")
+    W = synth.weight_f32(wl, lin)
+    l1, l2 = synth.lora_f32(wl, lin)
+    L1, L2 = synth.to_bf16_bits(l1), synth.to_bf16_bits(l2)
+    X = synth.to_bf16_bits(synth.x_f32(wl))
+    dY = synth.to_bf16_bits(synth.dy_f32(wl, M, N))
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+    Wd = oracle.dequant_weight(oracle.quantize_dq(W, CB), CB)
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(M, 48, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, M - 1]]))
+    Xf = oracle.bf16_to_f32(X).astype(np.float64)
+    Wf = oracle.bf16_to_f32(Wd).astype(np.float64)
+    L1f = oracle.bf16_to_f32(L1).astype(np.float64)
+    L2f = oracle.bf16_to_f32(L2).astype(np.float64)
+    dYf = oracle.bf16_to_f32(dY).astype(np.float64)
+    Yr, _ = oracle.forward(X[rows], Wd, L1, L2, s)
+    check_tol("Y[rows]", f32(Y)[rows], Yr)
+    Tf = Xf @ L1f
+    dT = s * (dYf @ L2f.T)
+    dXr = dYf[rows] @ Wf + dT[rows] @ L1f.T
+    check_tol("dX[rows]", f32(dX)[rows], dXr)
+    check_tol("T", f32(T), Tf)
+    check_tol("dL2", f32(dL2), s * (Tf.T @ dYf))
+    check_tol("dL1", f32(dL1), Xf.T @ dT)
+    # deterministic: a second run gives the same bits
+    Y2, _ = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX2, dL12, dL22 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    assert torch.equal(Y, Y2) and torch.equal(dX, dX2) and torch.equal(dL1, dL12) and torch.equal(dL2, dL22)
+
+
+# ------------------------------------------------------------------------------------------
+# SwiGLU glue
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [8, 1000, 4096 * 3 + 5])
+def test_swiglu_parity(n):
+    g = synth.to_bf16_bits(synth.normal_f32(500, (n,), 2.0))
+    u = synth.to_bf16_bits(synth.normal_f32(501, (n,), 1.0))
+    dh = synth.to_bf16_bits(synth.normal_f32(502, (n,), 1.0))
+    h = nf4.qlora_swiglu_fwd(d16(g), d16(u))
+    dg, du = nf4.qlora_swiglu_bwd(d16(dh), d16(g), d16(u))
+    torch.cuda.synchronize()
+    check_tol("h", f32(h), oracle.swiglu_fwd(g, u))
+    rg, ru = oracle.swiglu_bwd(dh, g, u)
+    check_tol("dg", f32(dg), rg)
+    check_tol("du", f32(du), ru)
