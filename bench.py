@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the NF4 QLoRA linear layer on one MI355X.
+
+One step = one forward + one backward pass (dX, dL1, dL2) of the frozen NF4 linear layer with its
+LoRA branch over one batch, through the C ABI (qlora_linear_fwd + qlora_linear_bwd), inputs
+already resident in HBM.  The default workload is the LLaMA-7B attention projection
+(W 4096x4096 NF4, block 64, double quantization block 256; 8 x 512 = 4096 tokens; r = 64,
+alpha = 16).  The headline value is algorithmic TFLOP/s (2MNK per dense product, LoRA at rank r).
+
+Also reported on the same JSON line:
+  roofline     the dominant kernel (the fused dequant-GEMM), timed live with HIP events recorded
+               by the library around each of its launches in the timed region
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+  gemv         decode-size forward (W 28672x8192, M = 1, 4, 16) in GB/s, weights rotated over
+               three replicas so the 256 MB last-level cache cannot hold them
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
+
+
+def linear_flops(M, N, K, r):
+    """Algorithmic flops of one forward + backward of the layer (2 per multiply-add)."""
+    fwd = 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+    bwd = 2 * M * N * K + 2 * M * N * r + 2 * r * M * N + 2 * K * M * r + 2 * M * r * K
+    return fwd, bwd
+
+
+def gemm_launch_flops(kind, M, N, K, r):
+    """Algorithmic flops of one fused dequant-GEMM launch (main product + LoRA extension)."""
+    return 2 * M * N * K + (2 * M * r * N if kind == 0 else 2 * M * r * K)
+
+
+def gemv_bytes(M, N, K, r):
+    """Algorithmic HBM bytes of one decode-size forward."""
+    nb = N * K // 64
+    return (N * K // 2 + nb + (nb + 255) // 256 * 4 + 4 + K * r * 2 + r * N * 2 + M * K * 2 + M * N * 2)
+
+
+def make_linear(torch, nf4, synth, wl, lin, M, dev, replicas=1):
+    import numpy as np
+    cb = nf4.nf4_build_codebook()
+    W = torch.from_numpy(synth.weight_f32(wl, lin)).to(dev)
+    w0 = nf4.NF4Weight.from_float(W, cb)
+    del W
+    ws = [w0]
+    for _ in range(replicas - 1):
+        ws.append(nf4.NF4Weight(w0.packed.clone(), w0.absmax_q.clone(), w0.absmax_scale.clone(),
+                                w0.absmax_mean.clone(), w0.rows, w0.cols, cb))
+    l1, l2 = synth.lora_f32(wl, lin)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    st = {
+        "w": ws, "L1": bf(l1), "L2": bf(l2),
+        "X": bf(synth.x_f32(wl, M=M, K=lin.K)),
+        "dY": bf(synth.dy_f32(wl, M, lin.N)),
+        "Y": torch.empty((M, lin.N), dtype=torch.bfloat16, device=dev),
+        "T": torch.empty((M, wl.r), dtype=torch.bfloat16, device=dev),
+        "dX": torch.empty((M, lin.K), dtype=torch.bfloat16, device=dev),
+        "dL1": torch.empty((lin.K, wl.r), dtype=torch.bfloat16, device=dev),
+        "dL2": torch.empty((wl.r, lin.N), dtype=torch.bfloat16, device=dev),
+        "ws": torch.empty(nf4.qlora_linear_workspace_size(M, lin.N, lin.K, wl.r), dtype=torch.uint8,
+                          device=dev),
+        "s": wl.scale, "M": M, "N": lin.N, "K": lin.K, "r": wl.r,
+    }
+    return st
+
+
+def step_linear(nf4, st, i=0):
+    w = st["w"][i % len(st["w"])]
+    nf4.qlora_linear_fwd(w, st["X"], st["L1"], st["L2"], st["s"], Y=st["Y"], T=st["T"], workspace=st["ws"])
+    nf4.qlora_linear_bwd(w, st["dY"], st["X"], st["L1"], st["L2"], st["T"], st["s"], dX=st["dX"],
+                         dL1=st["dL1"], dL2=st["dL2"], workspace=st["ws"])
+
+
+def cpu_baseline(synth, wl, lin, budget_s=10.0, sample_tokens=512):
+    """The oracle as it stands, on a bounded token sample of the same workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    W = synth.weight_f32(wl, lin)
+    l1, l2 = synth.lora_f32(wl, lin)
+    L1, L2 = synth.to_bf16_bits(l1), synth.to_bf16_bits(l2)
+    X = synth.to_bf16_bits(synth.x_f32(wl, M=sample_tokens, K=lin.K))
+    dY = synth.to_bf16_bits(synth.dy_f32(wl, sample_tokens, lin.N))
+    q = oracle.quantize_dq(W)
+    fwd, bwd = linear_flops(sample_tokens, lin.N, lin.K, wl.r)
+    reps, t_total = 0, 0.0
+    while reps < 1 or (t_total < budget_s and reps < 20):
+        t0 = time.perf_counter()
+        Wd = oracle.dequant_weight(q)
+        oracle.forward(X, Wd, L1, L2, wl.scale)
+        oracle.backward(dY, X, Wd, L1, L2, wl.scale)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": round((fwd + bwd) * reps / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{reps} oracle fwd+bwd passes over {sample_tokens} of the {wl.M} tokens "
+                   f"({lin.N}x{lin.K} weight double-dequantized by the oracle each pass, float64 "
+                   f"numpy products), {t_total:.1f} s"),
+    }
+
+
+def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
+    """Decode-size forward, weights rotated over 3 replicas (378 MB > 256 MB last-level cache)."""
+    wl = synth.WORKLOADS["gemv"]
+    lin = wl.linears[0]
+    out = {}
+    for M in (1, 4, 16):
+        st = make_linear(torch, nf4, synth, wl, lin, M, dev, replicas=3)
+        for i in range(warmup):
+            w = st["w"][i % 3]
+            nf4.qlora_linear_fwd(w, st["X"], st["L1"], st["L2"], st["s"], Y=st["Y"], T=st["T"],
+                                 workspace=st["ws"])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            w = st["w"][i % 3]
+            nf4.qlora_linear_fwd(w, st["X"], st["L1"], st["L2"], st["s"], Y=st["Y"], T=st["T"],
+                                 workspace=st["ws"])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        b = gemv_bytes(M, lin.N, lin.K, wl.r)
+        out[f"M{M}"] = {"us_per_call": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                        "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": b}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_attn")
+    ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
+              "data-parallel with one all-reduce of the LoRA gradients); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_codebook_amd as nf4
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    if wl.swiglu:
+        raise SystemExit("MLP workloads are measured by their own script path; use llama7b_attn")
+    lin = wl.linears[0]
+    M, N, K, r = wl.M, lin.N, lin.K, wl.r
+    print(f"[bench] workload {wl.name}: M={M} N={N} K={K} r={r}", file=sys.stderr, flush=True)
+    st = make_linear(torch, nf4, synth, wl, lin, M, dev)
+    for i in range(args.warmup):
+        step_linear(nf4, st, i)
+    torch.cuda.synchronize()
+
+    timer = nf4.GemmTimer(2 * args.steps + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    timer.arm()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step_linear(nf4, st, i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cnt = timer.disarm()
+    durs = timer.durations_ms(cnt)
+    timer.close()
+    ms = e0.elapsed_time(e1) / args.steps
+    fwd, bwd = linear_flops(M, N, K, r)
+    value = (fwd + bwd) / (ms * 1e-3) / 1e12
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
+          f"{value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    per_kind = {}
+    for kind, d in durs:
+        per_kind.setdefault(kind, []).append(d)
+    means = {k: sum(v) / len(v) for k, v in per_kind.items()}
+    dom = max(means, key=lambda k: means[k])
+    flops_launch = gemm_launch_flops(dom, M, N, K, r)
+    achieved = flops_launch / (means[dom] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+        "kernel": "dqgemm_kernel<" + ("true" if dom == 1 else "false") + "> (" +
+                  ("backward dX" if dom == 1 else "forward Y") + ")",
+        "avg_launch_us": round(means[dom] * 1e3, 2),
+        "flops_per_launch": flops_launch,
+        "launches_timed": len(per_kind[dom]),
+        "other_gemm_avg_us": {("bwd" if k == 1 else "fwd"): round(v * 1e3, 2) for k, v in means.items()},
+    }
+    print(f"[bench] dominant kernel: {roofline['kernel']} {roofline['avg_launch_us']} us, "
+          f"{roofline['achieved']} TFLOP/s ({roofline['frac'] * 100:.1f}% of peak)", file=sys.stderr,
+          flush=True)
+
+    gemv = None
+    if not args.no_gemv:
+        del st
+        torch.cuda.empty_cache()
+        gemv = bench_gemv(torch, nf4, synth, dev)
+        print(f"[bench] gemv {gemv}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(synth, wl, lin)
+        print(f"[bench] cpu baseline {cpu}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.notes}; W {N}x{K} NF4 (block 64, double-quant block 256), "
+                               f"{M} tokens, LoRA r={r} alpha={wl.alpha:g}, forward + backward (dX, dL1, dL2)",
+                   "M": M, "N": N, "K": K, "r": r, "flops_per_step": fwd + bwd},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if gemv is not None:
+        line["gemv"] = {"workload": "W 28672x8192 NF4 forward with LoRA r=64, weights rotated over 3 replicas",
+                        **gemv}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

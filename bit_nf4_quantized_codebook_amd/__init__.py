@@ -30,7 +30,7 @@ EXPORTS = (
     "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook", "nf4_quantize",
     "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_swiglu_fwd", "qlora_swiglu_bwd",
+    "qlora_swiglu_fwd", "qlora_swiglu_bwd", "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
 
 
@@ -77,6 +77,8 @@ def _load():
                                  ctypes.c_uint32, P, sz, P]),
         "qlora_swiglu_fwd": (i, [P, P, P, i64, P]),
         "qlora_swiglu_bwd": (i, [P, P, P, P, P, i64, P]),
+        "nf4_set_gemm_timing_events": (i, [P, P, P, i32]),
+        "nf4_gemm_timing_count": (i32, []),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -233,7 +235,7 @@ def qlora_linear_workspace_size(M: int, N: int, K: int, r: int) -> int:
 
 
 def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True, Y=None,
-                     workspace=None):
+                     workspace=None, T=None):
     """Y = X deq(W)^T + scale (X L1) L2.  Returns (Y, T) with T = X L1 (or None)."""
     torch = _torch()
     for t, n in ((X, "X"), (L1, "L1"), (L2, "L2")):
@@ -243,7 +245,8 @@ def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True,
         raise ValueError("shape mismatch")
     if Y is None:
         Y = torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device)
-    T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if keep_T else None
+    if T is None and keep_T:
+        T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
     wsb = qlora_linear_workspace_size(M, w.rows, w.cols, r)
     ws = _workspace(wsb, X.device, workspace)
     d = w.descriptor()
@@ -253,7 +256,7 @@ def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True,
 
 
 def qlora_linear_bwd(w: NF4Weight, dY, X, L1, L2, T, scale: float, need_dX: bool = True,
-                     dX=None, accumulate: bool = False, workspace=None):
+                     dX=None, accumulate: bool = False, workspace=None, dL1=None, dL2=None):
     """Returns (dX or None, dL1, dL2) for the layer above; W is not touched."""
     torch = _torch()
     for t, n in ((dY, "dY"), (X, "X"), (L1, "L1"), (L2, "L2")):
@@ -267,8 +270,10 @@ def qlora_linear_bwd(w: NF4Weight, dY, X, L1, L2, T, scale: float, need_dX: bool
         dX = torch.empty((M, w.cols), dtype=torch.bfloat16, device=X.device)
     if not need_dX:
         dX = None
-    dL1 = torch.empty((w.cols, r), dtype=torch.bfloat16, device=X.device)
-    dL2 = torch.empty((r, w.rows), dtype=torch.bfloat16, device=X.device)
+    if dL1 is None:
+        dL1 = torch.empty((w.cols, r), dtype=torch.bfloat16, device=X.device)
+    if dL2 is None:
+        dL2 = torch.empty((r, w.rows), dtype=torch.bfloat16, device=X.device)
     wsb = qlora_linear_workspace_size(M, w.rows, w.cols, r)
     ws = _workspace(wsb, X.device, workspace)
     d = w.descriptor()
@@ -298,3 +303,52 @@ def qlora_swiglu_bwd(dh, g, u):
     _check(lib.qlora_swiglu_bwd(_ptr(dh), _ptr(g), _ptr(u), _ptr(dg), _ptr(du), g.numel(),
                                 _stream(g.device)), "qlora_swiglu_bwd")
     return dg, du
+
+
+class GemmTimer:
+    """HIP events recorded by the library around each fused dequant-GEMM launch on this thread."""
+
+    def __init__(self, capacity: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = capacity
+        self.begin = (ctypes.c_void_p * capacity)()
+        self.end = (ctypes.c_void_p * capacity)()
+        self.kinds = (ctypes.c_int32 * capacity)()
+        for i in range(capacity):
+            for arr in (self.begin, self.end):
+                ev = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev.value
+
+    def arm(self):
+        _check(lib.nf4_set_gemm_timing_events(ctypes.cast(self.begin, ctypes.c_void_p),
+                                              ctypes.cast(self.end, ctypes.c_void_p),
+                                              ctypes.cast(self.kinds, ctypes.c_void_p), self.n),
+               "nf4_set_gemm_timing_events")
+
+    def disarm(self) -> int:
+        cnt = int(lib.nf4_gemm_timing_count())
+        _check(lib.nf4_set_gemm_timing_events(None, None, None, 0), "nf4_set_gemm_timing_events")
+        return cnt
+
+    def durations_ms(self, count: int):
+        """[(kind, ms)] of the recorded launches (call after a device synchronisation)."""
+        out = []
+        for i in range(count):
+            ms = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.begin[i], self.end[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((int(self.kinds[i]), float(ms.value)))
+        return out
+
+    def close(self):
+        for arr in (self.begin, self.end):
+            for i in range(self.n):
+                if arr[i]:
+                    self._hip.hipEventDestroy(arr[i])
+                    arr[i] = None

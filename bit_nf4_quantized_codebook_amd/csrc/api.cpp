@@ -174,9 +174,45 @@ int compute_T(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32
     return NF4_OK;
 }
 
+struct TimingState {
+    hipEvent_t *begin = nullptr, *end = nullptr;
+    int32_t *kinds = nullptr;
+    int32_t n = 0, count = 0;
+};
+thread_local TimingState g_timing;
+
 }  // namespace
 
+namespace nf4k {
+void timing_before(hipStream_t stream, int kind) {
+    if (g_timing.count < g_timing.n) {
+        (void)hipEventRecord(g_timing.begin[g_timing.count], stream);
+        if (g_timing.kinds) g_timing.kinds[g_timing.count] = kind;
+    }
+}
+void timing_after(hipStream_t stream) {
+    if (g_timing.count < g_timing.n) {
+        (void)hipEventRecord(g_timing.end[g_timing.count], stream);
+        ++g_timing.count;
+    }
+}
+}  // namespace nf4k
+
 extern "C" {
+
+int nf4_set_gemm_timing_events(void **begin, void **end, int32_t *kinds, int32_t n) {
+    if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
+    if (n > 0 && (!begin || !end)) return fail(NF4_ERR_NULL, "event arrays must be non-NULL");
+    g_timing.begin = reinterpret_cast<hipEvent_t *>(begin);
+    g_timing.end = reinterpret_cast<hipEvent_t *>(end);
+    g_timing.kinds = kinds;
+    g_timing.n = n;
+    g_timing.count = 0;
+    return NF4_OK;
+}
+
+int32_t nf4_gemm_timing_count(void) { return g_timing.count; }
+
 
 const char *nf4_status_string(int status) {
     switch (status) {

@@ -295,8 +295,11 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
+    timing_before(stream, BWD ? 1 : 0);
     hipLaunchKernelGGL(dqgemm_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), kSmemBytes, stream, a);
-    return hipGetLastError();
+    e = hipGetLastError();
+    timing_after(stream);
+    return e;
 }
 
 }  // namespace

@@ -41,6 +41,10 @@ hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s
 hipError_t launch_transpose(const uint16_t *in, int64_t R, int64_t C, uint16_t *out,
                             hipStream_t stream);
 
+// Optional per-thread timing events around the fused GEMM launches (see nf4.h).
+void timing_before(hipStream_t stream, int kind);
+void timing_after(hipStream_t stream);
+
 hipError_t launch_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t n,
                              hipStream_t stream);
 hipError_t launch_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,

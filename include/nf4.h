@@ -164,6 +164,17 @@ int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t 
 int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,
                      uint16_t *du, int64_t n, void *stream);
 
+/*
+ * Timing instrumentation (not part of the method).  While set on the calling thread, the library
+ * records begin[i] and end[i] (hipEvent_t handles created by the caller) on the launch stream
+ * immediately before and after the i-th subsequent launch of the fused dequant-GEMM kernels
+ * (forward and backward), for i < n; launches beyond n are not recorded.  nf4_gemm_timing_count()
+ * returns how many launches were recorded since the last set call.  Pass n = 0 to switch it off.
+ * kinds (output, optional): for each recorded launch, 0 = forward GEMM, 1 = backward GEMM.
+ */
+int nf4_set_gemm_timing_events(void **begin, void **end, int32_t *kinds, int32_t n);
+int32_t nf4_gemm_timing_count(void);
+
 #ifdef __cplusplus
 }
 #endif
