@@ -154,6 +154,10 @@ int check_linear_args(const nf4_weight *w, int64_t M, int32_t r, float scale) {
     if (w->cols % 64) return fail(NF4_ERR_UNSUPPORTED, "weight cols (K) must be a multiple of 64");
     if (w->rows % 8) return fail(NF4_ERR_UNSUPPORTED, "weight rows (N) must be a multiple of 8");
     if (!std::isfinite(scale)) return fail(NF4_ERR_ARG, "scale must be finite");
+    // kernels address each operand with 32-bit byte offsets
+    const int64_t lim = (int64_t)1 << 31;
+    if (w->rows * (w->cols / 2) >= lim || M * w->cols * 2 >= lim || M * w->rows * 2 >= lim)
+        return fail(NF4_ERR_UNSUPPORTED, "an operand exceeds 2 GiB");
     return NF4_OK;
 }
 

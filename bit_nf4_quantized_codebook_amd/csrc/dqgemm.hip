@@ -54,6 +54,22 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zeros, so tile edges need
+// no branches (a branch that zero-fills a register with a load in flight forces a full wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int64_t clamped = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)clamped, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // Tile index -> (tm, tn), keeping each XCD (blockIdx % 8) on a contiguous run of tiles so that
 // the tiles sharing A rows land on the same L2.
 __device__ __forceinline__ void tile_coords(int ntm, int ntn, int &tm, int &tn) {
@@ -89,109 +105,95 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
 
     const int main_steps = (int)((g.Kred + TK - 1) / TK);
     const int ext_steps = (g.r + TK - 1) / TK;
-    const int nsteps = main_steps + ext_steps;
 
     const float mean = g.mean[0];
     const int64_t wblk_per_row = g.wcols >> 6;
+    const int64_t wrow_bytes = g.wcols >> 1;
 
-    // ---- register staging for one step ----
-    // areg: A tile, 8 x 16 bytes per thread.
-    // bbuf: extension B tile (8 x 16 bytes), or the packed W bytes and their block constants:
-    //   forward  bbuf[0..1] = 32 packed bytes of one row, bbuf[2].x = E4M3 code, .y = c1 bits
-    //   backward bbuf[0..1] = 8 rows x 4 packed bytes, bbuf[2..3] = 8 codes, bbuf[4..5] = 8 c1 bits
-    u32x4 areg[8];
-    u32x4 bbuf[8];
+    // tile-relative buffer descriptors: reads past the end return zeros (no edge branches)
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + m0 * g.Kred, (g.M - m0) * g.Kred * 2);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.packed, g.wrows * wrow_bytes);
+    const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.wrows * wblk_per_row);
+    const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(g.c1, ((g.wrows * wblk_per_row + 255) >> 8) * 4);
 
-    auto gload = [&](int step) {
-        const bool ext = step >= main_steps;
-        // A operand: rows m0.., 64 reduction columns
-        const uint16_t *Abase = ext ? g.Ae : g.A;
-        const int64_t lda = ext ? (int64_t)g.r : g.Kred;
-        const int64_t kcol0 = ext ? (int64_t)(step - main_steps) * TK : (int64_t)step * TK;
-        const int64_t klim = ext ? (int64_t)g.r : g.Kred;
+    // A tile: chunk q of this thread covers row (tid >> 3) + 32 q, 8 reduction elements at seg
+    const int arow = tid >> 3, aseg = tid & 7;
+    const uint32_t a_off0 = (uint32_t)((arow * g.Kred + aseg * 8) * 2);
+    const uint32_t a_rowstep = (uint32_t)(32 * g.Kred * 2);
+    const bool a_tail = (g.Kred % TK) != 0;     // only the backward reduction (N) can be ragged
+
+    // W: forward thread owns row o0+tid; backward owns rows 8*ng.. x cols o0+8*kg..
+    const int kg = tid >> 3, ng = tid & 7;
+    int64_t w_row;            // forward: the W row; backward: the first reduction row of this thread
+    uint32_t w_off0, c2_off0;
+    if (!BWD) {
+        w_row = o0 + tid;
+        w_off0 = (uint32_t)(w_row * wrow_bytes);
+        c2_off0 = (uint32_t)(w_row * wblk_per_row);
+    } else {
+        w_row = ng * 8;
+        const int64_t kcol = o0 + kg * 8;
+        w_off0 = (uint32_t)(w_row * wrow_bytes + (kcol >> 1));
+        c2_off0 = (uint32_t)(w_row * wblk_per_row + (kcol >> 6));
+    }
+
+    struct Stage {
+        u32x4 a[8];
+        u32x4 w[2];        // forward: 32 packed bytes; backward: 8 rows x 4 bytes
+        uint32_t c2[8];
+        uint32_t c1[8];
+    };
+
+    // Loads of one step into a register stage.  Never behind a branch: a step past the end
+    // (prefetch beyond the last step) reads out of range, i.e. zeros, so the memory-counter
+    // waits stay exact across the software-pipelined loop.
+    auto gload = [&](int step, Stage &sg) {
+        const bool live = step < main_steps;
+        const uint32_t kb = (uint32_t)step * TK * 2;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int c = tid + NTHREADS * q;
-            const int row = c >> 3, seg = c & 7;
-            const int64_t gm = m0 + row, gk = kcol0 + seg * 8;
-            if (gm < g.M && gk < klim) areg[q] = ldg16(Abase + gm * lda + gk);
-            else areg[q] = u32x4{0, 0, 0, 0};
-        }
-        if (ext) {
-            // B extension rows are output columns, r-contiguous
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int c = tid + NTHREADS * q;
-                const int row = c >> 3, seg = c & 7;
-                const int64_t go = o0 + row, gk = kcol0 + seg * 8;
-                if (go < g.Nout && gk < (int64_t)g.r) bbuf[q] = ldg16(g.Be + go * g.r + gk);
-                else bbuf[q] = u32x4{0, 0, 0, 0};
-            }
-            return;
+            uint32_t off = a_off0 + q * a_rowstep + kb;
+            if (!live || (a_tail && (int64_t)step * TK + aseg * 8 >= g.Kred)) off = 0xFFFFFFF0u;
+            sg.a[q] = bload16(rA, off);
         }
         if (!BWD) {
-            // thread owns W row n = o0 + tid, bytes [step*32, step*32+32)
-            const int64_t n = o0 + tid;
-            if (n < g.wrows) {
-                const uint8_t *p = g.packed + n * (g.wcols >> 1) + (int64_t)step * 32;
-                bbuf[0] = ldg16(p);
-                bbuf[1] = ldg16(p + 16);
-                const int64_t b = n * wblk_per_row + step;
-                bbuf[2].x = g.c2[b];
-                bbuf[2].y = __float_as_uint(g.c1[b >> 8]);
-            } else {
-                bbuf[0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-                bbuf[1] = bbuf[0];
-                bbuf[2].x = 0;
-                bbuf[2].y = 0;
-            }
+            const uint32_t off = live ? w_off0 + (uint32_t)step * 32 : 0xFFFFFFE0u;
+            sg.w[0] = bload16(rW, off);
+            sg.w[1] = bload16(rW, off + 16);
+            const uint32_t b = live ? c2_off0 + (uint32_t)step : 0xFFFFFFF0u;
+            sg.c2[0] = bload1(rC2, b);
+            sg.c1[0] = bload4(rC1, live ? (b >> 8) * 4 : 0xFFFFFFF0u);
         } else {
-            // thread owns rows n0+8*ng .. +7 (reduction) x cols k0+8*kg .. +7 (output)
-            const int kg = tid >> 3, ng = tid & 7;
-            const int64_t kcol = o0 + kg * 8;
+            const uint32_t rstep = (uint32_t)((int64_t)step * TK * wrow_bytes);
+            const uint32_t bstep = (uint32_t)((int64_t)step * TK * wblk_per_row);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int64_t n = (int64_t)step * TK + ng * 8 + i;
-                uint32_t wv = 0x77777777u, cv = 0, sv = 0;
-                if (n < g.wrows && kcol < g.wcols) {
-                    wv = *reinterpret_cast<const uint32_t *>(g.packed + n * (g.wcols >> 1) + (kcol >> 1));
-                    const int64_t b = n * wblk_per_row + (kcol >> 6);
-                    cv = g.c2[b];
-                    sv = __float_as_uint(g.c1[b >> 8]);
-                }
-                bbuf[i >> 2][i & 3] = wv;
-                bbuf[2 + (i >> 2)][i & 3] = cv;
-                bbuf[4 + (i >> 2)][i & 3] = sv;
+                const uint32_t wo = w_off0 + rstep + (uint32_t)(i * wrow_bytes);
+                sg.w[i >> 2][i & 3] = bload4(rW, live ? wo : 0xFFFFFFF0u);
+                const uint32_t b = c2_off0 + bstep + (uint32_t)(i * wblk_per_row);
+                sg.c2[i] = bload1(rC2, live ? b : 0xFFFFFFF0u);
+                sg.c1[i] = bload4(rC1, live ? (b >> 8) * 4 : 0xFFFFFFF0u);
             }
         }
     };
 
-    auto swrite = [&](int step, int st) {
-        const bool ext = step >= main_steps;
+    // part `part` (0..3) of writing a loaded step into LDS stage st: A chunks 2*part, 2*part+1
+    // and a quarter of the dequantized B tile
+    auto swrite_part = [&](int step, const Stage &sg, int st, int part, float *scl) {
         uint16_t *Ad = As + st * TM * LDSK;
         uint16_t *Bd = Bs + st * TN * LDSK;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int c = tid + NTHREADS * q;
-            const int row = c >> 3, seg = c & 7;
-            *reinterpret_cast<u32x4 *>(Ad + row * LDSK + seg * 8) = areg[q];
-        }
-        if (ext) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int c = tid + NTHREADS * q;
-                const int row = c >> 3, seg = c & 7;
-                *reinterpret_cast<u32x4 *>(Bd + row * LDSK + seg * 8) = bbuf[q];
-            }
-            return;
+        for (int qq = 0; qq < 2; ++qq) {
+            const int q = part * 2 + qq;
+            *reinterpret_cast<u32x4 *>(Ad + (arow + 32 * q) * LDSK + aseg * 8) = sg.a[q];
         }
         if (!BWD) {
-            const float a = block_scale(bbuf[2].x, __uint_as_float(bbuf[2].y), mean);
-            uint32_t words[8] = {bbuf[0].x, bbuf[0].y, bbuf[0].z, bbuf[0].w,
-                                 bbuf[1].x, bbuf[1].y, bbuf[1].z, bbuf[1].w};
+            if (part == 0) scl[0] = block_scale(sg.c2[0], __uint_as_float(sg.c1[0]), mean);
+            const float a = scl[0];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const uint32_t w = words[d];
+            for (int dd = 0; dd < 2; ++dd) {
+                const int d = part * 2 + dd;
+                const uint32_t w = sg.w[d >> 2][d & 3];
                 u32x4 o;
                 o.x = pack_bf16x2(cbs[w & 15u] * a, cbs[(w >> 4) & 15u] * a);
                 o.y = pack_bf16x2(cbs[(w >> 8) & 15u] * a, cbs[(w >> 12) & 15u] * a);
@@ -200,22 +202,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
                 *reinterpret_cast<u32x4 *>(Bd + tid * LDSK + d * 8) = o;
             }
         } else {
-            const int kg = tid >> 3, ng = tid & 7;
-            float a[8];
-            uint32_t wreg[8];
+            if (part == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a[i] = block_scale(bbuf[2 + (i >> 2)][i & 3], __uint_as_float(bbuf[4 + (i >> 2)][i & 3]), mean);
-                wreg[i] = bbuf[i >> 2][i & 3];
+                for (int i = 0; i < 8; ++i) {
+                    const int64_t n = (int64_t)step * TK + w_row + i;
+                    const float a = block_scale(sg.c2[i], __uint_as_float(sg.c1[i]), mean);
+                    scl[i] = (n < g.wrows) ? a : 0.0f;     // reduction rows past N contribute 0
+                }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = part * 2 + jj;
                 const int sh = 4 * j;
                 u32x4 o;
-                o.x = pack_bf16x2(cbs[(wreg[0] >> sh) & 15u] * a[0], cbs[(wreg[1] >> sh) & 15u] * a[1]);
-                o.y = pack_bf16x2(cbs[(wreg[2] >> sh) & 15u] * a[2], cbs[(wreg[3] >> sh) & 15u] * a[3]);
-                o.z = pack_bf16x2(cbs[(wreg[4] >> sh) & 15u] * a[4], cbs[(wreg[5] >> sh) & 15u] * a[5]);
-                o.w = pack_bf16x2(cbs[(wreg[6] >> sh) & 15u] * a[6], cbs[(wreg[7] >> sh) & 15u] * a[7]);
+                o.x = pack_bf16x2(cbs[(sg.w[0].x >> sh) & 15u] * scl[0], cbs[(sg.w[0].y >> sh) & 15u] * scl[1]);
+                o.y = pack_bf16x2(cbs[(sg.w[0].z >> sh) & 15u] * scl[2], cbs[(sg.w[0].w >> sh) & 15u] * scl[3]);
+                o.z = pack_bf16x2(cbs[(sg.w[1].x >> sh) & 15u] * scl[4], cbs[(sg.w[1].y >> sh) & 15u] * scl[5]);
+                o.w = pack_bf16x2(cbs[(sg.w[1].z >> sh) & 15u] * scl[6], cbs[(sg.w[1].w >> sh) & 15u] * scl[7]);
                 *reinterpret_cast<u32x4 *>(Bd + (kg * 8 + j) * LDSK + ng * 8) = o;
             }
         }
@@ -229,43 +232,90 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto compute = [&](int st) {
+    const int r32 = lane & 31, hh = lane >> 5;
+    auto mfma_sub = [&](int st, int s) {
         const uint16_t *Asrc = As + st * TM * LDSK;
         const uint16_t *Bsrc = Bs + st * TN * LDSK;
-        const int r32 = lane & 31, h = lane >> 5;
+        bf16x8 af[4], bfr[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 af[4], bfr[4];
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8 *>(Asrc + (wm * 128 + i * 32 + r32) * LDSK + s * 16 + hh * 8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8 *>(Asrc + (wm * 128 + i * 32 + r32) * LDSK + s * 16 + h * 8);
+        for (int j = 0; j < 4; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8 *>(Bsrc + (wn * 128 + j * 32 + r32) * LDSK + s * 16 + hh * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8 *>(Bsrc + (wn * 128 + j * 32 + r32) * LDSK + s * 16 + h * 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);   // keep one sub-step of fragments live at a time
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
 
+    // ---- main loop ----
+    // LDS stages alternate per step.  Two register stages alternate too: the loads for step+2 are
+    // issued at the start of step (a full step of latency to hide), while the data of step+1 is
+    // dequantized into the other LDS stage in four parts interleaved with the four MFMA sub-steps.
     __syncthreads();   // codebook table visible
-    gload(0);
-    swrite(0, 0);
+    float scl[8];
+    Stage R0, R1;
+    gload(0, R0);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) swrite_part(0, R0, 0, part, scl);
+    gload(1, R1);
     __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const int st = step & 1;
-        const bool more = step + 1 < nsteps;
-        if (more) gload(step + 1);
-        compute(st);
-        if (more) swrite(step + 1, st ^ 1);
+    int step = 0;
+    for (; step + 1 < main_steps; step += 2) {
+        // even step: compute LDS stage 0, fill stage 1 with step+1 from R1
+        gload(step + 2, R0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            mfma_sub(0, s);
+            swrite_part(step + 1, R1, 1, s, scl);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        // odd step: compute stage 1, fill stage 0 with step+2 from R0 (zeros past the end;
+        // stage 0 is only read again if step+2 is a real step)
+        gload(step + 3, R1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            mfma_sub(1, s);
+            swrite_part(step + 2, R0, 0, s, scl);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+    }
+    if (step < main_steps) {   // odd number of steps: the last one sits in stage 0
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mfma_sub(0, s);
         __syncthreads();
     }
 
+    // ---- LoRA extension: [A | Ae] . [B ; Be], r/64 more steps (operands zero padded) ----
+    if (ext_steps > 0) {
+        const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
+        const __amdgpu_buffer_rsrc_t rBe = make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2);
+        for (int e = 0; e < ext_steps; ++e) {
+            const int st = (main_steps + e) & 1;
+            uint16_t *Ad = As + st * TM * LDSK;
+            uint16_t *Bd = Bs + st * TN * LDSK;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = arow + 32 * q;
+                const int64_t gk = (int64_t)e * TK + aseg * 8;
+                const bool ok = gk < g.r;
+                const u32x4 va = bload16(rAe, ok ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u);
+                const u32x4 vb = bload16(rBe, ok ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u);
+                *reinterpret_cast<u32x4 *>(Ad + row * LDSK + aseg * 8) = va;
+                *reinterpret_cast<u32x4 *>(Bd + row * LDSK + aseg * 8) = vb;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mfma_sub(st, s);
+            __syncthreads();
+        }
+    }
+
     // ---- epilogue: fp32 -> bf16, optional accumulate into C ----
-    const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -274,7 +324,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
             if (col >= g.Nout) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+                const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
                 if (row < g.M) {
                     uint16_t *p = g.C + row * g.Nout + col;
                     float x = acc[i][j][v];
