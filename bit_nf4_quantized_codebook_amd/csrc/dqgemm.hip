@@ -7,19 +7,26 @@
 // Two orientations of one kernel:
 //   forward  Y  = X  . deq(W)^T + (sT) . L2        reduction over K, output cols = W rows
 //   backward dX = dY . deq(W)   + dT  . L1^T       reduction over N, output cols = W cols
-// The LoRA product is appended as extra reduction steps ("K-extension"): A' = [A | Ae] and
-// B' = [deq(W) ; Be], so it costs r/64 more steps of the same MFMA loop and no extra pass.
+// The LoRA product is appended as extra reduction steps: A' = [A | Ae], B' = [deq(W) ; Be],
+// so it costs r/64 more steps of the same MFMA loop and no extra pass over the activations.
 //
-// Block tile 256 x 256 outputs, reduction step 64, 4 waves in 2 x 2, each wave 128 x 128 with
-// v_mfma_f32_32x32x16_bf16 (4 x 4 tiles, 256 fp32 accumulators per lane).  Both operands are
-// staged in LDS as bf16 rows of 64 reduction elements padded to 72 (bank-conflict free 16-byte
-// fragment reads), double buffered (144 KB of the 160 KB LDS).  The packed 4-bit W tile is read
-// from global memory once per block tile and dequantized by all 256 threads straight into the
-// LDS B tile: a' = fma(e4m3(c2), c1, mean) per (row, 64-block), w = bf16(cb[code] * a') with the
-// 16 codewords read from a 64-byte LDS table (16 distinct words: no bank conflicts).
-//  - forward: a thread owns one W row (one 64-block per step) and writes 8 x 16 bytes.
-//  - backward: a thread owns an 8 x 8 (rows x cols) nibble block and writes its transpose,
-//    8 reduction values per output column, so fragments stay contiguous along the reduction.
+// Block tile 256 x 256 outputs, reduction step 64 (one quantization block per W row), 4 waves
+// in 2 x 2, each 128 x 128 with v_mfma_f32_32x32x16_bf16 (16 tiles, 256 fp32 accumulators).
+//
+// A (activations, reduction-contiguous) goes straight from global memory to LDS with
+// buffer_load ... lds (no registers, no ds_write), 32 KB per stage, 16-byte chunks XOR-swizzled
+// by (row / 2) so the 16-byte fragment reads are bank-conflict free.
+//
+// B (the frozen weight) is dequantized by all 256 threads into LDS in natural row layout
+// [W row][W col], one thread per (row, 64-column block), i.e. one quantization block:
+//   a' = fma(e4m3(c2), c1, mean);  lut[j] = bf16(cb[j] * a') for the 16 codes
+// The 16-entry bf16 table lives in 8 registers as byte planes, and each packed dword (8 codes)
+// is expanded with v_perm_b32 byte selects (no LDS lookups, no per-element multiply).
+//   - forward: the W rows are the output columns, fragments are 16-byte row reads.
+//   - backward: the W rows are the reduction, fragments come from ds_read_b64_tr_b16, which
+//     transposes 4 x 16 bf16 blocks across each 16-lane group.
+// Register stages of W are fetched two steps ahead; the dequantization of step s+1 is spread
+// over the four MFMA sub-steps of step s.
 
 #include "common.h"
 #include "launch.h"
@@ -31,8 +38,19 @@ namespace {
 constexpr int TM = 256;          // output rows per block tile
 constexpr int TN = 256;          // output cols per block tile
 constexpr int TK = 64;           // reduction per step (= one quantization block)
-constexpr int LDSK = TK + 8;     // padded LDS row, bf16 elements (144 bytes)
 constexpr int NTHREADS = 256;
+constexpr int A_STAGE = TM * TK * 2;                 // 32 KB, swizzled, unpadded
+// s_waitcnt immediate: vmcnt <= 4 (the W loads issued after the A loads may stay in flight),
+// expcnt unchecked, lgkmcnt = 0.  gfx9 layout: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14
+constexpr int kWaitA = 4 | (7 << 4) | (0 << 8);
+
+template <bool BWD> struct BLayout;
+template <> struct BLayout<false> {                  // [256 W rows][64 + 8] bf16
+    static constexpr int ROWS = TN, ROWB = (TK + 8) * 2;
+};
+template <> struct BLayout<true> {                   // [64 W rows][256 + 16] bf16
+    static constexpr int ROWS = TK, ROWB = (TN + 16) * 2;
+};
 
 struct GemmArgs {
     const uint16_t *A;       // [M, Kred] bf16
@@ -50,9 +68,10 @@ struct GemmArgs {
     Codebook cb;
 };
 
-__device__ __forceinline__ u32x4 ldg16(const void *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer resource over [base, base + bytes): loads past the end return zeros, so tile edges need
 // no branches (a branch that zero-fills a register with a load in flight forces a full wait).
@@ -82,19 +101,77 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int &tm, int &tn) 
     tn = t % ntn;
 }
 
+// ---- the 16-entry bf16 table of one quantization block, as byte planes ----
+struct Lut {
+    uint32_t la0, la1, lb0, lb1;   // low bytes of entries 0-3, 4-7, 8-11, 12-15
+    uint32_t ha0, ha1, hb0, hb1;   // high bytes
+};
+
+__device__ __forceinline__ Lut make_lut(const Codebook &cb, float a) {
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = pack_bf16x2(cb.v[2 * j] * a, cb.v[2 * j + 1] * a);
+    Lut t;
+    t.la0 = __builtin_amdgcn_perm(p[1], p[0], 0x06040200u);
+    t.ha0 = __builtin_amdgcn_perm(p[1], p[0], 0x07050301u);
+    t.la1 = __builtin_amdgcn_perm(p[3], p[2], 0x06040200u);
+    t.ha1 = __builtin_amdgcn_perm(p[3], p[2], 0x07050301u);
+    t.lb0 = __builtin_amdgcn_perm(p[5], p[4], 0x06040200u);
+    t.hb0 = __builtin_amdgcn_perm(p[5], p[4], 0x07050301u);
+    t.lb1 = __builtin_amdgcn_perm(p[7], p[6], 0x06040200u);
+    t.hb1 = __builtin_amdgcn_perm(p[7], p[6], 0x07050301u);
+    return t;
+}
+
+// Look up 4 codes (one per byte of x, each 0..15): returns low and high bytes of the 4 entries.
+__device__ __forceinline__ void lut4(const Lut &t, uint32_t x, uint32_t &lo, uint32_t &hi) {
+    // v_perm selector 0..7 picks a byte of the 8-byte pair; 8..12 give 0 when both sources are
+    // 0 and >= 13 gives 0xFF: so perm(0, 0, x + 5) is 0xFF exactly where x >= 8.
+    const uint32_t m = __builtin_amdgcn_perm(0u, 0u, x + 0x05050505u);
+    const uint32_t xb = x ^ 0x08080808u;
+    const uint32_t la = __builtin_amdgcn_perm(t.la1, t.la0, x);
+    const uint32_t lb = __builtin_amdgcn_perm(t.lb1, t.lb0, xb);
+    const uint32_t ha = __builtin_amdgcn_perm(t.ha1, t.ha0, x);
+    const uint32_t hb = __builtin_amdgcn_perm(t.hb1, t.hb0, xb);
+    lo = (m & lb) | (~m & la);
+    hi = (m & hb) | (~m & ha);
+}
+
+// 8 packed codes (element i in bits 4i..4i+3) -> 8 bf16 in element order (4 dwords)
+__device__ __forceinline__ u32x4 dequant8(const Lut &t, uint32_t w) {
+    uint32_t le, he, lo, ho;
+    lut4(t, w & 0x0F0F0F0Fu, le, he);           // elements 0, 2, 4, 6
+    lut4(t, (w >> 4) & 0x0F0F0F0Fu, lo, ho);    // elements 1, 3, 5, 7
+    const uint32_t p0 = __builtin_amdgcn_perm(lo, le, 0x05010400u);
+    const uint32_t q0 = __builtin_amdgcn_perm(ho, he, 0x05010400u);
+    const uint32_t p1 = __builtin_amdgcn_perm(lo, le, 0x07030602u);
+    const uint32_t q1 = __builtin_amdgcn_perm(ho, he, 0x07030602u);
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(q0, p0, 0x05010400u);
+    o.y = __builtin_amdgcn_perm(q0, p0, 0x07030602u);
+    o.z = __builtin_amdgcn_perm(q1, p1, 0x05010400u);
+    o.w = __builtin_amdgcn_perm(q1, p1, 0x07030602u);
+    return o;
+}
+
 template <bool BWD>
 __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
-    extern __shared__ __align__(16) uint16_t smem[];
-    uint16_t *As = smem;                              // [2][TM][LDSK]
-    uint16_t *Bs = smem + 2 * TM * LDSK;              // [2][TN][LDSK]
-    float *cbs = reinterpret_cast<float *>(smem + 2 * (TM + TN) * LDSK);
+    typedef BLayout<BWD> BL;
+    constexpr int B_STAGE = BL::ROWS * BL::ROWB;
+    // separate LDS objects, so the compiler sees that the direct-to-LDS A loads never alias the
+    // B tile reads and adds no memory-counter waits of its own before them
+    // each stage is its own object: a read of stage 0 provably never aliases the loads in flight
+    // into stage 1 (and vice versa)
+    __shared__ __align__(16) uint8_t As0[A_STAGE];
+    __shared__ __align__(16) uint8_t As1[A_STAGE];
+    __shared__ __align__(16) uint8_t Bs0[B_STAGE];
+    __shared__ __align__(16) uint8_t Bs1[B_STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-
-    if (tid < 16) cbs[tid] = g.cb.v[tid];
+    const int r32 = lane & 31, hh = lane >> 5;
 
     const int ntm = (int)((g.M + TM - 1) / TM);
     const int ntn = (int)((g.Nout + TN - 1) / TN);
@@ -116,111 +193,64 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.wrows * wblk_per_row);
     const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(g.c1, ((g.wrows * wblk_per_row + 255) >> 8) * 4);
 
-    // A tile: chunk q of this thread covers row (tid >> 3) + 32 q, 8 reduction elements at seg
-    const int arow = tid >> 3, aseg = tid & 7;
-    const uint32_t a_off0 = (uint32_t)((arow * g.Kred + aseg * 8) * 2);
-    const uint32_t a_rowstep = (uint32_t)(32 * g.Kred * 2);
-    const bool a_tail = (g.Kred % TK) != 0;     // only the backward reduction (N) can be ragged
-
-    // W: forward thread owns row o0+tid; backward owns rows 8*ng.. x cols o0+8*kg..
-    const int kg = tid >> 3, ng = tid & 7;
-    int64_t w_row;            // forward: the W row; backward: the first reduction row of this thread
-    uint32_t w_off0, c2_off0;
-    if (!BWD) {
-        w_row = o0 + tid;
-        w_off0 = (uint32_t)(w_row * wrow_bytes);
-        c2_off0 = (uint32_t)(w_row * wblk_per_row);
-    } else {
-        w_row = ng * 8;
-        const int64_t kcol = o0 + kg * 8;
-        w_off0 = (uint32_t)(w_row * wrow_bytes + (kcol >> 1));
-        c2_off0 = (uint32_t)(w_row * wblk_per_row + (kcol >> 6));
+    // ---- A: direct global -> LDS.  Each wave issues 8 x 1 KB per step: instruction q writes
+    // LDS rows 8u..8u+7 (u = 8*wave + q); lane l -> row 8u + l/8, physical chunk l%8, which holds
+    // logical chunk (l%8) ^ ((row/2) % 8). ----
+    uint32_t a_voff[8];
+    int a_col[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 8 * (8 * wave + q) + (lane >> 3);
+        a_col[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+        a_voff[q] = (uint32_t)((row * g.Kred + a_col[q]) * 2);
     }
-
-    struct Stage {
-        u32x4 a[8];
-        u32x4 w[2];        // forward: 32 packed bytes; backward: 8 rows x 4 bytes
-        uint32_t c2[8];
-        uint32_t c1[8];
-    };
-
-    // Loads of one step into a register stage.  Never behind a branch: a step past the end
-    // (prefetch beyond the last step) reads out of range, i.e. zeros, so the memory-counter
-    // waits stay exact across the software-pipelined loop.
-    auto gload = [&](int step, Stage &sg) {
+    auto load_A = [&](int step, uint8_t *Ad) {
         const bool live = step < main_steps;
-        const uint32_t kb = (uint32_t)step * TK * 2;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            uint32_t off = a_off0 + q * a_rowstep + kb;
-            if (!live || (a_tail && (int64_t)step * TK + aseg * 8 >= g.Kred)) off = 0xFFFFFFF0u;
-            sg.a[q] = bload16(rA, off);
-        }
-        if (!BWD) {
-            const uint32_t off = live ? w_off0 + (uint32_t)step * 32 : 0xFFFFFFE0u;
-            sg.w[0] = bload16(rW, off);
-            sg.w[1] = bload16(rW, off + 16);
-            const uint32_t b = live ? c2_off0 + (uint32_t)step : 0xFFFFFFF0u;
-            sg.c2[0] = bload1(rC2, b);
-            sg.c1[0] = bload4(rC1, live ? (b >> 8) * 4 : 0xFFFFFFF0u);
-        } else {
-            const uint32_t rstep = (uint32_t)((int64_t)step * TK * wrow_bytes);
-            const uint32_t bstep = (uint32_t)((int64_t)step * TK * wblk_per_row);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t wo = w_off0 + rstep + (uint32_t)(i * wrow_bytes);
-                sg.w[i >> 2][i & 3] = bload4(rW, live ? wo : 0xFFFFFFF0u);
-                const uint32_t b = c2_off0 + bstep + (uint32_t)(i * wblk_per_row);
-                sg.c2[i] = bload1(rC2, live ? b : 0xFFFFFFF0u);
-                sg.c1[i] = bload4(rC1, live ? (b >> 8) * 4 : 0xFFFFFFF0u);
-            }
+            uint32_t off = a_voff[q] + (uint32_t)step * TK * 2;
+            // chunks past the reduction end (ragged backward N) and steps past the end read 0
+            if (!live || (int64_t)step * TK + a_col[q] >= g.Kred) off = 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rA, (lds_void *)(Ad + (8 * wave + q) * 1024), 16, off, 0, 0, 0);
         }
     };
 
-    // part `part` (0..3) of writing a loaded step into LDS stage st: A chunks 2*part, 2*part+1
-    // and a quarter of the dequantized B tile
-    auto swrite_part = [&](int step, const Stage &sg, int st, int part, float *scl) {
-        uint16_t *Ad = As + st * TM * LDSK;
-        uint16_t *Bd = Bs + st * TN * LDSK;
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int q = part * 2 + qq;
-            *reinterpret_cast<u32x4 *>(Ad + (arow + 32 * q) * LDSK + aseg * 8) = sg.a[q];
+    // ---- W: thread -> (row, 64-column block) ----
+    //   forward : W row o0 + tid, block = step
+    //   backward: W row step*64 + tid%64, block o0/64 + tid/64
+    const int bw_row = BWD ? (tid & 63) : tid;
+    const int bw_blk = BWD ? (tid >> 6) : 0;
+    struct WStage {
+        u32x4 w[2];
+        uint32_t c2, c1;
+    };
+    auto load_W = [&](int step, WStage &ws) {
+        const bool live = step < main_steps;
+        int64_t n, blk;
+        if (!BWD) { n = o0 + tid; blk = step; }
+        else { n = (int64_t)step * TK + bw_row; blk = (o0 >> 6) + bw_blk; }
+        const uint32_t off = (uint32_t)(n * wrow_bytes + blk * 32);
+        const uint32_t b = (uint32_t)(n * wblk_per_row + blk);
+        ws.w[0] = bload16(rW, live ? off : 0xFFFFFFF0u);
+        ws.w[1] = bload16(rW, live ? off + 16 : 0xFFFFFFF0u);
+        ws.c2 = bload1(rC2, live ? b : 0xFFFFFFF0u);
+        ws.c1 = bload4(rC1, live ? (b >> 8) * 4 : 0xFFFFFFF0u);
+    };
+    // dequantize a W stage: part `part` (0..3) handles packed dwords 2*part, 2*part+1
+    Lut lut;
+    auto write_B = [&](int step, const WStage &ws, uint8_t *Bst, int part) {
+        if (part == 0) {
+            float a = block_scale(ws.c2, __uint_as_float(ws.c1), mean);
+            if (BWD && (int64_t)step * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
+            lut = make_lut(g.cb, a);
         }
-        if (!BWD) {
-            if (part == 0) scl[0] = block_scale(sg.c2[0], __uint_as_float(sg.c1[0]), mean);
-            const float a = scl[0];
+        uint8_t *Bd = Bst + bw_row * BL::ROWB + bw_blk * 128;
 #pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                const int d = part * 2 + dd;
-                const uint32_t w = sg.w[d >> 2][d & 3];
-                u32x4 o;
-                o.x = pack_bf16x2(cbs[w & 15u] * a, cbs[(w >> 4) & 15u] * a);
-                o.y = pack_bf16x2(cbs[(w >> 8) & 15u] * a, cbs[(w >> 12) & 15u] * a);
-                o.z = pack_bf16x2(cbs[(w >> 16) & 15u] * a, cbs[(w >> 20) & 15u] * a);
-                o.w = pack_bf16x2(cbs[(w >> 24) & 15u] * a, cbs[(w >> 28) & 15u] * a);
-                *reinterpret_cast<u32x4 *>(Bd + tid * LDSK + d * 8) = o;
-            }
-        } else {
-            if (part == 0) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int64_t n = (int64_t)step * TK + w_row + i;
-                    const float a = block_scale(sg.c2[i], __uint_as_float(sg.c1[i]), mean);
-                    scl[i] = (n < g.wrows) ? a : 0.0f;     // reduction rows past N contribute 0
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = part * 2 + jj;
-                const int sh = 4 * j;
-                u32x4 o;
-                o.x = pack_bf16x2(cbs[(sg.w[0].x >> sh) & 15u] * scl[0], cbs[(sg.w[0].y >> sh) & 15u] * scl[1]);
-                o.y = pack_bf16x2(cbs[(sg.w[0].z >> sh) & 15u] * scl[2], cbs[(sg.w[0].w >> sh) & 15u] * scl[3]);
-                o.z = pack_bf16x2(cbs[(sg.w[1].x >> sh) & 15u] * scl[4], cbs[(sg.w[1].y >> sh) & 15u] * scl[5]);
-                o.w = pack_bf16x2(cbs[(sg.w[1].z >> sh) & 15u] * scl[6], cbs[(sg.w[1].w >> sh) & 15u] * scl[7]);
-                *reinterpret_cast<u32x4 *>(Bd + (kg * 8 + j) * LDSK + ng * 8) = o;
-            }
+        for (int dd = 0; dd < 2; ++dd) {
+            const int d = part * 2 + dd;
+            const uint32_t w = ws.w[d >> 2][d & 3];
+            *reinterpret_cast<u32x4 *>(Bd + d * 16) = dequant8(lut, w);
         }
     };
 
@@ -232,17 +262,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int r32 = lane & 31, hh = lane >> 5;
-    auto mfma_sub = [&](int st, int s) {
-        const uint16_t *Asrc = As + st * TM * LDSK;
-        const uint16_t *Bsrc = Bs + st * TN * LDSK;
+    // ---- fragments of sub-step s (16 reduction elements): lane (r32, hh) takes elements
+    // 16 s + 8 hh .. +7 of its row (A) / column (B) ----
+    auto frag_A = [&](const uint8_t *Ast, int s, int i) -> bf16x8 {
+        const int row = wm * 128 + i * 32 + r32;
+        const int c = (2 * s + hh) ^ ((row >> 1) & 7);
+        return *reinterpret_cast<const bf16x8 *>(Ast + row * 128 + c * 16);
+    };
+    auto frag_B = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
+        if (!BWD) {
+            const int row = wn * 128 + j * 32 + r32;
+            return *reinterpret_cast<const bf16x8 *>(Bst + row * BL::ROWB + (s * 16 + hh * 8) * 2);
+        } else {
+            // 16-lane group (hh, half): lane i of the group reads row 16s + 8hh + 4e + i/4,
+            // columns col0 + 4(i%4) .. +3; after the transpose, lane i holds column col0 + i.
+            const int i16 = lane & 15, half = (lane >> 4) & 1;
+            const int col0 = wn * 128 + j * 32 + half * 16;
+            const int rowb = s * 16 + hh * 8 + (i16 >> 2);
+            const uint8_t *base = Bst + (col0 + 4 * (i16 & 3)) * 2;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * BL::ROWB));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * BL::ROWB));
+            const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            return __builtin_bit_cast(bf16x8, v);
+        }
+    };
+    auto mfma_sub = [&](const uint8_t *Ast, const uint8_t *Bst, int s) {
         bf16x8 af[4], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = *reinterpret_cast<const bf16x8 *>(Asrc + (wm * 128 + i * 32 + r32) * LDSK + s * 16 + hh * 8);
+        for (int i = 0; i < 4; ++i) af[i] = frag_A(Ast, s, i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8 *>(Bsrc + (wn * 128 + j * 32 + r32) * LDSK + s * 16 + hh * 8);
+        for (int j = 0; j < 4; ++j) bfr[j] = frag_B(Bst, s, j);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -251,66 +300,78 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     };
 
     // ---- main loop ----
-    // LDS stages alternate per step.  Two register stages alternate too: the loads for step+2 are
-    // issued at the start of step (a full step of latency to hide), while the data of step+1 is
-    // dequantized into the other LDS stage in four parts interleaved with the four MFMA sub-steps.
-    __syncthreads();   // codebook table visible
-    float scl[8];
-    Stage R0, R1;
-    gload(0, R0);
+    // LDS stages alternate per step.  A for step+1 is loaded straight into LDS at the start of
+    // step; W for step+2 into registers at the start of step, and the W registers of step+1 are
+    // dequantized into the other B stage in four parts interleaved with the MFMA sub-steps.
+    WStage R0, R1;
+    load_A(0, As0);
+    load_W(0, R0);
 #pragma unroll
-    for (int part = 0; part < 4; ++part) swrite_part(0, R0, 0, part, scl);
-    gload(1, R1);
+    for (int part = 0; part < 4; ++part) write_B(0, R0, Bs0, part);
+    load_W(1, R1);
+    __builtin_amdgcn_s_waitcnt(0);     // A of step 0 landed (all counters drained)
     __syncthreads();
     int step = 0;
     for (; step + 1 < main_steps; step += 2) {
-        // even step: compute LDS stage 0, fill stage 1 with step+1 from R1
-        gload(step + 2, R0);
+        load_A(step + 1, As1);
+        load_W(step + 2, R0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            mfma_sub(0, s);
-            swrite_part(step + 1, R1, 1, s, scl);
+            mfma_sub(As0, Bs0, s);
+            write_B(step + 1, R1, Bs1, s);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // A of step+1 (issued before the 4 W loads of step+2) has landed; LDS writes done
+        __builtin_amdgcn_s_waitcnt(kWaitA);
         __syncthreads();
-        // odd step: compute stage 1, fill stage 0 with step+2 from R0 (zeros past the end;
-        // stage 0 is only read again if step+2 is a real step)
-        gload(step + 3, R1);
+        load_A(step + 2, As0);
+        load_W(step + 3, R1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            mfma_sub(1, s);
-            swrite_part(step + 2, R0, 0, s, scl);
+            mfma_sub(As1, Bs1, s);
+            write_B(step + 2, R0, Bs0, s);   // zeros past the end; stage 0 is read again only if live
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitA);
         __syncthreads();
     }
     if (step < main_steps) {   // odd number of steps: the last one sits in stage 0
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mfma_sub(0, s);
+        for (int s = 0; s < 4; ++s) mfma_sub(As0, Bs0, s);
         __syncthreads();
     }
 
-    // ---- LoRA extension: [A | Ae] . [B ; Be], r/64 more steps (operands zero padded) ----
+    // ---- LoRA extension: [A | Ae] . [B ; Be], r/64 more steps (zero padded past r) ----
     if (ext_steps > 0) {
         const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
         const __amdgpu_buffer_rsrc_t rBe = make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2);
         for (int e = 0; e < ext_steps; ++e) {
             const int st = (main_steps + e) & 1;
-            uint16_t *Ad = As + st * TM * LDSK;
-            uint16_t *Bd = Bs + st * TN * LDSK;
+            uint8_t *Ast = st ? As1 : As0;
+            uint8_t *Bst = st ? Bs1 : Bs0;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int row = arow + 32 * q;
-                const int64_t gk = (int64_t)e * TK + aseg * 8;
-                const bool ok = gk < g.r;
-                const u32x4 va = bload16(rAe, ok ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u);
-                const u32x4 vb = bload16(rBe, ok ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u);
-                *reinterpret_cast<u32x4 *>(Ad + row * LDSK + aseg * 8) = va;
-                *reinterpret_cast<u32x4 *>(Bd + row * LDSK + aseg * 8) = vb;
+                const int row = (tid >> 3) + 32 * q, chunk = tid & 7;
+                const int64_t gk = (int64_t)e * TK + chunk * 8;
+                const uint32_t off = gk < g.r ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u;
+                const u32x4 va = bload16(rAe, off);
+                const u32x4 vb = bload16(rBe, off);
+                const int pc = chunk ^ ((row >> 1) & 7);
+                *reinterpret_cast<u32x4 *>(Ast + row * 128 + pc * 16) = va;
+                if (!BWD) {
+                    *reinterpret_cast<u32x4 *>(Bst + row * BL::ROWB + chunk * 16) = vb;
+                } else {
+                    // backward B stage is [reduction j][output col]: scatter the 8 r-values
+                    const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        *reinterpret_cast<uint16_t *>(Bst + (chunk * 8 + t) * BL::ROWB + row * 2) =
+                            (uint16_t)(wv[t >> 1] >> (16 * (t & 1)));
+                }
             }
             __syncthreads();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) mfma_sub(st, s);
+            for (int s = 0; s < 4; ++s) mfma_sub(Ast, Bst, s);
             __syncthreads();
         }
     }
@@ -336,18 +397,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     }
 }
 
-constexpr size_t kSmemBytes = (size_t)2 * (TM + TN) * LDSK * sizeof(uint16_t) + 16 * sizeof(float);
-
 template <bool BWD>
 hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dqgemm_kernel<BWD>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
-    if (e != hipSuccess) return e;
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
     timing_before(stream, BWD ? 1 : 0);
-    hipLaunchKernelGGL(dqgemm_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), kSmemBytes, stream, a);
-    e = hipGetLastError();
+    hipLaunchKernelGGL(dqgemm_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
 }
