@@ -36,9 +36,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // OCP FP8 E4M3 -> float (exact; codes 0x7F/0xFF are NaN and never produced here).
+// Branch-free: |v| = (8 [e > 0] + m) * 2^(max(e, 1) - 10), which covers subnormals (e = 0).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    const uint32_t sig = m | (min(e, 1u) << 3);
+    const float mag = __builtin_amdgcn_ldexpf((float)sig, (int)max(e, 1u) - 10);
     return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 

@@ -154,6 +154,23 @@ __device__ __forceinline__ u32x4 dequant8(const Lut &t, uint32_t w) {
     return o;
 }
 
+// Same 8 codes in "planar" order (elements 0, 2, 4, 6, 1, 3, 5, 7): 4 byte-interleaves fewer.
+// Used where the 8 values land on output columns (backward), which the epilogue permutes back.
+__device__ __forceinline__ u32x4 dequant8_planar(const Lut &t, uint32_t w) {
+    uint32_t le, he, lo, ho;
+    lut4(t, w & 0x0F0F0F0Fu, le, he);
+    lut4(t, (w >> 4) & 0x0F0F0F0Fu, lo, ho);
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(he, le, 0x05010400u);   // elements 0, 2
+    o.y = __builtin_amdgcn_perm(he, le, 0x07030602u);   // elements 4, 6
+    o.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);   // elements 1, 3
+    o.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);   // elements 5, 7
+    return o;
+}
+
+// column held at position p (0..7) of an 8-column group after dequant8_planar
+__device__ __forceinline__ int planar_col(int p) { return ((p & 3) << 1) | (p >> 2); }
+
 template <bool BWD>
 __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     typedef BLayout<BWD> BL;
@@ -169,7 +186,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, hh = lane >> 5;
 
@@ -204,15 +221,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         a_col[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
         a_voff[q] = (uint32_t)((row * g.Kred + a_col[q]) * 2);
     }
+    const int kred32 = (int)g.Kred;
     auto load_A = [&](int step, uint8_t *Ad) {
-        const bool live = step < main_steps;
+        // reduction columns left from this step on; <= 0 past the last step (loads read zeros),
+        // < 64 on a ragged backward last step (its columns past N read zeros)
+        const int rem = kred32 - step * TK;
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        lds_u8 *dst = (lds_u8 *)Ad + wave * 8192;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             uint32_t off = a_voff[q] + (uint32_t)step * TK * 2;
-            // chunks past the reduction end (ragged backward N) and steps past the end read 0
-            if (!live || (int64_t)step * TK + a_col[q] >= g.Kred) off = 0xFFFFFFF0u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rA, (lds_void *)(Ad + (8 * wave + q) * 1024), 16, off, 0, 0, 0);
+            if (a_col[q] >= rem) off = 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(dst + q * 1024), 16, off, 0, 0, 0);
         }
     };
 
@@ -250,7 +270,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         for (int dd = 0; dd < 2; ++dd) {
             const int d = part * 2 + dd;
             const uint32_t w = ws.w[d >> 2][d & 3];
-            *reinterpret_cast<u32x4 *>(Bd + d * 16) = dequant8(lut, w);
+            *reinterpret_cast<u32x4 *>(Bd + d * 16) = BWD ? dequant8_planar(lut, w) : dequant8(lut, w);
         }
     };
 
@@ -286,17 +306,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
             return __builtin_bit_cast(bf16x8, v);
         }
     };
-    auto mfma_sub = [&](const uint8_t *Ast, const uint8_t *Bst, int s) {
-        bf16x8 af[4], bfr[4];
+    struct Frags {
+        bf16x8 a[4], b[4];
+    };
+    auto load_frags = [&](const uint8_t *Ast, const uint8_t *Bst, int s, Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag_A(Ast, s, i);
+        for (int i = 0; i < 4; ++i) f.a[i] = frag_A(Ast, s, i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = frag_B(Bst, s, j);
+        for (int j = 0; j < 4; ++j) f.b[j] = frag_B(Bst, s, j);
+    };
+    auto mma = [&](const Frags &f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    auto mfma_sub = [&](const uint8_t *Ast, const uint8_t *Bst, int s) {
+        Frags f;
+        load_frags(Ast, Bst, s, f);
+        mma(f);
+    };
+
+    // Interleave one sub-step: its 16 MFMAs, the fragment reads of the next sub-step, a quarter
+    // of the next step's dequantization (VALU + 2 LDS writes) and the direct-to-LDS A loads.
+    // MFMA (32 cycles each) and VALU issue from the same wave co-execute when interleaved.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // 5 VALU
+            if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            if (k == 9 || k == 13) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+            if (k == 2 || k == 6 || k == 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+        }
+    };
+
+    // one step: compute stage (Ac, Bc), fill stage Bn with the dequantized W registers `ws` of
+    // step `wstep`; fragments run one sub-step ahead
+    auto half_step = [&](const uint8_t *Ac, const uint8_t *Bc, uint8_t *Bn, int wstep, const WStage &ws) {
+        Frags f0, f1;
+        load_frags(Ac, Bc, 0, f0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Frags &cur = (s & 1) ? f1 : f0;
+            Frags &nxt = (s & 1) ? f0 : f1;
+            if (s < 3) load_frags(Ac, Bc, s + 1, nxt);
+            mma(cur);
+            write_B(wstep, ws, Bn, s);
+            interleave();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // ---- main loop ----
@@ -315,23 +375,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     for (; step + 1 < main_steps; step += 2) {
         load_A(step + 1, As1);
         load_W(step + 2, R0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            mfma_sub(As0, Bs0, s);
-            write_B(step + 1, R1, Bs1, s);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        half_step(As0, Bs0, Bs1, step + 1, R1);
         // A of step+1 (issued before the 4 W loads of step+2) has landed; LDS writes done
         __builtin_amdgcn_s_waitcnt(kWaitA);
         __syncthreads();
         load_A(step + 2, As0);
         load_W(step + 3, R1);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            mfma_sub(As1, Bs1, s);
-            write_B(step + 2, R0, Bs0, s);   // zeros past the end; stage 0 is read again only if live
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        half_step(As1, Bs1, Bs0, step + 2, R0);   // zeros past the end; read again only if live
         __builtin_amdgcn_s_waitcnt(kWaitA);
         __syncthreads();
     }
@@ -361,11 +411,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
                 if (!BWD) {
                     *reinterpret_cast<u32x4 *>(Bst + row * BL::ROWB + chunk * 16) = vb;
                 } else {
-                    // backward B stage is [reduction j][output col]: scatter the 8 r-values
+                    // backward B stage is [reduction j][output col], columns in the planar order of
+                    // the main steps (column c of an 8-group sits at position (c%2)*4 + c/2)
                     const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+                    const int pos = (row & ~7) | ((row & 1) << 2) | ((row & 7) >> 1);
 #pragma unroll
                     for (int t = 0; t < 8; ++t)
-                        *reinterpret_cast<uint16_t *>(Bst + (chunk * 8 + t) * BL::ROWB + row * 2) =
+                        *reinterpret_cast<uint16_t *>(Bst + (chunk * 8 + t) * BL::ROWB + pos * 2) =
                             (uint16_t)(wv[t >> 1] >> (16 * (t & 1)));
                 }
             }
@@ -376,21 +428,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         }
     }
 
-    // ---- epilogue: fp32 -> bf16, optional accumulate into C ----
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    // ---- epilogue: fp32 -> bf16 ----
+    // Lane (r32, hh) of tile (i, j) holds column j*32 + r32 (permuted back for the backward's
+    // planar dequant order) and rows i*32 + 8*(v/4) + 4*hh + v%4.  Stores go through a buffer
+    // descriptor: rows past M fall outside it, row offsets are scalars, the column offset is a
+    // per-lane constant, so no per-element address arithmetic remains.
+    const int colw = BWD ? ((r32 & ~7) | planar_col(r32 & 7)) : r32;
+    if (!g.accumulate) {
+        const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
+        const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh * 4) * row_bytes) +
+                                  (uint32_t)((o0 + wn * 128 + colw) * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t col = o0 + wn * 128 + j * 32 + r32;
-            if (col >= g.Nout) continue;
+            if (o0 + wn * 128 + j * 32 + colw >= g.Nout) continue;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
-                if (row < g.M) {
-                    uint16_t *p = g.C + row * g.Nout + col;
-                    float x = acc[i][j][v];
-                    if (g.accumulate) x += bf16_to_f32(*p);
-                    *p = (uint16_t)f32_to_bf16(x);
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    const uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
+                    const uint32_t soff = rows * row_bytes;
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rC, lane_off + j * 64, soff, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rC, lane_off + j * 64,
+                                                          soff + row_bytes, 0);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = o0 + wn * 128 + j * 32 + colw;
+                if (col >= g.Nout) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                    if (row < g.M) {
+                        uint16_t *p = g.C + row * g.Nout + col;
+                        *p = (uint16_t)f32_to_bf16(acc[i][j][v] + bf16_to_f32(*p));
+                    }
                 }
             }
         }
