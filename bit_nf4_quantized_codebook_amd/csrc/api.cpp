@@ -118,7 +118,7 @@ constexpr int64_t kTile = 64;
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
-    size_t off_L1t, off_L2t, off_T, off_sT, off_dT, off_P, total;
+    size_t off_T, off_sT, off_dT, off_P, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -131,8 +131,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     p.msL2 = nf4k::choose_split(rt * ((N + kTile - 1) / kTile), mt);
     p.msL1 = nf4k::choose_split(((K + kTile - 1) / kTile) * rt, mt);
     size_t off = 0;
-    p.off_L1t = off; off += round256((size_t)r * K * 2);
-    p.off_L2t = off; off += round256((size_t)N * r * 2);
     p.off_T = off;   off += round256((size_t)M * r * 2);
     p.off_sT = off;  off += round256((size_t)M * r * 2);
     p.off_dT = off;  off += round256((size_t)M * r * 2);
@@ -169,10 +167,8 @@ T *ws_at(void *ws, size_t off) {
 // T (unscaled) and/or s*T, both bf16 [M, r], from X [M, K] and L1 [K, r]
 int compute_T(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32_t r, float scale,
               uint16_t *T_out, uint16_t *sT_out, const Plan &p, void *ws, hipStream_t s) {
-    uint16_t *L1t = ws_at<uint16_t>(ws, p.off_L1t);
     float *P = ws_at<float>(ws, p.off_P);
-    NF4_CHECK_HIP(nf4k::launch_transpose(L1, K, r, L1t, s), "transpose L1");
-    NF4_CHECK_HIP(nf4k::launch_skinny_nt(X, L1t, P, M, r, K, p.ksT, s), "T = X L1");
+    NF4_CHECK_HIP(nf4k::launch_skinny_nt(X, L1, /*b_rows_k=*/true, P, M, r, K, p.ksT, s), "T = X L1");
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksT, M * r, 1.0f, T_out, scale, sT_out, s),
                   "T reduce");
     return NF4_OK;
@@ -325,11 +321,9 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
-    uint16_t *L2t = ws_at<uint16_t>(workspace, p.off_L2t);
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
-    NF4_CHECK_HIP(nf4k::launch_transpose(L2, r, N, L2t, s), "transpose L2");
-    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2t, r, M, Y, s), "fused dequant GEMM (fwd)");
+    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
     return NF4_OK;
 }
 
@@ -360,7 +354,7 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
         Tuse = Tb;
     }
     // dT = s dY L2^T  (L2 [r, N] is already the row-major transpose the product needs)
-    NF4_CHECK_HIP(nf4k::launch_skinny_nt(dY, L2, P, M, r, N, p.ksdT, s), "dT = dY L2^T");
+    NF4_CHECK_HIP(nf4k::launch_skinny_nt(dY, L2, /*b_rows_k=*/false, P, M, r, N, p.ksdT, s), "dT = dY L2^T");
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksdT, M * r, scale, dT, 0.0f, nullptr, s), "dT reduce");
     // dL2 = s T^T dY
     NF4_CHECK_HIP(nf4k::launch_skinny_tn(Tuse, dY, P, M, r, N, p.msL2, s), "dL2 = T^T dY");

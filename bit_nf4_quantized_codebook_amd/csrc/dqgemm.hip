@@ -44,12 +44,19 @@ constexpr int A_STAGE = TM * TK * 2;                 // 32 KB, swizzled, unpadde
 // expcnt unchecked, lgkmcnt = 0.  gfx9 layout: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14
 constexpr int kWaitA = 4 | (7 << 4) | (0 << 8);
 
+// B stage layouts: rows of 64 reduction elements ([out col][red], 144-byte rows) or rows of 256
+// output columns ([red][out col], 544-byte rows).  The main loop uses the first in the forward and
+// the second in the backward; the LoRA extension step uses the other one (its B operand, L2 [r, N]
+// or L1 [K, r], is read in its natural layout), so a stage is sized for both.
+constexpr int ROWB_RED = (TK + 8) * 2;     // [256][64 + 8]
+constexpr int ROWB_OUT = (TN + 16) * 2;    // [64][256 + 16]
+constexpr int B_STAGE_BYTES = (TN * ROWB_RED > TK * ROWB_OUT) ? TN * ROWB_RED : TK * ROWB_OUT;
 template <bool BWD> struct BLayout;
-template <> struct BLayout<false> {                  // [256 W rows][64 + 8] bf16
-    static constexpr int ROWS = TN, ROWB = (TK + 8) * 2;
+template <> struct BLayout<false> {
+    static constexpr int ROWS = TN, ROWB = ROWB_RED;
 };
-template <> struct BLayout<true> {                   // [64 W rows][256 + 16] bf16
-    static constexpr int ROWS = TK, ROWB = (TN + 16) * 2;
+template <> struct BLayout<true> {
+    static constexpr int ROWS = TK, ROWB = ROWB_OUT;
 };
 
 struct GemmArgs {
@@ -58,8 +65,8 @@ struct GemmArgs {
     const uint8_t *c2;       // E4M3 block constants
     const float *c1;         // 256-block multipliers
     const float *mean;       // [1]
-    const uint16_t *Ae;      // [M, r] bf16 (extension A)
-    const uint16_t *Be;      // [Nout, r] bf16 (extension B, row = output column)
+    const uint16_t *Ae;      // [M, r] bf16 (extension A: s T forward, dT backward)
+    const uint16_t *Be;      // forward: L2 [r, Nout]; backward: L1 [Nout, r]  (natural layouts)
     uint16_t *C;             // [M, Nout] bf16
     int64_t M, Nout, Kred;
     int64_t wrows, wcols;
@@ -174,7 +181,7 @@ __device__ __forceinline__ int planar_col(int p) { return ((p & 3) << 1) | (p >>
 template <bool BWD>
 __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     typedef BLayout<BWD> BL;
-    constexpr int B_STAGE = BL::ROWS * BL::ROWB;
+    constexpr int B_STAGE = B_STAGE_BYTES;
     // separate LDS objects, so the compiler sees that the direct-to-LDS A loads never alias the
     // B tile reads and adds no memory-counter waits of its own before them
     // each stage is its own object: a read of stage 0 provably never aliases the loads in flight
@@ -289,6 +296,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         const int c = (2 * s + hh) ^ ((row >> 1) & 7);
         return *reinterpret_cast<const bf16x8 *>(Ast + row * 128 + c * 16);
     };
+    // B fragment from a [out col][red] tile (row reads) or a [red][out col] tile (transposing reads)
+    auto frag_rowread = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
+        const int row = wn * 128 + j * 32 + r32;
+        return *reinterpret_cast<const bf16x8 *>(Bst + row * ROWB_RED + (s * 16 + hh * 8) * 2);
+    };
+    auto frag_trread = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
+        const int i16 = lane & 15, half = (lane >> 4) & 1;
+        const int col0 = wn * 128 + j * 32 + half * 16;
+        const int rowb = s * 16 + hh * 8 + (i16 >> 2);
+        const uint8_t *base = Bst + (col0 + 4 * (i16 & 3)) * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * ROWB_OUT));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * ROWB_OUT));
+        const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    };
     auto frag_B = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
         if (!BWD) {
             const int row = wn * 128 + j * 32 + r32;
@@ -392,38 +414,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     }
 
     // ---- LoRA extension: [A | Ae] . [B ; Be], r/64 more steps (zero padded past r) ----
+    // forward : Be = L2 [r, N]: tile [j][out col] (544-byte rows), transposing fragment reads
+    // backward: Be = L1 [K, r]: tile [out col][j] (144-byte rows, columns at their planar
+    //           positions), row fragment reads
     if (ext_steps > 0) {
         const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
-        const __amdgpu_buffer_rsrc_t rBe = make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2);
+        const __amdgpu_buffer_rsrc_t rBe = BWD ? make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2)
+                                               : make_rsrc(g.Be, (int64_t)g.r * g.Nout * 2);
         for (int e = 0; e < ext_steps; ++e) {
             const int st = (main_steps + e) & 1;
             uint8_t *Ast = st ? As1 : As0;
             uint8_t *Bst = st ? Bs1 : Bs0;
+            const int j0 = e * TK;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
+                // A: row (tid/8) + 32 q, reduction chunk tid % 8 (columns past r read zeros)
                 const int row = (tid >> 3) + 32 * q, chunk = tid & 7;
-                const int64_t gk = (int64_t)e * TK + chunk * 8;
-                const uint32_t off = gk < g.r ? (uint32_t)((row * (int64_t)g.r + gk) * 2) : 0xFFFFFFF0u;
+                const int jj = j0 + chunk * 8;
+                const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0xFFFFFFF0u;
                 const u32x4 va = bload16(rAe, off);
-                const u32x4 vb = bload16(rBe, off);
-                const int pc = chunk ^ ((row >> 1) & 7);
-                *reinterpret_cast<u32x4 *>(Ast + row * 128 + pc * 16) = va;
-                if (!BWD) {
-                    *reinterpret_cast<u32x4 *>(Bst + row * BL::ROWB + chunk * 16) = vb;
-                } else {
-                    // backward B stage is [reduction j][output col], columns in the planar order of
-                    // the main steps (column c of an 8-group sits at position (c%2)*4 + c/2)
-                    const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+                *reinterpret_cast<u32x4 *>(Ast + row * 128 + (chunk ^ ((row >> 1) & 7)) * 16) = va;
+                if (BWD) {
+                    // B: output column o0 + row, reduction chunk
+                    const u32x4 vb = bload16(rBe, off);
                     const int pos = (row & ~7) | ((row & 1) << 2) | ((row & 7) >> 1);
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        *reinterpret_cast<uint16_t *>(Bst + (chunk * 8 + t) * BL::ROWB + pos * 2) =
-                            (uint16_t)(wv[t >> 1] >> (16 * (t & 1)));
+                    *reinterpret_cast<u32x4 *>(Bst + pos * ROWB_RED + chunk * 16) = vb;
+                } else {
+                    // B: reduction row j0 + tid/32 + 8 q, output columns o0 + 8 (tid % 32)
+                    const int jr = j0 + (tid >> 5) + 8 * q, oc = (tid & 31) * 8;
+                    const uint32_t ob = (jr < g.r) ? (uint32_t)(((int64_t)jr * g.Nout + o0 + oc) * 2) : 0xFFFFFFF0u;
+                    const u32x4 vb = bload16(rBe, ob);
+                    *reinterpret_cast<u32x4 *>(Bst + ((tid >> 5) + 8 * q) * ROWB_OUT + oc * 2) = vb;
                 }
             }
             __syncthreads();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) mfma_sub(Ast, Bst, s);
+            for (int s = 0; s < 4; ++s) {
+                Frags f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f.a[i] = frag_A(Ast, s, i);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f.b[j] = BWD ? frag_rowread(Bst, s, j) : frag_trread(Bst, s, j);
+                mma(f);
+            }
             __syncthreads();
         }
     }
@@ -489,12 +522,12 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
-                             const uint16_t *L2t, int32_t r, int64_t M, uint16_t *Y,
+                             const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream) {
     GemmArgs a;
     a.A = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
-    a.Ae = sT; a.Be = L2t; a.C = Y;
+    a.Ae = sT; a.Be = L2; a.C = Y;
     a.M = M; a.Nout = w.rows; a.Kred = w.cols;
     a.wrows = w.rows; a.wcols = w.cols;
     a.r = r; a.accumulate = 0;

@@ -25,21 +25,20 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
                           uint16_t *out, hipStream_t stream);
 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
-                             const uint16_t *L2t, int32_t r, int64_t M, uint16_t *Y,
+                             const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream);
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
                              bool accumulate, hipStream_t stream);
 
 int choose_split(int64_t tiles, int64_t red_steps);
-hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *Bt, float *P, int64_t M, int32_t R,
-                            int64_t Kred, int nsplit, hipStream_t stream);
+// b_rows_k: B given as [Kred, R] (true) or as [R, Kred] (false)
+hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *B, bool b_rows_k, float *P, int64_t M,
+                            int32_t R, int64_t Kred, int nsplit, hipStream_t stream);
 hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int64_t M, int64_t Pn,
                             int64_t Qn, int nsplit, hipStream_t stream);
 hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
                                   float s2, uint16_t *out2, hipStream_t stream);
-hipError_t launch_transpose(const uint16_t *in, int64_t R, int64_t C, uint16_t *out,
-                            hipStream_t stream);
 
 // Optional per-thread timing events around the fused GEMM launches (see nf4.h).
 void timing_before(hipStream_t stream, int kind);

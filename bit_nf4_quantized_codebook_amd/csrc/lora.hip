@@ -3,12 +3,16 @@
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
 // section 4 eq. (3) (Y = XW + s X L1 L2) and section 3.5 (gradients for L1, L2 only).
 //
-// These are skinny products whose cost is one pass over an [M, K] or [M, N] activation:
-//   skinny_nt:  P[ks] = A[:, chunk ks] . Bt[:, chunk ks]^T     (T = X L1, dT = s dY L2^T)
-//   skinny_tn:  P[ms] = U[rows ms, :]^T . V[rows ms, :]        (dL2 = s T^T dY, dL1 = X^T dT)
-// Both write float32 partials over a split of the reduction (enough block tiles to fill the
-// 256 CUs), and reduce_partials sums them in a fixed order, scales, and rounds to bf16 once.
-// MFMA v_mfma_f32_32x32x16_bf16 on 64 x 64 block tiles, 4 waves of 32 x 32.
+// Each product is one streaming pass over an [M, K] or [M, N] activation with a rank-r (<= 128)
+// partner, so the kernels are built for HBM bandwidth: a block tile is 64 x 64 outputs, the
+// reduction is split over enough block tiles to fill the 256 CUs, every thread keeps four
+// reduction steps of 16-byte loads in flight, and float32 partials are summed afterwards in a
+// fixed order (deterministic).  Operands sit in LDS in their natural row-major layout; when the
+// reduction runs along rows, fragments are read with ds_read_b64_tr_b16 (4 x 16 transposes per
+// 16-lane group), so no operand is ever transposed in memory.
+//   skinny_nt:  P[ks] = A[:, chunk ks] . B          A [M, Kred];  B = Bk [Kred, R] or Bt [R, Kred]
+//   skinny_tn:  P[ms] = U[rows ms, :]^T . V[rows ms, :]    U [M, Pn], V [M, Qn]
+// MFMA v_mfma_f32_32x32x16_bf16, 4 waves of 32 x 32.
 
 #include "common.h"
 #include "launch.h"
@@ -18,161 +22,238 @@ namespace nf4k {
 namespace {
 
 constexpr int ST = 64;          // block tile (both output dims) and reduction step
-constexpr int LDP = ST + 8;     // padded LDS row (bf16)
+constexpr int NSTAGE = 4;       // reduction steps in flight per block tile
+constexpr int ROWB = (ST + 8) * 2;   // padded LDS row, bytes (144: conflict-free 16-byte reads)
 
-__device__ __forceinline__ u32x4 ldg16z(const uint16_t *p, bool ok) {
-    return ok ? *reinterpret_cast<const u32x4 *>(p) : u32x4{0, 0, 0, 0};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int64_t clamped = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)clamped, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-// P[ks][m][j] = sum_{k in chunk ks} A[m][k] * Bt[j][k];  A [M, Kred], Bt [R, Kred] (row-major)
+// 16-byte fragment of row `row` (the M/N index), reduction elements 16 s + 8 hh .. +7 of a tile
+// stored [row][reduction]
+__device__ __forceinline__ bf16x8 frag_rows(const uint8_t *t, int row, int s, int hh) {
+    return *reinterpret_cast<const bf16x8 *>(t + row * ROWB + (s * 16 + hh * 8) * 2);
+}
+// same fragment from a tile stored [reduction][col]: two transposing reads
+__device__ __forceinline__ bf16x8 frag_tr(const uint8_t *t, int col0, int s, int lane) {
+    const int i16 = lane & 15, hh = lane >> 5, half = (lane >> 4) & 1;
+    const int rowb = s * 16 + hh * 8 + (i16 >> 2);
+    const uint8_t *base = t + (col0 + half * 16 + 4 * (i16 & 3)) * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * ROWB));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * ROWB));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Each thread moves 2 x 16 bytes of each 64 x 64 operand tile per step: tile row = tid/8 (+32),
+// 16-byte chunk = tid%8.
+struct TileLoad {
+    u32x4 v[2];
+};
+
+// P[ks][m][j] = sum_{k in chunk ks} A[m][k] * B(k, j)
+//   B_ROWS_K = true : B given as Bk [Kred, R] (row k), tile stored [k][j] -> transposing reads
+//   B_ROWS_K = false: B given as Bt [R, Kred] (row j), tile stored [j][k] -> row reads
+template <bool B_ROWS_K>
 __global__ __launch_bounds__(256) void skinny_nt_kernel(const uint16_t *__restrict__ A,
-                                                        const uint16_t *__restrict__ Bt,
+                                                        const uint16_t *__restrict__ B,
                                                         float *__restrict__ P, int64_t M, int32_t R,
                                                         int64_t Kred, int64_t kchunk) {
-    __shared__ __align__(16) uint16_t As[ST * LDP];
-    __shared__ __align__(16) uint16_t Bs[ST * LDP];
+    __shared__ __align__(16) uint8_t As[NSTAGE][ST * ROWB];
+    __shared__ __align__(16) uint8_t Bs[NSTAGE][ST * ROWB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, hh = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.x * ST;
     const int j0 = blockIdx.y * ST;
-    const int ks = blockIdx.z;
-    const int64_t kbeg = (int64_t)ks * kchunk;
+    const int64_t kbeg = (int64_t)blockIdx.z * kchunk;
     const int64_t kend = (kbeg + kchunk < Kred) ? kbeg + kchunk : Kred;
-    f32x16 acc = {};
-    const int r32 = lane & 31, h = lane >> 5;
-    for (int64_t k0 = kbeg; k0 < kend; k0 += ST) {
+    const int nsteps = kend > kbeg ? (int)((kend - kbeg + ST - 1) / ST) : 0;
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + m0 * Kred, (M - m0) * Kred * 2);
+    const __amdgpu_buffer_rsrc_t rB = B_ROWS_K ? make_rsrc(B, Kred * (int64_t)R * 2)
+                                               : make_rsrc(B + (int64_t)j0 * Kred, ((int64_t)R - j0) * Kred * 2);
+    const int trow = tid >> 3, tch = tid & 7;
+
+    auto load = [&](int step, TileLoad &a, TileLoad &b) {
+        const int64_t k0 = kbeg + (int64_t)step * ST;
+        const bool live = step < nsteps;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + 256 * q;
-            const int row = c >> 3, seg = c & 7;
-            const int64_t gk = k0 + seg * 8;
-            const bool kin = gk < kend;
-            u32x4 va = ldg16z(A + (m0 + row) * Kred + gk, kin && (m0 + row) < M);
-            u32x4 vb = ldg16z(Bt + (int64_t)(j0 + row) * Kred + gk, kin && (j0 + row) < R);
-            *reinterpret_cast<u32x4 *>(As + row * LDP + seg * 8) = va;
-            *reinterpret_cast<u32x4 *>(Bs + row * LDP + seg * 8) = vb;
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 32 * h;
+            // A: row m0+row, columns k0 + 8 tch; columns past the chunk end read zeros
+            const int64_t ka = k0 + tch * 8;
+            a.v[h] = bload16(rA, (live && ka < kend) ? (uint32_t)((row * Kred + ka) * 2) : 0xFFFFFFF0u);
+            if (B_ROWS_K) {
+                // B tile row = k0 + row, columns j0 + 8 tch (j < R)
+                const int64_t kb = k0 + row;
+                const bool ok = live && kb < kend && j0 + tch * 8 < R;
+                b.v[h] = bload16(rB, ok ? (uint32_t)((kb * R + j0 + tch * 8) * 2) : 0xFFFFFFF0u);
+            } else {
+                // B tile row = j0 + row, columns k0 + 8 tch
+                b.v[h] = bload16(rB, (live && ka < kend) ? (uint32_t)((row * Kred + ka) * 2) : 0xFFFFFFF0u);
+            }
         }
+    };
+    auto store = [&](int slot, const TileLoad &a, const TileLoad &b) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 32 * h;
+            *reinterpret_cast<u32x4 *>(&As[slot][row * ROWB + tch * 16]) = a.v[h];
+            *reinterpret_cast<u32x4 *>(&Bs[slot][row * ROWB + tch * 16]) = b.v[h];
+        }
+    };
+
+    f32x16 acc = {};
+    TileLoad la[NSTAGE], lb[NSTAGE];
+    for (int g0 = 0; g0 < nsteps; g0 += NSTAGE) {
+#pragma unroll
+        for (int u = 0; u < NSTAGE; ++u) load(g0 + u, la[u], lb[u]);
+#pragma unroll
+        for (int u = 0; u < NSTAGE; ++u) store(u, la[u], lb[u]);
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 a = *reinterpret_cast<const bf16x8 *>(As + (wm * 32 + r32) * LDP + s * 16 + h * 8);
-            bf16x8 b = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 32 + r32) * LDP + s * 16 + h * 8);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        for (int u = 0; u < NSTAGE; ++u) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 fa = frag_rows(As[u], wm * 32 + r32, s, hh);
+                const bf16x8 fb = B_ROWS_K ? frag_tr(Bs[u], wn * 32, s, lane)
+                                           : frag_rows(Bs[u], wn * 32 + r32, s, hh);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+            }
         }
         __syncthreads();
     }
     const int col = j0 + wn * 32 + r32;
     if (col < R) {
-        float *Pk = P + (int64_t)ks * M * R;
+        float *Pk = P + (int64_t)blockIdx.z * M * R;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + wm * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+            const int64_t row = m0 + wm * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
             if (row < M) Pk[row * R + col] = acc[v];
         }
     }
 }
 
-// P[ms][p][q] = sum_{m in chunk ms} U[m][p] * V[m][q];  U [M, Pn], V [M, Qn] (row-major)
+// P[ms][p][q] = sum_{m in chunk ms} U[m][p] * V[m][q];  U [M, Pn], V [M, Qn] (row-major).
+// Both tiles are stored [m][p] / [m][q] and read with transposing fragment loads.
 __global__ __launch_bounds__(256) void skinny_tn_kernel(const uint16_t *__restrict__ U,
                                                         const uint16_t *__restrict__ V,
                                                         float *__restrict__ P, int64_t M, int64_t Pn,
                                                         int64_t Qn, int64_t mchunk) {
-    __shared__ __align__(16) uint16_t Us[ST * LDP];   // [p][m]
-    __shared__ __align__(16) uint16_t Vs[ST * LDP];   // [q][m]
+    __shared__ __align__(16) uint8_t Us[NSTAGE][ST * ROWB];
+    __shared__ __align__(16) uint8_t Vs[NSTAGE][ST * ROWB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, hh = lane >> 5;
     const int64_t p0 = (int64_t)blockIdx.x * ST;
     const int64_t q0 = (int64_t)blockIdx.y * ST;
-    const int ms = blockIdx.z;
-    const int64_t mbeg = (int64_t)ms * mchunk;
+    const int64_t mbeg = (int64_t)blockIdx.z * mchunk;
     const int64_t mend = (mbeg + mchunk < M) ? mbeg + mchunk : M;
-    f32x16 acc = {};
-    const int r32 = lane & 31, h = lane >> 5;
-    for (int64_t mm = mbeg; mm < mend; mm += ST) {
+    const int nsteps = mend > mbeg ? (int)((mend - mbeg + ST - 1) / ST) : 0;
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(U, M * Pn * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V, M * Qn * 2);
+    const int trow = tid >> 3, tch = tid & 7;
+    const bool pok = p0 + tch * 8 < Pn, qok = q0 + tch * 8 < Qn;
+
+    auto load = [&](int step, TileLoad &a, TileLoad &b) {
+        const int64_t mm = mbeg + (int64_t)step * ST;
+        const bool live = step < nsteps;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + 256 * q;
-            const int row = c >> 3, seg = c & 7;          // row = m offset, seg = 8 columns
-            const int64_t gm = mm + row;
-            const bool min_ = gm < mend;
-            u32x4 vu = ldg16z(U + gm * Pn + p0 + seg * 8, min_ && (p0 + seg * 8) < Pn);
-            u32x4 vv = ldg16z(V + gm * Qn + q0 + seg * 8, min_ && (q0 + seg * 8) < Qn);
-            const uint32_t wu[4] = {vu.x, vu.y, vu.z, vu.w};
-            const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                Us[(seg * 8 + e) * LDP + row] = (uint16_t)(wu[e >> 1] >> (16 * (e & 1)));
-                Vs[(seg * 8 + e) * LDP + row] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int64_t gm = mm + trow + 32 * h;
+            const bool ok = live && gm < mend;
+            a.v[h] = bload16(rU, (ok && pok) ? (uint32_t)((gm * Pn + p0 + tch * 8) * 2) : 0xFFFFFFF0u);
+            b.v[h] = bload16(rV, (ok && qok) ? (uint32_t)((gm * Qn + q0 + tch * 8) * 2) : 0xFFFFFFF0u);
         }
+    };
+    auto store = [&](int slot, const TileLoad &a, const TileLoad &b) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 32 * h;
+            *reinterpret_cast<u32x4 *>(&Us[slot][row * ROWB + tch * 16]) = a.v[h];
+            *reinterpret_cast<u32x4 *>(&Vs[slot][row * ROWB + tch * 16]) = b.v[h];
+        }
+    };
+
+    f32x16 acc = {};
+    TileLoad la[NSTAGE], lb[NSTAGE];
+    for (int g0 = 0; g0 < nsteps; g0 += NSTAGE) {
+#pragma unroll
+        for (int u = 0; u < NSTAGE; ++u) load(g0 + u, la[u], lb[u]);
+#pragma unroll
+        for (int u = 0; u < NSTAGE; ++u) store(u, la[u], lb[u]);
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 a = *reinterpret_cast<const bf16x8 *>(Us + (wm * 32 + r32) * LDP + s * 16 + h * 8);
-            bf16x8 b = *reinterpret_cast<const bf16x8 *>(Vs + (wn * 32 + r32) * LDP + s * 16 + h * 8);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        for (int u = 0; u < NSTAGE; ++u) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 fa = frag_tr(Us[u], wm * 32, s, lane);
+                const bf16x8 fb = frag_tr(Vs[u], wn * 32, s, lane);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+            }
         }
         __syncthreads();
     }
     const int64_t col = q0 + wn * 32 + r32;
     if (col < Qn) {
-        float *Pk = P + (int64_t)ms * Pn * Qn;
+        float *Pk = P + (int64_t)blockIdx.z * Pn * Qn;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int64_t row = p0 + wm * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
+            const int64_t row = p0 + wm * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
             if (row < Pn) Pk[row * Qn + col] = acc[v];
         }
     }
 }
 
-// out[i] = bf16(s1 * sum_k P[k][i]) (k ascending); out2 (optional) = bf16(s2 * same sum)
+// out[i] = bf16(s1 * sum_k P[k][i]) (k ascending); out2 (optional) = bf16(s2 * same sum).
+// Four elements per thread (n is a multiple of 4 for every caller: r % 8 == 0).
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ P, int nsplit,
                                                               int64_t n, float s1, uint16_t *__restrict__ out,
                                                               float s2, uint16_t *__restrict__ out2) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+    typedef float f32v4 __attribute__((ext_vector_type(4)));
+    const int64_t n4 = n >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float acc = P[i];
-        for (int k = 1; k < nsplit; ++k) acc += P[(int64_t)k * n + i];
-        if (out) out[i] = (uint16_t)f32_to_bf16(s1 * acc);
-        if (out2) out2[i] = (uint16_t)f32_to_bf16(s2 * acc);
-    }
-}
-
-// out[c][r] = in[r][c], bf16, via a 64 x 64 LDS tile
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ in, int64_t R,
-                                                        int64_t C, uint16_t *__restrict__ out) {
-    __shared__ uint16_t t[64][65];
-    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int rr = e >> 6, cc = e & 63;
-        const int64_t gr = r0 + rr, gc = c0 + cc;
-        t[rr][cc] = (gr < R && gc < C) ? in[gr * C + gc] : (uint16_t)0;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int cc = e >> 6, rr = e & 63;
-        const int64_t gr = r0 + rr, gc = c0 + cc;
-        if (gr < R && gc < C) out[gc * R + gr] = t[rr][cc];
+        f32v4 acc = reinterpret_cast<const f32v4 *>(P)[i];
+        for (int k = 1; k < nsplit; ++k) acc += reinterpret_cast<const f32v4 *>(P + (int64_t)k * n)[i];
+        if (out) {
+            uint2 o = {pack_bf16x2(s1 * acc.x, s1 * acc.y), pack_bf16x2(s1 * acc.z, s1 * acc.w)};
+            reinterpret_cast<uint2 *>(out)[i] = o;
+        }
+        if (out2) {
+            uint2 o = {pack_bf16x2(s2 * acc.x, s2 * acc.y), pack_bf16x2(s2 * acc.z, s2 * acc.w)};
+            reinterpret_cast<uint2 *>(out2)[i] = o;
+        }
     }
 }
 
 }  // namespace
 
 int choose_split(int64_t tiles, int64_t red_steps) {
-    // aim for >= 512 block tiles in flight, each with >= 4 reduction steps
+    // aim for >= 512 block tiles in flight, each with >= 8 reduction steps
     int64_t s = (512 + tiles - 1) / tiles;
-    if (s > red_steps / 4) s = red_steps / 4;
+    if (s > red_steps / 8) s = red_steps / 8;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return (int)s;
 }
 
-hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *Bt, float *P, int64_t M, int32_t R,
-                            int64_t Kred, int nsplit, hipStream_t stream) {
+hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *B, bool b_rows_k, float *P, int64_t M,
+                            int32_t R, int64_t Kred, int nsplit, hipStream_t stream) {
     const int64_t steps = (Kred + ST - 1) / ST;
     const int64_t per = (steps + nsplit - 1) / nsplit;
     dim3 grid((unsigned)((M + ST - 1) / ST), (unsigned)((R + ST - 1) / ST), (unsigned)nsplit);
-    hipLaunchKernelGGL(skinny_nt_kernel, grid, dim3(256), 0, stream, A, Bt, P, M, R, Kred, per * ST);
+    if (b_rows_k)
+        hipLaunchKernelGGL(skinny_nt_kernel<true>, grid, dim3(256), 0, stream, A, B, P, M, R, Kred, per * ST);
+    else
+        hipLaunchKernelGGL(skinny_nt_kernel<false>, grid, dim3(256), 0, stream, A, B, P, M, R, Kred, per * ST);
     return hipGetLastError();
 }
 
@@ -187,17 +268,11 @@ hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int6
 
 hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
                                   float s2, uint16_t *out2, hipStream_t stream) {
-    int64_t g = (n + 255) / 256;
-    if (g > 256 * 16) g = 256 * 16;
+    int64_t g = ((n >> 2) + 255) / 256;
+    if (g > 256 * 8) g = 256 * 8;
     if (g < 1) g = 1;
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)g), dim3(256), 0, stream, P, nsplit, n, s1,
                        out, s2, out2);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose(const uint16_t *in, int64_t R, int64_t C, uint16_t *out, hipStream_t stream) {
-    dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, in, R, C, out);
     return hipGetLastError();
 }
 
