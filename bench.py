@@ -158,6 +158,7 @@ def main():
     ap.add_argument("--workload", default="llama7b_attn")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +176,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.gemv_only:
+        print(json.dumps({"gemv": bench_gemv(torch, nf4, synth, dev)}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     if wl.swiglu:
         raise SystemExit("MLP workloads are measured by their own script path; use llama7b_attn")

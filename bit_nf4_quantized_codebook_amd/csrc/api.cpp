@@ -115,6 +115,7 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // Workspace plan of the linear layer (identical for the size query and the calls)
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
+constexpr int64_t kGemvMaxM = 16;     // token counts served by the weight-streaming GEMV
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
@@ -323,7 +324,10 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
-    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
+    if (M <= kGemvMaxM)
+        NF4_CHECK_HIP(nf4k::launch_gemv_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
+    else
+        NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
     return NF4_OK;
 }
 

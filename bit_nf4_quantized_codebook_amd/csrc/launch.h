@@ -27,6 +27,9 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream);
+// decode-size forward (M <= 16): sT = s X L1 (bf16 [M, r]) computed beforehand
+hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
+                           const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
                              bool accumulate, hipStream_t stream);

@@ -162,6 +162,9 @@ SHAPES = [
     (4, 256, 512, 32),
     (16, 1024, 1024, 128),
     (513, 264, 640, 24),
+    (3, 200, 1344, 16),        # decode-size path: ragged K (not a multiple of 256 or 1024)
+    (16, 72, 2112, 64),
+    (2, 1032, 3072, 8),
 ]
 
 
@@ -280,3 +283,24 @@ def test_swiglu_parity(n):
     rg, ru = oracle.swiglu_bwd(dh, g, u)
     check_tol("dg", f32(dg), rg)
     check_tol("du", f32(du), ru)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemv_full_size(M):
+    """Decode-size forward at full size (W 28672 x 8192, r = 64), all outputs against the oracle."""
+    wl = synth.WORKLOADS["gemv"]
+    lin = wl.linears[0]
+    N, K, r, s = lin.N, lin.K, wl.r, wl.scale
+    _say(f"gemv full size M={M} N={N} K={K}")
+    W = synth.weight_f32(wl, lin)
+    l1, l2 = synth.lora_f32(wl, lin)
+    L1, L2 = synth.to_bf16_bits(l1), synth.to_bf16_bits(l2)
+    X = synth.to_bf16_bits(synth.x_f32(wl, M=M, K=K))
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+    Y, T = nf4.qlora_linear_fwd(w, d16(X), d16(L1), d16(L2), s)
+    torch.cuda.synchronize()
+    Wd = oracle.dequant_weight(oracle.quantize_dq(W, CB), CB)
+    del W
+    Yr, Tr = oracle.forward(X, Wd, L1, L2, s)
+    check_tol("Y", f32(Y), Yr)
+    check_tol("T", f32(T), Tr)
