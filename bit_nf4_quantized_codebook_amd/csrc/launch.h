@@ -27,9 +27,15 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream);
-// decode-size forward (M <= 16): sT = s X L1 (bf16 [M, r]) computed beforehand
-hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
-                           const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
+// decode-size forward (M <= 16): two launches; Yp and Tp are fp32 scratch of the sizes gemv_plan gives
+struct GemvPlan {
+    int nseg, nkc;
+    size_t yp_floats, tp_floats;
+};
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r);
+hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                           float scale, int32_t r, int64_t M, uint16_t *Y, uint16_t *T_out, float *Yp,
+                           float *Tp, hipStream_t stream);
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
                              bool accumulate, hipStream_t stream);
