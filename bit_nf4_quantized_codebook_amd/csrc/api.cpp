@@ -115,7 +115,8 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // Workspace plan of the linear layer (identical for the size query and the calls)
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
-constexpr int64_t kGemvMaxM = 16;     // token counts served by the weight-streaming GEMV
+constexpr int64_t kDecodeMaxM = 4;    // token counts served by the table-decode GEMV
+constexpr int64_t kGemvMaxM = 16;     // token counts served by a weight-streaming GEMV
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
@@ -141,7 +142,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     pmax = pmax > (size_t)p.msL1 * K * r ? pmax : (size_t)p.msL1 * K * r;
     p.off_P = off;   off += round256(pmax * 4);
     p.off_Yp = p.off_Tp = off;
-    if (M <= kGemvMaxM) {
+    if (M <= kDecodeMaxM) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
@@ -327,7 +328,7 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
     if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (M <= kGemvMaxM) {
+    if (M <= kDecodeMaxM) {
         NF4_CHECK_HIP(nf4k::launch_gemv_fwd(view_of(w), X, L1, L2, scale, r, M, Y, T_out,
                                             ws_at<float>(workspace, p.off_Yp), ws_at<float>(workspace, p.off_Tp), s),
                       "dequant GEMV (fwd)");
@@ -336,7 +337,10 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
-    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
+    if (M <= kGemvMaxM)
+        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
+    else
+        NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
     return NF4_OK;
 }
 

@@ -1,4 +1,4 @@
-// Decode-size forward (M <= 16 tokens) of the QLoRA linear layer (gfx950):
+// Decode-size forward (M <= 4 tokens) of the QLoRA linear layer (gfx950):
 //   Y = X deq(W)^T + s (X L1) L2
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
@@ -7,21 +7,21 @@
 // This shape streams the 4-bit weight once from HBM; the work to hide behind that stream is the
 // decoding of the codes.  Two launches:
 //
-// gemv_main_kernel: workgroups of 4 waves.  "W" workgroups own 64 weight rows and one K segment
-//   (the segment split four ways over the waves); "T" workgroups compute K-slices of T = X L1.
-//   - v_mfma_f32_4x4x4_16b_bf16 with A broadcast (CBSZ = 4, ABID = s): B lane l is weight row
-//     n0 + l, so 16 blocks x 4 columns = 64 rows per instruction and M <= 4 wastes no row; one
-//     8-byte X fragment per lane covers a whole 64-column quantization block (lane 4 b + i holds
-//     X[i][4 b .. 4 b + 3] of the block, broadcast by ABID = b).
+// gemv_main_kernel: workgroups of 8 waves.  "T" workgroups (first in the grid, so dispatched
+//   first) compute K-slices of T = X L1; "W" workgroups own 64 weight rows and one K segment.
+//   - v_mfma_f32_4x4x4_16b_bf16: B lane l holds 4 codes of one weight row, so M <= 4 tokens waste
+//     no MFMA row; A (X) is broadcast inside pairs of blocks (CBSZ = 1).
+//   - every weight load reads whole 128-byte lines: a load covers 8 rows x 128 bytes and each
+//     lane's 16 bytes feed 8 MFMAs directly (no LDS staging of W).
 //   - codes are decoded through a pair table in LDS: entry e (one packed byte) holds the bf16
 //     codebook values of its two nibbles; 64 copies side by side so that lane l always reads
-//     bank l (conflict-free).  The address is one v_perm (byte of the code word next to the lane
-//     offset), the lookup one ds_read_b32 per two weights.
+//     bank l (conflict-free).  The address is one v_perm (the code byte next to the lane offset),
+//     the lookup one ds_read_b32 per two weights.
 //   - the table is the plain codebook, so each block is accumulated on its own and the block
 //     constant a = c2 * s2 + mean (eq. 6, rebuilt in fp32) multiplies the fp32 partial:
 //     y = sum_blocks a_b sum_{k in b} x_k cb[q_k].  This equals X deq(W)^T up to rounding, with
 //     the codebook rounded to bf16 instead of each product cb * a.
-//   - W, X and the block constants of a 4-block macro step are fetched two steps ahead.
+//   - the block constants of the workgroup's rows and K segment are staged in LDS once.
 // gemv_epilogue_kernel: sums the K-segment partials of X deq(W)^T and the K-slices of T, rounds
 //   s T to bf16 and adds (s T) L2, stores bf16 Y (and T when asked).
 
@@ -377,13 +377,13 @@ __device__ void t_part(const GemvArgs &g, uint32_t *lds, int t) {
     }
 }
 
-// Per m-tile count: row sets per wave (RS), row halves per workgroup (RH) and register stages
-// (NST), chosen so that a wave stays within 128 registers (four waves per SIMD).
+// Row sets per wave (RS), row groups per workgroup (RH) and register stages (NST), chosen so
+// that a wave stays within 128 registers (four waves per SIMD).  MT = 1: up to 4 tokens.
 template <int MT>
 struct WCfg {
-    static constexpr int RS = MT == 4 ? 1 : 2;
+    static constexpr int RS = 2;
     static constexpr int RH = 4;
-    static constexpr int NST = MT == 4 ? 1 : 2;
+    static constexpr int NST = 2;
     static constexpr int ROWS = 8 * RS * RH;
 };
 
@@ -509,11 +509,7 @@ hipError_t launch_mt(const GemvArgs &a, const EpiArgs &e, int grid_main, hipStre
     return hipGetLastError();
 }
 
-int m_tiles(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
-int rows_per_wg(int64_t M) {
-    const int mt = m_tiles(M);
-    return mt == 1 ? WCfg<1>::ROWS : (mt == 2 ? WCfg<2>::ROWS : WCfg<4>::ROWS);
-}
+int rows_per_wg(int64_t) { return WCfg<1>::ROWS; }
 
 }  // namespace
 
@@ -556,11 +552,8 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
     EpiArgs e;
     e.Yp = Yp; e.Tp = Tp; e.L2 = L2; e.Y = Y; e.T_out = T_out;
     e.M = M; e.N = w.rows; e.r = r; e.nseg = p.nseg; e.nkc = p.nkc; e.scale = scale;
-    switch (m_tiles(M)) {
-    case 1: return launch_mt<1>(a, e, grid, stream);
-    case 2: return launch_mt<2>(a, e, grid, stream);
-    default: return launch_mt<4>(a, e, grid, stream);
-    }
+    if (M > 4) return hipErrorInvalidValue;           // larger token counts take another path
+    return launch_mt<1>(a, e, grid, stream);
 }
 
 }  // namespace nf4k

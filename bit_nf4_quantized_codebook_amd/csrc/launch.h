@@ -27,7 +27,10 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream);
-// decode-size forward (M <= 16): two launches; Yp and Tp are fp32 scratch of the sizes gemv_plan gives
+// 4 < M <= 16 tokens: sT = s X L1 (bf16 [M, r]) computed beforehand
+hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
+                                const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
+// decode-size forward (M <= 4): two launches; Yp and Tp are fp32 scratch of the sizes gemv_plan gives
 struct GemvPlan {
     int nseg, nkc;
     size_t yp_floats, tp_floats;
