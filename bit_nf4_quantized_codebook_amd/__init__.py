@@ -58,6 +58,12 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_nf4_quantized_codebook_amd.build` "
                           "or __graft_entry__.build()")
+    # torch ships its own HIP runtime under the same soname; loading torch first makes the library
+    # bind to that one copy, so the tensors' device memory and the kernels share one runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     i = ctypes.c_int
@@ -306,10 +312,11 @@ def qlora_swiglu_bwd(dh, g, u):
 
 
 class GemmTimer:
-    """HIP events recorded by the library around each fused dequant-GEMM launch on this thread."""
+    """HIP events bound by the library to each instrumented kernel launch (fused GEMMs, GEMV) on
+    this thread."""
 
     def __init__(self, capacity: int):
-        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime already loaded (by soname)
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                   ctypes.c_void_p]

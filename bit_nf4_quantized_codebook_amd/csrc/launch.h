@@ -52,7 +52,8 @@ hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int6
 hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
                                   float s2, uint16_t *out2, hipStream_t stream);
 
-// Optional per-thread timing events around the fused GEMM launches (see nf4.h).
+// Optional per-thread timing events recorded on the launch stream right before and after each
+// instrumented launch (see nf4.h).
 void timing_before(hipStream_t stream, int kind);
 void timing_after(hipStream_t stream);
 

@@ -167,10 +167,12 @@ int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, u
 /*
  * Timing instrumentation (not part of the method).  While set on the calling thread, the library
  * records begin[i] and end[i] (hipEvent_t handles created by the caller) on the launch stream
- * immediately before and after the i-th subsequent launch of the fused dequant-GEMM kernels
- * (forward and backward), for i < n; launches beyond n are not recorded.  nf4_gemm_timing_count()
- * returns how many launches were recorded since the last set call.  Pass n = 0 to switch it off.
- * kinds (output, optional): for each recorded launch, 0 = forward GEMM, 1 = backward GEMM.
+ * immediately before and after the i-th subsequent launch of an instrumented kernel -- the fused
+ * dequant-GEMMs (forward and backward) and the weight-streaming GEMV main kernels -- for i < n;
+ * launches beyond n are not recorded.
+ * nf4_gemm_timing_count() returns how many launches were recorded since the last set call.
+ * Pass n = 0 to switch it off.  kinds (output, optional): for each recorded launch, 0 = forward
+ * GEMM, 1 = backward GEMM, 2 = GEMV.
  */
 int nf4_set_gemm_timing_events(void **begin, void **end, int32_t *kinds, int32_t n);
 int32_t nf4_gemm_timing_count(void);

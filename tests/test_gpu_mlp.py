@@ -1,0 +1,157 @@
+"""GPU parity of the MLP workloads: the LLaMA-7B MLP chain and the heavy-tailed 65B MLP layer.
+
+The chain is gate and up (QLoRA linears) -> SwiGLU -> down (QLoRA linear), forward and backward,
+run through the C ABI exactly as a caller would, with dX of gate and up accumulated into one
+buffer.  Each stage is checked against the float64 oracle on the GPU's own bf16 inputs to that
+stage (so an error cannot hide behind the next stage's rounding): token rows are sampled for the
+[M, N] outputs, the adapter gradients are checked in full.  Tolerances: rel-Frobenius <= 5e-3 and
+max-abs <= 2e-2 * max|ref|.  The 65B layer adds a bit-exact check of quantize, double quant and
+dequant on a heavy-tailed weight (1 % of the entries from a ten times wider normal).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_nf4_quantized_codebook_amd as nf4  # noqa: E402
+
+DEV = torch.device("cuda:0")
+CB = nf4.nf4_build_codebook()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def d16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def h16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64(bits):
+    return oracle.bf16_to_f32(bits).astype(np.float64)
+
+
+def check_tol(name, got, ref):
+    rf, ma = oracle.rel_fro(got, ref), oracle.max_abs_ratio(got, ref)
+    _say(f"  {name}: rel_fro {rf:.3e}  max_abs/max|ref| {ma:.3e}")
+    assert rf <= oracle.REL_FRO_TOL, (name, rf)
+    assert ma <= oracle.MAX_ABS_TOL, (name, ma)
+
+
+class Layer:
+    """One QLoRA linear of a workload: device NF4 weight + adapters, and the oracle's bf16 deq(W)."""
+
+    def __init__(self, wl, lin):
+        W = synth.weight_f32(wl, lin)
+        l1, l2 = synth.lora_f32(wl, lin)
+        self.L1, self.L2 = synth.to_bf16_bits(l1), synth.to_bf16_bits(l2)
+        self.w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
+        self.q = oracle.quantize_dq(W, CB)
+        self.Wd = oracle.dequant_weight(self.q, CB)        # bf16 bits [N, K]
+        self.dL1d, self.dL2d = d16(self.L1), d16(self.L2)
+        self.N, self.K = lin.N, lin.K
+
+
+def _rows(M, n=32, seed=11):
+    r = np.random.default_rng(seed).choice(M, n, replace=False)
+    return np.unique(np.concatenate([r, [0, M - 1]]))
+
+
+def _check_fwd(name, layer, Xbits, Ygpu, s, rows):
+    Yr, _ = oracle.forward(Xbits[rows], layer.Wd, layer.L1, layer.L2, s)
+    check_tol(f"{name} Y[rows]", Ygpu[rows].astype(np.float64), Yr)
+
+
+def _check_bwd(name, layer, dYbits, Xbits, dXgpu, dL1gpu, dL2gpu, s, rows):
+    """dX on sampled rows, dL1 and dL2 in full (they reduce over every token)."""
+    X, dY = f64(Xbits), f64(dYbits)
+    L1, L2 = f64(layer.L1), f64(layer.L2)
+    T = X @ L1
+    dT = s * (dY @ L2.T)
+    check_tol(f"{name} dL2", dL2gpu, s * (T.T @ dY))
+    check_tol(f"{name} dL1", dL1gpu, X.T @ dT)
+    if dXgpu is not None:
+        dXr = dY[rows] @ f64(layer.Wd) + dT[rows] @ L1.T
+        check_tol(f"{name} dX[rows]", dXgpu[rows], dXr)
+
+
+def test_llama7b_mlp_chain():
+    """C3: gate, up (11008 x 4096), SwiGLU, down (4096 x 11008); 4096 tokens, r = 64."""
+    wl = synth.WORKLOADS["llama7b_mlp"]
+    M, s = wl.M, wl.scale
+    gate, up, down = (Layer(wl, lin) for lin in wl.linears)
+    _say(f"{wl.name}: M={M}, gate/up {gate.N}x{gate.K}, down {down.N}x{down.K}")
+    X = synth.to_bf16_bits(synth.x_f32(wl, M=M, K=gate.K))
+    dY = synth.to_bf16_bits(synth.dy_f32(wl, M, down.N))
+    Xd, dYd = d16(X), d16(dY)
+
+    G, Tg = nf4.qlora_linear_fwd(gate.w, Xd, gate.dL1d, gate.dL2d, s)
+    U, Tu = nf4.qlora_linear_fwd(up.w, Xd, up.dL1d, up.dL2d, s)
+    H = nf4.qlora_swiglu_fwd(G, U)
+    Y, Td = nf4.qlora_linear_fwd(down.w, H, down.dL1d, down.dL2d, s)
+    dH, dL1_down, dL2_down = nf4.qlora_linear_bwd(down.w, dYd, H, down.dL1d, down.dL2d, Td, s)
+    dG, dU = nf4.qlora_swiglu_bwd(dH, G, U)
+    dX, dL1_gate, dL2_gate = nf4.qlora_linear_bwd(gate.w, dG, Xd, gate.dL1d, gate.dL2d, Tg, s)
+    _, dL1_up, dL2_up = nf4.qlora_linear_bwd(up.w, dU, Xd, up.dL1d, up.dL2d, Tu, s, dX=dX,
+                                             accumulate=True)
+    torch.cuda.synchronize()
+
+    rows = _rows(M)
+    Gb, Ub, Hb, dHb, dGb, dUb = (h16(t) for t in (G, U, H, dH, dG, dU))
+    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    _check_fwd("gate", gate, X, to64(G), s, rows)
+    _check_fwd("up", up, X, to64(U), s, rows)
+    check_tol("swiglu h[rows]", to64(H)[rows], oracle.swiglu_fwd(Gb[rows], Ub[rows]))
+    _check_fwd("down", down, Hb, to64(Y), s, rows)
+    _check_bwd("down", down, dY, Hb, to64(dH), to64(dL1_down), to64(dL2_down), s, rows)
+    rg, ru = oracle.swiglu_bwd(dHb[rows], Gb[rows], Ub[rows])
+    check_tol("swiglu dg[rows]", to64(dG)[rows], rg)
+    check_tol("swiglu du[rows]", to64(dU)[rows], ru)
+    # gate and up adapters in full; dX = both branches summed
+    _check_bwd("gate", gate, dGb, X, None, to64(dL1_gate), to64(dL2_gate), s, rows)
+    _check_bwd("up", up, dUb, X, None, to64(dL1_up), to64(dL2_up), s, rows)
+    dX_ref = 0.0
+    for layer, dYb in ((gate, dGb), (up, dUb)):
+        dYl = f64(dYb)
+        dT = s * (dYl[rows] @ f64(layer.L2).T)
+        dX_ref = dX_ref + dYl[rows] @ f64(layer.Wd) + dT @ f64(layer.L1).T
+    check_tol("dX[rows] (gate + up)", to64(dX)[rows], dX_ref)
+
+
+def test_llama65b_heavy_tail_layer():
+    """C4 gate (22016 x 8192, 1 % heavy-tailed entries): storage bit-exact, then one layer's
+    forward and backward on 2048 tokens."""
+    wl = synth.WORKLOADS["llama65b_mlp"]
+    lin = wl.linears[0]
+    M, s = wl.M, wl.scale
+    _say(f"{wl.name} {lin.name}: {lin.N}x{lin.K}, M={M}")
+    layer = Layer(wl, lin)
+    w = layer.w
+    assert np.array_equal(w.packed.cpu().numpy(), layer.q["packed"])
+    assert np.array_equal(w.absmax_q.cpu().numpy(), layer.q["codes"])
+    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), layer.q["scales"].view(np.uint32))
+    assert np.array_equal(w.absmax_mean.cpu().numpy().view(np.uint32),
+                          np.asarray([layer.q["mean"]], np.float32).view(np.uint32))
+    assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(layer.Wd.shape), layer.Wd)
+
+    X = synth.to_bf16_bits(synth.x_f32(wl, M=M, K=lin.K))
+    dY = synth.to_bf16_bits(synth.dy_f32(wl, M, lin.N))
+    Xd, dYd = d16(X), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, layer.dL1d, layer.dL2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, layer.dL1d, layer.dL2d, T, s)
+    torch.cuda.synchronize()
+    rows = _rows(M)
+    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    _check_fwd(lin.name, layer, X, to64(Y), s, rows)
+    _check_bwd(lin.name, layer, dY, X, to64(dX), to64(dL1), to64(dL2), s, rows)
