@@ -32,6 +32,33 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 
+# HBM traffic of the fused GEMMs at the llama7b_attn workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+#   python bench.py --steps 3 --warmup 1 --no-gemv --no-cpu-baseline
+# scaled by what the same counters read for a plain copy of exactly 1 GiB
+# (python bench.py --copy-calibration: FETCH_SIZE 524301 KiB, WRITE_SIZE 1048576 KiB), i.e.
+# FETCH_SIZE counts half the bytes read on this GPU.  Valid only for the kernel sources they were
+# taken on: if the hashed sources differ, traffic is reported as null.
+FETCH_SCALE = 1048576.0 / 524301.3
+WRITE_SCALE = 1048576.0 / 1048576.0
+GEMM_TRAFFIC_KIB = {0: (52707.8, 32870.1), 1: (52697.5, 32882.4)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
+GEMM_TRAFFIC_SOURCES = {
+    "csrc/dqgemm.hip": "061c7ef11103c55a5be27d496390223422c22ed931f2e8e293076cc3b39c0d0b",
+    "csrc/common.h": "3975181d65e4c262f2112e4e2d21fc7735ca999cfcefb5d48a6ef191879916d6",
+}
+
+
+def gemm_traffic_bytes(kind):
+    """Calibrated HBM bytes per launch of the fused GEMM of this kind, or None if stale."""
+    import hashlib
+    pkg = os.path.join(ROOT, "bit_nf4_quantized_codebook_amd")
+    for rel, digest in GEMM_TRAFFIC_SOURCES.items():
+        with open(os.path.join(pkg, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    fetch, write = GEMM_TRAFFIC_KIB[kind]
+    return int(round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024))
+
 
 def linear_flops(M, N, K, r):
     """Algorithmic flops of one forward + backward of the layer (2 per multiply-add)."""
@@ -159,6 +186,9 @@ def main():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of exactly 1 GiB, 5 times (the reference kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -176,6 +206,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
     if args.gemv_only:
         print(json.dumps({"gemv": bench_gemv(torch, nf4, synth, dev)}), flush=True)
         return
@@ -219,7 +258,11 @@ def main():
     achieved = flops_launch / (means[dom] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic_bytes(dom),
+        # operand reads + output write of one launch (bwd: dY, W, dT, L1 -> dX; fwd: X, W, sT, L2 -> Y)
+        "traffic_algorithmic": ((M * N * 2 if dom == 1 else M * K * 2) + N * K // 2 + N * K // 64 +
+                                (N * K // 64 + 255) // 256 * 4 + 4 + M * r * 2 +
+                                (K * r * 2 + M * K * 2 if dom == 1 else r * N * 2 + M * N * 2)),
         "kernel": "dqgemm_kernel<" + ("true" if dom == 1 else "false") + "> (" +
                   ("backward dX" if dom == 1 else "forward Y") + ")",
         "avg_launch_us": round(means[dom] * 1e3, 2),
