@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 
-# HBM traffic of the fused GEMMs at the llama7b_attn workload, from two rocprofv3 --pmc runs
+# HBM traffic of the GEMMs at the llama7b_attn workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
 #   python bench.py --steps 3 --warmup 1 --no-gemv --no-cpu-baseline
 # scaled by what the same counters read for a plain copy of exactly 1 GiB
@@ -41,16 +41,15 @@ METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 # taken on: if the hashed sources differ, traffic is reported as null.
 FETCH_SCALE = 1048576.0 / 524301.3
 WRITE_SCALE = 1048576.0 / 1048576.0
-GEMM_TRAFFIC_KIB = {0: (52707.8, 32870.1), 1: (52697.5, 32882.4)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
-GEMM_TRAFFIC_SOURCES = {
-    "csrc/dqgemm.hip": "061c7ef11103c55a5be27d496390223422c22ed931f2e8e293076cc3b39c0d0b",
-    "csrc/common.h": "3975181d65e4c262f2112e4e2d21fc7735ca999cfcefb5d48a6ef191879916d6",
-}
+GEMM_TRAFFIC_KIB = {}   # kind -> (FETCH_SIZE, WRITE_SIZE); empty: not measured on these sources
+GEMM_TRAFFIC_SOURCES = {}
 
 
 def gemm_traffic_bytes(kind):
-    """Calibrated HBM bytes per launch of the fused GEMM of this kind, or None if stale."""
+    """Calibrated HBM bytes per launch of the GEMM of this kind, or None if stale or unmeasured."""
     import hashlib
+    if kind not in GEMM_TRAFFIC_KIB:
+        return None
     pkg = os.path.join(ROOT, "bit_nf4_quantized_codebook_amd")
     for rel, digest in GEMM_TRAFFIC_SOURCES.items():
         with open(os.path.join(pkg, rel), "rb") as f:
@@ -68,7 +67,7 @@ def linear_flops(M, N, K, r):
 
 
 def gemm_launch_flops(kind, M, N, K, r):
-    """Algorithmic flops of one fused dequant-GEMM launch (main product + LoRA extension)."""
+    """Algorithmic flops of one GEMM launch (main product + LoRA extension)."""
     return 2 * M * N * K + (2 * M * r * N if kind == 0 else 2 * M * r * K)
 
 
@@ -259,12 +258,12 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic_bytes(dom),
-        # operand reads + output write of one launch (bwd: dY, W, dT, L1 -> dX; fwd: X, W, sT, L2 -> Y)
-        "traffic_algorithmic": ((M * N * 2 if dom == 1 else M * K * 2) + N * K // 2 + N * K // 64 +
-                                (N * K // 64 + 255) // 256 * 4 + 4 + M * r * 2 +
+        # operand reads + output write of one launch (bwd: dY, W^T bf16, dT, L1 -> dX; fwd: X, W bf16,
+        # sT, L2 -> Y); at this token count the weight is expanded to bf16 by a pass of its own
+        "traffic_algorithmic": ((M * N * 2 if dom == 1 else M * K * 2) + N * K * 2 + M * r * 2 +
                                 (K * r * 2 + M * K * 2 if dom == 1 else r * N * 2 + M * N * 2)),
-        "kernel": "dqgemm_kernel<" + ("true" if dom == 1 else "false") + "> (" +
-                  ("backward dX" if dom == 1 else "forward Y") + ")",
+        "kernel": "gemm_bf16_kernel<" + ("true" if dom == 1 else "false") + "> (" +
+                  ("backward dX" if dom == 1 else "forward Y") + ", bf16-expanded weight)",
         "avg_launch_us": round(means[dom] * 1e3, 2),
         "flops_per_launch": flops_launch,
         "launches_timed": len(per_kind[dom]),

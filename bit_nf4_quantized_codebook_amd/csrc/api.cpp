@@ -117,10 +117,17 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 constexpr int64_t kTile = 64;
 constexpr int64_t kDecodeMaxM = 4;    // token counts served by the table-decode GEMV
 constexpr int64_t kGemvMaxM = 16;     // token counts served by a weight-streaming GEMV
+// From this many tokens on, the weight is expanded to bf16 once per call and multiplied by a plain
+// bf16 GEMM: the expansion pass costs about 2.5 bytes of HBM traffic per weight, while dequantizing
+// inside the GEMM repeats the work once per 256-row tile of tokens and its VALU work does not hide
+// under the MFMAs on gfx950.
+constexpr int64_t kExpandMinM = 1024;
+// the bf16 copy of the weight is addressed with 32-bit byte offsets
+bool use_expand(int64_t M, int64_t N, int64_t K) { return M >= kExpandMinM && N * K * 2 < ((int64_t)1 << 31); }
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
-    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, total;
+    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, off_Wd, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -141,7 +148,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     pmax = pmax > (size_t)p.msL2 * r * N ? pmax : (size_t)p.msL2 * r * N;
     pmax = pmax > (size_t)p.msL1 * K * r ? pmax : (size_t)p.msL1 * K * r;
     p.off_P = off;   off += round256(pmax * 4);
-    p.off_Yp = p.off_Tp = off;
+    p.off_Yp = p.off_Tp = p.off_Wd = off;
+    if (use_expand(M, N, K)) {
+        p.off_Wd = off;  off += round256((size_t)N * K * 2);
+    }
     if (M <= kDecodeMaxM) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
@@ -303,9 +313,14 @@ int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
     if (!aligned16(out_bf16)) return fail(NF4_ERR_ALIGN, "out_bf16 must be 16-byte aligned");
     const int64_t numel = w->rows * w->cols;
     if (numel % 2) return fail(NF4_ERR_SHAPE, "rows*cols must be even");
-    NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, numel,
-                                       w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
-                  "dequant");
+    if (numel % 64 == 0)   // whole blocks: the table-lookup expansion
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, out_bf16,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                      "dequant");
+    else
+        NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, numel,
+                                           w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
+                      "dequant");
     return NF4_OK;
 }
 
@@ -337,10 +352,15 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
-    if (M <= kGemvMaxM)
+    if (M <= kGemvMaxM) {
         NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
-    else
+    } else if (use_expand(M, N, K)) {
+        uint16_t *Wd = ws_at<uint16_t>(workspace, p.off_Wd);
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, s), "weight expansion");
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
+    } else {
         NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
+    }
     return NF4_OK;
 }
 
@@ -382,10 +402,17 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr, s),
                   "dL1 reduce");
     // dX = dY deq(W) + dT L1^T
-    if (dX)
+    if (dX && use_expand(M, N, K)) {
+        uint16_t *WdT = ws_at<uint16_t>(workspace, p.off_Wd);
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/true, WdT, s), "weight expansion");
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd(dY, WdT, dT, L1, r, M, N, K, dX,
+                                                 (flags & QLORA_DX_ACCUMULATE) != 0, s),
+                      "bf16 GEMM (bwd)");
+    } else if (dX) {
         NF4_CHECK_HIP(nf4k::launch_dqgemm_bwd(view_of(w), dY, dT, L1, r, M, dX,
                                               (flags & QLORA_DX_ACCUMULATE) != 0, s),
                       "fused dequant GEMM (bwd)");
+    }
     return NF4_OK;
 }
 

@@ -1,0 +1,307 @@
+// K-extended bf16 MFMA GEMM of the QLoRA linear layer at large token counts (gfx950):
+//   C = [A | Ae] . [B | Be]^T         (optionally C += ...)
+//   forward : A = X [M, K],  B = deq(W) [N, K],  Ae = sT [M, r],  Be^T = L2 [r, N]
+//   backward: A = dY [M, N], B = deq(W)^T [K, N], Ae = dT [M, r], Be = L1 [K, r]
+// B is the frozen weight after the double dequantization to bf16, written by a separate pass
+// (row-major for the forward, transposed for the backward), so both products read B with the
+// reduction index contiguous.
+//
+// Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
+// section 3.5 eq. (5) (forward: the BF16 weight from eq. (6) times X, plus the LoRA term) and the
+// backward description (gradient to X through the BF16 weight); section 4 eq. (3) (scalar s).
+//
+// Block tile 256 x 256 outputs, reduction step 64, 4 waves in 2 x 2, each 128 x 128 with
+// v_mfma_f32_32x32x16_bf16 (16 tiles, 256 fp32 accumulators).  Both operands go straight from
+// global memory to LDS (buffer_load ... lds: no registers, no ds_write), two 32 KB stages each,
+// 128-byte rows whose 16-byte chunks are XOR-swizzled by (row / 2) so the fragment reads are
+// bank-conflict free.  The LoRA product is appended as r/64 more reduction steps.
+
+#include "common.h"
+#include "dqtile.h"
+#include "launch.h"
+
+namespace nf4k {
+
+namespace {
+
+constexpr int TM = 256;
+constexpr int TN = 256;
+constexpr int TK = 64;
+constexpr int NTHREADS = 256;
+constexpr int STAGE = TM * TK * 2;          // 32 KB per operand stage
+constexpr int EXT_ROWB = (TN / 2 + 16) * 2; // forward LoRA B tile: two halves [64 j][128 n + 16]
+
+struct GemmArgs {
+    const uint16_t *A;    // [M, Kred]
+    const uint16_t *B;    // [Nout, Kred]
+    const uint16_t *Ae;   // [M, r]
+    const uint16_t *Be;   // forward: L2 [r, Nout]; backward: L1 [Nout, r]
+    uint16_t *C;          // [M, Nout]
+    int64_t M, Nout, Kred;
+    int32_t r;
+    uint32_t accumulate;
+};
+
+template <bool BWD>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
+    // one LDS object per stage: a fragment read of one stage provably never aliases the
+    // direct-to-LDS loads in flight into the other
+    __shared__ __align__(16) uint8_t As0[STAGE];
+    __shared__ __align__(16) uint8_t As1[STAGE];
+    __shared__ __align__(16) uint8_t Bs0[STAGE];
+    __shared__ __align__(16) uint8_t Bs1[STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, hh = lane >> 5;
+
+    const int ntm = (int)((g.M + TM - 1) / TM);
+    const int ntn = (int)((g.Nout + TN - 1) / TN);
+    int tm, tn;
+    tile_coords(ntm, ntn, tm, tn);
+    const int64_t m0 = (int64_t)tm * TM;
+    const int64_t n0 = (int64_t)tn * TN;
+    const int main_steps = (int)((g.Kred + TK - 1) / TK);
+    const int ext_steps = (g.r + TK - 1) / TK;
+
+    // tile-relative descriptors: rows past M (or Nout) read zeros
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + m0 * g.Kred, (g.M - m0) * g.Kred * 2);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + n0 * g.Kred, (g.Nout - n0) * g.Kred * 2);
+
+    // ---- loads: instruction q of wave w writes stage rows 8u .. 8u+7 (u = 8w + q); lane l
+    // takes row 8u + l/8 and physical chunk l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
+    // (row/2) % 8 = (4q + l/16) % 8: the lane's column depends only on the parity of q. ----
+    int a_col[2];
+    uint32_t voff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = 8 * (8 * wave + q) + (lane >> 3);
+        a_col[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+        voff[q] = (uint32_t)(((lane >> 3) * g.Kred + a_col[q]) * 2);
+    }
+    const uint32_t wave_off = (uint32_t)(64 * wave * g.Kred * 2);
+    const uint32_t row8_off = (uint32_t)(8 * g.Kred * 2);
+    const int kred32 = (int)g.Kred;
+    // Columns at or past Kred (a ragged last step, or the steps past the end) read zeros.  The
+    // whole offset sits in the lane offset (the scalar offset is 0), so rows past the end of the
+    // operand are out of range for the descriptor's bound check.
+    auto load = [&](__amdgpu_buffer_rsrc_t r, int step, uint8_t *st) {
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        lds_u8 *dst = (lds_u8 *)st + wave * 8192;
+        const int rem = kred32 - step * TK;
+        const uint32_t base = wave_off + (uint32_t)step * (TK * 2);
+        const uint32_t v0 = a_col[0] < rem ? voff[0] + base : 0x80000000u;
+        const uint32_t v1 = a_col[1] < rem ? voff[1] + base : 0x80000000u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t v = ((q & 1) ? v1 : v0) + (uint32_t)q * row8_off;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + q * 1024), 16, v, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // fragment of sub-step s (16 reduction elements): lane (r32, hh) takes elements
+    // 16 s + 8 hh .. +7 of its row; (row/2) % 8 = (r32/2) % 8 for every 32-row group
+    uint32_t lds_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) lds_off[s] = (uint32_t)(r32 * 128 + (((2 * s + hh) ^ ((r32 >> 1) & 7)) * 16));
+    struct Frags {
+        bf16x8 a[4], b[4];
+    };
+    auto read = [&](const uint8_t *Ast, const uint8_t *Bst, int s, Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *reinterpret_cast<const bf16x8 *>(Ast + lds_off[s] + (wm * 128 + 32 * i) * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            f.b[j] = *reinterpret_cast<const bf16x8 *>(Bst + lds_off[s] + (wn * 128 + 32 * j) * 128);
+    };
+    auto mma = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    // one step: compute stages (Ac, Bc) while the next step streams into (An, Bn); fragment
+    // reads run one sub-step ahead of the MFMAs
+    auto step_body = [&](int step, const uint8_t *Ac, const uint8_t *Bc, uint8_t *An, uint8_t *Bn) {
+        load(rA, step + 1, An);
+        load(rB, step + 1, Bn);
+        Frags f0, f1;
+        read(Ac, Bc, 0, f0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Frags &cur = (s & 1) ? f1 : f0;
+            Frags &nxt = (s & 1) ? f0 : f1;
+            if (s < 3) read(Ac, Bc, s + 1, nxt);
+            mma(cur);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next step landed (this wave's loads) and this wave's fragment reads are done
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8));
+        __syncthreads();
+    };
+
+    load(rA, 0, As0);
+    load(rB, 0, Bs0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int step = 0;
+    for (; step + 1 < main_steps; step += 2) {
+        step_body(step, As0, Bs0, As1, Bs1);
+        step_body(step + 1, As1, Bs1, As0, Bs0);
+    }
+    if (step < main_steps) step_body(step, As0, Bs0, As1, Bs1);   // odd count: the last one
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- LoRA extension: r/64 more steps (zero padded past r) ----
+    //   A tile: Ae rows m0.., columns j (same swizzled layout, straight to LDS), in As0
+    //   forward : Be^T = L2 [r, Nout]: rows j, columns n -> two halves [64 j][128 + 16] in
+    //             Bs0 / Bs1, transposing fragment reads
+    //   backward: Be = L1 [Nout, r]: rows n, columns j -> swizzled layout in Bs0, row reads
+    if (ext_steps > 0) {
+        const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
+        const __amdgpu_buffer_rsrc_t rBe = BWD ? make_rsrc(g.Be + n0 * g.r, (g.Nout - n0) * (int64_t)g.r * 2)
+                                               : make_rsrc(g.Be, (int64_t)g.r * g.Nout * 2);
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        for (int e = 0; e < ext_steps; ++e) {
+            const int j0 = e * TK;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = 8 * (8 * wave + q) + (lane >> 3);
+                const int jj = j0 + a_col[q & 1];
+                const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe, (lds_void *)((lds_u8 *)As0 + wave * 8192 + q * 1024),
+                                                         16, off, 0, 0, 0);
+                if (BWD)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rBe, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
+                                                             16, off, 0, 0, 0);
+            }
+            if (!BWD) {
+                // L2 rows j0 .. j0+63, columns n0 .. n0+255: 16-byte chunks through registers
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int jr = (tid >> 5) + 8 * q, ch = tid & 31;
+                    const int64_t col = n0 + ch * 8;
+                    const bool ok = j0 + jr < g.r && col < g.Nout;
+                    const u32x4 v = bload16(rBe, ok ? (uint32_t)(((int64_t)(j0 + jr) * g.Nout + col) * 2) : 0x80000000u);
+                    uint8_t *Bh = (ch < 16) ? Bs0 : Bs1;
+                    *reinterpret_cast<u32x4 *>(Bh + jr * EXT_ROWB + (ch & 15) * 16) = v;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                Frags f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f.a[i] = *reinterpret_cast<const bf16x8 *>(As0 + lds_off[s] + (wm * 128 + 32 * i) * 128);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (BWD) {
+                        f.b[j] = *reinterpret_cast<const bf16x8 *>(Bs0 + lds_off[s] + (wn * 128 + 32 * j) * 128);
+                    } else {
+                        // 16-lane group (hh, half): lane i reads rows 16 s + 8 hh + i/4 (+4),
+                        // columns c0 + 4 (i%4) .. +3; after the transpose lane i holds column c0 + i
+                        const int i16 = lane & 15, half = (lane >> 4) & 1;
+                        const uint8_t *Bh = wn ? Bs1 : Bs0;
+                        const int c0 = 32 * j + 16 * half;
+                        const int rowb = 16 * s + 8 * hh + (i16 >> 2);
+                        const uint8_t *base = Bh + (c0 + 4 * (i16 & 3)) * 2;
+                        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * EXT_ROWB));
+                        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * EXT_ROWB));
+                        const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        f.b[j] = __builtin_bit_cast(bf16x8, v);
+                    }
+                }
+                mma(f);
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: fp32 -> bf16.  Lane (r32, hh) of tile (i, j) holds column
+    // wn*128 + 32 j + r32 and rows wm*128 + 32 i + 8 (v/4) + 4 hh + v%4 ----
+    if (!g.accumulate) {
+        const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
+        const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh * 4) * row_bytes) + (uint32_t)((n0 + wn * 128 + r32) * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (n0 + wn * 128 + j * 32 + r32 >= g.Nout) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    const uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
+                    const uint32_t soff = rows * row_bytes;
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rC, lane_off + j * 64, soff, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rC, lane_off + j * 64,
+                                                          soff + row_bytes, 0);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + wn * 128 + j * 32 + r32;
+                if (col >= g.Nout) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                    if (row < g.M) {
+                        uint16_t *p = g.C + row * g.Nout + col;
+                        *p = (uint16_t)f32_to_bf16(acc[i][j][v] + bf16_to_f32(*p));
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <bool BWD>
+hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
+    const int ntm = (int)((a.M + TM - 1) / TM);
+    const int ntn = (int)((a.Nout + TN - 1) / TN);
+    timing_before(stream, BWD ? 1 : 0);
+    hipLaunchKernelGGL(gemm_bf16_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    timing_after(stream);
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream) {
+    GemmArgs a;
+    a.A = X; a.B = Wd; a.Ae = sT; a.Be = L2; a.C = Y;
+    a.M = M; a.Nout = N; a.Kred = K; a.r = r; a.accumulate = 0;
+    return launch_impl<false>(a, stream);
+}
+
+hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
+                                hipStream_t stream) {
+    GemmArgs a;
+    a.A = dY; a.B = WdT; a.Ae = dT; a.Be = L1; a.C = dX;
+    a.M = M; a.Nout = K; a.Kred = N; a.r = r; a.accumulate = accumulate ? 1u : 0u;
+    return launch_impl<true>(a, stream);
+}
+
+}  // namespace nf4k

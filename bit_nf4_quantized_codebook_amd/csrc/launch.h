@@ -39,6 +39,14 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r);
 hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                            float scale, int32_t r, int64_t M, uint16_t *Y, uint16_t *T_out, float *Yp,
                            float *Tp, hipStream_t stream);
+// large token counts: the weight is expanded to bf16 once per call (rows [N, K] for the forward,
+// transposed [K, N] for the backward), then a K-extended bf16 GEMM
+hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, hipStream_t stream);
+hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
+hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
+                                hipStream_t stream);
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
                              bool accumulate, hipStream_t stream);

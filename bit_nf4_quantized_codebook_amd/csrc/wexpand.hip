@@ -1,0 +1,111 @@
+// Double dequantization of the whole frozen weight to bf16, as the operand of the bf16 GEMM used
+// at large token counts (gfx950).  Two layouts:
+//   rows:       out [N, K] = deq(W)      (the forward reads W rows along the reduction)
+//   transposed: out [K, N] = deq(W)^T    (the backward reduces over N)
+//
+// Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
+// section 3.5 eq. (6): w = bf16(cb[code] * a'), a' = fma(e4m3(c2), c1, mean), one rounding.
+//
+// Each 64-weight block builds its 16-entry bf16 table once (16 products, 8 conversions) and
+// expands its codes with v_perm_b32 byte selects; the kernels are bound by HBM (0.5 B read and
+// 2 B written per weight).
+
+#include "common.h"
+#include "dqtile.h"
+#include "launch.h"
+
+namespace nf4k {
+
+namespace {
+
+struct ExpandArgs {
+    const uint8_t *packed;
+    const uint8_t *c2;
+    const float *c1;
+    const float *mean;
+    uint16_t *out;
+    int64_t N, K;
+    Codebook cb;
+};
+
+// Row layout: 8 lanes per block, one packed dword (8 weights) each, so a wave reads 256
+// contiguous packed bytes and writes 1 KB of contiguous bf16 per store.  The 8 lanes of a block
+// each build its table (the kernel is bound by HBM, not VALU).  Blocks run over the row-major
+// flattening, so this needs only N*K % 64 == 0.
+__global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
+    const int64_t nwords = (g.N * g.K) >> 3;
+    const float mean = g.mean[0];
+    for (int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x; wi < nwords; wi += (int64_t)gridDim.x * 256) {
+        const int64_t b = wi >> 3;
+        const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g.packed) + wi);
+        const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean));
+        __builtin_nontemporal_store(dequant8(t, w), reinterpret_cast<u32x4 *>(g.out) + wi);
+    }
+}
+
+// Transposed layout, one 64 x 64 tile (64 W rows n0.., one block column kb) per workgroup:
+// thread t expands 16 weights of row n0 + t/4 (columns 16 (t%4) ..) into an LDS tile [k][n],
+// then writes 16 consecutive n of one output row k.
+constexpr int TROW = 64 + 8;   // LDS row (k) length in bf16, padded
+__global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
+    __shared__ uint16_t tile[64 * TROW];
+    const int tid = threadIdx.x;
+    const int64_t nbk = g.K >> 6;
+    const int64_t ntn = (g.N + 63) >> 6;
+    const int64_t kb = blockIdx.x / ntn;
+    const int64_t n0 = (blockIdx.x % ntn) * 64;
+    const float mean = g.mean[0];
+    {
+        const int nl = tid >> 2, q = tid & 3;
+        const int64_t n = n0 + nl;
+        uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (n < g.N) {
+            const int64_t b = n * nbk + kb;
+            const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean));
+            const uint2 w = *reinterpret_cast<const uint2 *>(g.packed + b * 32 + q * 8);
+            const u32x4 lo = dequant8(t, w.x), hi = dequant8(t, w.y);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tile[(16 * q + e) * TROW + nl] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    {
+        const int kl = tid >> 2, q = tid & 3;
+        const int64_t k = kb * 64 + kl;
+        const int64_t n = n0 + 16 * q;
+        const u32x4 *s = reinterpret_cast<const u32x4 *>(tile + kl * TROW + 16 * q);
+        const u32x4 a = s[0], c = s[1];
+        uint16_t *dst = g.out + k * g.N + n;
+        if (n + 16 <= g.N) {
+            __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(dst));
+            __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(dst) + 1);
+        } else {
+            // N % 8 == 0: the last tile ends on an 8-column boundary
+            if (n < g.N) __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(dst));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, hipStream_t stream) {
+    ExpandArgs a;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.out = out; a.N = w.rows; a.K = w.cols;
+    for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
+    if (!transposed) {
+        const int64_t nwords = (w.rows * w.cols) >> 3;
+        int64_t grid = (nwords + 255) / 256;
+        if (grid > 256 * 64) grid = 256 * 64;
+        if (grid < 1) grid = 1;
+        hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    } else {
+        const int64_t tiles = ((w.rows + 63) / 64) * (w.cols / 64);
+        hipLaunchKernelGGL(expand_transposed_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace nf4k

@@ -165,6 +165,10 @@ SHAPES = [
     (3, 200, 1344, 16),        # decode-size path: ragged K (not a multiple of 256 or 1024)
     (16, 72, 2112, 64),
     (2, 1032, 3072, 8),
+    # from 1024 tokens on: bf16 expansion of the weight + K-extended bf16 GEMM
+    (1024, 520, 384, 16),      # ragged N (the backward's reduction), odd number of K steps
+    (1100, 264, 640, 24),      # ragged M and N
+    (1040, 1032, 320, 128),    # two LoRA extension steps
 ]
 
 
@@ -198,6 +202,30 @@ def test_linear_fwd_bwd_parity(M, N, K, r):
     nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s, dX=acc, accumulate=True)
     torch.cuda.synchronize()
     check_tol("dX+=", f32(acc), g["dX"] + f32(base))
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 520, 384), (1088, 264, 1024), (300, 264, 256)])
+def test_one_hot_rows_select_the_weight_bit_exact(M, N, K):
+    """L2 = 0 and one-hot activations: every output is one dequantized weight times 1.0 plus exact
+    zeros, so the forward gives deq(W)^T and the backward deq(W) bit for bit.  From 1024 tokens this
+    pins the bf16 expansion of the weight in both layouts (rows for the forward, transposed for the
+    backward) through the GEMMs; below it, the fused dequantization."""
+    _say(f"one-hot M={M} N={N} K={K}")
+    r, s = 16, 0.5
+    w, Wd, _, L1, L2, _ = _make_layer(M, N, K, r, seed=500 + M, zero_l2=True)
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(min(M, K)), np.arange(min(M, K))] = 1.0
+    dY = np.zeros((M, N), np.float32)
+    dY[np.arange(min(M, N)), np.arange(min(M, N))] = 1.0
+    Xd, dYd = d16(synth.to_bf16_bits(X)), d16(synth.to_bf16_bits(dY))
+    Y, T = nf4.qlora_linear_fwd(w, Xd, d16(L1), d16(L2), s)
+    dX, _, _ = nf4.qlora_linear_bwd(w, dYd, Xd, d16(L1), d16(L2), T, s)
+    torch.cuda.synchronize()
+    Wd2 = Wd.reshape(N, K)
+    k, n = min(M, K), min(M, N)
+    assert np.array_equal(h16(Y)[:k], Wd2.T[:k])
+    assert not h16(Y)[k:].any()
+    assert np.array_equal(h16(dX)[:n], Wd2[:n])
 
 
 @pytest.mark.parametrize("M,N,K,r", [(64, 256, 256, 8), (40, 520, 384, 16)])
