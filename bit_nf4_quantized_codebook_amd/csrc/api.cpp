@@ -145,8 +145,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     p.off_dT = off;  off += round256((size_t)M * r * 2);
     size_t pmax = (size_t)p.ksT * M * r;
     pmax = pmax > (size_t)p.ksdT * M * r ? pmax : (size_t)p.ksdT * M * r;
-    pmax = pmax > (size_t)p.msL2 * r * N ? pmax : (size_t)p.msL2 * r * N;
-    pmax = pmax > (size_t)p.msL1 * K * r ? pmax : (size_t)p.msL1 * K * r;
+    // dL2 and dL1 run in one launch: their partials sit side by side
+    const size_t ptn = (size_t)p.msL2 * r * N + (size_t)p.msL1 * K * r;
+    pmax = pmax > ptn ? pmax : ptn;
     p.off_P = off;   off += round256(pmax * 4);
     p.off_Yp = p.off_Tp = p.off_Wd = off;
     if (use_expand(M, N, K)) {
@@ -187,8 +188,8 @@ int compute_T(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32
               uint16_t *T_out, uint16_t *sT_out, const Plan &p, void *ws, hipStream_t s) {
     float *P = ws_at<float>(ws, p.off_P);
     NF4_CHECK_HIP(nf4k::launch_skinny_nt(X, L1, /*b_rows_k=*/true, P, M, r, K, p.ksT, s), "T = X L1");
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksT, M * r, 1.0f, T_out, scale, sT_out, s),
-                  "T reduce");
+    const nf4k::Reduction red{P, p.ksT, M * r, 1.0f, T_out, scale, sT_out};
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red, nullptr, s), "T reduce");
     return NF4_OK;
 }
 
@@ -392,15 +393,17 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     }
     // dT = s dY L2^T  (L2 [r, N] is already the row-major transpose the product needs)
     NF4_CHECK_HIP(nf4k::launch_skinny_nt(dY, L2, /*b_rows_k=*/false, P, M, r, N, p.ksdT, s), "dT = dY L2^T");
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.ksdT, M * r, scale, dT, 0.0f, nullptr, s), "dT reduce");
-    // dL2 = s T^T dY
-    NF4_CHECK_HIP(nf4k::launch_skinny_tn(Tuse, dY, P, M, r, N, p.msL2, s), "dL2 = T^T dY");
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.msL2, (int64_t)r * N, scale, dL2, 0.0f, nullptr, s),
-                  "dL2 reduce");
-    // dL1 = X^T dT
-    NF4_CHECK_HIP(nf4k::launch_skinny_tn(X, dT, P, M, K, r, p.msL1, s), "dL1 = X^T dT");
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(P, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr, s),
-                  "dL1 reduce");
+    const nf4k::Reduction red_dT{P, p.ksdT, M * r, scale, dT, 0.0f, nullptr};
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dT, nullptr, s), "dT reduce");
+    // dL2 = s T^T dY and dL1 = X^T dT, independent: one launch for both products, one for both
+    // reductions (the partials side by side)
+    float *P1 = P + (size_t)p.msL2 * r * N;
+    const nf4k::TnProduct tn_dL2{Tuse, dY, P, r, N, p.msL2};
+    const nf4k::TnProduct tn_dL1{X, dT, P1, K, r, p.msL1};
+    NF4_CHECK_HIP(nf4k::launch_skinny_tn(tn_dL2, &tn_dL1, M, s), "dL2 = T^T dY, dL1 = X^T dT");
+    const nf4k::Reduction red_dL2{P, p.msL2, (int64_t)r * N, scale, dL2, 0.0f, nullptr};
+    const nf4k::Reduction red_dL1{P1, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr};
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
     // dX = dY deq(W) + dT L1^T
     if (dX && use_expand(M, N, K)) {
         uint16_t *WdT = ws_at<uint16_t>(workspace, p.off_Wd);

@@ -55,10 +55,27 @@ int choose_split(int64_t tiles, int64_t red_steps);
 // b_rows_k: B given as [Kred, R] (true) or as [R, Kred] (false)
 hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *B, bool b_rows_k, float *P, int64_t M,
                             int32_t R, int64_t Kred, int nsplit, hipStream_t stream);
-hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int64_t M, int64_t Pn,
-                            int64_t Qn, int nsplit, hipStream_t stream);
-hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
-                                  float s2, uint16_t *out2, hipStream_t stream);
+// P[ms] = U[rows ms, :]^T . V[rows ms, :] (U [M, Pn], V [M, Qn]); one launch for one product, or
+// two independent ones (b non-NULL)
+struct TnProduct {
+    const uint16_t *U, *V;
+    float *P;
+    int64_t Pn, Qn;
+    int nsplit;
+};
+hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream);
+// out = bf16(s1 * sum of the nsplit partials), out2 (optional) = bf16(s2 * same); one launch for one
+// or two reductions
+struct Reduction {
+    const float *P;
+    int nsplit;
+    int64_t n;
+    float s1;
+    uint16_t *out;
+    float s2;
+    uint16_t *out2;
+};
+hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream);
 
 // Optional per-thread timing events recorded on the launch stream right before and after each
 // instrumented launch (see nf4.h).

@@ -144,17 +144,37 @@ __global__ __launch_bounds__(256) void skinny_nt_kernel(const uint16_t *__restri
 
 // P[ms][p][q] = sum_{m in chunk ms} U[m][p] * V[m][q];  U [M, Pn], V [M, Qn] (row-major).
 // Both tiles are stored [m][p] / [m][q] and read with transposing fragment loads.
-__global__ __launch_bounds__(256) void skinny_tn_kernel(const uint16_t *__restrict__ U,
-                                                        const uint16_t *__restrict__ V,
-                                                        float *__restrict__ P, int64_t M, int64_t Pn,
-                                                        int64_t Qn, int64_t mchunk) {
+// One launch serves one or two independent products (the backward runs dL2 and dL1 together):
+// blocks [0, nb0) take product 0, the rest product 1; within a product, block b is tile
+// (b % tx, (b / tx) % ty) of reduction chunk b / (tx ty).
+struct TnProb {
+    const uint16_t *U, *V;
+    float *P;
+    int64_t Pn, Qn, mchunk;
+    int32_t tx, ty;
+};
+struct TnGroup {
+    TnProb p[2];
+    int64_t M;
+    uint32_t nb0;
+};
+__global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
     __shared__ __align__(16) uint8_t Us[NSTAGE][ST * ROWB];
     __shared__ __align__(16) uint8_t Vs[NSTAGE][ST * ROWB];
+    const int second = blockIdx.x >= grp.nb0;
+    const TnProb &pr = grp.p[second];
+    const uint16_t *__restrict__ U = pr.U;
+    const uint16_t *__restrict__ V = pr.V;
+    float *__restrict__ P = pr.P;
+    const int64_t M = grp.M, Pn = pr.Pn, Qn = pr.Qn, mchunk = pr.mchunk;
+    const uint32_t b = blockIdx.x - (second ? grp.nb0 : 0u);
+    const uint32_t bx = b % (uint32_t)pr.tx, by = (b / (uint32_t)pr.tx) % (uint32_t)pr.ty;
+    const uint32_t bz = b / ((uint32_t)pr.tx * (uint32_t)pr.ty);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, hh = lane >> 5;
-    const int64_t p0 = (int64_t)blockIdx.x * ST;
-    const int64_t q0 = (int64_t)blockIdx.y * ST;
-    const int64_t mbeg = (int64_t)blockIdx.z * mchunk;
+    const int64_t p0 = (int64_t)bx * ST;
+    const int64_t q0 = (int64_t)by * ST;
+    const int64_t mbeg = (int64_t)bz * mchunk;
     const int64_t mend = (mbeg + mchunk < M) ? mbeg + mchunk : M;
     const int nsteps = mend > mbeg ? (int)((mend - mbeg + ST - 1) / ST) : 0;
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(U, M * Pn * 2);
@@ -203,7 +223,7 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(const uint16_t *__restri
     }
     const int64_t col = q0 + wn * 32 + r32;
     if (col < Qn) {
-        float *Pk = P + (int64_t)blockIdx.z * Pn * Qn;
+        float *Pk = P + (int64_t)bz * Pn * Qn;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t row = p0 + wm * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
@@ -213,14 +233,32 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(const uint16_t *__restri
 }
 
 // out[i] = bf16(s1 * sum_k P[k][i]) (k ascending); out2 (optional) = bf16(s2 * same sum).
-// Four elements per thread (n is a multiple of 4 for every caller: r % 8 == 0).
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ P, int nsplit,
-                                                              int64_t n, float s1, uint16_t *__restrict__ out,
-                                                              float s2, uint16_t *__restrict__ out2) {
+// Four elements per thread (n is a multiple of 4 for every caller: r % 8 == 0).  One launch
+// serves one or two reductions: blocks [0, nb0) take the first, the rest the second.
+struct RedProb {
+    const float *P;
+    int64_t n;
+    uint16_t *out, *out2;
+    float s1, s2;
+    int32_t nsplit;
+};
+struct RedGroup {
+    RedProb p[2];
+    uint32_t nb0, nb1;
+};
+__global__ __launch_bounds__(256) void reduce_partials_kernel(RedGroup grp) {
     typedef float f32v4 __attribute__((ext_vector_type(4)));
+    const int second = blockIdx.x >= grp.nb0;
+    const RedProb &pr = grp.p[second];
+    const float *__restrict__ P = pr.P;
+    uint16_t *__restrict__ out = pr.out;
+    uint16_t *__restrict__ out2 = pr.out2;
+    const int64_t n = pr.n;
+    const int nsplit = pr.nsplit;
+    const float s1 = pr.s1, s2 = pr.s2;
     const int64_t n4 = n >> 2;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = blockIdx.x - (second ? grp.nb0 : 0u), nblk = second ? grp.nb1 : grp.nb0;
+    for (int64_t i = blk * blockDim.x + threadIdx.x; i < n4; i += nblk * blockDim.x) {
         f32v4 acc = reinterpret_cast<const f32v4 *>(P)[i];
         for (int k = 1; k < nsplit; ++k) acc += reinterpret_cast<const f32v4 *>(P + (int64_t)k * n)[i];
         if (out) {
@@ -257,22 +295,47 @@ hipError_t launch_skinny_nt(const uint16_t *A, const uint16_t *B, bool b_rows_k,
     return hipGetLastError();
 }
 
-hipError_t launch_skinny_tn(const uint16_t *U, const uint16_t *V, float *P, int64_t M, int64_t Pn,
-                            int64_t Qn, int nsplit, hipStream_t stream) {
+namespace {
+TnProb tn_prob(const TnProduct &t, int64_t M, uint32_t &nblocks) {
     const int64_t steps = (M + ST - 1) / ST;
-    const int64_t per = (steps + nsplit - 1) / nsplit;
-    dim3 grid((unsigned)((Pn + ST - 1) / ST), (unsigned)((Qn + ST - 1) / ST), (unsigned)nsplit);
-    hipLaunchKernelGGL(skinny_tn_kernel, grid, dim3(256), 0, stream, U, V, P, M, Pn, Qn, per * ST);
+    const int64_t per = (steps + t.nsplit - 1) / t.nsplit;
+    TnProb p;
+    p.U = t.U; p.V = t.V; p.P = t.P; p.Pn = t.Pn; p.Qn = t.Qn; p.mchunk = per * ST;
+    p.tx = (int32_t)((t.Pn + ST - 1) / ST);
+    p.ty = (int32_t)((t.Qn + ST - 1) / ST);
+    nblocks = (uint32_t)p.tx * (uint32_t)p.ty * (uint32_t)t.nsplit;
+    return p;
+}
+RedProb red_prob(const Reduction &r, uint32_t &nblocks) {
+    RedProb p;
+    p.P = r.P; p.n = r.n; p.out = r.out; p.out2 = r.out2; p.s1 = r.s1; p.s2 = r.s2; p.nsplit = r.nsplit;
+    int64_t g = ((r.n >> 2) + 255) / 256;
+    if (g > 256 * 8) g = 256 * 8;
+    if (g < 1) g = 1;
+    nblocks = (uint32_t)g;
+    return p;
+}
+}  // namespace
+
+hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream) {
+    TnGroup g;
+    uint32_t n0 = 0, n1 = 0;
+    g.p[0] = tn_prob(a, M, n0);
+    g.p[1] = b ? tn_prob(*b, M, n1) : g.p[0];
+    g.M = M;
+    g.nb0 = n0;
+    hipLaunchKernelGGL(skinny_tn_kernel, dim3(n0 + (b ? n1 : 0u)), dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 
-hipError_t launch_reduce_partials(const float *P, int nsplit, int64_t n, float s1, uint16_t *out,
-                                  float s2, uint16_t *out2, hipStream_t stream) {
-    int64_t g = ((n >> 2) + 255) / 256;
-    if (g > 256 * 8) g = 256 * 8;
-    if (g < 1) g = 1;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)g), dim3(256), 0, stream, P, nsplit, n, s1,
-                       out, s2, out2);
+hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream) {
+    RedGroup g;
+    uint32_t n0 = 0, n1 = 0;
+    g.p[0] = red_prob(a, n0);
+    g.p[1] = b ? red_prob(*b, n1) : g.p[0];
+    g.nb0 = n0;
+    g.nb1 = b ? n1 : n0;
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(n0 + (b ? n1 : 0u)), dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
 
 // Transposed layout, one 64 x 64 tile (64 W rows n0.., one block column kb) per workgroup:
 // thread t expands 16 weights of row n0 + t/4 (columns 16 (t%4) ..) into an LDS tile [k][n],
-// then writes 16 consecutive n of one output row k.
+// then writes 16 consecutive n of one output row k.  In the tile, the 16-column group of n is
+// XOR-ed with k/16, so the 2-byte writes of the four column groups of a wave land on different
+// banks.
 constexpr int TROW = 64 + 8;   // LDS row (k) length in bf16, padded
 __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
     __shared__ uint16_t tile[64 * TROW];
@@ -68,14 +70,14 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
             v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) tile[(16 * q + e) * TROW + nl] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 16; ++e) tile[(16 * q + e) * TROW + (nl ^ (16 * q))] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
     }
     __syncthreads();
     {
         const int kl = tid >> 2, q = tid & 3;
         const int64_t k = kb * 64 + kl;
         const int64_t n = n0 + 16 * q;
-        const u32x4 *s = reinterpret_cast<const u32x4 *>(tile + kl * TROW + 16 * q);
+        const u32x4 *s = reinterpret_cast<const u32x4 *>(tile + kl * TROW + 16 * (q ^ ((kl >> 4) & 3)));
         const u32x4 a = s[0], c = s[1];
         uint16_t *dst = g.out + k * g.N + n;
         if (n + 16 <= g.N) {
