@@ -183,12 +183,21 @@ T *ws_at(void *ws, size_t off) {
     return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
-// T (unscaled) and/or s*T, both bf16 [M, r], from X [M, K] and L1 [K, r]
+// T (unscaled) and/or s*T, both bf16 [M, r], from X [M, K] and L1 [K, r]: the split-K partials
+// (launched here), and the reduction that sums them (launched by the caller, on its own or with
+// the weight expansion)
+nf4k::Reduction T_partials(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32_t r, float scale,
+                           uint16_t *T_out, uint16_t *sT_out, const Plan &p, void *ws, hipStream_t s,
+                           hipError_t *err) {
+    float *P = ws_at<float>(ws, p.off_P);
+    *err = nf4k::launch_skinny_nt(X, L1, /*b_rows_k=*/true, P, M, r, K, p.ksT, s);
+    return nf4k::Reduction{P, p.ksT, M * r, 1.0f, T_out, scale, sT_out};
+}
 int compute_T(const uint16_t *X, const uint16_t *L1, int64_t M, int64_t K, int32_t r, float scale,
               uint16_t *T_out, uint16_t *sT_out, const Plan &p, void *ws, hipStream_t s) {
-    float *P = ws_at<float>(ws, p.off_P);
-    NF4_CHECK_HIP(nf4k::launch_skinny_nt(X, L1, /*b_rows_k=*/true, P, M, r, K, p.ksT, s), "T = X L1");
-    const nf4k::Reduction red{P, p.ksT, M * r, 1.0f, T_out, scale, sT_out};
+    hipError_t e;
+    const nf4k::Reduction red = T_partials(X, L1, M, K, r, scale, T_out, sT_out, p, ws, s, &e);
+    NF4_CHECK_HIP(e, "T = X L1");
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(red, nullptr, s), "T reduce");
     return NF4_OK;
 }
@@ -315,7 +324,7 @@ int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
     const int64_t numel = w->rows * w->cols;
     if (numel % 2) return fail(NF4_ERR_SHAPE, "rows*cols must be even");
     if (numel % 64 == 0)   // whole blocks: the table-lookup expansion
-        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, out_bf16,
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, out_bf16, nullptr,
                                                  reinterpret_cast<hipStream_t>(stream)),
                       "dequant");
     else
@@ -351,14 +360,21 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
         return NF4_OK;
     }
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
+    if (M > kGemvMaxM && use_expand(M, N, K)) {
+        // T's partials, then one launch that expands the weight and sums them, then the GEMM
+        uint16_t *Wd = ws_at<uint16_t>(workspace, p.off_Wd);
+        hipError_t e;
+        const nf4k::Reduction red = T_partials(X, L1, M, K, r, scale, T_out, sT, p, workspace, s, &e);
+        NF4_CHECK_HIP(e, "T = X L1");
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s),
+                      "weight expansion + T reduce");
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
+        return NF4_OK;
+    }
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
     if (M <= kGemvMaxM) {
         NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
-    } else if (use_expand(M, N, K)) {
-        uint16_t *Wd = ws_at<uint16_t>(workspace, p.off_Wd);
-        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, s), "weight expansion");
-        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
     } else {
         NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
     }
@@ -394,7 +410,14 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     // dT = s dY L2^T  (L2 [r, N] is already the row-major transpose the product needs)
     NF4_CHECK_HIP(nf4k::launch_skinny_nt(dY, L2, /*b_rows_k=*/false, P, M, r, N, p.ksdT, s), "dT = dY L2^T");
     const nf4k::Reduction red_dT{P, p.ksdT, M * r, scale, dT, 0.0f, nullptr};
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dT, nullptr, s), "dT reduce");
+    // at large M, one launch expands the weight (transposed) and sums dT's partials
+    const bool expand = dX && use_expand(M, N, K);
+    uint16_t *WdT = ws_at<uint16_t>(workspace, p.off_Wd);
+    if (expand)
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/true, WdT, &red_dT, s),
+                      "weight expansion + dT reduce");
+    else
+        NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dT, nullptr, s), "dT reduce");
     // dL2 = s T^T dY and dL1 = X^T dT, independent: one launch for both products, one for both
     // reductions (the partials side by side)
     float *P1 = P + (size_t)p.msL2 * r * N;
@@ -405,9 +428,7 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     const nf4k::Reduction red_dL1{P1, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr};
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
     // dX = dY deq(W) + dT L1^T
-    if (dX && use_expand(M, N, K)) {
-        uint16_t *WdT = ws_at<uint16_t>(workspace, p.off_Wd);
-        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/true, WdT, s), "weight expansion");
+    if (expand) {
         NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd(dY, WdT, dT, L1, r, M, N, K, dX,
                                                  (flags & QLORA_DX_ACCUMULATE) != 0, s),
                       "bf16 GEMM (bwd)");

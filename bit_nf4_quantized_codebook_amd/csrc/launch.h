@@ -6,6 +6,8 @@
 
 namespace nf4k {
 
+struct Reduction;
+
 struct WeightView {
     const uint8_t *packed;
     const uint8_t *c2;
@@ -41,7 +43,9 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
                            float *Tp, hipStream_t stream);
 // large token counts: the weight is expanded to bf16 once per call (rows [N, K] for the forward,
 // transposed [K, N] for the backward), then a K-extended bf16 GEMM
-hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, hipStream_t stream);
+// red (optional): a partials reduction carried by extra workgroups of the same launch
+hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
+                                hipStream_t stream);
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
@@ -76,6 +80,8 @@ struct Reduction {
     uint16_t *out2;
 };
 hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream);
+struct RedProb;
+RedProb red_prob(const Reduction &r, uint32_t &nblocks);
 
 // Optional per-thread timing events recorded on the launch stream right before and after each
 // instrumented launch (see nf4.h).

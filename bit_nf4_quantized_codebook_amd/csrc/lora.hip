@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "reduce.h"
 
 namespace nf4k {
 
@@ -232,44 +233,14 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
     }
 }
 
-// out[i] = bf16(s1 * sum_k P[k][i]) (k ascending); out2 (optional) = bf16(s2 * same sum).
-// Four elements per thread (n is a multiple of 4 for every caller: r % 8 == 0).  One launch
-// serves one or two reductions: blocks [0, nb0) take the first, the rest the second.
-struct RedProb {
-    const float *P;
-    int64_t n;
-    uint16_t *out, *out2;
-    float s1, s2;
-    int32_t nsplit;
-};
+// One launch serves one or two reductions: blocks [0, nb0) take the first, the rest the second.
 struct RedGroup {
     RedProb p[2];
     uint32_t nb0, nb1;
 };
 __global__ __launch_bounds__(256) void reduce_partials_kernel(RedGroup grp) {
-    typedef float f32v4 __attribute__((ext_vector_type(4)));
     const int second = blockIdx.x >= grp.nb0;
-    const RedProb &pr = grp.p[second];
-    const float *__restrict__ P = pr.P;
-    uint16_t *__restrict__ out = pr.out;
-    uint16_t *__restrict__ out2 = pr.out2;
-    const int64_t n = pr.n;
-    const int nsplit = pr.nsplit;
-    const float s1 = pr.s1, s2 = pr.s2;
-    const int64_t n4 = n >> 2;
-    const int64_t blk = blockIdx.x - (second ? grp.nb0 : 0u), nblk = second ? grp.nb1 : grp.nb0;
-    for (int64_t i = blk * blockDim.x + threadIdx.x; i < n4; i += nblk * blockDim.x) {
-        f32v4 acc = reinterpret_cast<const f32v4 *>(P)[i];
-        for (int k = 1; k < nsplit; ++k) acc += reinterpret_cast<const f32v4 *>(P + (int64_t)k * n)[i];
-        if (out) {
-            uint2 o = {pack_bf16x2(s1 * acc.x, s1 * acc.y), pack_bf16x2(s1 * acc.z, s1 * acc.w)};
-            reinterpret_cast<uint2 *>(out)[i] = o;
-        }
-        if (out2) {
-            uint2 o = {pack_bf16x2(s2 * acc.x, s2 * acc.y), pack_bf16x2(s2 * acc.z, s2 * acc.w)};
-            reinterpret_cast<uint2 *>(out2)[i] = o;
-        }
-    }
+    reduce_partials_block(grp.p[second], blockIdx.x - (second ? grp.nb0 : 0u), second ? grp.nb1 : grp.nb0);
 }
 
 }  // namespace
@@ -306,16 +277,14 @@ TnProb tn_prob(const TnProduct &t, int64_t M, uint32_t &nblocks) {
     nblocks = (uint32_t)p.tx * (uint32_t)p.ty * (uint32_t)t.nsplit;
     return p;
 }
+}  // namespace
+
 RedProb red_prob(const Reduction &r, uint32_t &nblocks) {
     RedProb p;
     p.P = r.P; p.n = r.n; p.out = r.out; p.out2 = r.out2; p.s1 = r.s1; p.s2 = r.s2; p.nsplit = r.nsplit;
-    int64_t g = ((r.n >> 2) + 255) / 256;
-    if (g > 256 * 8) g = 256 * 8;
-    if (g < 1) g = 1;
-    nblocks = (uint32_t)g;
+    nblocks = reduce_blocks(r.n);
     return p;
 }
-}  // namespace
 
 hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream) {
     TnGroup g;

@@ -13,11 +13,14 @@
 #include "common.h"
 #include "dqtile.h"
 #include "launch.h"
+#include "reduce.h"
 
 namespace nf4k {
 
 namespace {
 
+// nexp workgroups expand the weight; nred more (optional) sum a set of split-reduction partials
+// that the caller needs at the same point of the stream
 struct ExpandArgs {
     const uint8_t *packed;
     const uint8_t *c2;
@@ -26,6 +29,8 @@ struct ExpandArgs {
     uint16_t *out;
     int64_t N, K;
     Codebook cb;
+    RedProb red;
+    uint32_t nexp, nred;
 };
 
 // Row layout: 8 lanes per block, one packed dword (8 weights) each, so a wave reads 256
@@ -33,9 +38,13 @@ struct ExpandArgs {
 // each build its table (the kernel is bound by HBM, not VALU).  Blocks run over the row-major
 // flattening, so this needs only N*K % 64 == 0.
 __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
+    if (blockIdx.x >= g.nexp) {
+        reduce_partials_block(g.red, blockIdx.x - g.nexp, g.nred);
+        return;
+    }
     const int64_t nwords = (g.N * g.K) >> 3;
     const float mean = g.mean[0];
-    for (int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x; wi < nwords; wi += (int64_t)gridDim.x * 256) {
+    for (int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x; wi < nwords; wi += (int64_t)g.nexp * 256) {
         const int64_t b = wi >> 3;
         const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g.packed) + wi);
         const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean));
@@ -51,6 +60,10 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
 constexpr int TROW = 64 + 8;   // LDS row (k) length in bf16, padded
 __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
     __shared__ uint16_t tile[64 * TROW];
+    if (blockIdx.x >= g.nexp) {
+        reduce_partials_block(g.red, blockIdx.x - g.nexp, g.nred);
+        return;
+    }
     const int tid = threadIdx.x;
     const int64_t nbk = g.K >> 6;
     const int64_t ntn = (g.N + 63) >> 6;
@@ -80,32 +93,37 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
         const u32x4 *s = reinterpret_cast<const u32x4 *>(tile + kl * TROW + 16 * (q ^ ((kl >> 4) & 3)));
         const u32x4 a = s[0], c = s[1];
         uint16_t *dst = g.out + k * g.N + n;
+        // plain stores: the four 32-byte pieces of a 128-byte row segment combine in L2
         if (n + 16 <= g.N) {
-            __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(dst));
-            __builtin_nontemporal_store(c, reinterpret_cast<u32x4 *>(dst) + 1);
+            reinterpret_cast<u32x4 *>(dst)[0] = a;
+            reinterpret_cast<u32x4 *>(dst)[1] = c;
         } else {
             // N % 8 == 0: the last tile ends on an 8-column boundary
-            if (n < g.N) __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(dst));
+            if (n < g.N) reinterpret_cast<u32x4 *>(dst)[0] = a;
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, hipStream_t stream) {
+hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
+                                hipStream_t stream) {
     ExpandArgs a;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
     a.out = out; a.N = w.rows; a.K = w.cols;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
+    a.nred = 0;
+    if (red) a.red = red_prob(*red, a.nred);
     if (!transposed) {
         const int64_t nwords = (w.rows * w.cols) >> 3;
         int64_t grid = (nwords + 255) / 256;
         if (grid > 256 * 64) grid = 256 * 64;
         if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        a.nexp = (uint32_t)grid;
+        hipLaunchKernelGGL(expand_rows_kernel, dim3(a.nexp + a.nred), dim3(256), 0, stream, a);
     } else {
-        const int64_t tiles = ((w.rows + 63) / 64) * (w.cols / 64);
-        hipLaunchKernelGGL(expand_transposed_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+        a.nexp = (uint32_t)(((w.rows + 63) / 64) * (w.cols / 64));
+        hipLaunchKernelGGL(expand_transposed_kernel, dim3(a.nexp + a.nred), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }
