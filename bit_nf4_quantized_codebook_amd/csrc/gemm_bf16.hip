@@ -132,19 +132,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
-    // one step: compute stages (Ac, Bc) while the next step streams into (An, Bn); fragment
-    // reads run one sub-step ahead of the MFMAs
+    // Fragment reads run one sub-step ahead of the MFMAs.  The schedule is pinned: left alone, the
+    // scheduler sinks the next sub-step's reads below the current MFMAs (their registers can then
+    // be reused), and every sub-step starts by waiting out the LDS latency.  Here each of the
+    // first 8 MFMAs of a sub-step is followed by one fragment read, and the step's 16
+    // direct-to-LDS loads go out between the MFMAs of the first sub-step.
+    auto interleave = [&](int nvmem) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // 1 MFMA
+            if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // 1 DS read
+            if (k < nvmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 VMEM
+        }
+    };
+    // one step: compute stages (Ac, Bc) while the next step streams into (An, Bn)
     auto step_body = [&](int step, const uint8_t *Ac, const uint8_t *Bc, uint8_t *An, uint8_t *Bn) {
-        load(rA, step + 1, An);
-        load(rB, step + 1, Bn);
         Frags f0, f1;
         read(Ac, Bc, 0, f0);
+        load(rA, step + 1, An);
+        load(rB, step + 1, Bn);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             Frags &cur = (s & 1) ? f1 : f0;
             Frags &nxt = (s & 1) ? f0 : f1;
             if (s < 3) read(Ac, Bc, s + 1, nxt);
             mma(cur);
+            interleave(s == 0 ? 16 : 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         // the next step landed (this wave's loads) and this wave's fragment reads are done
