@@ -178,6 +178,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Lane indices for the code after the main loop, recomputed (mbcnt) rather than kept live
+    // across it: held over the loop they were spilled, and a kernel with scratch memory costs
+    // several microseconds more to dispatch.
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int r32_e = lane_e & 31, hh_e = lane_e >> 5;
+
     // ---- LoRA extension: r/64 more steps (zero padded past r) ----
     //   A tile: Ae rows m0.., columns j (same swizzled layout, straight to LDS), in As0
     //   forward : Be^T = L2 [r, Nout]: rows j, columns n -> two halves [64 j][128 + 16] in
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
             const int j0 = e * TK;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int row = 8 * (8 * wave + q) + (lane >> 3);
+                const int row = 8 * (8 * wave + q) + (lane_e >> 3);
                 const int jj = j0 + a_col[q & 1];
                 const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0x80000000u;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe, (lds_void *)((lds_u8 *)As0 + wave * 8192 + q * 1024),
@@ -228,10 +234,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
                     } else {
                         // 16-lane group (hh, half): lane i reads rows 16 s + 8 hh + i/4 (+4),
                         // columns c0 + 4 (i%4) .. +3; after the transpose lane i holds column c0 + i
-                        const int i16 = lane & 15, half = (lane >> 4) & 1;
+                        const int i16 = lane_e & 15, half = (lane_e >> 4) & 1;
                         const uint8_t *Bh = wn ? Bs1 : Bs0;
                         const int c0 = 32 * j + 16 * half;
-                        const int rowb = 16 * s + 8 * hh + (i16 >> 2);
+                        const int rowb = 16 * s + 8 * hh_e + (i16 >> 2);
                         const uint8_t *base = Bh + (c0 + 4 * (i16 & 3)) * 2;
                         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * EXT_ROWB));
                         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * EXT_ROWB));
@@ -250,10 +256,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
         const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
-        const uint32_t lane_off = (uint32_t)((wm * 128 + hh * 4) * row_bytes) + (uint32_t)((n0 + wn * 128 + r32) * 2);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((n0 + wn * 128 + r32_e) * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (n0 + wn * 128 + j * 32 + r32 >= g.Nout) continue;
+            if (n0 + wn * 128 + j * 32 + r32_e >= g.Nout) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -272,11 +278,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + wn * 128 + j * 32 + r32;
+                const int64_t col = n0 + wn * 128 + j * 32 + r32_e;
                 if (col >= g.Nout) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                    const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh_e * 4 + (v & 3);
                     if (row < g.M) {
                         uint16_t *p = g.C + row * g.Nout + col;
                         *p = (uint16_t)f32_to_bf16(acc[i][j][v] + bf16_to_f32(*p));
