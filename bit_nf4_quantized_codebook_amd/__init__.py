@@ -338,6 +338,16 @@ class GemmTimer:
                                               ctypes.cast(self.kinds, ctypes.c_void_p), self.n),
                "nf4_set_gemm_timing_events")
 
+    def arm_at(self, offset: int, n: int):
+        """Record the next n instrumented launches into slots offset .. offset + n - 1."""
+        if offset < 0 or n < 0 or offset + n > self.n:
+            raise ValueError("timing slots out of range")
+        size = ctypes.sizeof(ctypes.c_void_p)
+        _check(lib.nf4_set_gemm_timing_events(ctypes.c_void_p(ctypes.addressof(self.begin) + offset * size),
+                                              ctypes.c_void_p(ctypes.addressof(self.end) + offset * size),
+                                              ctypes.c_void_p(ctypes.addressof(self.kinds) + offset * 4), n),
+               "nf4_set_gemm_timing_events")
+
     def disarm(self) -> int:
         cnt = int(lib.nf4_gemm_timing_count())
         _check(lib.nf4_set_gemm_timing_events(None, None, None, 0), "nf4_set_gemm_timing_events")
