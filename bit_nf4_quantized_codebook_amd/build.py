@@ -32,14 +32,33 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+def _scratch_kernels(remarks: str) -> list:
+    """Kernels whose per-lane scratch (register spills) is non-zero, from the resource remarks."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[-Rpass")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if n > 0:
+                bad.append((name, n))
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", src, "-o", obj]
+    else:
+        cmd += ["-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    # every kernel here is written to fit its registers: a spill is a build error
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory: {bad}")
     return obj
 
 

@@ -115,7 +115,6 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // Workspace plan of the linear layer (identical for the size query and the calls)
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
-constexpr int64_t kDecodeMaxM = 4;    // token counts served by the table-decode GEMV
 constexpr int64_t kGemvMaxM = 16;     // token counts served by a weight-streaming GEMV
 // From this many tokens on, the weight is expanded to bf16 once per call and multiplied by a plain
 // bf16 GEMM: the expansion pass costs about 2.5 bytes of HBM traffic per weight, while dequantizing
@@ -153,7 +152,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     if (use_expand(M, N, K)) {
         p.off_Wd = off;  off += round256((size_t)N * K * 2);
     }
-    if (M <= kDecodeMaxM) {
+    if (nf4k::gemv_fits(M, N, K, r)) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
@@ -353,7 +352,7 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
     if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (M <= kDecodeMaxM) {
+    if (nf4k::gemv_fits(M, N, K, r)) {
         NF4_CHECK_HIP(nf4k::launch_gemv_fwd(view_of(w), X, L1, L2, scale, r, M, Y, T_out,
                                             ws_at<float>(workspace, p.off_Yp), ws_at<float>(workspace, p.off_Tp), s),
                       "dequant GEMV (fwd)");
@@ -403,8 +402,13 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     const uint16_t *Tuse = T;
     if (!Tuse) {
         uint16_t *Tb = ws_at<uint16_t>(workspace, p.off_T);
-        rc = compute_T(X, L1, M, K, r, 1.0f, Tb, nullptr, p, workspace, s);
-        if (rc) return rc;
+        if (nf4k::gemv_fits(M, N, K, r)) {
+            // the decode-size forward's partials and summation order: T has the forward's bits
+            NF4_CHECK_HIP(nf4k::launch_gemv_T(X, L1, r, M, K, ws_at<float>(workspace, p.off_Tp), Tb, s), "T = X L1");
+        } else {
+            rc = compute_T(X, L1, M, K, r, 1.0f, Tb, nullptr, p, workspace, s);
+            if (rc) return rc;
+        }
         Tuse = Tb;
     }
     // dT = s dY L2^T  (L2 [r, N] is already the row-major transpose the product needs)

@@ -4,67 +4,54 @@
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
 // section 3.5 eq. (5) / eq. (6); section 4 eq. (3).
 //
-// This shape streams the 4-bit weight once from HBM; the work to hide behind that stream is the
-// decoding of the codes.  Two launches:
+// This shape streams the 4-bit weight once from HBM; everything else has to hide behind that
+// stream.  Two launches:
 //
-// gemv_main_kernel: workgroups of 8 waves.  "T" workgroups (first in the grid, so dispatched
-//   first) compute K-slices of T = X L1; "W" workgroups own 64 weight rows and one K segment.
-//   - v_mfma_f32_4x4x4_16b_bf16: B lane l holds 4 codes of one weight row, so M <= 4 tokens waste
-//     no MFMA row; A (X) is broadcast inside pairs of blocks (CBSZ = 1).
-//   - every weight load reads whole 128-byte lines: a load covers 8 rows x 128 bytes and each
-//     lane's 16 bytes feed 8 MFMAs directly (no LDS staging of W).
+// gemv_t_kernel: T = X L1 in slices of 64 M' rows of L1 (M' = 1, 2, 4: M rounded up; fp32
+//   partials, summed by the next launch).
+//
+// gemv_rows_kernel: one workgroup of up to 16 waves per CU owns a run of R weight rows over the
+//   whole reduction, so it finishes its outputs itself:
+//   - KW waves side by side cover one row: lane l of wave k always takes the same 16 bytes of a
+//     row (32 columns, half a quantization block), so its X values are loaded once and stay in
+//     registers for every row.  The workgroup runs S = 16 / KW such row streams, each walking its
+//     rows with U loads in flight per lane.
 //   - codes are decoded through a pair table in LDS: entry e (one packed byte) holds the bf16
-//     codebook values of its two nibbles; 64 copies side by side so that lane l always reads
-//     bank l (conflict-free).  The address is one v_perm (the code byte next to the lane offset),
-//     the lookup one ds_read_b32 per two weights.
-//   - the table is the plain codebook, so each block is accumulated on its own and the block
-//     constant a = c2 * s2 + mean (eq. 6, rebuilt in fp32) multiplies the fp32 partial:
+//     codebook values of its two nibbles, 64 copies side by side so that lane l reads bank l.
+//     The address is one v_perm (the code byte next to the lane offset), the lookup one
+//     ds_read_b32, the product one v_dot2_f32_bf16 per token.
+//   - the table is the plain codebook, so each half-block partial is scaled afterwards by its
+//     block constant a = fma(e4m3(c2), c1, mean) (eq. 6, fp32), staged with the codes in LDS:
 //     y = sum_blocks a_b sum_{k in b} x_k cb[q_k].  This equals X deq(W)^T up to rounding, with
 //     the codebook rounded to bf16 instead of each product cb * a.
-//   - the block constants of the workgroup's rows and K segment are staged in LDS once.
-// gemv_epilogue_kernel: sums the K-segment partials of X deq(W)^T and the K-slices of T, rounds
-//   s T to bf16 and adds (s T) L2, stores bf16 Y (and T when asked).
+//   - the lane partials of BR rows are summed across the wave with lane swaps and DPP, across the
+//     KW waves in LDS; the LoRA term (s T) L2 of the workgroup's rows (s T rounded to bf16, L2
+//     staged in LDS at the start) is added before the bf16 store.
 
 #include "common.h"
+#include "dqtile.h"
 #include "launch.h"
 
 namespace nf4k {
 
 namespace {
 
-constexpr int NWAVE = 8;                       // waves per main-kernel workgroup
-constexpr int NTHR = 64 * NWAVE;
-constexpr int EWAVE = 4;                       // waves per epilogue workgroup
-constexpr int MACRO_BLOCKS = 4;                // quantization blocks (of 64 columns) per macro step
-constexpr int TCHUNK = 64 * 4 * NWAVE;         // K columns of T per T workgroup (four blocks per wave)
-constexpr int TAB_COPIES = 64;                 // table copies: lane l reads copy l (bank l)
-constexpr int SEG_BLOCKS = 128;                // max quantization blocks per K segment of a workgroup
-constexpr int C2_ROW = SEG_BLOCKS + 4;         // staged code row (bytes): rows start one bank apart
-constexpr int C1_MAX = 512;                    // max second-level constants per workgroup
-constexpr uint32_t OOB = 0xFFFFFE00u;          // buffer offset past any range: loads return 0
+constexpr uint32_t OOB = 0x80000000u;          // buffer offset past any range: loads return 0
+constexpr int MAX_WAVES = 16;
+constexpr int TAB_COPIES = 64;                 // lane l reads copy l
+constexpr int TAB_WORDS = 256 * TAB_COPIES;    // 64 KB
+constexpr int C2_CAP = 16384;                  // staged code bytes per workgroup
+constexpr int C1_CAP = C2_CAP / 256 + 2;       // staged second-level constants
+constexpr int R_MAX = 128;                     // rows per workgroup
+constexpr int R_MAX_LORA = 128;                // r
+constexpr int PART_CAP = 2048;                 // KW * R * MM partial sums
+constexpr int CSUM_CAP = 8192;                 // chunk sums of T's partials per workgroup
+constexpr int T_THREADS = 256;
+// rows of L1 per T workgroup: short slices spread the 1 MB-scale L1 read over many CUs (one CU
+// alone pulls only a few tens of GB/s); their partials are summed by the consumer
+constexpr int t_rows(int mm) { return 64 * mm; }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t clamped = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)clamped, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int V>
 struct IntC {
@@ -78,482 +65,535 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-// C += A[block ABID] (broadcast to all 16 blocks) x B
-template <int ABID>
-__device__ __forceinline__ f32x4 mfma4(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
-                                                  c, 4, ABID, 0);
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    // lanes whose source is outside the 16-lane row read 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-struct GemvArgs {
+// bf16 codebook value of code j (selects over the kernel-argument copy; no indexed registers)
+__device__ __forceinline__ uint32_t cb_bf16(const Codebook &cb, uint32_t j) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v = (j == (uint32_t)q) ? cb.v[q] : v;
+    return f32_to_bf16(v);
+}
+
+// ---------------------------------------------------------------------------------------------
+// T = X L1, slice of t_rows(MM) rows of L1 per workgroup: Tp[slice][m][j]
+// ---------------------------------------------------------------------------------------------
+struct TArgs {
+    const uint16_t *X;       // [M, K]
+    const uint16_t *L1;      // [K, r]
+    float *Tp;               // [nkc, M, r]
+    int64_t M, K;
+    int32_t r;
+};
+
+// T's slice partials are summed in chunks of 8 slices, each chunk from -0 in slice order, then the
+// chunk sums from -0 in order.  Both consumers (the row kernel and the backward's recompute of T)
+// run exactly these additions, so T has the same bits in the forward and the backward.
+__device__ __forceinline__ void tp_chunk_load(__amdgpu_buffer_rsrc_t rT, int nkc, int E, int e, int c, bool ok,
+                                              float (&v)[8]) {
+    // conditions combined with & (not &&): the offset stays a select, with no branch around the load
+    const bool base_ok = ok & (e < E);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t off = (uint32_t)(((8 * c + q) * E + e) * 4);
+        v[q] = __uint_as_float(bload4(rT, (base_ok & (8 * c + q < nkc)) ? off : OOB));
+    }
+}
+__device__ __forceinline__ float tp_chunk_add(int nkc, int c, const float (&v)[8]) {
+    float t = -0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (8 * c + q < nkc) t += v[q];
+    return t;
+}
+__device__ __forceinline__ float tp_chunk_sum(__amdgpu_buffer_rsrc_t rT, int nkc, int E, int e, int c) {
+    float v[8];
+    tp_chunk_load(rT, nkc, E, e, c, true, v);
+    return tp_chunk_add(nkc, c, v);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int LGKM0_IMM = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// workgroup barrier for LDS traffic only: loads still in flight (weight rows, LDS copies issued
+// later) stay in flight; __syncthreads would wait for them
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(LGKM0_IMM);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// T (unscaled, bf16) from the partials alone: thread per element
+__global__ __launch_bounds__(256) void gemv_tsum_kernel(const float *Tp, int nkc, int E, uint16_t *T) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(Tp, (int64_t)nkc * E * 4);
+    float t = -0.0f;
+    for (int c = 0; c < (nkc + 7) >> 3; ++c) t += tp_chunk_sum(rT, nkc, E, e, c);
+    if (e < E) T[e] = (uint16_t)f32_to_bf16(t);
+}
+
+template <int MM>
+__global__ __launch_bounds__(T_THREADS) void gemv_t_kernel(TArgs a) {
+    constexpr int T_ROWS = t_rows(MM);
+    constexpr int T_PT = 4 * MM;                  // 16-byte L1 pieces per thread (r <= 128)
+    __shared__ float xs[MM][T_ROWS];
+    __shared__ __align__(16) float red[MM * T_THREADS * 8];   // [m][row lane][r]
+    __shared__ float red2[MM * (T_THREADS + R_MAX_LORA)];    // [m][group][r]
+    const int tid = threadIdx.x;
+    const int CG = a.r >> 3;                      // 16-byte column groups of an L1 row
+    const int RPS = T_THREADS / CG;               // rows per load step
+    const int cg = tid % CG, rl = tid / CG;
+    const int64_t k0 = (int64_t)blockIdx.x * T_ROWS;
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, a.M * a.K * 2);
+    const __amdgpu_buffer_rsrc_t rL1 = make_rsrc(a.L1, a.K * a.r * 2);
+
+    u32x4 v[T_PT];
+#pragma unroll
+    for (int i = 0; i < T_PT; ++i) {
+        const int k = rl + RPS * i;
+        const bool ok = rl < RPS && k < T_ROWS && k0 + k < a.K;
+        v[i] = bload16(rL1, ok ? (uint32_t)(((k0 + k) * a.r + 8 * cg) * 2) : OOB);
+    }
+    constexpr int NXD = MM * T_ROWS / 2;          // dwords of the X chunk
+#pragma unroll
+    for (int q = 0; q < (NXD + T_THREADS - 1) / T_THREADS; ++q) {
+        const int i = tid + T_THREADS * q;        // dword i: token m, columns 2 kp, 2 kp + 1
+        const int m = i / (T_ROWS / 2), kp = i % (T_ROWS / 2);
+        if (i < NXD) {
+            const bool ok = m < a.M && k0 + 2 * kp < a.K;
+            const uint32_t xv = bload4(rX, ok ? (uint32_t)((m * a.K + k0 + 2 * kp) * 2) : OOB);
+            xs[m][2 * kp] = bf16_to_f32(xv & 0xFFFFu);
+            xs[m][2 * kp + 1] = bf16_to_f32(xv >> 16);
+        }
+    }
+    __syncthreads();
+    float acc[MM][8];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[m][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < T_PT; ++i) {
+        const int k = min(rl + RPS * i, T_ROWS - 1);  // invalid pieces are zero
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t wv = v[i][e >> 1];
+            const float l = bf16_to_f32((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+#pragma unroll
+            for (int m = 0; m < MM; ++m) acc[m][e] = __builtin_fmaf(xs[m][k], l, acc[m][e]);
+        }
+    }
+    // sum over the RPS row lanes of each column: groups of 8 row lanes (the last may be short),
+    // then the groups
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+        reinterpret_cast<f32x4 *>(red)[(m * T_THREADS + tid) * 2] = f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        reinterpret_cast<f32x4 *>(red)[(m * T_THREADS + tid) * 2 + 1] = f32x4{acc[m][4], acc[m][5], acc[m][6], acc[m][7]};
+    }
+    __syncthreads();
+    const int G1 = (RPS + 7) >> 3;                // groups of 8 row lanes per column
+    for (int t0 = tid; t0 < G1 * a.r; t0 += T_THREADS) {
+        const int g = t0 / a.r, j = t0 - g * a.r;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            float t = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int rl2 = 8 * g + q;
+                if (rl2 < RPS) t += red[(m * T_THREADS + rl2 * CG) * 8 + j];
+            }
+            red2[(m * G1 + g) * a.r + j] = t;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < MM * a.r; e += T_THREADS) {
+        const int m = e / a.r, j = e - m * a.r;
+        float t = 0.0f;
+        for (int g = 0; g < G1; ++g) t += red2[(m * G1 + g) * a.r + j];
+        if (m < a.M) a.Tp[((int64_t)blockIdx.x * a.M + m) * a.r + j] = t;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// X deq(W)^T + (s T) L2 for R rows per workgroup
+// ---------------------------------------------------------------------------------------------
+struct RowsArgs {
     const uint16_t *X;       // [M, K]
     const uint8_t *packed;   // [N, K/2]
     const uint8_t *c2;
     const float *c1;
     const float *mean;
-    const uint16_t *L1;      // [K, r]
-    float *Yp;               // [S, M, N] fp32 partials of X deq(W)^T
-    float *Tp;               // [nkc, M, r] fp32 partials of X L1
+    const uint16_t *L2;      // [r, N]
+    const float *Tp;         // [nkc, M, r]
+    uint16_t *Y;             // [M, N]
+    uint16_t *T_out;         // [M, r] or null
     int64_t M, N, K;
-    int32_t r, nseg, nrg, nt;   // K segments, 64-row groups, T workgroups
+    int32_t r, nkc, KW, S, RS, R;
+    float scale;
     Codebook cb;
 };
 
-// X fragment of one 64-column block for m-tile mt: lane (b = l / 4, i = l % 4) holds
-// X[4 mt + i][k0 + 4 b .. + 3]
-__device__ __forceinline__ u32x2 load_xfrag(__amdgpu_buffer_rsrc_t rX, const GemvArgs &g, int lane, int mt,
-                                            int64_t blk, bool live) {
-    const int64_t m = mt * 4 + (lane & 3);
-    const int64_t k = blk * 64 + 4 * (lane >> 2);
-    const bool ok = live && m < g.M && blk < (g.K >> 6);
-    return bload8(rX, ok ? (uint32_t)((m * g.K + k) * 2) : OOB);
-}
-
-// C += A[block 2 g + ABID of each pair g of blocks] x B
-template <int ABID>
-__device__ __forceinline__ f32x4 mfma4_g2(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
-                                                  c, 1, ABID, 0);
-}
-
-// Work of one workgroup: RH x RS sets of 8 weight rows over one K segment.  Wave (h, k) of the
-// NWAVE = RH x KW waves takes row sets h RS .. h RS + RS - 1 and every KW-th macro step of the
-// segment starting at k, so that neighbouring waves read neighbouring bytes of the same rows.
-// A macro step is four quantization blocks (256 columns, one 128-byte line of each row); its
-// load q covers the 8 rows of row set q: lane l takes row 8 q + l % 8, bytes 16 (l / 8) .. + 15,
-// so every load reads whole lines.  Those 16 bytes (32 columns, inside one quantization block)
-// are the B operand of 8 MFMAs: MFMA t uses codes 4 t .. 4 t + 3.  The 8 lanes of one chunk g
-// form broadcast pair g (blocks 2 g, 2 g + 1; rows 0..3 and 4..7), whose A operand (X) comes
-// from block 2 g + t / 4: lane 8 g + 4 v + i holds X[i][32 g + 16 v .. + 15] for MFMAs 4 v .. 4 v + 3.
-// Macro steps stream through a ring of NST register stages.
-template <int MT, int RS, int RH, int NST>
-__device__ void w_part(const GemvArgs &g, uint32_t *tab, int rg, int seg) {
-    constexpr int KW = NWAVE / RH;
-    constexpr int R = 8 * RS * RH;                       // rows of the workgroup
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wh = wave / KW, wk = wave % KW;
-    const int64_t n0 = (int64_t)rg * R;
-    const int64_t nw0 = n0 + wh * (8 * RS);              // first row of this wave
-    const int64_t wrow = g.K >> 1, nblk = g.K >> 6;
-    const int64_t nmacro = (nblk + MACRO_BLOCKS - 1) / MACRO_BLOCKS;
-    const int64_t per_seg = (nmacro + g.nseg - 1) / g.nseg;
-    const int64_t s0 = min((int64_t)seg * per_seg, nmacro), s1 = min(s0 + per_seg, nmacro);
-
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.packed + nw0 * wrow, (g.N - nw0) * wrow);
-    const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.N * nblk);
-    const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(g.c1, ((g.N * nblk + 255) >> 8) * 4);
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.X, g.M * g.K * 2);
-    const float mean = g.mean[0];
-
-    const int G = lane >> 3, rl = lane & 7;            // chunk of the macro step, row in an 8-row set
-    const int xv = (lane >> 2) & 1, xi = lane & 3;     // X half (MFMAs 4 xv ..) and token of this lane
-    // byte offsets of row set 0; row set q adds 8 q rows (wave-uniform)
-    const uint32_t wb = (uint32_t)(rl * wrow + 16 * G), wstep = (uint32_t)(8 * wrow);
-    uint32_t xb[MT];
-    bool xrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int64_t m = mt * 4 + xi;
-        xrow[mt] = m < g.M;
-        xb[mt] = (uint32_t)((m * g.K + 32 * G + 16 * xv) * 2);
-    }
-
-    struct Stage {
-        u32x4 w[RS];            // rows 8 q + rl: 32 codes each
-        u32x4 x[MT][2];         // X[4 mt + xi][32 G + 16 xv + 8 h .. + 7]
-    };
-    // Loads past the wave's range need no guard except X: W then reads other finite data (or
-    // zeros past the end), which the zero X fragments cancel.
-    auto load = [&](int64_t ms, Stage &S) {
-        const uint32_t wo = (uint32_t)(ms * (MACRO_BLOCKS * 32));
-#pragma unroll
-        for (int q = 0; q < RS; ++q) S.w[q] = bload16(rW, wb + q * wstep + wo);
-        // 32-bit lane-uniform test plus a per-lane mask: no branches around the loads
-        const uint32_t msu = (uint32_t)ms;
-        const uint32_t xo = msu * (MACRO_BLOCKS * 128);
-        const bool live = msu < (uint32_t)s1 && msu * MACRO_BLOCKS + (uint32_t)(G >> 1) < (uint32_t)nblk;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint32_t xa = (live && xrow[mt]) ? xb[mt] + xo : OOB;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) S.x[mt][h] = bload16(rX, xa + 16 * h);
-        }
-    };
-
-    // the first NST macro steps are in flight before the tables are built
-    Stage st[NST];
-    const int64_t msb = s0 + wk;                         // first macro step of this wave
-#pragma unroll
-    for (int i = 0; i < NST; ++i) load(msb + (int64_t)i * KW, st[i]);
-
-    // ---- block constants of the workgroup's rows and K segment, staged in LDS once ----
-    // (per-lane loads of single code bytes would touch a cache line each)
-    __shared__ uint8_t c2s[R * C2_ROW];
-    __shared__ float c1s[C1_MAX];
-    const int64_t b_lo = s0 * MACRO_BLOCKS, b_hi = min(s1 * MACRO_BLOCKS, nblk);
-    const int nb = (int)(b_hi - b_lo);
-    const int64_t c1_lo = (n0 * nblk + b_lo) >> 8;
-    {
-        for (int i = tid; i < R * SEG_BLOCKS; i += NTHR) {
-            const int row = i / SEG_BLOCKS, b = i % SEG_BLOCKS;
-            c2s[row * C2_ROW + b] = (uint8_t)bload1(rC2, b < nb ? (uint32_t)((n0 + row) * nblk + b_lo + b) : OOB);
-        }
-        const int64_t c1_hi = ((n0 + R - 1) * nblk + b_hi - 1) >> 8;
-        for (int i = tid; i <= (int)(c1_hi - c1_lo); i += NTHR)
-            c1s[i] = __uint_as_float(bload4(rC1, (uint32_t)((c1_lo + i) * 4)));
-    }
-
-    // ---- LDS pair table: entry e, copy c at byte e * 256 + 4 c ----
-    __shared__ uint32_t cbh[16];
-    if (tid < 16) {
-        float v = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v = (tid == j) ? g.cb.v[j] : v;
-        cbh[tid] = f32_to_bf16(v);
-    }
-    __syncthreads();
-    {
-        const int c = tid & 63;
-#pragma unroll 8
-        for (int q = 0; q < 256 / NWAVE; ++q) {
-            const int e = wave + NWAVE * q;
-            tab[e * TAB_COPIES + c] = cbh[e & 15] | (cbh[e >> 4] << 16);
-        }
-    }
-    __syncthreads();
-
-    const uint32_t lb = (uint32_t)lane << 2;
-    const char *tabc = reinterpret_cast<const char *>(tab);
-    f32x4 acc[RS][MT];
-#pragma unroll
-    for (int q = 0; q < RS; ++q)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // B fragments of MFMA t for the row sets (two table lookups each)
-    auto lookup = [&](const Stage &S, auto tc, u32x2 (&bv)[RS]) {
-        constexpr int t = decltype(tc)::value;
-        // byte 2 t (2 t + 1) of the chunk goes to address bits 8..15 next to the lane offset
-        constexpr uint32_t sel0 = 0x0C0C0000u | ((4u + 2u * (t & 1)) << 8);
-        constexpr uint32_t sel1 = 0x0C0C0000u | ((5u + 2u * (t & 1)) << 8);
-#pragma unroll
-        for (int q = 0; q < RS; ++q) {
-            const uint32_t wd = S.w[q][t >> 1];
-            bv[q].x = *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(wd, lb, sel0));
-            bv[q].y = *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(wd, lb, sel1));
-        }
-    };
-    // Each row set and 32-column chunk is one quantization block: its 8 MFMAs accumulate from
-    // zero and the block constant then scales the fp32 partial.  Lookups run one MFMA step ahead.
-    auto compute = [&](const Stage &S, int64_t ms) {
-        // block constants of this step: row 8 q + rl, block 4 ms + G / 2 (eq. 6, fp32)
-        float a[RS];
-#pragma unroll
-        for (int q = 0; q < RS; ++q) {
-            const int row = wh * (8 * RS) + 8 * q + rl;
-            const int b = (int)(ms * MACRO_BLOCKS - b_lo) + (G >> 1);
-            const int bc = b < nb ? b : 0;                  // past the segment: X is zero
-            const int64_t qi = (n0 + row) * nblk + b_lo + bc;
-            a[q] = block_scale(c2s[row * C2_ROW + bc], c1s[(int)((qi >> 8) - c1_lo)], mean);
-        }
-        f32x4 tmp[RS][MT];
-#pragma unroll
-        for (int q = 0; q < RS; ++q)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) tmp[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x2 bv[2][RS];
-        lookup(S, IntC<0>{}, bv[0]);
-        static_for<0, 8>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            if constexpr (t + 1 < 8) lookup(S, IntC<t + 1>{}, bv[(t + 1) % 2]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                // X of MFMA t: elements 4 (t % 4) .. + 3 of this lane's 16-element half
-                const u32x4 &xx = S.x[mt][(t % 4) >> 1];
-                const u32x2 xf = (t & 1) ? u32x2{xx.z, xx.w} : u32x2{xx.x, xx.y};
-#pragma unroll
-                for (int q = 0; q < RS; ++q) tmp[q][mt] = mfma4_g2<t / 4>(xf, bv[t % 2][q], tmp[q][mt]);
-            }
-        });
-#pragma unroll
-        for (int q = 0; q < RS; ++q)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[q][mt] += a[q] * tmp[q][mt];
-    };
-
-    for (int64_t ms = msb; ms < s1; ms += NST * KW) {
-        static_for<0, NST>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            compute(st[i], ms + i * KW);
-            load(ms + (i + NST) * KW, st[i]);
-        });
-    }
-
-    // ---- the eight chunks of a row live in lanes rl, rl + 8, ..., rl + 56 ----
-#pragma unroll
-    for (int q = 0; q < RS; ++q)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = acc[q][mt][i];
-                v += __shfl_xor(v, 8);
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                acc[q][mt][i] = v;
-            }
-    // ---- sum the KW waves of each row set through LDS (the table is no longer read) ----
-    __syncthreads();
-    f32x4 *red = reinterpret_cast<f32x4 *>(tab);            // [wave][q][mt][rl]
-    if (G == 0) {
-#pragma unroll
-        for (int q = 0; q < RS; ++q)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) red[((wave * RS + q) * MT + mt) * 8 + rl] = acc[q][mt];
-    }
-    __syncthreads();
-    float *Yp = g.Yp + (int64_t)seg * g.M * g.N;
-    for (int idx = tid; idx < MT * 4 * R; idx += NTHR) {
-        const int m = idx / R, nl = idx % R;                // nl = 8 (h RS + q) + rl
-        const int mt = m >> 2, i = m & 3;
-        const int h = nl / (8 * RS), q = (nl / 8) % RS, r8 = nl & 7;
-        float v = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KW; ++k) v += red[(((h * KW + k) * RS + q) * MT + mt) * 8 + r8][i];
-        if (m < g.M && n0 + nl < g.N) Yp[m * g.N + n0 + nl] = v;
-    }
-}
-
-template <int MT>
-__device__ void t_part(const GemvArgs &g, uint32_t *lds, int t) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rt = (g.r + 63) >> 6;
-    const int kc = t / rt, ct = t % rt;
-    const int64_t c = (int64_t)ct * 64 + lane;          // this lane's T column
-    const int64_t nblk = g.K >> 6;
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.X, g.M * g.K * 2);
-    const __amdgpu_buffer_rsrc_t rL1 = make_rsrc(g.L1, g.K * g.r * 2);
-
-    f32x4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int64_t blk0 = ((int64_t)kc * TCHUNK + wave * (TCHUNK / NWAVE)) >> 6;
-#pragma unroll 1
-    for (int b = 0; b < TCHUNK / NWAVE / 64; ++b) {
-        const int64_t blk = blk0 + b;
-        const bool live = blk < nblk;
-        u32x2 xf[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xf[mt] = load_xfrag(rX, g, lane, mt, blk, live);
-        uint32_t e[64];
-        const uint32_t cbase = (live && c < g.r) ? (uint32_t)((blk * 64 * g.r + c) * 2) : OOB;
-        const uint32_t rstride = (uint32_t)(g.r * 2);
-#pragma unroll
-        for (int q = 0; q < 64; ++q) e[q] = bload2(rL1, cbase == OOB ? OOB : cbase + q * rstride);
-        static_for<0, 16>([&](auto sc) {
-            constexpr int s = decltype(sc)::value;
-            u32x2 bv;
-            bv.x = __builtin_amdgcn_perm(e[4 * s + 1], e[4 * s], 0x05040100u);
-            bv.y = __builtin_amdgcn_perm(e[4 * s + 3], e[4 * s + 2], 0x05040100u);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma4<s>(xf[mt], bv, acc[mt]);
-        });
-    }
-    f32x4 *red = reinterpret_cast<f32x4 *>(lds);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
-    __syncthreads();
-    float *Tp = g.Tp + (int64_t)kc * g.M * g.r;
-    for (int idx = tid; idx < MT * 4 * 64; idx += NTHR) {
-        const int m = idx >> 6, cl = idx & 63;
-        const int mt = m >> 2, i = m & 3;
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) v += red[(w * MT + mt) * 64 + cl][i];
-        const int64_t cc = (int64_t)ct * 64 + cl;
-        if (m < g.M && cc < g.r) Tp[m * g.r + cc] = v;
-    }
-}
-
-// Row sets per wave (RS), row groups per workgroup (RH) and register stages (NST), chosen so
-// that a wave stays within 128 registers (four waves per SIMD).  MT = 1: up to 4 tokens.
-template <int MT>
-struct WCfg {
-    static constexpr int RS = 2;
-    static constexpr int RH = 4;
-    static constexpr int NST = 2;
-    static constexpr int ROWS = 8 * RS * RH;
-};
-
-template <int MT>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_main_kernel(GemvArgs g) {
-    __shared__ __align__(16) uint32_t tab[256 * TAB_COPIES];
-    // the T workgroups come first so that they are dispatched first
-    const int wg = blockIdx.x;
-    if (wg < g.nt)
-        t_part<MT>(g, tab, wg);
-    else
-        w_part<MT, WCfg<MT>::RS, WCfg<MT>::RH, WCfg<MT>::NST>(g, tab, (wg - g.nt) % g.nrg, (wg - g.nt) / g.nrg);
-}
-
-struct EpiArgs {
-    const float *Yp;         // [S, M, N]
-    const float *Tp;         // [nkc, M, r]
-    const uint16_t *L2;      // [r, N]
-    uint16_t *Y;             // [M, N]
-    uint16_t *T_out;         // [M, r] or null
-    int64_t M, N;
-    int32_t r, nseg, nkc;
-    float scale;
-};
-
-// One workgroup per 64 output columns: s T is rebuilt from the K-slice partials, each wave adds
-// a quarter of the r terms of (s T) L2 for every token, and the quarters meet in LDS.  All global
-// loads are unconditional buffer loads (out-of-range ones return zero) issued before the first
-// barrier, so the kernel waits for memory once.
-template <int MT>
-__global__ __launch_bounds__(256) void gemv_epilogue_kernel(EpiArgs e) {
-    constexpr int MM = 4 * MT;
-    constexpr int TB = 16;                        // T partials per entry loaded together
-    __shared__ float sT[MM][128];
-    __shared__ float part[EWAVE][MM][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * 64, n = n0 + lane;
-    const int jq = e.r / EWAVE, j0 = wave * jq;   // r <= 128 and a multiple of 8: jq <= 32
-    const int E = (int)e.M * e.r;
-    const __amdgpu_buffer_rsrc_t rL2 = make_rsrc(e.L2, (int64_t)e.r * e.N * 2);
-    const __amdgpu_buffer_rsrc_t rY = make_rsrc(e.Yp, (int64_t)e.nseg * e.M * e.N * 4);
-    const __amdgpu_buffer_rsrc_t rT = make_rsrc(e.Tp, (int64_t)e.nkc * E * 4);
-
-    uint32_t l2raw[32];
-#pragma unroll
-    for (int q = 0; q < 32; ++q)
-        l2raw[q] = bload2(rL2, (q < jq && n < e.N) ? (uint32_t)(((int64_t)(j0 + q) * e.N + n) * 2) : OOB);
-    // base products of this thread's outputs (m, column) = (idx / 64, idx % 64), summed over segments
-    float ybase[MT];
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        const int idx = tid + 256 * j, m = idx >> 6;
-        const int64_t nn = n0 + (idx & 63);
-        const bool ok = m < e.M && nn < e.N;
-        float y = 0.0f;
-        for (int sg = 0; sg < e.nseg; ++sg)
-            y += __uint_as_float(bload4(rY, ok ? (uint32_t)((((int64_t)sg * e.M + m) * e.N + nn) * 4) : OOB));
-        ybase[j] = y;
-    }
-    // T partials of this thread's entries of s T (at most MM * 128 / 256 = 2 MT entries)
-    float tsum[2 * MT];
-#pragma unroll
-    for (int j = 0; j < 2 * MT; ++j) {
-        const int idx = tid + 256 * j;
-        float t = 0.0f;
-        for (int k0 = 0; k0 < e.nkc; k0 += TB) {
-            float v[TB];
-#pragma unroll
-            for (int q = 0; q < TB; ++q)
-                v[q] = __uint_as_float(bload4(rT, (idx < E && k0 + q < e.nkc)
-                                                     ? (uint32_t)(((int64_t)(k0 + q) * E + idx) * 4) : OOB));
-#pragma unroll
-            for (int q = 0; q < TB; ++q) t += v[q];
-        }
-        tsum[j] = t;
-    }
-    // s T rounded to bf16, zero outside [0, M) x [0, r)
-#pragma unroll
-    for (int j = 0; j < MM * 128 / 256; ++j) {
-        const int idx = tid + 256 * j;
-        reinterpret_cast<float *>(sT)[idx] = 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2 * MT; ++j) {
-        const int idx = tid + 256 * j;
-        if (idx < E) {
-            if (blockIdx.x == 0 && e.T_out) e.T_out[idx] = (uint16_t)f32_to_bf16(tsum[j]);
-            sT[idx / e.r][idx % e.r] = bf16_to_f32(f32_to_bf16(e.scale * tsum[j]));
-        }
-    }
-    __syncthreads();
+// Sum p[g][m] over the 64 lanes for each row g of the batch.  Afterwards the lane `holder` of
+// row g (BR = 8: lane 8 g + 7; BR = 4: lane 16 g + 15) has the total.
+template <int BR, int MM>
+__device__ __forceinline__ void reduce_rows(float (&p)[BR][MM], float (&out)[MM], int lane) {
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-        float acc = 0.0f;
+        // lane bit 5: rows g and g + BR/2 trade halves
+        float q[BR / 2];
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int j = min(j0 + q, 127);          // past r: l2 is zero and sT is zero
-            acc = __builtin_fmaf(sT[m][j], bf16_to_f32(l2raw[q] & 0xFFFFu), acc);
+        for (int g = 0; g < BR / 2; ++g) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[g][m]),
+                                                             __float_as_uint(p[g + BR / 2][m]), false, false);
+            q[g] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // row g + (BR/2) bit5
         }
-        part[wave][m][lane] = acc;
-    }
-    __syncthreads();
+        // lane bit 4: rows g and g + BR/4 of what is left
+        float u[BR / 4];
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        const int idx = tid + 256 * j, m = idx >> 6, nl = idx & 63;
-        const int64_t nn = n0 + nl;
-        if (m < e.M && nn < e.N) {
-            const float y = ybase[j] + part[0][m][nl] + part[1][m][nl] + part[2][m][nl] + part[3][m][nl];
-            e.Y[m * e.N + nn] = (uint16_t)f32_to_bf16(y);
+        for (int g = 0; g < BR / 4; ++g) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(q[g]),
+                                                             __float_as_uint(q[g + BR / 4]), false, false);
+            u[g] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
+        float t;
+        if constexpr (BR == 8) {
+            // lane bit 3: exchange with lane ^ 8 (rotate the 16-lane row by 8)
+            const bool b3 = (lane >> 3) & 1;
+            const float keep = b3 ? u[1] : u[0], send = b3 ? u[0] : u[1];
+            t = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128, 0xF, 0xF, false));
+            // the 8 lanes of a group: prefix sums end in lane 8 g + 7
+            t += dpp<0x111>(t);
+            t += dpp<0x112>(t);
+            t += dpp<0x114>(t);
+        } else {
+            t = u[0];
+            t += dpp<0x111>(t);
+            t += dpp<0x112>(t);
+            t += dpp<0x114>(t);
+            t += dpp<0x118>(t);
+        }
+        out[m] = t;
     }
 }
 
-template <int MT>
-hipError_t launch_mt(const GemvArgs &a, const EpiArgs &e, int grid_main, hipStream_t stream) {
-    timing_before(stream, 2);
-    hipLaunchKernelGGL(gemv_main_kernel<MT>, dim3(grid_main), dim3(NTHR), 0, stream, a);
-    hipError_t err = hipGetLastError();
-    timing_after(stream);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(gemv_epilogue_kernel<MT>, dim3((unsigned)((e.N + 63) / 64)), dim3(256), 0, stream, e);
+template <int MM, int BR, int U, int NWMAX>
+__global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
+    // ring of 2 U register slots, loads U rows ahead: row i sits in slot i % 2U, and the load of
+    // row i + U lands in a slot whose row is already consumed, so no value moves between
+    // registers (a move would wait for the load).  One loop iteration covers ITER rows.
+    constexpr int RING = 2 * U;
+    constexpr int ITER = BR > RING ? BR : RING;
+    static_assert(ITER % BR == 0 && ITER % RING == 0, "static ring slots per iteration");
+    // staging areas are filled by whole-wave DMA copies (1 KB or 256 bytes per wave and step)
+    __shared__ __align__(16) uint32_t tab[TAB_WORDS];
+    __shared__ __align__(16) uint32_t c2s[(C2_CAP + 2048) / 4];
+    __shared__ __align__(16) float c1s[128];
+    __shared__ float part[PART_CAP];              // [KW][R][MM]
+    __shared__ float sTs[4 * R_MAX_LORA];         // [MM][r]
+    __shared__ __align__(16) uint16_t l2s[R_MAX_LORA * R_MAX];   // [r][R]
+    __shared__ uint32_t cbh[16];
+    __shared__ float csum[CSUM_CAP];              // chunk sums of T's partials
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nthr = blockDim.x, nw = nthr >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = wave / a.KW, kw = wave - s * a.KW;
+    const int64_t n0 = (int64_t)blockIdx.x * a.R;
+    const int nrows = (int)min((int64_t)a.R, a.N - n0);
+    const int64_t nblk = a.K >> 6, wrow = a.K >> 1;
+    const int nchunk = (int)(a.K >> 5);
+    const int c = kw * 64 + lane;                 // this lane's 16-byte chunk of every row
+    const bool lane_ok = c < nchunk;
+    const int rs0 = s * a.RS;                     // first local row of this stream
+    auto lrow = [&](int i) { return rs0 + i; };    // local row of the stream's i-th row
+
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.packed, a.N * wrow);
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, a.M * a.K * 2);
+    auto wload = [&](int i) -> u32x4 {
+        const bool ok = lane_ok & (i < a.RS) & (lrow(i) < nrows);
+        const uint32_t off = (uint32_t)((n0 + lrow(i)) * wrow + 16 * c);
+        return bload16(rW, ok ? off : OOB);
+    };
+
+    // ---- prologue.  Issue order: the LDS copies (codes, second-level constants, L2 columns), X,
+    //      the first chunk of T's partials, then the first U weight rows.  The waits below stop
+    //      short of the weight rows, which stream in while the workgroup sets up. ----
+    const int64_t q0 = n0 * nblk;                 // first code of the workgroup
+    const int nc2 = nrows * (int)nblk;
+    const uintptr_t c2a = reinterpret_cast<uintptr_t>(a.c2 + q0);
+    const int sh = (int)(c2a & 15);               // 16-byte pieces from the aligned address below
+    const int n16 = (nc2 + sh + 15) >> 4;         // (never past the page holding the last code)
+    {
+        const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(reinterpret_cast<const void *>(c2a - sh), (int64_t)n16 * 16);
+        for (int i0 = wave * 64; i0 < n16; i0 += nthr)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rC2, (lds_void *)((lds_u8 *)c2s + i0 * 16), 16,
+                                                     (uint32_t)((i0 + lane) * 16), 0, 0, 0);
+    }
+    const int64_t c1lo = q0 >> 8;
+    const int nc1 = (int)(((q0 + nc2 - 1) >> 8) - c1lo + 1);
+    if (wave < 2) {
+        const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(a.c1, ((a.N * nblk + 255) >> 8) * 4);
+        const int i = wave * 64 + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rC1, (lds_void *)((lds_u8 *)c1s + wave * 256), 4,
+                                                 i < nc1 ? (uint32_t)((c1lo + i) * 4) : OOB, 0, 0, 0);
+    }
+    // L2 columns of the rows (used at the end): piece i = (j, p8) is L2[j][n0 + 8 p8 .. + 7]
+    {
+        const int R8 = a.R >> 3, npc = a.r * R8;
+        const __amdgpu_buffer_rsrc_t rL2 = make_rsrc(a.L2, (int64_t)a.r * a.N * 2);
+        for (int i0 = wave * 64; i0 < npc; i0 += nthr) {
+            const int i = i0 + lane;
+            const int j = i / R8, p8 = i - j * R8;
+            const bool ok = i < npc && 8 * p8 < nrows;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rL2, (lds_void *)((lds_u8 *)l2s + i0 * 16), 16,
+                                                     ok ? (uint32_t)(((int64_t)j * a.N + n0 + 8 * p8) * 2) : OOB,
+                                                     0, 0, 0);
+        }
+    }
+    // X[m][32 c + 2 i .. + 1] as bf16 pairs
+    uint32_t x[MM][16];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const u32x4 v = bload16(rX, (lane_ok && m < a.M) ? (uint32_t)((m * a.K + 32 * c) * 2 + 16 * h) : OOB);
+            x[m][4 * h] = v.x; x[m][4 * h + 1] = v.y; x[m][4 * h + 2] = v.z; x[m][4 * h + 3] = v.w;
+        }
+    // T's partials: pair p = (chunk p / EM, element p % EM); this thread's first pair
+    const int E = (int)a.M * a.r, EM = MM * a.r, nch = (a.nkc + 7) >> 3, npair = nch * EM;
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(a.Tp, (int64_t)a.nkc * E * 4);
+    const int pc0 = tid / EM, pe0 = tid - pc0 * EM;
+    float tv[8];
+    tp_chunk_load(rT, a.nkc, E, pe0, pc0, tid < npair, tv);
+    const float mean = a.mean[0];                 // (a load pending inside the loop would drain the ring)
+    __builtin_amdgcn_sched_barrier(0);            // the weight rows go out last
+    u32x4 ring[RING];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ring[u] = wload(u);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // pair table: dword e * 64 + copy holds cb[e & 15] | cb[e >> 4] << 16 (no loads involved)
+    if (tid < 16) cbh[tid] = cb_bf16(a.cb, (uint32_t)tid);
+    lds_barrier();
+    for (int i = tid; i < TAB_WORDS / 4; i += nthr) {
+        const uint32_t e = (uint32_t)i >> 4;
+        const uint32_t v = cbh[e & 15u] | (cbh[e >> 4] << 16);
+        reinterpret_cast<u32x4 *>(tab)[i] = u32x4{v, v, v, v};
+    }
+    // s T rounded to bf16 (zero past M): chunk sums, then the chunks in order
+    if (tid < npair) csum[tid] = tp_chunk_add(a.nkc, pc0, tv);
+    for (int p = tid + nthr; p < npair; p += nthr) {
+        const int cc = p / EM, e = p - cc * EM;
+        csum[p] = tp_chunk_sum(rT, a.nkc, E, e, cc);
+    }
+    lds_barrier();
+    for (int e = tid; e < EM; e += nthr) {
+        float t = -0.0f;
+        for (int cc = 0; cc < nch; ++cc) t += csum[cc * EM + e];
+        sTs[e] = e < E ? bf16_to_f32(f32_to_bf16(a.scale * t)) : 0.0f;
+        if (blockIdx.x == 0 && a.T_out && e < E) a.T_out[e] = (uint16_t)f32_to_bf16(t);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(U));     // all but the weight rows: the LDS copies landed
+    lds_barrier();
+
+    // ---- the rows of this stream ----
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    const uint8_t *c2b = reinterpret_cast<const uint8_t *>(c2s) + sh;
+    const uint32_t lb = (uint32_t)lane << 2;
+    const int bcol = min(c >> 1, (int)nblk - 1);  // quantization block of the lane's columns
+    const int gsel = BR == 8 ? (lane >> 3) : (lane >> 4);
+    const bool holder = BR == 8 ? ((lane & 7) == 7) : ((lane & 15) == 15);
+    const int nit = (a.RS + ITER - 1) / ITER;
+    for (int it = 0; it < nit; ++it) {
+        static_for<0, ITER / BR>([&](auto sbc) {
+            constexpr int sb = decltype(sbc)::value;
+            float p[BR][MM];
+            static_for<0, BR>([&](auto rc) {
+                constexpr int rq = decltype(rc)::value;
+                constexpr int rr = sb * BR + rq;          // row within the iteration
+                const int i = it * ITER + rr;
+                const u32x4 w = ring[rr % RING];
+                // the load of row i + U goes out here, before row i's arithmetic (left to
+                // itself the scheduler bunches the loads late and the ring stops hiding them)
+                __builtin_amdgcn_sched_barrier(0);
+                ring[(rr + U) % RING] = wload(i + U);
+                __builtin_amdgcn_sched_barrier(0);
+                // rows past the stream read zero codes; their clamped constant keeps sums finite
+                const int rl = min(lrow(i), nrows - 1);
+                const int qi = rl * (int)nblk + bcol;
+                const float sc = block_scale(c2b[qi], c1s[(int)(((q0 + qi) >> 8) - c1lo)], mean);
+                float d[MM];
+#pragma unroll
+                for (int m = 0; m < MM; ++m) d[m] = 0.0f;
+                static_for<0, 16>([&](auto bc) {
+                    constexpr int bi = decltype(bc)::value;
+                    constexpr uint32_t sel = 0x0C0C0000u | ((4u + (bi & 3)) << 8);
+                    const uint32_t pr =
+                        *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(w[bi >> 2], lb, sel));
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) d[m] = dot2(pr, x[m][bi], d[m]);
+                });
+#pragma unroll
+                for (int m = 0; m < MM; ++m) p[rq][m] = sc * d[m];
+            });
+            float res[MM];
+            reduce_rows<BR, MM>(p, res, lane);
+            const int i = it * ITER + sb * BR + gsel;
+            if (holder && i < a.RS && lrow(i) < nrows) {
+#pragma unroll
+                for (int m = 0; m < MM; ++m) part[(kw * a.R + lrow(i)) * MM + m] = res[m];
+            }
+        });
+    }
+    __syncthreads();
+
+    // ---- sum the KW waves of each row, add (s T) L2, store bf16: 8 lanes per output, lane q
+    //      of the 8 taking every 8th term of the r-long dot product ----
+    const int jn = a.r >> 3;
+    for (int i0 = 0; i0 < a.R * MM * 8; i0 += nthr) {     // uniform trip count (DPP below)
+        const int idx = (i0 + tid) >> 3, q = tid & 7;
+        const int m = idx / a.R, rl = idx - m * a.R;
+        const bool ok = idx < a.R * MM && m < a.M && rl < nrows;
+        float lo = 0.0f;
+        if (ok) {
+            for (int jj = 0; jj < jn; ++jj) {
+                const int j = 8 * jj + q;
+                lo = __builtin_fmaf(sTs[m * a.r + j], bf16_to_f32(l2s[j * a.R + rl]), lo);
+            }
+            if (q < a.KW) {
+                for (int k = q; k < a.KW; k += 8) lo += part[(k * a.R + rl) * MM + m];
+            }
+        }
+        lo += dpp<0x111>(lo);
+        lo += dpp<0x112>(lo);
+        lo += dpp<0x114>(lo);
+        if (ok && q == 7) a.Y[m * a.N + n0 + rl] = (uint16_t)f32_to_bf16(lo);
+    }
+}
+
+struct RowsPlan {
+    int KW, S, R, RS, grid;
+};
+
+// waves per workgroup: 16 (four per SIMD, 128 registers each); 12 for four tokens, whose X
+// values take 64 registers per lane
+int max_waves(int mm) { return mm > 2 ? 12 : MAX_WAVES; }
+
+RowsPlan rows_plan(int64_t N, int64_t K, int mm) {
+    RowsPlan p;
+    const int64_t nchunk = K >> 5, nblk = K >> 6;
+    const int nwmax = max_waves(mm);
+    p.KW = (int)((nchunk + 63) / 64);
+    p.S = p.KW <= nwmax ? nwmax / p.KW : 0;
+    // one workgroup per CU when the rows allow it
+    int64_t R = (N + 255) / 256;
+    R = (R + 7) & ~(int64_t)7;
+    int64_t cap = R_MAX;
+    if (cap > C2_CAP / nblk) cap = C2_CAP / nblk;
+    if (cap > PART_CAP / (4 * p.KW)) cap = PART_CAP / (4 * p.KW);
+    cap &= ~(int64_t)7;
+    if (R > cap) R = cap;
+    p.R = (int)R;
+    p.RS = p.S > 0 ? (int)((R + p.S - 1) / p.S) : 0;
+    p.grid = R > 0 ? (int)((N + R - 1) / R) : 0;
+    (void)mm;
+    return p;
+}
+
+int mm_of(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : 4); }
+int t_slices(int64_t M, int64_t K) { return (int)((K + t_rows(mm_of(M)) - 1) / t_rows(mm_of(M))); }
+
+template <int MM>
+hipError_t launch_t(const TArgs &t, int nkc, hipStream_t stream) {
+    hipLaunchKernelGGL(gemv_t_kernel<MM>, dim3(nkc), dim3(T_THREADS), 0, stream, t);
     return hipGetLastError();
 }
 
-int rows_per_wg(int64_t) { return WCfg<1>::ROWS; }
+template <int MM>
+hipError_t launch_mm(const TArgs &t, const RowsArgs &a, int nkc, int threads, int grid, hipStream_t stream) {
+    hipError_t err = launch_t<MM>(t, nkc, stream);
+    if (err != hipSuccess) return err;
+    timing_before(stream, 2);
+    hipLaunchKernelGGL((gemv_rows_kernel<MM, 4, 2, (MM > 2 ? 12 : MAX_WAVES)>), dim3(grid), dim3(threads), 0, stream, a);
+    err = hipGetLastError();
+    timing_after(stream);
+    return err;
+}
 
 }  // namespace
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     GemvPlan p;
-    const int64_t nrg = (N + rows_per_wg(M) - 1) / rows_per_wg(M);
-    const int64_t nmacro = ((K >> 6) + MACRO_BLOCKS - 1) / MACRO_BLOCKS;
-    // about two workgroups per CU (16 waves), each wave keeping at least two macro steps
-    int64_t s = 512 / nrg;
-    if (s > nmacro / 8) s = nmacro / 8;
-    if (s < 1) s = 1;
-    // a segment's block constants fit the LDS staging area
-    const int64_t min_seg = (nmacro * MACRO_BLOCKS + SEG_BLOCKS - 1) / SEG_BLOCKS;
-    if (s < min_seg) s = min_seg;
-    p.nseg = (int)s;
-    p.nkc = (int)((K + TCHUNK - 1) / TCHUNK);
-    p.yp_floats = (size_t)s * M * N;
+    (void)N;
+    p.nseg = 1;
+    p.nkc = t_slices(M, K);
+    p.yp_floats = 0;
     p.tp_floats = (size_t)p.nkc * M * r;
-    (void)r;
     return p;
+}
+
+hipError_t launch_gemv_T(const uint16_t *X, const uint16_t *L1, int32_t r, int64_t M, int64_t K, float *Tp,
+                        uint16_t *T, hipStream_t stream) {
+    if (M < 1 || M > 4 || r < 8 || r > R_MAX_LORA || r % 8) return hipErrorInvalidValue;
+    TArgs t;
+    t.X = X; t.L1 = L1; t.Tp = Tp; t.M = M; t.K = K; t.r = r;
+    const int nkc = t_slices(M, K);
+    hipError_t err;
+    switch (mm_of(M)) {
+        case 1: err = launch_t<1>(t, nkc, stream); break;
+        case 2: err = launch_t<2>(t, nkc, stream); break;
+        default: err = launch_t<4>(t, nkc, stream); break;
+    }
+    if (err != hipSuccess) return err;
+    const int E = (int)M * r;
+    hipLaunchKernelGGL(gemv_tsum_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, Tp, nkc, E, T);
+    return hipGetLastError();
+}
+
+bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t r) {
+    if (M < 1 || M > 4 || r < 8 || r > R_MAX_LORA || r % 8 || N % 8 || K % 64) return false;
+    const int mm = mm_of(M);
+    const RowsPlan p = rows_plan(N, K, mm);
+    const int64_t nch = (t_slices(M, K) + 7) / 8;
+    return p.S >= 1 && p.R >= 8 && p.R <= R_MAX && p.R * (K >> 6) <= C2_CAP && (int64_t)p.KW * p.R * mm <= PART_CAP &&
+           nch * mm * r <= CSUM_CAP;
 }
 
 hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                            float scale, int32_t r, int64_t M, uint16_t *Y, uint16_t *T_out, float *Yp,
                            float *Tp, hipStream_t stream) {
-    const GemvPlan p = gemv_plan(M, w.rows, w.cols, r);
-    // second-level constants of one workgroup's rows must fit the LDS staging area
-    if ((rows_per_wg(M) - 1) * (w.cols / 64) / 256 + 3 > C1_MAX) return hipErrorNotSupported;
-    GemvArgs a;
+    (void)Yp;
+    if (M < 1 || M > 4) return hipErrorInvalidValue;   // larger token counts take another path
+    if (!gemv_fits(M, w.rows, w.cols, r)) return hipErrorNotSupported;
+    const int mm = mm_of(M);
+    const GemvPlan g = gemv_plan(M, w.rows, w.cols, r);
+    const RowsPlan p = rows_plan(w.rows, w.cols, mm);
+    const int threads = p.S * p.KW * 64;
+    TArgs t;
+    t.X = X; t.L1 = L1; t.Tp = Tp; t.M = M; t.K = w.cols; t.r = r;
+    RowsArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
-    a.L1 = L1; a.Yp = Yp; a.Tp = Tp;
-    a.M = M; a.N = w.rows; a.K = w.cols; a.r = r;
-    a.nseg = p.nseg;
-    a.nrg = (int)((w.rows + rows_per_wg(M) - 1) / rows_per_wg(M));
+    a.L2 = L2; a.Tp = Tp; a.Y = Y; a.T_out = T_out;
+    a.M = M; a.N = w.rows; a.K = w.cols;
+    a.r = r; a.nkc = g.nkc; a.KW = p.KW; a.S = p.S; a.RS = p.RS; a.R = p.R;
+    a.scale = scale;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
-    const int rt = (r + 63) / 64;
-    a.nt = p.nkc * rt;
-    const int grid = a.nrg * a.nseg + a.nt;
-    EpiArgs e;
-    e.Yp = Yp; e.Tp = Tp; e.L2 = L2; e.Y = Y; e.T_out = T_out;
-    e.M = M; e.N = w.rows; e.r = r; e.nseg = p.nseg; e.nkc = p.nkc; e.scale = scale;
-    if (M > 4) return hipErrorInvalidValue;           // larger token counts take another path
-    return launch_mt<1>(a, e, grid, stream);
+    switch (mm) {
+        case 1: return launch_mm<1>(t, a, g.nkc, threads, p.grid, stream);
+        case 2: return launch_mm<2>(t, a, g.nkc, threads, p.grid, stream);
+        default: return launch_mm<4>(t, a, g.nkc, threads, p.grid, stream);
+    }
 }
 
 }  // namespace nf4k

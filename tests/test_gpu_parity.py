@@ -165,6 +165,13 @@ SHAPES = [
     (3, 200, 1344, 16),        # decode-size path: ragged K (not a multiple of 256 or 1024)
     (16, 72, 2112, 64),
     (2, 1032, 3072, 8),
+    (1, 3000, 8192, 64),       # decode-size: four waves per row, ragged last row group
+    (2, 3000, 11008, 128),     # decode-size: six waves per row (the last part-filled), r = 128
+    (4, 1000, 22016, 64),      # decode-size, four tokens: eleven waves per row
+    (4, 64, 26624, 8),         # a row too long for one workgroup's waves: the wide GEMV takes it
+    (3, 8, 64, 8),             # one quantization block per row, a single row group
+    (1, 8192, 16384, 64),      # decode-size: several reduction batches per row stream
+    (2, 8192, 16384, 16),
     # from 1024 tokens on: bf16 expansion of the weight + K-extended bf16 GEMM
     (1024, 520, 384, 16),      # ragged N (the backward's reduction), odd number of K steps
     (1100, 264, 640, 24),      # ragged M and N
