@@ -1,13 +1,12 @@
-// Fused double-dequantize + bf16 MFMA GEMM for the QLoRA linear layer (gfx950).
+// Fused double-dequantize + bf16 MFMA GEMM for the backward of the QLoRA linear layer at
+// 16 < M < 1024 tokens (gfx950):
+//   dX = dY . deq(W) + dT . L1^T       reduction over N (the W rows), output cols = W cols
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
-// section 3.5 eq. (5) (forward), eq. (6) (double dequantization to BF16) and the backward
-// description (gradient to X through the BF16 weight only); section 4 eq. (3) (scalar s).
+// section 3.5 eq. (6) (double dequantization to BF16) and the backward description (gradient to
+// X through the BF16 weight only); section 4 eq. (3) (scalar s, inside dT).
 //
-// Two orientations of one kernel:
-//   forward  Y  = X  . deq(W)^T + (sT) . L2        reduction over K, output cols = W rows
-//   backward dX = dY . deq(W)   + dT  . L1^T       reduction over N, output cols = W cols
-// The LoRA product is appended as extra reduction steps: A' = [A | Ae], B' = [deq(W) ; Be],
+// The LoRA product is appended as extra reduction steps: A' = [dY | dT], B' = [deq(W) ; L1^T],
 // so it costs r/64 more steps of the same MFMA loop and no extra pass over the activations.
 //
 // Block tile 256 x 256 outputs, reduction step 64 (one quantization block per W row), 4 waves
@@ -21,10 +20,9 @@
 // [W row][W col], one thread per (row, 64-column block), i.e. one quantization block:
 //   a' = fma(e4m3(c2), c1, mean);  lut[j] = bf16(cb[j] * a') for the 16 codes
 // The 16-entry bf16 table lives in 8 registers as byte planes, and each packed dword (8 codes)
-// is expanded with v_perm_b32 byte selects (no LDS lookups, no per-element multiply).
-//   - forward: the W rows are the output columns, fragments are 16-byte row reads.
-//   - backward: the W rows are the reduction, fragments come from ds_read_b64_tr_b16, which
-//     transposes 4 x 16 bf16 blocks across each 16-lane group.
+// is expanded with v_perm_b32 byte selects (no LDS lookups, no per-element multiply).  The W rows
+// are the reduction, so fragments come from ds_read_b64_tr_b16, which transposes 4 x 16 bf16
+// blocks across each 16-lane group.
 // Register stages of W are fetched two steps ahead; the dequantization of step s+1 is spread
 // over the four MFMA sub-steps of step s.
 
@@ -45,20 +43,12 @@ constexpr int A_STAGE = TM * TK * 2;                 // 32 KB, swizzled, unpadde
 // expcnt unchecked, lgkmcnt = 0.  gfx9 layout: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14
 constexpr int kWaitA = 4 | (7 << 4) | (0 << 8);
 
-// B stage layouts: rows of 64 reduction elements ([out col][red], 144-byte rows) or rows of 256
-// output columns ([red][out col], 544-byte rows).  The main loop uses the first in the forward and
-// the second in the backward; the LoRA extension step uses the other one (its B operand, L2 [r, N]
-// or L1 [K, r], is read in its natural layout), so a stage is sized for both.
+// B stage layouts: the main loop's dequantized W step is [red][out col] (544-byte rows); the
+// LoRA extension step's L1 [K, r] is read in its natural layout, [out col][red] (144-byte rows).
+// A stage is sized for both.
 constexpr int ROWB_RED = (TK + 8) * 2;     // [256][64 + 8]
 constexpr int ROWB_OUT = (TN + 16) * 2;    // [64][256 + 16]
 constexpr int B_STAGE_BYTES = (TN * ROWB_RED > TK * ROWB_OUT) ? TN * ROWB_RED : TK * ROWB_OUT;
-template <bool BWD> struct BLayout;
-template <> struct BLayout<false> {
-    static constexpr int ROWS = TN, ROWB = ROWB_RED;
-};
-template <> struct BLayout<true> {
-    static constexpr int ROWS = TK, ROWB = ROWB_OUT;
-};
 
 struct GemmArgs {
     const uint16_t *A;       // [M, Kred] bf16
@@ -66,8 +56,8 @@ struct GemmArgs {
     const uint8_t *c2;       // E4M3 block constants
     const float *c1;         // 256-block multipliers
     const float *mean;       // [1]
-    const uint16_t *Ae;      // [M, r] bf16 (extension A: s T forward, dT backward)
-    const uint16_t *Be;      // forward: L2 [r, Nout]; backward: L1 [Nout, r]  (natural layouts)
+    const uint16_t *Ae;      // dT [M, r] bf16 (extension A)
+    const uint16_t *Be;      // L1 [Nout, r] (natural layout)
     uint16_t *C;             // [M, Nout] bf16
     int64_t M, Nout, Kred;
     int64_t wrows, wcols;
@@ -77,9 +67,7 @@ struct GemmArgs {
 };
 
 
-template <bool BWD>
-__global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
-    typedef BLayout<BWD> BL;
+__global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     constexpr int B_STAGE = B_STAGE_BYTES;
     // separate LDS objects, so the compiler sees that the direct-to-LDS A loads never alias the
     // B tile reads and adds no memory-counter waits of its own before them
@@ -130,7 +118,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     const int kred32 = (int)g.Kred;
     auto load_A = [&](int step, uint8_t *Ad) {
         // reduction columns left from this step on; <= 0 past the last step (loads read zeros),
-        // < 64 on a ragged backward last step (its columns past N read zeros)
+        // < 64 on a ragged last step (its columns past N read zeros)
         const int rem = kred32 - step * TK;
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
         lds_u8 *dst = (lds_u8 *)Ad + wave * 8192;
@@ -142,20 +130,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         }
     };
 
-    // ---- W: thread -> (row, 64-column block) ----
-    //   forward : W row o0 + tid, block = step
-    //   backward: W row step*64 + tid%64, block o0/64 + tid/64
-    const int bw_row = BWD ? (tid & 63) : tid;
-    const int bw_blk = BWD ? (tid >> 6) : 0;
+    // ---- W: thread -> (W row step*64 + tid%64, 64-column block o0/64 + tid/64) ----
+    const int bw_row = tid & 63;
+    const int bw_blk = tid >> 6;
     struct WStage {
         u32x4 w[2];
         uint32_t c2, c1;
     };
     auto load_W = [&](int step, WStage &ws) {
         const bool live = step < main_steps;
-        int64_t n, blk;
-        if (!BWD) { n = o0 + tid; blk = step; }
-        else { n = (int64_t)step * TK + bw_row; blk = (o0 >> 6) + bw_blk; }
+        const int64_t n = (int64_t)step * TK + bw_row, blk = (o0 >> 6) + bw_blk;
         const uint32_t off = (uint32_t)(n * wrow_bytes + blk * 32);
         const uint32_t b = (uint32_t)(n * wblk_per_row + blk);
         ws.w[0] = bload16(rW, live ? off : 0xFFFFFFF0u);
@@ -168,15 +152,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     auto write_B = [&](int step, const WStage &ws, uint8_t *Bst, int part) {
         if (part == 0) {
             float a = block_scale(ws.c2, __uint_as_float(ws.c1), mean);
-            if (BWD && (int64_t)step * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
+            if ((int64_t)step * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
             lut = make_lut(g.cb, a);
         }
-        uint8_t *Bd = Bst + bw_row * BL::ROWB + bw_blk * 128;
+        uint8_t *Bd = Bst + bw_row * ROWB_OUT + bw_blk * 128;
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd) {
             const int d = part * 2 + dd;
             const uint32_t w = ws.w[d >> 2][d & 3];
-            *reinterpret_cast<u32x4 *>(Bd + d * 16) = BWD ? dequant8_planar(lut, w) : dequant8(lut, w);
+            *reinterpret_cast<u32x4 *>(Bd + d * 16) = dequant8_planar(lut, w);
         }
     };
 
@@ -195,12 +179,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         const int c = (2 * s + hh) ^ ((row >> 1) & 7);
         return *reinterpret_cast<const bf16x8 *>(Ast + row * 128 + c * 16);
     };
-    // B fragment from a [out col][red] tile (row reads) or a [red][out col] tile (transposing reads)
+    // B fragment of the extension step, from its [out col][red] tile (row reads)
     auto frag_rowread = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
         const int row = wn * 128 + j * 32 + r32;
         return *reinterpret_cast<const bf16x8 *>(Bst + row * ROWB_RED + (s * 16 + hh * 8) * 2);
     };
-    auto frag_trread = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
+    // B fragment of a main-loop step, from its [red][out col] tile: 16-lane group (hh, half):
+    // lane i of the group reads row 16s + 8hh + i/4 (+4), columns col0 + 4(i%4) .. +3; after
+    // the transpose, lane i holds column col0 + i.
+    auto frag_B = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
         const int i16 = lane & 15, half = (lane >> 4) & 1;
         const int col0 = wn * 128 + j * 32 + half * 16;
         const int rowb = s * 16 + hh * 8 + (i16 >> 2);
@@ -209,23 +196,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * ROWB_OUT));
         const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8, v);
-    };
-    auto frag_B = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
-        if (!BWD) {
-            const int row = wn * 128 + j * 32 + r32;
-            return *reinterpret_cast<const bf16x8 *>(Bst + row * BL::ROWB + (s * 16 + hh * 8) * 2);
-        } else {
-            // 16-lane group (hh, half): lane i of the group reads row 16s + 8hh + 4e + i/4,
-            // columns col0 + 4(i%4) .. +3; after the transpose, lane i holds column col0 + i.
-            const int i16 = lane & 15, half = (lane >> 4) & 1;
-            const int col0 = wn * 128 + j * 32 + half * 16;
-            const int rowb = s * 16 + hh * 8 + (i16 >> 2);
-            const uint8_t *base = Bst + (col0 + 4 * (i16 & 3)) * 2;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * BL::ROWB));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * BL::ROWB));
-            const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            return __builtin_bit_cast(bf16x8, v);
-        }
     };
     struct Frags {
         bf16x8 a[4], b[4];
@@ -312,14 +282,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
         __syncthreads();
     }
 
-    // ---- LoRA extension: [A | Ae] . [B ; Be], r/64 more steps (zero padded past r) ----
-    // forward : Be = L2 [r, N]: tile [j][out col] (544-byte rows), transposing fragment reads
-    // backward: Be = L1 [K, r]: tile [out col][j] (144-byte rows, columns at their planar
-    //           positions), row fragment reads
+    // ---- LoRA extension: [dY | dT] . [deq(W) ; L1^T], r/64 more steps (zero padded past r) ----
+    // L1 [K, r]: tile [out col][j] (144-byte rows, columns at their planar positions), row reads
     if (ext_steps > 0) {
         const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
-        const __amdgpu_buffer_rsrc_t rBe = BWD ? make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2)
-                                               : make_rsrc(g.Be, (int64_t)g.r * g.Nout * 2);
+        const __amdgpu_buffer_rsrc_t rBe = make_rsrc(g.Be + o0 * g.r, (g.Nout - o0) * (int64_t)g.r * 2);
         for (int e = 0; e < ext_steps; ++e) {
             const int st = (main_steps + e) & 1;
             uint8_t *Ast = st ? As1 : As0;
@@ -333,18 +300,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
                 const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0xFFFFFFF0u;
                 const u32x4 va = bload16(rAe, off);
                 *reinterpret_cast<u32x4 *>(Ast + row * 128 + (chunk ^ ((row >> 1) & 7)) * 16) = va;
-                if (BWD) {
-                    // B: output column o0 + row, reduction chunk
-                    const u32x4 vb = bload16(rBe, off);
-                    const int pos = (row & ~7) | ((row & 1) << 2) | ((row & 7) >> 1);
-                    *reinterpret_cast<u32x4 *>(Bst + pos * ROWB_RED + chunk * 16) = vb;
-                } else {
-                    // B: reduction row j0 + tid/32 + 8 q, output columns o0 + 8 (tid % 32)
-                    const int jr = j0 + (tid >> 5) + 8 * q, oc = (tid & 31) * 8;
-                    const uint32_t ob = (jr < g.r) ? (uint32_t)(((int64_t)jr * g.Nout + o0 + oc) * 2) : 0xFFFFFFF0u;
-                    const u32x4 vb = bload16(rBe, ob);
-                    *reinterpret_cast<u32x4 *>(Bst + ((tid >> 5) + 8 * q) * ROWB_OUT + oc * 2) = vb;
-                }
+                // B: output column o0 + row, reduction chunk
+                const u32x4 vb = bload16(rBe, off);
+                const int pos = (row & ~7) | ((row & 1) << 2) | ((row & 7) >> 1);
+                *reinterpret_cast<u32x4 *>(Bst + pos * ROWB_RED + chunk * 16) = vb;
             }
             __syncthreads();
 #pragma unroll
@@ -353,7 +312,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) f.a[i] = frag_A(Ast, s, i);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) f.b[j] = BWD ? frag_rowread(Bst, s, j) : frag_trread(Bst, s, j);
+                for (int j = 0; j < 4; ++j) f.b[j] = frag_rowread(Bst, s, j);
                 mma(f);
             }
             __syncthreads();
@@ -361,11 +320,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     }
 
     // ---- epilogue: fp32 -> bf16 ----
-    // Lane (r32, hh) of tile (i, j) holds column j*32 + r32 (permuted back for the backward's
-    // planar dequant order) and rows i*32 + 8*(v/4) + 4*hh + v%4.  Stores go through a buffer
+    // Lane (r32, hh) of tile (i, j) holds column j*32 + r32 (permuted back from the planar
+    // dequant order) and rows i*32 + 8*(v/4) + 4*hh + v%4.  Stores go through a buffer
     // descriptor: rows past M fall outside it, row offsets are scalars, the column offset is a
     // per-lane constant, so no per-element address arithmetic remains.
-    const int colw = BWD ? ((r32 & ~7) | planar_col(r32 & 7)) : r32;
+    const int colw = (r32 & ~7) | planar_col(r32 & 7);
     if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
         const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
@@ -407,12 +366,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_kernel(GemmArgs g) {
     }
 }
 
-template <bool BWD>
 hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
-    timing_before(stream, BWD ? 1 : 0);
-    hipLaunchKernelGGL(dqgemm_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    timing_before(stream, 1);
+    hipLaunchKernelGGL(dqgemm_bwd_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
@@ -431,7 +389,7 @@ hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint
     a.wrows = w.rows; a.wcols = w.cols;
     a.r = r; a.accumulate = accumulate ? 1u : 0u;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
-    return launch_impl<true>(a, stream);
+    return launch_impl(a, stream);
 }
 
 }  // namespace nf4k

@@ -1,5 +1,5 @@
-// Device helpers shared by the fused dequant-GEMM kernels (gfx950): buffer descriptors, the
-// XCD-aware tile order, and the per-block 16-entry bf16 table with its v_perm_b32 lookups.
+// Device helpers shared by the kernels (gfx950): buffer descriptors and loads, the XCD-aware tile
+// order, and the per-block 16-entry bf16 table with its v_perm_b32 lookups.
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
 // section 3.5 eq. (6): each weight element is cb[code] * a' rounded once to bf16, with

@@ -19,6 +19,7 @@
 // Epilogue: 2 more MFMAs add s T L2 (A = s T, B = a strided gather of L2), then bf16 stores.
 
 #include "common.h"
+#include "dqtile.h"
 #include "launch.h"
 
 namespace nf4k {
@@ -31,69 +32,8 @@ constexpr int XWIN = 1024;                     // X window (columns)
 constexpr int XROW = XWIN + 8;                 // padded LDS row (elements): rows start 4 banks apart
 constexpr int MACRO = 256;                     // columns per macro step (4 blocks)
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t clamped = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)clamped, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
-}
 __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-
-struct Lut {
-    uint32_t la0, la1, lb0, lb1, ha0, ha1, hb0, hb1;
-};
-
-__device__ __forceinline__ Lut make_lut(const Codebook &cb, float a) {
-    uint32_t p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = pack_bf16x2(cb.v[2 * j] * a, cb.v[2 * j + 1] * a);
-    Lut t;
-    t.la0 = __builtin_amdgcn_perm(p[1], p[0], 0x06040200u);
-    t.ha0 = __builtin_amdgcn_perm(p[1], p[0], 0x07050301u);
-    t.la1 = __builtin_amdgcn_perm(p[3], p[2], 0x06040200u);
-    t.ha1 = __builtin_amdgcn_perm(p[3], p[2], 0x07050301u);
-    t.lb0 = __builtin_amdgcn_perm(p[5], p[4], 0x06040200u);
-    t.hb0 = __builtin_amdgcn_perm(p[5], p[4], 0x07050301u);
-    t.lb1 = __builtin_amdgcn_perm(p[7], p[6], 0x06040200u);
-    t.hb1 = __builtin_amdgcn_perm(p[7], p[6], 0x07050301u);
-    return t;
-}
-
-__device__ __forceinline__ void lut4(const Lut &t, uint32_t x, uint32_t &lo, uint32_t &hi) {
-    // perm(0, 0, x + 5) is 0xFF exactly where x >= 8 (selectors 8..12 give 0 on zero sources,
-    // >= 13 give 0xFF)
-    const uint32_t m = __builtin_amdgcn_perm(0u, 0u, x + 0x05050505u);
-    const uint32_t xb = x ^ 0x08080808u;
-    const uint32_t la = __builtin_amdgcn_perm(t.la1, t.la0, x);
-    const uint32_t lb = __builtin_amdgcn_perm(t.lb1, t.lb0, xb);
-    const uint32_t ha = __builtin_amdgcn_perm(t.ha1, t.ha0, x);
-    const uint32_t hb = __builtin_amdgcn_perm(t.hb1, t.hb0, xb);
-    lo = (m & lb) | (~m & la);
-    hi = (m & hb) | (~m & ha);
-}
-
-// 8 codes -> bf16 in planar order: (e0,e2), (e4,e6), (e1,e3), (e5,e7)
-__device__ __forceinline__ u32x4 dequant8_planar(const Lut &t, uint32_t w) {
-    uint32_t le, he, lo, ho;
-    lut4(t, w & 0x0F0F0F0Fu, le, he);
-    lut4(t, (w >> 4) & 0x0F0F0F0Fu, lo, ho);
-    u32x4 o;
-    o.x = __builtin_amdgcn_perm(he, le, 0x05010400u);
-    o.y = __builtin_amdgcn_perm(he, le, 0x07030602u);
-    o.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);
-    o.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
-    return o;
 }
 
 // natural 8 bf16 (4 dwords: pairs (0,1),(2,3),(4,5),(6,7)) -> planar order

@@ -15,6 +15,7 @@
 // MFMA v_mfma_f32_32x32x16_bf16, 4 waves of 32 x 32.
 
 #include "common.h"
+#include "dqtile.h"
 #include "launch.h"
 #include "reduce.h"
 
@@ -26,17 +27,6 @@ constexpr int ST = 64;          // block tile (both output dims) and reduction s
 constexpr int NSTAGE = 4;       // reduction steps in flight per block tile
 constexpr int ROWB = (ST + 8) * 2;   // padded LDS row, bytes (144: conflict-free 16-byte reads)
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t clamped = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)clamped, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
 
 // 16-byte fragment of row `row` (the M/N index), reduction elements 16 s + 8 hh .. +7 of a tile
 // stored [row][reduction]
