@@ -1,4 +1,4 @@
-// Decode-size forward (M <= 4 tokens) of the QLoRA linear layer (gfx950):
+// Decode-size forward (M <= 8 tokens) of the QLoRA linear layer (gfx950):
 //   Y = X deq(W)^T + s (X L1) L2
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
@@ -7,26 +7,31 @@
 // This shape streams the 4-bit weight once from HBM; everything else has to hide behind that
 // stream.  Two launches:
 //
-// gemv_t_kernel: T = X L1 in slices of 64 M' rows of L1 (M' = 1, 2, 4: M rounded up; fp32
-//   partials, summed by the next launch).
+// T's partials: gemv_t_kernel computes T = X L1 in slices of 64 M' rows of L1 (M' = 1, 2, 4: M
+//   rounded up) for M <= 4; from 5 tokens the split-K skinny product of the LoRA kernels does.
+//   Either way the fp32 partials are summed by the next launch in a fixed chunked order.
 //
 // gemv_rows_kernel: one workgroup of up to 16 waves per CU owns a run of R weight rows over the
 //   whole reduction, so it finishes its outputs itself:
-//   - KW waves side by side cover one row: lane l of wave k always takes the same 16 bytes of a
-//     row (32 columns, half a quantization block), so its X values are loaded once and stay in
+//   - KW waves side by side cover a row; a lane always takes the same 16-byte chunks (32
+//     columns, half a quantization block), so its X values are loaded once and stay in
 //     registers for every row.  The workgroup runs S = 16 / KW such row streams, each walking its
 //     rows with U loads in flight per lane.
+//   - one token: the 64 lanes of a wave take 64 chunks of the same row, one v_dot2_f32_bf16 per
+//     code pair.  2 to 8 tokens: lane 4 b + j takes chunk b of row j of a 4-row group, and each
+//     chunk feeds 8 v_mfma_f32_4x4x4_16b_bf16 per group of 4 tokens (v_dot2 issues at about a
+//     quarter of the VALU rate, so more than one token goes to the matrix cores).
 //   - codes are decoded through a pair table in LDS: entry e (one packed byte) holds the bf16
 //     codebook values of its two nibbles, 64 copies side by side so that lane l reads bank l.
 //     The address is one v_perm (the code byte next to the lane offset), the lookup one
-//     ds_read_b32, the product one v_dot2_f32_bf16 per token.
+//     ds_read_b32.
 //   - the table is the plain codebook, so each half-block partial is scaled afterwards by its
 //     block constant a = fma(e4m3(c2), c1, mean) (eq. 6, fp32), staged with the codes in LDS:
 //     y = sum_blocks a_b sum_{k in b} x_k cb[q_k].  This equals X deq(W)^T up to rounding, with
 //     the codebook rounded to bf16 instead of each product cb * a.
-//   - the lane partials of BR rows are summed across the wave with lane swaps and DPP, across the
-//     KW waves in LDS; the LoRA term (s T) L2 of the workgroup's rows (s T rounded to bf16, L2
-//     staged in LDS at the start) is added before the bf16 store.
+//   - lane partials are summed across the wave with lane swaps and DPP, across the KW waves in
+//     LDS; the LoRA term (s T) L2 of the workgroup's rows (s T rounded to bf16, L2 staged in LDS
+//     at the start) is added before the bf16 store.
 
 #include "common.h"
 #include "dqtile.h"
@@ -44,8 +49,9 @@ constexpr int C2_CAP = 16384;                  // staged code bytes per workgrou
 constexpr int C1_CAP = C2_CAP / 256 + 2;       // staged second-level constants
 constexpr int R_MAX = 128;                     // rows per workgroup
 constexpr int R_MAX_LORA = 128;                // r
-constexpr int PART_CAP = 2048;                 // KW * R * MM partial sums
-constexpr int CSUM_CAP = 8192;                 // chunk sums of T's partials per workgroup
+constexpr int CSUM_CAP = 8192;                 // shared scratch: T's chunk sums, then the row partials
+constexpr int PART_CAP = 2048;                 // KW * R partial sums (one token)
+constexpr int RES_OFF = 4096;                  // 4x4-MFMA layout: batch partials below, row sums above
 constexpr int T_THREADS = 256;
 // rows of L1 per T workgroup: short slices spread the 1 MB-scale L1 read over many CUs (one CU
 // alone pulls only a few tens of GB/s); their partials are summed by the consumer
@@ -285,23 +291,62 @@ __device__ __forceinline__ void reduce_rows(float (&p)[BR][MM], float (&out)[MM]
     }
 }
 
-template <int MM, int BR, int U, int NWMAX>
+// Lane partials of the 4 x 4 MFMA layout, f32x4 c = tokens 0..3 of the lane's row j = lane % 4 at
+// block b = lane / 4: summed over the 16 blocks.  Afterwards lane l with (l & 12) == 12 holds
+// row l % 4, token 2 (l >> 5) + ((l >> 4) & 1).
+__device__ __forceinline__ float reduce_blocks4(f32x4 c) {
+    // lane bit 5: tokens 0, 1 stay in the lower half-wave, 2, 3 in the upper
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c.x), __float_as_uint(c.z), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c.y), __float_as_uint(c.w), false, false);
+    const float q0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const float q1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+    // lane bit 4: token 2 b5 + b4
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
+    float t = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+    // lane bits 2, 3 (same row j, four blocks of the 16-lane row): prefix sums end in lanes 12..15
+    t += dpp<0x114>(t);
+    t += dpp<0x118>(t);
+    return t;
+}
+
+// C += A B over 16 independent 4 x 4 x 4 blocks (bf16 inputs, fp32 accumulation)
+__device__ __forceinline__ f32x4 mfma4x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, u32x2{a0, a1}),
+                                                  __builtin_bit_cast(s16x4, u32x2{b0, b1}), c, 0, 0, 0);
+}
+
+// MF = false: one token (M = 1): lanes of a wave take 64 consecutive 16-byte chunks of the same
+//   row, products with v_dot2_f32_bf16, BR rows summed per cross-lane reduction.
+// MF = true: MM = 4 or 8 tokens: lane 4 b + j takes chunk b of row j of a 4-row group, and
+//   each 16-byte chunk (32 codes) feeds 8 v_mfma_f32_4x4x4_16b_bf16 per group of 4 tokens
+//   (B = the four rows' decoded pairs, A = X of four tokens over the same 4 columns).
+//   v_dot2_f32_bf16 issues at about a quarter of the VALU rate, so beyond one token the
+//   products go to the matrix cores.  The cross-wave sums run per batch of ITER row steps.
+template <int MM, int BR, int U, int NWMAX, bool MF>
 __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
-    // ring of 2 U register slots, loads U rows ahead: row i sits in slot i % 2U, and the load of
-    // row i + U lands in a slot whose row is already consumed, so no value moves between
-    // registers (a move would wait for the load).  One loop iteration covers ITER rows.
+    // ring of 2 U register slots, loads U row steps ahead: step i sits in slot i % 2U, and the
+    // load of step i + U lands in a slot whose step is already consumed, so no value moves
+    // between registers (a move would wait for the load).  One loop iteration covers ITER steps.
     constexpr int RING = 2 * U;
     constexpr int ITER = BR > RING ? BR : RING;
     static_assert(ITER % BR == 0 && ITER % RING == 0, "static ring slots per iteration");
+    constexpr int NX = MF ? MM / 4 : MM;        // X register groups (tokens, or groups of 4)
+    constexpr int ROWS_STEP = MF ? 4 : 1;        // rows per row step and lane group
+    constexpr int LANES_ROW = MF ? 16 : 64;      // 16-byte chunks of a row per wave and step
+    constexpr int BROWS = ITER * ROWS_STEP;      // rows per batch of the cross-wave sums (MF)
     // staging areas are filled by whole-wave DMA copies (1 KB or 256 bytes per wave and step)
     __shared__ __align__(16) uint32_t tab[TAB_WORDS];
     __shared__ __align__(16) uint32_t c2s[(C2_CAP + 2048) / 4];
     __shared__ __align__(16) float c1s[128];
-    __shared__ float part[PART_CAP];              // [KW][R][MM]
-    __shared__ float sTs[4 * R_MAX_LORA];         // [MM][r]
+    __shared__ float sTs[MM * R_MAX_LORA];        // [MM][r]
     __shared__ __align__(16) uint16_t l2s[R_MAX_LORA * R_MAX];   // [r][R]
     __shared__ uint32_t cbh[16];
-    __shared__ float csum[CSUM_CAP];              // chunk sums of T's partials
+    // T's chunk sums in the prologue; afterwards the wave partials of the rows
+    //   MF = false: part [KW][R][MM];  MF = true: part [wave][BROWS][MM] and res [R][MM] at RES_OFF
+    __shared__ float scr[CSUM_CAP];
+    float *csum = scr, *part = scr, *res = scr + RES_OFF;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -312,21 +357,23 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
     const int nrows = (int)min((int64_t)a.R, a.N - n0);
     const int64_t nblk = a.K >> 6, wrow = a.K >> 1;
     const int nchunk = (int)(a.K >> 5);
-    const int c = kw * 64 + lane;                 // this lane's 16-byte chunk of every row
+    const int c = kw * LANES_ROW + (MF ? (lane >> 2) : lane);   // this lane's 16-byte chunk of a row
+    const int jrow = MF ? (lane & 3) : 0;         // its row in a 4-row group
     const bool lane_ok = c < nchunk;
     const int rs0 = s * a.RS;                     // first local row of this stream
-    auto lrow = [&](int i) { return rs0 + i; };    // local row of the stream's i-th row
+    const int nsteps = a.RS / ROWS_STEP;          // row steps of a stream
+    auto lrow = [&](int i) { return rs0 + ROWS_STEP * i + jrow; };   // this lane's row at step i
 
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.packed, a.N * wrow);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, a.M * a.K * 2);
     auto wload = [&](int i) -> u32x4 {
-        const bool ok = lane_ok & (i < a.RS) & (lrow(i) < nrows);
+        const bool ok = lane_ok & (i < nsteps) & (lrow(i) < nrows);
         const uint32_t off = (uint32_t)((n0 + lrow(i)) * wrow + 16 * c);
         return bload16(rW, ok ? off : OOB);
     };
 
     // ---- prologue.  Issue order: the LDS copies (codes, second-level constants, L2 columns), X,
-    //      the first chunk of T's partials, then the first U weight rows.  The waits below stop
+    //      the first chunk of T's partials, then the first U weight steps.  The waits below stop
     //      short of the weight rows, which stream in while the workgroup sets up. ----
     const int64_t q0 = n0 * nblk;                 // first code of the workgroup
     const int nc2 = nrows * (int)nblk;
@@ -360,15 +407,19 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
                                                      0, 0, 0);
         }
     }
-    // X[m][32 c + 2 i .. + 1] as bf16 pairs
-    uint32_t x[MM][16];
+    // X[token][32 c + 2 i .. + 1] as bf16 pairs; token q (MF = false) or 4 q + jrow (MF = true)
+    uint32_t x[NX][16];
 #pragma unroll
-    for (int m = 0; m < MM; ++m)
+    for (int q = 0; q < NX; ++q) {
+        const int tok = MF ? 4 * q + jrow : q;
+        const bool ok = lane_ok & (tok < a.M);
+        const uint32_t off = (uint32_t)((tok * a.K + 32 * c) * 2);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            const u32x4 v = bload16(rX, (lane_ok && m < a.M) ? (uint32_t)((m * a.K + 32 * c) * 2 + 16 * h) : OOB);
-            x[m][4 * h] = v.x; x[m][4 * h + 1] = v.y; x[m][4 * h + 2] = v.z; x[m][4 * h + 3] = v.w;
+            const u32x4 v = bload16(rX, ok ? off + 16 * h : OOB);
+            x[q][4 * h] = v.x; x[q][4 * h + 1] = v.y; x[q][4 * h + 2] = v.z; x[q][4 * h + 3] = v.w;
         }
+    }
     // T's partials: pair p = (chunk p / EM, element p % EM); this thread's first pair
     const int E = (int)a.M * a.r, EM = MM * a.r, nch = (a.nkc + 7) >> 3, npair = nch * EM;
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(a.Tp, (int64_t)a.nkc * E * 4);
@@ -404,60 +455,103 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
         if (blockIdx.x == 0 && a.T_out && e < E) a.T_out[e] = (uint16_t)f32_to_bf16(t);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(U));     // all but the weight rows: the LDS copies landed
-    lds_barrier();
+    lds_barrier();                                // (and the chunk sums were read: scr is free)
 
-    // ---- the rows of this stream ----
+    // ---- the row steps of this stream ----
     const char *tabc = reinterpret_cast<const char *>(tab);
     const uint8_t *c2b = reinterpret_cast<const uint8_t *>(c2s) + sh;
     const uint32_t lb = (uint32_t)lane << 2;
     const int bcol = min(c >> 1, (int)nblk - 1);  // quantization block of the lane's columns
-    const int gsel = BR == 8 ? (lane >> 3) : (lane >> 4);
-    const bool holder = BR == 8 ? ((lane & 7) == 7) : ((lane & 15) == 15);
-    const int nit = (a.RS + ITER - 1) / ITER;
-    for (int it = 0; it < nit; ++it) {
-        static_for<0, ITER / BR>([&](auto sbc) {
-            constexpr int sb = decltype(sbc)::value;
-            float p[BR][MM];
-            static_for<0, BR>([&](auto rc) {
-                constexpr int rq = decltype(rc)::value;
-                constexpr int rr = sb * BR + rq;          // row within the iteration
+    // decode step i's 16 bytes (32 codes) into 16 bf16 pairs; returns the block constant
+    auto decode = [&](int i, const u32x4 &w, uint32_t (&pr)[16]) -> float {
+        // rows past the stream read zero codes; their clamped constant keeps sums finite
+        const int rl = min(lrow(i), nrows - 1);
+        const int qi = rl * (int)nblk + bcol;
+        static_for<0, 16>([&](auto bc) {
+            constexpr int bi = decltype(bc)::value;
+            constexpr uint32_t sel = 0x0C0C0000u | ((4u + (bi & 3)) << 8);
+            pr[bi] = *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(w[bi >> 2], lb, sel));
+        });
+        return block_scale(c2b[qi], c1s[(int)(((q0 + qi) >> 8) - c1lo)], mean);
+    };
+    const int nit = (nsteps + ITER - 1) / ITER;
+    if constexpr (!MF) {
+        const int gsel = BR == 8 ? (lane >> 3) : (lane >> 4);
+        const bool holder = BR == 8 ? ((lane & 7) == 7) : ((lane & 15) == 15);
+        for (int it = 0; it < nit; ++it) {
+            static_for<0, ITER / BR>([&](auto sbc) {
+                constexpr int sb = decltype(sbc)::value;
+                float p[BR][MM];
+                static_for<0, BR>([&](auto rc) {
+                    constexpr int rq = decltype(rc)::value;
+                    constexpr int rr = sb * BR + rq;      // step within the iteration
+                    const int i = it * ITER + rr;
+                    const u32x4 w = ring[rr % RING];
+                    // the load of step i + U goes out here, before step i's arithmetic (left to
+                    // itself the scheduler bunches the loads late and the ring stops hiding them)
+                    __builtin_amdgcn_sched_barrier(0);
+                    ring[(rr + U) % RING] = wload(i + U);
+                    __builtin_amdgcn_sched_barrier(0);
+                    uint32_t pr[16];
+                    const float sc = decode(i, w, pr);
+                    float d[MM];
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) d[m] = 0.0f;
+#pragma unroll
+                    for (int bi = 0; bi < 16; ++bi)
+#pragma unroll
+                        for (int m = 0; m < MM; ++m) d[m] = dot2(pr[bi], x[m][bi], d[m]);
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) p[rq][m] = sc * d[m];
+                });
+                float rs[MM];
+                reduce_rows<BR, MM>(p, rs, lane);
+                const int i = it * ITER + sb * BR + gsel;
+                if (holder && i < nsteps && lrow(i) < nrows) {
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) part[(kw * a.R + lrow(i)) * MM + m] = rs[m];
+                }
+            });
+        }
+    } else {
+        const bool holder = (lane & 12) == 12;
+        const int htok = 2 * (lane >> 5) + ((lane >> 4) & 1);   // token (within a group) held
+        for (int it = 0; it < nit; ++it) {
+            static_for<0, ITER>([&](auto rc) {
+                constexpr int rr = decltype(rc)::value;
                 const int i = it * ITER + rr;
                 const u32x4 w = ring[rr % RING];
-                // the load of row i + U goes out here, before row i's arithmetic (left to
-                // itself the scheduler bunches the loads late and the ring stops hiding them)
                 __builtin_amdgcn_sched_barrier(0);
                 ring[(rr + U) % RING] = wload(i + U);
                 __builtin_amdgcn_sched_barrier(0);
-                // rows past the stream read zero codes; their clamped constant keeps sums finite
-                const int rl = min(lrow(i), nrows - 1);
-                const int qi = rl * (int)nblk + bcol;
-                const float sc = block_scale(c2b[qi], c1s[(int)(((q0 + qi) >> 8) - c1lo)], mean);
-                float d[MM];
+                uint32_t pr[16];
+                const float sc = decode(i, w, pr);
 #pragma unroll
-                for (int m = 0; m < MM; ++m) d[m] = 0.0f;
-                static_for<0, 16>([&](auto bc) {
-                    constexpr int bi = decltype(bc)::value;
-                    constexpr uint32_t sel = 0x0C0C0000u | ((4u + (bi & 3)) << 8);
-                    const uint32_t pr =
-                        *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(w[bi >> 2], lb, sel));
+                for (int q = 0; q < NX; ++q) {
+                    f32x4 cq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int m = 0; m < MM; ++m) d[m] = dot2(pr, x[m][bi], d[m]);
-                });
-#pragma unroll
-                for (int m = 0; m < MM; ++m) p[rq][m] = sc * d[m];
+                    for (int t = 0; t < 8; ++t) cq = mfma4x4(x[q][2 * t], x[q][2 * t + 1], pr[2 * t], pr[2 * t + 1], cq);
+                    const float v = reduce_blocks4(sc * cq);
+                    if (holder) part[(wave * BROWS + ROWS_STEP * rr + jrow) * MM + 4 * q + htok] = v;
+                }
             });
-            float res[MM];
-            reduce_rows<BR, MM>(p, res, lane);
-            const int i = it * ITER + sb * BR + gsel;
-            if (holder && i < a.RS && lrow(i) < nrows) {
-#pragma unroll
-                for (int m = 0; m < MM; ++m) part[(kw * a.R + lrow(i)) * MM + m] = res[m];
+            // the KW waves of each row meet here: batch `it` of every stream
+            lds_barrier();
+            for (int e = tid; e < a.S * BROWS * MM; e += nthr) {
+                const int ss = e / (BROWS * MM), rem = e - ss * (BROWS * MM);
+                const int br = rem / MM, m = rem - br * MM;
+                float t = 0.0f;
+                for (int k = 0; k < a.KW; ++k) t += part[((ss * a.KW + k) * BROWS + br) * MM + m];
+                const int st = it * ITER + br / ROWS_STEP;          // the row's step in its stream
+                const int row = ss * a.RS + ROWS_STEP * st + (br % ROWS_STEP);
+                if (st < nsteps && row < nrows) res[row * MM + m] = t;
             }
-        });
+            lds_barrier();
+        }
     }
     __syncthreads();
 
-    // ---- sum the KW waves of each row, add (s T) L2, store bf16: 8 lanes per output, lane q
+    // ---- rows' sums (over the KW waves), plus (s T) L2, stored bf16: 8 lanes per output, lane q
     //      of the 8 taking every 8th term of the r-long dot product ----
     const int jn = a.r >> 3;
     for (int i0 = 0; i0 < a.R * MM * 8; i0 += nthr) {     // uniform trip count (DPP below)
@@ -470,7 +564,9 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
                 const int j = 8 * jj + q;
                 lo = __builtin_fmaf(sTs[m * a.r + j], bf16_to_f32(l2s[j * a.R + rl]), lo);
             }
-            if (q < a.KW) {
+            if constexpr (MF) {
+                if (q == 0) lo += res[rl * MM + m];
+            } else if (q < a.KW) {
                 for (int k = q; k < a.KW; k += 8) lo += part[(k * a.R + rl) * MM + m];
             }
         }
@@ -485,33 +581,41 @@ struct RowsPlan {
     int KW, S, R, RS, grid;
 };
 
-// waves per workgroup: 16 (four per SIMD, 128 registers each); 12 for four tokens, whose X
-// values take 64 registers per lane
-int max_waves(int mm) { return mm > 2 ? 12 : MAX_WAVES; }
+// The row kernel serves M = 1 with dot products (mm = 1) and M = 2..8 with the 4 x 4 MFMA layout
+// (mm = 4 or 8 tokens).  Beyond 8 tokens the 4 x 4 x 4 MFMAs (a fraction of the rate of the large
+// shapes) bound it: 16 tokens took 70 us against 63 us for the 16 x 16 x 32 GEMV.
+int rows_mm(int64_t M) { return M == 1 ? 1 : (M <= 4 ? 4 : 8); }
 
 RowsPlan rows_plan(int64_t N, int64_t K, int mm) {
     RowsPlan p;
+    const bool mf = mm > 1;
     const int64_t nchunk = K >> 5, nblk = K >> 6;
-    const int nwmax = max_waves(mm);
-    p.KW = (int)((nchunk + 63) / 64);
-    p.S = p.KW <= nwmax ? nwmax / p.KW : 0;
-    // one workgroup per CU when the rows allow it
+    p.KW = (int)((nchunk + (mf ? 15 : 63)) / (mf ? 16 : 64));
+    p.S = p.KW <= MAX_WAVES ? MAX_WAVES / p.KW : 0;
+    // one workgroup per CU when the rows allow it; each stream a whole number of 4-row groups
+    const int64_t unit = mf ? 8 * (p.S > 0 ? p.S : 1) : 8;
     int64_t R = (N + 255) / 256;
-    R = (R + 7) & ~(int64_t)7;
+    R = (R + unit - 1) / unit * unit;
     int64_t cap = R_MAX;
     if (cap > C2_CAP / nblk) cap = C2_CAP / nblk;
-    if (cap > PART_CAP / (4 * p.KW)) cap = PART_CAP / (4 * p.KW);
-    cap &= ~(int64_t)7;
+    if (!mf && cap > PART_CAP / p.KW) cap = PART_CAP / p.KW;
+    if (mf && cap > (CSUM_CAP - RES_OFF) / mm) cap = (CSUM_CAP - RES_OFF) / mm;
+    cap = cap / unit * unit;
     if (R > cap) R = cap;
     p.R = (int)R;
-    p.RS = p.S > 0 ? (int)((R + p.S - 1) / p.S) : 0;
+    p.RS = p.S > 0 ? (int)(R / p.S) : 0;
+    if (!mf && p.S > 0) p.RS = (int)((R + p.S - 1) / p.S);
     p.grid = R > 0 ? (int)((N + R - 1) / R) : 0;
-    (void)mm;
     return p;
 }
 
-int mm_of(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : 4); }
+int mm_of(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : 4); }   // tokens of the T kernel
 int t_slices(int64_t M, int64_t K) { return (int)((K + t_rows(mm_of(M)) - 1) / t_rows(mm_of(M))); }
+// T's partials: the slice kernel below for M <= 4, the split-K skinny product above
+int t_parts(int64_t M, int64_t K, int32_t r) {
+    if (M <= 4) return t_slices(M, K);
+    return choose_split(((M + 63) / 64) * ((r + 63) / 64), (K + 63) / 64);
+}
 
 template <int MM>
 hipError_t launch_t(const TArgs &t, int nkc, hipStream_t stream) {
@@ -519,13 +623,27 @@ hipError_t launch_t(const TArgs &t, int nkc, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_t_parts(const uint16_t *X, const uint16_t *L1, int32_t r, int64_t M, int64_t K, float *Tp,
+                          hipStream_t stream) {
+    const int nkc = t_parts(M, K, r);
+    if (M > 4) return launch_skinny_nt(X, L1, /*b_rows_k=*/true, Tp, M, r, K, nkc, stream);
+    TArgs t;
+    t.X = X; t.L1 = L1; t.Tp = Tp; t.M = M; t.K = K; t.r = r;
+    switch (mm_of(M)) {
+        case 1: return launch_t<1>(t, nkc, stream);
+        case 2: return launch_t<2>(t, nkc, stream);
+        default: return launch_t<4>(t, nkc, stream);
+    }
+}
+
 template <int MM>
-hipError_t launch_mm(const TArgs &t, const RowsArgs &a, int nkc, int threads, int grid, hipStream_t stream) {
-    hipError_t err = launch_t<MM>(t, nkc, stream);
-    if (err != hipSuccess) return err;
+hipError_t launch_rows(const RowsArgs &a, int threads, int grid, hipStream_t stream) {
     timing_before(stream, 2);
-    hipLaunchKernelGGL((gemv_rows_kernel<MM, 4, 2, (MM > 2 ? 12 : MAX_WAVES)>), dim3(grid), dim3(threads), 0, stream, a);
-    err = hipGetLastError();
+    if constexpr (MM == 1)
+        hipLaunchKernelGGL((gemv_rows_kernel<1, 4, 2, MAX_WAVES, false>), dim3(grid), dim3(threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemv_rows_kernel<MM, 4, 2, MAX_WAVES, true>), dim3(grid), dim3(threads), 0, stream, a);
+    const hipError_t err = hipGetLastError();
     timing_after(stream);
     return err;
 }
@@ -536,7 +654,7 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     GemvPlan p;
     (void)N;
     p.nseg = 1;
-    p.nkc = t_slices(M, K);
+    p.nkc = t_parts(M, K, r);
     p.yp_floats = 0;
     p.tp_floats = (size_t)p.nkc * M * r;
     return p;
@@ -544,43 +662,36 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
 
 hipError_t launch_gemv_T(const uint16_t *X, const uint16_t *L1, int32_t r, int64_t M, int64_t K, float *Tp,
                         uint16_t *T, hipStream_t stream) {
-    if (M < 1 || M > 4 || r < 8 || r > R_MAX_LORA || r % 8) return hipErrorInvalidValue;
-    TArgs t;
-    t.X = X; t.L1 = L1; t.Tp = Tp; t.M = M; t.K = K; t.r = r;
-    const int nkc = t_slices(M, K);
-    hipError_t err;
-    switch (mm_of(M)) {
-        case 1: err = launch_t<1>(t, nkc, stream); break;
-        case 2: err = launch_t<2>(t, nkc, stream); break;
-        default: err = launch_t<4>(t, nkc, stream); break;
-    }
+    if (M < 1 || M > 8 || r < 8 || r > R_MAX_LORA || r % 8) return hipErrorInvalidValue;
+    hipError_t err = launch_t_parts(X, L1, r, M, K, Tp, stream);
     if (err != hipSuccess) return err;
     const int E = (int)M * r;
-    hipLaunchKernelGGL(gemv_tsum_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, Tp, nkc, E, T);
+    hipLaunchKernelGGL(gemv_tsum_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, Tp, t_parts(M, K, r), E, T);
     return hipGetLastError();
 }
 
 bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t r) {
-    if (M < 1 || M > 4 || r < 8 || r > R_MAX_LORA || r % 8 || N % 8 || K % 64) return false;
-    const int mm = mm_of(M);
+    if (M < 1 || M > 8 || r < 8 || r > R_MAX_LORA || r % 8 || N % 8 || K % 64) return false;
+    const int mm = rows_mm(M);
     const RowsPlan p = rows_plan(N, K, mm);
-    const int64_t nch = (t_slices(M, K) + 7) / 8;
-    return p.S >= 1 && p.R >= 8 && p.R <= R_MAX && p.R * (K >> 6) <= C2_CAP && (int64_t)p.KW * p.R * mm <= PART_CAP &&
-           nch * mm * r <= CSUM_CAP;
+    const int64_t nch = (t_parts(M, K, r) + 7) / 8;
+    if (p.S < 1 || p.R < 8 || p.R > R_MAX || p.R * (K >> 6) > C2_CAP || nch * mm * r > CSUM_CAP) return false;
+    if (mm == 1) return (int64_t)p.KW * p.R <= PART_CAP;
+    // cross-wave partials of one batch, and the row sums
+    return (int64_t)p.S * p.KW * 16 * mm <= RES_OFF && (int64_t)p.R * mm <= CSUM_CAP - RES_OFF;   // 16 rows a batch
 }
 
 hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                            float scale, int32_t r, int64_t M, uint16_t *Y, uint16_t *T_out, float *Yp,
                            float *Tp, hipStream_t stream) {
     (void)Yp;
-    if (M < 1 || M > 4) return hipErrorInvalidValue;   // larger token counts take another path
     if (!gemv_fits(M, w.rows, w.cols, r)) return hipErrorNotSupported;
-    const int mm = mm_of(M);
+    const int mm = rows_mm(M);
     const GemvPlan g = gemv_plan(M, w.rows, w.cols, r);
     const RowsPlan p = rows_plan(w.rows, w.cols, mm);
     const int threads = p.S * p.KW * 64;
-    TArgs t;
-    t.X = X; t.L1 = L1; t.Tp = Tp; t.M = M; t.K = w.cols; t.r = r;
+    hipError_t err = launch_t_parts(X, L1, r, M, w.cols, Tp, stream);
+    if (err != hipSuccess) return err;
     RowsArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
@@ -590,9 +701,9 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
     a.scale = scale;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
     switch (mm) {
-        case 1: return launch_mm<1>(t, a, g.nkc, threads, p.grid, stream);
-        case 2: return launch_mm<2>(t, a, g.nkc, threads, p.grid, stream);
-        default: return launch_mm<4>(t, a, g.nkc, threads, p.grid, stream);
+        case 1: return launch_rows<1>(a, threads, p.grid, stream);
+        case 4: return launch_rows<4>(a, threads, p.grid, stream);
+        default: return launch_rows<8>(a, threads, p.grid, stream);
     }
 }
 

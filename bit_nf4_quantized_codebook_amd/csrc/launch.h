@@ -32,13 +32,13 @@ hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint1
 // 4 < M <= 16 tokens: sT = s X L1 (bf16 [M, r]) computed beforehand
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
-// decode-size forward (M <= 4): two launches; Tp is fp32 scratch of the size gemv_plan gives (Yp unused)
+// decode-size forward (M <= 8): two launches; Tp is fp32 scratch of the size gemv_plan gives (Yp unused)
 struct GemvPlan {
     int nseg, nkc;
     size_t yp_floats, tp_floats;
 };
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int32_t r);
-// whether launch_gemv_fwd takes this shape (M <= 4 and the reduction fits one workgroup's waves)
+// whether launch_gemv_fwd takes this shape (M <= 8 and the reduction fits one workgroup's waves)
 bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t r);
 // T (bf16 [M, r]) exactly as launch_gemv_fwd computes it: its partials into Tp, then their sum
 hipError_t launch_gemv_T(const uint16_t *X, const uint16_t *L1, int32_t r, int64_t M, int64_t K, float *Tp,
