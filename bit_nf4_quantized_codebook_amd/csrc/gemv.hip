@@ -7,8 +7,8 @@
 // This shape streams the 4-bit weight once from HBM; everything else has to hide behind that
 // stream.  Two launches:
 //
-// T's partials: gemv_t_kernel computes T = X L1 in slices of 64 M' rows of L1 (M' = 1, 2, 4: M
-//   rounded up) for M <= 4; from 5 tokens the split-K skinny product of the LoRA kernels does.
+// T's partials: gemv_t_kernel computes T = X L1 in slices of 64 rows of L1 for M <= 4; from 5
+//   tokens the split-K skinny product of the LoRA kernels does.
 //   Either way the fp32 partials are summed by the next launch in a fixed chunked order.
 //
 // gemv_rows_kernel: one workgroup of up to 16 waves per CU owns a run of R weight rows over the
@@ -55,7 +55,7 @@ constexpr int RES_OFF = 4096;                  // 4x4-MFMA layout: batch partial
 constexpr int T_THREADS = 256;
 // rows of L1 per T workgroup: short slices spread the 1 MB-scale L1 read over many CUs (one CU
 // alone pulls only a few tens of GB/s); their partials are summed by the consumer
-constexpr int t_rows(int mm) { return 64 * mm; }
+constexpr int T_ROWS = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -89,7 +89,7 @@ __device__ __forceinline__ uint32_t cb_bf16(const Codebook &cb, uint32_t j) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// T = X L1, slice of t_rows(MM) rows of L1 per workgroup: Tp[slice][m][j]
+// T = X L1, slice of T_ROWS rows of L1 per workgroup: Tp[slice][m][j]
 // ---------------------------------------------------------------------------------------------
 struct TArgs {
     const uint16_t *X;       // [M, K]
@@ -149,8 +149,7 @@ __global__ __launch_bounds__(256) void gemv_tsum_kernel(const float *Tp, int nkc
 
 template <int MM>
 __global__ __launch_bounds__(T_THREADS) void gemv_t_kernel(TArgs a) {
-    constexpr int T_ROWS = t_rows(MM);
-    constexpr int T_PT = 4 * MM;                  // 16-byte L1 pieces per thread (r <= 128)
+    constexpr int T_PT = 4;                       // 16-byte L1 pieces per thread (r <= 128)
     __shared__ float xs[MM][T_ROWS];
     __shared__ __align__(16) float red[MM * T_THREADS * 8];   // [m][row lane][r]
     __shared__ float red2[MM * (T_THREADS + R_MAX_LORA)];    // [m][group][r]
@@ -423,9 +422,14 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
     // T's partials: pair p = (chunk p / EM, element p % EM); this thread's first pair
     const int E = (int)a.M * a.r, EM = MM * a.r, nch = (a.nkc + 7) >> 3, npair = nch * EM;
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(a.Tp, (int64_t)a.nkc * E * 4);
-    const int pc0 = tid / EM, pe0 = tid - pc0 * EM;
-    float tv[8];
-    tp_chunk_load(rT, a.nkc, E, pe0, pc0, tid < npair, tv);
+    // (the first PF pairs of each thread are loaded here; the 4 x 4 layout sums 4 M' x r elements)
+    constexpr int PF = MF ? 4 : 1;
+    float tv[PF][8];
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+        const int p = tid + f * nthr, pc = p / EM;
+        tp_chunk_load(rT, a.nkc, E, p - pc * EM, pc, p < npair, tv[f]);
+    }
     const float mean = a.mean[0];                 // (a load pending inside the loop would drain the ring)
     __builtin_amdgcn_sched_barrier(0);            // the weight rows go out last
     u32x4 ring[RING];
@@ -442,8 +446,12 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
         reinterpret_cast<u32x4 *>(tab)[i] = u32x4{v, v, v, v};
     }
     // s T rounded to bf16 (zero past M): chunk sums, then the chunks in order
-    if (tid < npair) csum[tid] = tp_chunk_add(a.nkc, pc0, tv);
-    for (int p = tid + nthr; p < npair; p += nthr) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+        const int p = tid + f * nthr;
+        if (p < npair) csum[p] = tp_chunk_add(a.nkc, p / EM, tv[f]);
+    }
+    for (int p = tid + PF * nthr; p < npair; p += nthr) {
         const int cc = p / EM, e = p - cc * EM;
         csum[p] = tp_chunk_sum(rT, a.nkc, E, e, cc);
     }
@@ -610,10 +618,10 @@ RowsPlan rows_plan(int64_t N, int64_t K, int mm) {
 }
 
 int mm_of(int64_t M) { return M == 1 ? 1 : (M == 2 ? 2 : 4); }   // tokens of the T kernel
-int t_slices(int64_t M, int64_t K) { return (int)((K + t_rows(mm_of(M)) - 1) / t_rows(mm_of(M))); }
+int t_slices(int64_t K) { return (int)((K + T_ROWS - 1) / T_ROWS); }
 // T's partials: the slice kernel below for M <= 4, the split-K skinny product above
 int t_parts(int64_t M, int64_t K, int32_t r) {
-    if (M <= 4) return t_slices(M, K);
+    if (M <= 4) return t_slices(K);
     return choose_split(((M + 63) / 64) * ((r + 63) / 64), (K + 63) / 64);
 }
 
