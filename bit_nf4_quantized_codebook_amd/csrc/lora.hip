@@ -24,7 +24,10 @@ namespace nf4k {
 namespace {
 
 constexpr int ST = 64;          // block tile (both output dims) and reduction step
-constexpr int NSTAGE = 4;       // reduction steps in flight per block tile
+constexpr int NSTAGE = 4;       // reduction steps in flight per block tile (skinny_nt)
+// skinny_tn: two steps per tile and half the LDS, so four workgroups share a CU and fill each
+// other's load waits (dL2 + dL1: 16.6 against 18.9 us at 4096 tokens; skinny_nt gained nothing)
+constexpr int NSTAGE_TN = 2;
 constexpr int ROWB = (ST + 8) * 2;   // padded LDS row, bytes (144: conflict-free 16-byte reads)
 
 
@@ -150,8 +153,8 @@ struct TnGroup {
     uint32_t nb0;
 };
 __global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
-    __shared__ __align__(16) uint8_t Us[NSTAGE][ST * ROWB];
-    __shared__ __align__(16) uint8_t Vs[NSTAGE][ST * ROWB];
+    __shared__ __align__(16) uint8_t Us[NSTAGE_TN][ST * ROWB];
+    __shared__ __align__(16) uint8_t Vs[NSTAGE_TN][ST * ROWB];
     const int second = blockIdx.x >= grp.nb0;
     const TnProb &pr = grp.p[second];
     const uint16_t *__restrict__ U = pr.U;
@@ -194,15 +197,15 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
     };
 
     f32x16 acc = {};
-    TileLoad la[NSTAGE], lb[NSTAGE];
-    for (int g0 = 0; g0 < nsteps; g0 += NSTAGE) {
+    TileLoad la[NSTAGE_TN], lb[NSTAGE_TN];
+    for (int g0 = 0; g0 < nsteps; g0 += NSTAGE_TN) {
 #pragma unroll
-        for (int u = 0; u < NSTAGE; ++u) load(g0 + u, la[u], lb[u]);
+        for (int u = 0; u < NSTAGE_TN; ++u) load(g0 + u, la[u], lb[u]);
 #pragma unroll
-        for (int u = 0; u < NSTAGE; ++u) store(u, la[u], lb[u]);
+        for (int u = 0; u < NSTAGE_TN; ++u) store(u, la[u], lb[u]);
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < NSTAGE; ++u) {
+        for (int u = 0; u < NSTAGE_TN; ++u) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const bf16x8 fa = frag_tr(Us[u], wm * 32, s, lane);
