@@ -175,6 +175,8 @@ SHAPES = [
     (8, 3000, 8192, 64),       # 4x4-MFMA decode layout, two token groups, ragged row group
     (12, 2000, 4096, 32),      # four token groups (tokens 12..15 padding), two row streams
     (5, 512, 8192, 16),
+    (4, 520, 2048, 128),       # 4x4-MFMA decode layout with r = 128, four row streams
+    (1, 1000, 4096, 128),      # one-token decode layout with r = 128
     # from 1024 tokens on: bf16 expansion of the weight + K-extended bf16 GEMM
     (1024, 520, 384, 16),      # ragged N (the backward's reduction), odd number of K steps
     (1100, 264, 640, 24),      # ragged M and N
