@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     // Columns at or past Kred (a ragged last step, or the steps past the end) read zeros.  The
     // whole offset sits in the lane offset (the scalar offset is 0), so rows past the end of the
     // operand are out of range for the descriptor's bound check.
-    auto load = [&](__amdgpu_buffer_rsrc_t r, int step, uint8_t *st) {
+    auto load = [&](__amdgpu_buffer_rsrc_t r, int step, uint8_t *st, int q0 = 0, int q1 = 8) {
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
         lds_u8 *dst = (lds_u8 *)st + wave * 8192;
         const int rem = kred32 - step * TK;
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
         const uint32_t v1 = a_col[1] < rem ? voff[1] + base : 0x80000000u;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+            if (q < q0 || q >= q1) continue;
             const uint32_t v = ((q & 1) ? v1 : v0) + (uint32_t)q * row8_off;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + q * 1024), 16, v, 0, 0, 0);
         }
@@ -135,40 +136,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     // Fragment reads run one sub-step ahead of the MFMAs.  The schedule is pinned: left alone, the
     // scheduler sinks the next sub-step's reads below the current MFMAs (their registers can then
     // be reused), and every sub-step starts by waiting out the LDS latency.  Here each of the
-    // first 8 MFMAs of a sub-step is followed by one fragment read, and the step's 16
-    // direct-to-LDS loads go out between the MFMAs of the first sub-step.
+    // first 8 MFMAs of a sub-step is followed by one fragment read, and in a sub-step that
+    // carries loads every second MFMA is followed by one direct-to-LDS load (8 per sub-step):
+    // the 64 loads of a step per CU, issued together, overfill the texture unit's address queue,
+    // and the MFMAs queued behind them in each wave stall.
     auto interleave = [&](int nvmem) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // 1 MFMA
-            if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // 1 DS read
-            if (k < nvmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // 1 VMEM
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // 1 MFMA
+            if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // 1 DS read
+            if ((k & 1) && (k >> 1) < nvmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM
         }
     };
-    // one step: compute stages (Ac, Bc) while the next step streams into (An, Bn)
-    auto step_body = [&](int step, const uint8_t *Ac, const uint8_t *Bc, uint8_t *An, uint8_t *Bn) {
-        Frags f0, f1;
-        read(Ac, Bc, 0, f0);
-        load(rA, step + 1, An);
-        load(rB, step + 1, Bn);
+    // One step computes stage (Ac, Bc) while step + 1 lands in (An, Bn).  The workgroup barrier
+    // sits between sub-steps 2 and 3: by then every wave has its sub-step 3 fragments in
+    // registers, so after it stage c is free for the loads of step + 2, and stage n (step + 1)
+    // is complete, so its first fragments are read while sub-step 3's 16 MFMAs run.  (With the
+    // barrier at the end of the step, each step opened with its MFMAs waiting on those reads.)
+    // The loads of step + 2 go out in two halves, rows q 0-3 of each wave in sub-step 3 and q
+    // 4-7 in sub-step 0 of the next step, at least three sub-steps before the barrier that
+    // waits for them.  On entry f0 holds, or is receiving, sub-step 0 of stage c.
+    Frags f0, f1;
+    auto step_body = [&](int step, uint8_t *Ac, uint8_t *Bc, uint8_t *An, uint8_t *Bn) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 3; ++s) {
             Frags &cur = (s & 1) ? f1 : f0;
             Frags &nxt = (s & 1) ? f0 : f1;
-            if (s < 3) read(Ac, Bc, s + 1, nxt);
+            if (s == 0) {
+                load(rA, step + 1, An, 4, 8);
+                load(rB, step + 1, Bn, 4, 8);
+            }
+            read(Ac, Bc, s + 1, nxt);
             mma(cur);
-            interleave(s == 0 ? 16 : 0);
+            interleave(s == 0 ? 8 : 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the next step landed (this wave's loads) and this wave's fragment reads are done
+        // step + 1 landed (this wave's loads) and this wave's fragment reads of stage c are done
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8));
         __syncthreads();
+        read(An, Bn, 0, f0);
+        load(rA, step + 2, Ac, 0, 4);
+        load(rB, step + 2, Bc, 0, 4);
+        mma(f1);
+        interleave(8);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     load(rA, 0, As0);
     load(rB, 0, Bs0);
+    load(rA, 1, As1, 0, 4);
+    load(rB, 1, Bs1, 0, 4);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    read(As0, Bs0, 0, f0);
     int step = 0;
     for (; step + 1 < main_steps; step += 2) {
         step_body(step, As0, Bs0, As1, Bs1);
