@@ -9,8 +9,13 @@ Quantized LLMs" study notes, gitcode.csdn.net/6a0046f754b52172bc72e356, unless n
 
 * ``codebook``      -- section 3.2, eq. (4) and the asymmetric exact-zero construction;
                        section 5.1.2, Fig. 7 text (8 values on one half, 7 on the other, plus 0).
+* ``codebook_int4``, ``codebook_fp4`` -- the 4-bit integer and 4-bit float types NF4 is compared
+                       with (abstract page gitcode.csdn.net/69bbdcd90a2f6a37c5989d83, section 1;
+                       study notes, section 5.1.2); the pages give no layout, so each is a
+                       reading stated in its docstring.
 * ``quantize``      -- section 3.1 (flatten, blocks of B, one constant per block), eq. (1) in its
-                       absmax form, section 3.2 step 3 (absmax normalisation to [-1, 1]).
+                       absmax form, section 3.2 step 3 (absmax normalisation to [-1, 1]).  Any
+                       ascending 16-entry table; equal neighbours allowed (the lower index wins).
 * ``double_quant``  -- section 3.3 (mean-centred 8-bit float constants, block 256).
 * ``dequant``       -- section 3.5, eq. (6), with eq. (2) at each level; output in BF16.
 * ``forward``       -- section 3.5 eq. (5) with the scalar s of eq. (3) (section 4, LoRA).
@@ -142,6 +147,35 @@ def codebook(delta: float = DELTA_DEFAULT) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_codebook failed (%d)" % rc)
     return out
+
+
+def codebook_int4() -> np.ndarray:
+    """4-bit integer codebook over the absmax-normalised value n = x / absmax.
+
+    Neither page defines the Int4 type it compares NF4 against (abstract page, section 1;
+    study notes, section 5.1.2).  Reading: eq. (1) of section 3.1 at 4 bits, round(7 / absmax *
+    x) in [-7, 7], i.e. the codeword k / 7; the 16 codes are the two's complement integers
+    k = -8 .. 7 in ascending order (code c holds k = c - 8).  k = -8 (value -8/7) lies outside
+    [-1, 1] and is never the nearest codeword."""
+    return np.array([(c - 8) / 7.0 for c in range(16)], dtype=np.float64).astype(np.float32)
+
+
+def codebook_fp4() -> np.ndarray:
+    """4-bit float codebook over n = x / absmax.
+
+    The pages compare NF4 with FP4 (study notes, section 5.1.2, and Table 3 there) but do not
+    give its layout.  Reading: E2M1 (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), divided by its largest magnitude 6 so that absmax maps
+    to +-1.  In ascending order the sign-and-magnitude codes give 15 distinct values: the
+    negative zero sits next to the positive one, both stored as +0.0, and the nearest-codeword
+    rule (ties to the lower index) never produces the second."""
+    mags = []
+    for e in range(4):            # exponent field
+        for m in range(2):        # mantissa field
+            mags.append(m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m))
+    mags.sort()
+    vals = [-v / 6.0 for v in reversed(mags)] + [v / 6.0 for v in mags]
+    return np.array([v if v != 0.0 else 0.0 for v in vals], dtype=np.float64).astype(np.float32)
 
 
 def quantize(W, cb=None, block: int = BLOCK):

@@ -144,12 +144,13 @@ def _exact_codes(W, cb, block):
     W = np.asarray(W, np.float32).reshape(-1)
     out = []
     cbf = [Fraction(float(c)) for c in cb]
+    zc = next(j for j in range(16) if cb[j] == 0)
     for b0 in range(0, W.size, block):
         blk = W[b0:b0 + block]
         a = np.max(np.abs(blk))
         for x in blk:
             if a == 0:
-                out.append(7)
+                out.append(zc)
                 continue
             n = Fraction(float(np.float32(x) / np.float32(a)))      # IEEE float32 division
             d = [abs(n - c) for c in cbf]
@@ -208,6 +209,92 @@ def test_quantize_codebook_round_trip_is_lossless():
         codes = oracle.unpack(packed, W.size)
         assert np.array_equal(codes, np.tile(np.arange(16, dtype=np.uint8), 4))
         assert np.array_equal(cb[codes] * absmax[0], W)
+
+
+# ---- alternative 4-bit types (Int4, FP4): readings, pinned to eq. (1) and to torch's E2M1 ----
+
+def _e2m1():
+    """torch's reference E2M1 codec (its MX test helpers: encode rounds to nearest even and
+    saturates, decode maps the 4-bit codes).  Those helpers import the test-only package
+    ``expecttest``, absent from this image; a stand-in module supplies its one name."""
+    import sys
+    import types
+    import unittest
+    if "expecttest" not in sys.modules:
+        try:
+            import expecttest  # noqa: F401
+        except ImportError:
+            stub = types.ModuleType("expecttest")
+            stub.TestCase = unittest.TestCase
+            sys.modules["expecttest"] = stub
+    try:
+        from torch.testing._internal.common_quantized import _f32_to_floatx_unpacked, _floatx_unpacked_to_f32
+    except Exception as e:  # pragma: no cover - depends on the torch build
+        pytest.skip("torch's E2M1 reference codec is not importable: %s" % e)
+    return (lambda x: _f32_to_floatx_unpacked(x, 2, 1)), (lambda c: _floatx_unpacked_to_f32(c, 2, 1))
+
+
+def test_int4_codebook_quantize_is_eq1_at_4_bits():
+    """Nearest Int4 codeword of n = x / absmax is eq. (1) with 2^3 - 1 = 7 levels per side."""
+    cb = oracle.codebook_int4()
+    assert np.all(np.diff(cb) > 0) and cb[8] == 0.0
+    W = np.concatenate([synth.normal_f32(61, (64, 64), 0.02).reshape(-1),
+                        (synth.uniform(62, 32 * 64) * 6.0 - 3.0).astype(np.float32)])
+    packed, absmax = oracle.quantize(W, cb)
+    codes = oracle.unpack(packed, W.size).astype(np.int64)
+    n = (W.reshape(-1, 64) / absmax[:, None]).astype(np.float32).reshape(-1)   # fp32 division
+    t = 7.0 * n.astype(np.float64)
+    ref = np.rint(t)
+    tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-6
+    assert tie.sum() < 4
+    assert np.array_equal((codes - 8)[~tie], ref[~tie].astype(np.int64))
+    assert codes.min() >= 1                      # k = -8 is never produced
+    assert set(np.unique(codes - 8)) <= set(range(-7, 8))
+    # every block's absmax element maps to +-7 exactly
+    blk = codes.reshape(-1, 64)
+    assert np.all(np.max(np.abs(blk - 8), axis=1) == 7)
+
+
+def test_int4_ties_go_to_the_lower_index():
+    cb = oracle.codebook_int4()
+    # 7 n = k + 1/2 exactly representable: n = (2k + 1) / 14 with absmax 1 in the block
+    W = np.zeros(64, dtype=np.float32)
+    W[0] = 1.0
+    ks = np.arange(-7, 7)
+    W[1:1 + ks.size] = ((2 * ks + 1) / 14.0).astype(np.float32)
+    packed, _ = oracle.quantize(W, cb)
+    codes = oracle.unpack(packed, W.size)
+    assert np.array_equal(codes[1:1 + ks.size], _exact_codes(W, cb, 64)[1:1 + ks.size])
+
+
+def test_fp4_codebook_is_e2m1_over_its_max():
+    enc, dec = _e2m1()
+    vals = dec(torch.arange(16, dtype=torch.uint8)).double().numpy()
+    cb = oracle.codebook_fp4()
+    assert cb.size == 16 and np.all(np.diff(cb) >= 0)
+    assert np.count_nonzero(cb == 0.0) == 2 and not np.any(np.signbit(cb[cb == 0.0]))
+    assert np.max(vals) == 6.0
+    assert np.array_equal(np.unique(cb), np.unique((vals / 6.0).astype(np.float32)))
+    assert np.array_equal(cb, -cb[::-1])
+
+
+def test_fp4_quantize_is_e2m1_rounding_of_6n():
+    """Nearest FP4 codeword of n is the E2M1 rounding of 6 n (away from the rounding ties)."""
+    enc, dec = _e2m1()
+    cb = oracle.codebook_fp4()
+    W = np.concatenate([synth.normal_f32(63, (64, 64), 0.02).reshape(-1),
+                        (synth.uniform(64, 32 * 64) * 2.0 - 1.0).astype(np.float32)])
+    packed, absmax = oracle.quantize(W, cb)
+    codes = oracle.unpack(packed, W.size)
+    n = (W.reshape(-1, 64) / absmax[:, None]).astype(np.float32).reshape(-1)
+    ref = dec(enc(torch.from_numpy(6.0 * n.astype(np.float64)).float())).double().numpy()
+    grid = np.unique(np.abs(dec(torch.arange(8, dtype=torch.uint8)).double().numpy()))
+    mids = (grid[:-1] + grid[1:]) / 2
+    near_tie = np.min(np.abs(np.abs(6.0 * n.astype(np.float64))[:, None] - mids[None, :]), axis=1) < 1e-5
+    assert near_tie.sum() < 8
+    assert np.array_equal(cb[codes][~near_tie], (ref[~near_tie] / 6.0).astype(np.float32))
+    assert np.array_equal(codes[~near_tie], _exact_codes(W, cb, 64)[~near_tie])
+    assert not np.any(codes == 8)                # the second zero slot is never produced
 
 
 def test_quantize_invariants_random():
