@@ -27,7 +27,8 @@ DQ_BLOCK = 256
 
 #: Symbols the C ABI exports (include/nf4.h).
 EXPORTS = (
-    "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook", "nf4_quantize",
+    "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook",
+    "nf4_build_int4_codebook", "nf4_build_fp4_codebook", "nf4_quantize",
     "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
@@ -73,6 +74,8 @@ def _load():
         "nf4_last_error": (ctypes.c_char_p, []),
         "nf4_version": (ctypes.c_char_p, []),
         "nf4_build_codebook": (i, [P, ctypes.c_double]),
+        "nf4_build_int4_codebook": (i, [P]),
+        "nf4_build_fp4_codebook": (i, [P]),
         "nf4_quantize": (i, [P, i64, i32, P, P, P, P]),
         "nf4_double_quant_workspace_size": (sz, [i64, i32]),
         "nf4_double_quant": (i, [P, i64, i32, P, P, P, P, sz, P]),
@@ -154,6 +157,20 @@ def nf4_build_codebook(delta: float = 0.0) -> np.ndarray:
     """The 16 NF4 codewords (host, float32, ascending); delta 0 selects the default."""
     out = np.zeros(16, dtype=np.float32)
     _check(lib.nf4_build_codebook(ctypes.c_void_p(out.ctypes.data), float(delta)), "nf4_build_codebook")
+    return out
+
+
+def nf4_build_int4_codebook() -> np.ndarray:
+    """The 4-bit integer table (k / 7, k = -8 .. 7), host float32, ascending."""
+    out = np.zeros(16, dtype=np.float32)
+    _check(lib.nf4_build_int4_codebook(ctypes.c_void_p(out.ctypes.data)), "nf4_build_int4_codebook")
+    return out
+
+
+def nf4_build_fp4_codebook() -> np.ndarray:
+    """The 4-bit float (E2M1 / 6) table, host float32, ascending, two zero entries."""
+    out = np.zeros(16, dtype=np.float32)
+    _check(lib.nf4_build_fp4_codebook(ctypes.c_void_p(out.ctypes.data)), "nf4_build_fp4_codebook")
     return out
 
 

@@ -75,16 +75,27 @@ float threshold_below_midpoint(float a, float b) {
     return t;
 }
 
+// Ascending (equal neighbours allowed), finite, containing 0; the zero code is the first 0 entry.
 int check_codebook(const float cb[16], int *zero_code) {
     int z = -1;
     for (int j = 0; j < 16; ++j) {
         if (!std::isfinite(cb[j])) return fail(NF4_ERR_ARG, "codebook entries must be finite");
-        if (j > 0 && !(cb[j - 1] < cb[j])) return fail(NF4_ERR_ARG, "codebook must be strictly ascending");
-        if (cb[j] == 0.0f) z = j;
+        if (j > 0 && !(cb[j - 1] <= cb[j])) return fail(NF4_ERR_ARG, "codebook must be ascending");
+        if (cb[j] == 0.0f && z < 0) z = j;
     }
     if (z < 0) return fail(NF4_ERR_ARG, "codebook must contain 0.0f");
     *zero_code = z;
     return NF4_OK;
+}
+
+// Decision thresholds of the nearest-codeword search: the code is the number of thresholds
+// strictly below n.  thr[j] separates codes j and j + 1; for equal neighbours code j + 1 must never
+// win (ties go to the lower index), so its threshold is the next one up (+inf past the end).
+void code_thresholds(const float cb[16], float thr[15]) {
+    for (int j = 14; j >= 0; --j) {
+        if (cb[j] == cb[j + 1]) thr[j] = (j == 14) ? INFINITY : thr[j + 1];
+        else thr[j] = threshold_below_midpoint(cb[j], cb[j + 1]);
+    }
 }
 
 int check_weight(const nf4_weight *w) {
@@ -273,6 +284,26 @@ int nf4_build_codebook(float out_codebook[16], double delta) {
     return NF4_OK;
 }
 
+int nf4_build_int4_codebook(float out_codebook[16]) {
+    if (!out_codebook) return fail(NF4_ERR_NULL, "out_codebook is NULL");
+    // two's complement k = -8 .. 7 over 7 (eq. (1) at 4 bits maps absmax to 7)
+    for (int c = 0; c < 16; ++c) out_codebook[c] = (float)((double)(c - 8) / 7.0);
+    return NF4_OK;
+}
+
+int nf4_build_fp4_codebook(float out_codebook[16]) {
+    if (!out_codebook) return fail(NF4_ERR_NULL, "out_codebook is NULL");
+    // E2M1 magnitudes: exponent field 0 is subnormal (m / 2), else 2^(e - 1) (1 + m / 2)
+    double mag[8];
+    for (int e = 0; e < 4; ++e)
+        for (int m = 0; m < 2; ++m) mag[2 * e + m] = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+    for (int i = 0; i < 8; ++i) {
+        out_codebook[7 - i] = (float)(-mag[i] / 6.0) + 0.0f;   // + 0.0f: the negative zero stored as +0
+        out_codebook[8 + i] = (float)(mag[i] / 6.0);
+    }
+    return NF4_OK;
+}
+
 int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codebook[16],
                  uint8_t *packed, float *absmax, void *stream) {
     if (!codebook) return fail(NF4_ERR_NULL, "codebook is NULL");
@@ -285,7 +316,7 @@ int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codeb
     if (!W || !packed || !absmax) return fail(NF4_ERR_NULL, "W, packed and absmax must be non-NULL");
     if (!aligned16(W) || !aligned16(packed)) return fail(NF4_ERR_ALIGN, "W and packed must be 16-byte aligned");
     float thr[15];
-    for (int j = 0; j < 15; ++j) thr[j] = threshold_below_midpoint(codebook[j], codebook[j + 1]);
+    code_thresholds(codebook, thr);
     NF4_CHECK_HIP(nf4k::launch_quantize(W, numel, thr, (uint32_t)zc, packed, absmax,
                                         reinterpret_cast<hipStream_t>(stream)),
                   "quantize");

@@ -64,19 +64,38 @@ const char *nf4_version(void);
 int nf4_build_codebook(float out_codebook[16], double delta);
 
 /*
+ * The 4-bit types NF4 is compared with -- abstract page (gitcode.csdn.net/69bbdcd90a2f6a37c5989d83),
+ * section 1 (NF4 against 4-bit integers and 4-bit floats), and the study notes, section 5.1.2
+ * (Table 2; QLoRA with FP4 and NF4 in Table 3).  The pages define neither layout; these tables
+ * are readings.  Both go through the same quantize / dequant / linear entry points as NF4 (the
+ * kernels only look codes up in the 16-entry table), so a weight quantized with one of them is
+ * used by passing the same table in nf4_weight.codebook.
+ *   nf4_build_int4_codebook: eq. (1) at 4 bits, round(7 x / absmax) in [-7, 7]: out[c] = (c - 8) / 7,
+ *     the two's complement integers -8 .. 7 over 7 (out[8] = 0; out[0] = -8/7 is never nearest).
+ *   nf4_build_fp4_codebook: E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6) over 6, ascending: out[0] = -1, out[7] = out[8] = 0 (E2M1's
+ *     negative zero is stored as +0 and never produced), out[15] = +1.
+ *   out_codebook: HOST float[16].  Host-only and synchronous.  NF4_ERR_NULL on a NULL pointer.
+ */
+int nf4_build_int4_codebook(float out_codebook[16]);
+int nf4_build_fp4_codebook(float out_codebook[16]);
+
+/*
  * Level-1 block-wise quantization -- section 3.1 (flatten, n = numel/B blocks of B consecutive
  * elements, one constant per block; eq. (1) in absmax form) and section 3.2 step 3 (absmax
  * normalisation to [-1, 1]).
  *   W:        device float32 [numel], the row-major flattening of the weight.
  *   numel:    >= 0.  A short last block's absmax covers only its valid elements.
  *   block:    must be 64 (section 3.5), else NF4_ERR_UNSUPPORTED.
- *   codebook: HOST float[16], strictly ascending, containing 0.0f (typically from
- *             nf4_build_codebook).  Copied into the kernel arguments.
+ *   codebook: HOST float[16], ascending, containing 0.0f (from nf4_build_codebook, or
+ *             nf4_build_int4_codebook / nf4_build_fp4_codebook).  Equal neighbours are allowed:
+ *             the lower index is the one produced.  Copied into the kernel arguments.
  *   packed:   device uint8 [ceil(numel/2)].  Element 2i in bits 0-3 of byte i, element 2i+1 in
  *             bits 4-7; an odd tail is padded with the zero code.
  *   absmax:   device float32 [ceil(numel/64)], the per-block max |x|.
  * Per element: n = fp32(x / absmax) (IEEE division), code = nearest codeword, ties to the lower
- * index; an all-zero block gets the zero code everywhere.  Inputs must be finite.
+ * index; an all-zero block gets the zero code (the first 0.0f entry) everywhere.  Inputs must be
+ * finite.
  * W and packed must be 16-byte aligned.
  */
 int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codebook[16],

@@ -46,6 +46,14 @@ def test_codebook_bit_exact_with_oracle(delta):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+def test_int4_and_fp4_codebooks_bit_exact_with_oracle():
+    for got, ref in ((nf4.nf4_build_int4_codebook(), oracle.codebook_int4()),
+                     (nf4.nf4_build_fp4_codebook(), oracle.codebook_fp4())):
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert lib.nf4_build_int4_codebook(None) == ENULL
+    assert lib.nf4_build_fp4_codebook(None) == ENULL
+
+
 def test_codebook_errors():
     out = np.zeros(16, np.float32)
     p = ctypes.c_void_p(out.ctypes.data)
@@ -70,6 +78,9 @@ def test_quantize_argument_errors():
     assert lib.nf4_quantize(None, 64, 64, cbp, fake, fake, None) == ENULL
     assert lib.nf4_quantize(mis, 64, 64, cbp, fake, fake, None) == EALIGN
     assert lib.nf4_quantize(None, 0, 64, cbp, None, None, None) == OK       # empty input
+    eq = cb.copy()
+    eq[5] = eq[6]                                # equal neighbours: accepted (the lower index wins)
+    assert lib.nf4_quantize(None, 0, 64, ctypes.c_void_p(eq.ctypes.data), None, None, None) == OK
     bad = cb.copy()
     bad[3], bad[4] = bad[4], bad[3]
     assert lib.nf4_quantize(fake, 64, 64, ctypes.c_void_p(bad.ctypes.data), fake, fake, None) == EARG

@@ -216,6 +216,85 @@ def test_linear_fwd_bwd_parity(M, N, K, r):
     check_tol("dX+=", f32(acc), g["dX"] + f32(base))
 
 
+# ------------------------------------------------------------------------------------------
+# The 4-bit types NF4 is compared with (Int4, FP4): same entry points, other 16-entry tables
+# ------------------------------------------------------------------------------------------
+
+ALT_CB = {"int4": (nf4.nf4_build_int4_codebook, oracle.codebook_int4),
+          "fp4": (nf4.nf4_build_fp4_codebook, oracle.codebook_fp4)}
+
+
+def _alt_cb(kind):
+    lib_cb, ref_cb = ALT_CB[kind]
+    cb = lib_cb()
+    assert np.array_equal(cb.view(np.uint32), ref_cb().view(np.uint32))
+    return cb
+
+
+@pytest.mark.parametrize("kind", ["int4", "fp4"])
+def test_alt_codebook_quantize_dq_dequant_bit_exact(kind):
+    _say(f"alt codebook quantize/dq/dequant: {kind}")
+    cb = _alt_cb(kind)
+    c64 = cb.astype(np.float64)
+    mids = ((c64[:-1] + c64[1:]) / 2).astype(np.float32)
+    adv = np.concatenate([mids, np.nextafter(mids, np.float32(2)), np.nextafter(mids, np.float32(-2)),
+                          np.float32([1e-30, -1e-30, 1e-8, -1e-8, 0.0, -0.0])])
+    blk = np.resize(np.concatenate([[np.float32(1.0)], adv]), 64).astype(np.float32)
+    W = np.concatenate([blk * np.float32(sc) for sc in (1.0, 0.37, 3e-5, 1700.0)] +
+                       [np.tile(cb, 4) * np.float32(2.0 ** -3), np.zeros(64, np.float32),
+                        synth.normal_f32(131, (520 * 384,), 0.02)]).astype(np.float32)
+    W = W[: (W.size // 64) * 64]
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    packed, absmax = nf4.nf4_quantize(Wd, cb)
+    torch.cuda.synchronize()
+    p_ref, a_ref = oracle.quantize(W, cb)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), a_ref.view(np.uint32))
+    if kind == "fp4":     # the second zero slot (code 8) is never produced
+        codes = oracle.unpack(p_ref, W.size)
+        assert not np.any(codes == 8)
+    w = nf4.NF4Weight.from_float(Wd.reshape(-1, 64), cb)
+    q = oracle.quantize_dq(W.reshape(-1, 64), cb)
+    assert np.array_equal(w.absmax_q.cpu().numpy(), q["codes"])
+    assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(-1), oracle.dequant_weight(q, cb).reshape(-1))
+
+
+ALT_SHAPES = [
+    (1, 3000, 8192, 64),       # one-token decode layout
+    (4, 520, 2048, 128),       # 4x4-MFMA decode layout
+    (12, 2000, 4096, 32),      # 16x16x32 GEMV
+    (300, 520, 384, 16),       # fused dequant GEMM
+    (1100, 264, 640, 24),      # bf16 expansion + K-extended GEMM
+]
+
+
+@pytest.mark.parametrize("kind", ["int4", "fp4"])
+@pytest.mark.parametrize("M,N,K,r", ALT_SHAPES)
+def test_alt_codebook_linear_parity(kind, M, N, K, r):
+    _say(f"alt codebook linear: {kind} M={M} N={N} K={K} r={r}")
+    cb = _alt_cb(kind)
+    s = 16.0 / r
+    seed = 900 + M + N
+    W = synth.normal_f32(seed, (N, K), 0.02)
+    X = synth.to_bf16_bits(synth.normal_f32(seed + 1, (M, K), 1.0))
+    L1 = synth.to_bf16_bits(synth.normal_f32(seed + 2, (K, r), 1.0 / r))
+    L2 = synth.to_bf16_bits(synth.normal_f32(seed + 3, (r, N), 0.01))
+    dY = synth.to_bf16_bits(synth.normal_f32(seed + 4, (M, N), 1.0))
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), cb)
+    Wq = oracle.dequant_weight(oracle.quantize_dq(W, cb), cb)
+    assert np.array_equal(h16(nf4.nf4_dequant(w)), Wq)
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    Yr, Tr = oracle.forward(X, Wq, L1, L2, s)
+    g = oracle.backward(dY, X, Wq, L1, L2, s)
+    check_tol("Y", f32(Y), Yr)
+    check_tol("dX", f32(dX), g["dX"])
+    check_tol("dL1", f32(dL1), g["dL1"])
+    check_tol("dL2", f32(dL2), g["dL2"])
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 520, 384), (1088, 264, 1024), (300, 264, 256)])
 def test_one_hot_rows_select_the_weight_bit_exact(M, N, K):
     """L2 = 0 and one-hot activations: every output is one dequantized weight times 1.0 plus exact
