@@ -269,6 +269,37 @@ def dequant_weight(q, cb=None) -> np.ndarray:
     return dequant(q["packed"], q["codes"], q["scales"], q["mean"], n, cb).reshape(q["shape"])
 
 
+def bits_per_parameter(dq: bool, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> float:
+    """Storage per weight (section 3.3's accounting): 4-bit codes plus one float32 constant per
+    block, or with DQ one 8-bit code per block plus one float32 per dq_block constants (the
+    single float32 mean is not counted)."""
+    return 4.0 + (8.0 / block + 32.0 / (block * dq_block) if dq else 32.0 / block)
+
+
+def quant_error(W, cb=None, dq: bool = True) -> dict:
+    """Quantization error of ``W`` under table ``cb`` (the comparison of section 5.1.2, on
+    synthetic weights): the weight is quantized, double-quantized when ``dq``, dequantized to
+    bf16 (eq. 6, or eq. 2 at one level without DQ), and compared with W in float64.
+
+    Returns mse and max_abs of (deq - W), the count of elements per code (occupancy), the
+    entropy of that distribution in bits, and bits_per_param."""
+    W = np.ascontiguousarray(W, dtype=np.float32).reshape(-1)
+    cb = codebook() if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
+    n = W.size
+    packed, absmax = quantize(W, cb)
+    if dq:
+        codes, scales, mean = double_quant(absmax)
+        deq = dequant(packed, codes, scales, mean, n, cb)
+    else:
+        deq = dequant_plain(packed, absmax, n, cb)
+    err = bf16_to_f32(deq).astype(np.float64) - W.astype(np.float64)
+    occ = np.bincount(unpack(packed, n), minlength=16).astype(np.int64)
+    p = occ[occ > 0] / float(n)
+    return {"mse": float(np.mean(err * err)), "max_abs": float(np.max(np.abs(err))),
+            "occupancy": occ, "entropy_bits": float(-np.sum(p * np.log2(p))),
+            "bits_per_param": bits_per_parameter(dq)}
+
+
 # ------------------------------------------------------------------------------------------
 # QLoRA linear layer, float64 (section 3.5 eq. 5 with the s of eq. 3)
 # W is stored [N_out, K_in]; the pages' W (h x o) is its transpose, so Y = X deq(W)^T + ...

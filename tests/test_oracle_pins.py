@@ -384,6 +384,50 @@ def test_memory_accounting_golden():
     assert round((single - dq) * s65["params"] / 8 / 1e9) == s65["gigabytes"]
 
 
+# ---- quantization-error statistics (NF4 against Int4 and FP4, with and without DQ) ----
+
+def test_quant_error_bits_per_param_golden():
+    g = GOLDEN["constant_overhead_bits"]
+    assert oracle.bits_per_parameter(False) - 4 == g["fp32_per_64"]
+    assert round(oracle.bits_per_parameter(True) - 4, 3) == g["double_quant"]
+    assert round(oracle.bits_per_parameter(False) - oracle.bits_per_parameter(True), 3) == g["saving"]
+
+
+def test_quant_error_exact_cases():
+    # FP4 on its bf16-exact codewords (0, +-1/2, +-1) times powers of two: no error at all
+    # (with DQ every block needs the same absmax: then the codes are 0 and a' is the mean exactly)
+    base = np.float32([-1.0, -0.5, 0.0, 0.5, 1.0])
+    for dq, exps in ((False, (-8, 0, 5)), (True, (5, 5, 5))):
+        W = np.concatenate([np.resize(base, 64) * np.float32(2.0 ** e) for e in exps]).astype(np.float32)
+        r = oracle.quant_error(W, oracle.codebook_fp4(), dq=dq)
+        assert r["mse"] == 0.0 and r["max_abs"] == 0.0
+        assert r["occupancy"].sum() == W.size
+    # NF4 on its own codewords (absmax 1 in every block): each code once per 16 elements, 4 bits
+    # of entropy, and the only error is bf16's rounding of the codewords (torch's cast)
+    cb = oracle.codebook()
+    W = np.tile(cb, 32).astype(np.float32)
+    ref = torch.from_numpy(W).to(torch.bfloat16).double().numpy() - W.astype(np.float64)
+    for dq in (False, True):
+        r = oracle.quant_error(W, cb, dq=dq)
+        assert np.all(r["occupancy"] == W.size // 16)
+        assert abs(r["entropy_bits"] - 4.0) < 1e-12
+        assert math.isclose(r["mse"], float(np.mean(ref * ref)), rel_tol=1e-12)
+        assert r["max_abs"] == float(np.max(np.abs(ref)))
+
+
+def test_quant_error_nf4_beats_int4_and_fp4_on_normal_weights():
+    """[S] 5.1.2: NF4 is clearly better than the 4-bit float and integer types.  On normally
+    distributed weights its error is the lowest and its codes are the most evenly used."""
+    W = synth.normal_f32(71, (256, 1024), 0.02)
+    res = {k: oracle.quant_error(W, cb, dq=True)
+           for k, cb in (("nf4", oracle.codebook()), ("int4", oracle.codebook_int4()), ("fp4", oracle.codebook_fp4()))}
+    assert res["nf4"]["mse"] < res["fp4"]["mse"] < res["int4"]["mse"]
+    assert res["nf4"]["entropy_bits"] > res["fp4"]["entropy_bits"] > res["int4"]["entropy_bits"]
+    # DQ saves 0.373 bits per weight for a small increase of the error
+    plain = oracle.quant_error(W, oracle.codebook(), dq=False)
+    assert plain["mse"] <= res["nf4"]["mse"] < 1.01 * plain["mse"]
+
+
 def test_double_quant_constant_and_single_block():
     a = np.full(1000, 0.0371, dtype=np.float32)
     codes, scales, mean = oracle.double_quant(a)
