@@ -181,6 +181,65 @@ def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
     return out
 
 
+def qerror_gpu(torch, nf4, W, cb, dq=True):
+    """Quantization error of the float32 device weight W [rows, cols] under the 16-entry table cb,
+    from the library's own quantize / double quant / dequant (eq. 6, or eq. 2 at one level without
+    DQ): mse and max_abs of (deq - W) in float64, the element count per code, its entropy in bits,
+    and the stored bits per weight (codes, block constants and, with DQ, the mean)."""
+    n = W.numel()
+    if dq:
+        w = nf4.NF4Weight.from_float(W, cb)
+        packed = w.packed
+        deq = nf4.nf4_dequant(w).reshape(-1)
+        stored = packed.numel() + w.absmax_q.numel() + 4 * w.absmax_scale.numel() + 4 * w.absmax_mean.numel()
+    else:
+        packed, absmax = nf4.nf4_quantize(W.reshape(-1), cb)
+        deq = nf4.nf4_dequant_single(packed, absmax, n, cb)
+        stored = packed.numel() + 4 * absmax.numel()
+    err = deq.double() - W.reshape(-1).double()
+    codes = torch.stack([packed & 15, packed >> 4], dim=1).reshape(-1)[:n]
+    occ = torch.bincount(codes.long(), minlength=16).cpu().numpy()
+    import numpy as np
+    p = occ[occ > 0] / float(n)
+    return {"mse": float((err * err).mean()), "max_abs": float(err.abs().max()), "occupancy": occ,
+            "entropy_bits": float(-(p * np.log2(p)).sum()), "bits_per_param": 8.0 * stored / n}
+
+
+def bench_qerror(torch, nf4, synth, dev):
+    """NF4 against Int4 and FP4, with and without DQ, on a 4096 x 4096 weight drawn N(0, 0.02)
+    and with 1 % of entries from N(0, 0.2) (heavy tail); times quantize + dequant per weight."""
+    import numpy as np
+    tables = {"nf4": nf4.nf4_build_codebook(), "int4": nf4.nf4_build_int4_codebook(),
+              "fp4": nf4.nf4_build_fp4_codebook()}
+    dists = {"normal": synth.normal_f32(1000, (4096, 4096), 0.02),
+             "heavy_tail": synth.heavy_tail_f32(1000, 6000, (4096, 4096), 0.02, 0.2, 0.01)}
+    rows = []
+    for dname, Wh in dists.items():
+        W = torch.from_numpy(Wh).to(dev)
+        var = float((W.double() ** 2).mean())
+        for cname, cb in tables.items():
+            for dq in (True, False):
+                st = qerror_gpu(torch, nf4, W, cb, dq)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(5):
+                    if dq:
+                        nf4.nf4_dequant(nf4.NF4Weight.from_float(W, cb))
+                    else:
+                        pk, am = nf4.nf4_quantize(W.reshape(-1), cb)
+                        nf4.nf4_dequant_single(pk, am, W.numel(), cb)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1e3 / 5
+                rows.append({"weights": dname, "type": cname, "dq": dq, "mse": st["mse"],
+                             "snr_db": round(10 * np.log10(var / st["mse"]), 3),
+                             "max_abs": st["max_abs"], "entropy_bits": round(st["entropy_bits"], 4),
+                             "bits_per_param": round(st["bits_per_param"], 4),
+                             "occupancy": [int(v) for v in st["occupancy"]],
+                             "quantize_dequant_ms": round(ms, 3)})
+        del W
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +249,9 @@ def main():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
+    ap.add_argument("--qerror", action="store_true",
+                    help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
+                         "normal and heavy-tail 4096 x 4096 weights (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of exactly 1 GiB, 5 times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -221,6 +283,10 @@ def main():
         return
     if args.gemv_only:
         print(json.dumps({"gemv": bench_gemv(torch, nf4, synth, dev)}), flush=True)
+        return
+    if args.qerror:
+        print(json.dumps({"workload": "qerror: 4-bit types on synthetic 4096x4096 weights",
+                          "rows": bench_qerror(torch, nf4, synth, dev)}), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     if wl.swiglu:

@@ -6,8 +6,9 @@ current torch stream, and all arithmetic runs in the library's HIP kernels.  If 
 not built, importing the binding raises; there is no fallback path.
 
 Names follow the C ABI:
-  nf4_build_codebook, nf4_quantize, nf4_double_quant, nf4_dequant,
-  qlora_linear_fwd, qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd.
+  nf4_build_codebook, nf4_build_int4_codebook, nf4_build_fp4_codebook, nf4_quantize,
+  nf4_double_quant, nf4_dequant, nf4_dequant_single, qlora_linear_fwd, qlora_linear_bwd,
+  qlora_swiglu_fwd, qlora_swiglu_bwd.
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ DQ_BLOCK = 256
 EXPORTS = (
     "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook",
     "nf4_build_int4_codebook", "nf4_build_fp4_codebook", "nf4_quantize",
-    "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant",
+    "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant", "nf4_dequant_single",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
@@ -80,6 +81,7 @@ def _load():
         "nf4_double_quant_workspace_size": (sz, [i64, i32]),
         "nf4_double_quant": (i, [P, i64, i32, P, P, P, P, sz, P]),
         "nf4_dequant": (i, [W, P, P]),
+        "nf4_dequant_single": (i, [P, P, i64, i32, P, P, P]),
         "qlora_linear_workspace_size": (sz, [i64, i64, i64, i32]),
         "qlora_linear_fwd": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P, sz, P]),
         "qlora_linear_bwd": (i, [W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P,
@@ -246,6 +248,18 @@ def nf4_dequant(w: NF4Weight):
     out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=w.device)
     d = w.descriptor()
     _check(lib.nf4_dequant(ctypes.byref(d), _ptr(out), _stream(w.device)), "nf4_dequant")
+    return out
+
+
+def nf4_dequant_single(packed, absmax, numel: int, codebook=None, block: int = BLOCK):
+    """Single-level dequantization (float32 block constants, no DQ): bf16 [numel] device tensor."""
+    torch = _torch()
+    _need(packed, torch.uint8, "packed")
+    _need(absmax, torch.float32, "absmax")
+    cb = nf4_build_codebook() if codebook is None else np.ascontiguousarray(codebook, dtype=np.float32)
+    out = torch.empty(numel, dtype=torch.bfloat16, device=packed.device)
+    _check(lib.nf4_dequant_single(_ptr(packed), _ptr(absmax), numel, block, ctypes.c_void_p(cb.ctypes.data),
+                                  _ptr(out), _stream(packed.device)), "nf4_dequant_single")
     return out
 
 

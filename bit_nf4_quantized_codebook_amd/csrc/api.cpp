@@ -358,9 +358,27 @@ int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
                                                  reinterpret_cast<hipStream_t>(stream)),
                       "dequant");
     else
-        NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, numel,
-                                           w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
+        NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, nullptr,
+                                           numel, w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
                       "dequant");
+    return NF4_OK;
+}
+
+int nf4_dequant_single(const uint8_t *packed, const float *absmax, int64_t numel, int32_t block,
+                       const float codebook[16], uint16_t *out_bf16, void *stream) {
+    if (!codebook) return fail(NF4_ERR_NULL, "codebook is NULL");
+    if (numel < 0) return fail(NF4_ERR_SHAPE, "numel must be >= 0");
+    if (block != 64) return fail(NF4_ERR_UNSUPPORTED, "block must be 64");
+    int zc;
+    int rc = check_codebook(codebook, &zc);
+    if (rc) return rc;
+    if (numel == 0) return NF4_OK;
+    if (!packed || !absmax || !out_bf16) return fail(NF4_ERR_NULL, "packed, absmax and out_bf16 must be non-NULL");
+    if (!aligned16(packed) || !aligned16(out_bf16))
+        return fail(NF4_ERR_ALIGN, "packed and out_bf16 must be 16-byte aligned");
+    NF4_CHECK_HIP(nf4k::launch_dequant(packed, nullptr, nullptr, nullptr, absmax, numel, codebook, out_bf16,
+                                       reinterpret_cast<hipStream_t>(stream)),
+                  "single-level dequant");
     return NF4_OK;
 }
 

@@ -22,9 +22,10 @@ hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], u
 size_t double_quant_ws(int64_t nb);
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, float *scales,
                                float *mean, void *ws, hipStream_t stream);
+// absmax_plain != NULL: one-level dequantization (eq. 2) with those float32 block constants
 hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const float *absmax_scale,
-                          const float *absmax_mean, int64_t numel, const float cb[16],
-                          uint16_t *out, hipStream_t stream);
+                          const float *absmax_mean, const float *absmax_plain, int64_t numel,
+                          const float cb[16], uint16_t *out, hipStream_t stream);
 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,

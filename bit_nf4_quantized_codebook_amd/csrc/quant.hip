@@ -154,24 +154,28 @@ __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__
 }
 
 // ------------------------------------------------------------------------------------------
-// Standalone double dequantization (eq. 6): one packed dword (8 weights) per lane.
+// Standalone dequantization: one packed dword (8 weights) per lane.  Double dequantization
+// (eq. 6) when absmax_plain is NULL; otherwise eq. (2) at one level, the block constant taken
+// from the float32 absmax array as stored by the first quantization level.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ packed,
                                                       const uint8_t *__restrict__ absmax_q,
                                                       const float *__restrict__ absmax_scale,
                                                       const float *__restrict__ absmax_mean,
+                                                      const float *__restrict__ absmax_plain,
                                                       int64_t numel, Codebook cbk,
                                                       uint16_t *__restrict__ out) {
     __shared__ float cb[16];
     if (threadIdx.x < 16) cb[threadIdx.x] = cbk.v[threadIdx.x];
     __syncthreads();
-    const float mean = absmax_mean[0];
+    const bool plain = absmax_plain != nullptr;
+    const float mean = plain ? 0.0f : absmax_mean[0];
     const int64_t nwords = (numel + 7) >> 3;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords;
          w += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e0 = w << 3;
         const int64_t b = e0 >> 6;
-        const float a = block_scale(absmax_q[b], absmax_scale[b >> 8], mean);
+        const float a = plain ? absmax_plain[b] : block_scale(absmax_q[b], absmax_scale[b >> 8], mean);
         uint32_t word;
         if (e0 + 8 <= numel) {
             word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(packed) + w);
@@ -257,14 +261,14 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, 
 }
 
 hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const float *absmax_scale,
-                          const float *absmax_mean, int64_t numel, const float cb[16],
-                          uint16_t *out, hipStream_t stream) {
+                          const float *absmax_mean, const float *absmax_plain, int64_t numel,
+                          const float cb[16], uint16_t *out, hipStream_t stream) {
     if (numel == 0) return hipSuccess;
     Codebook c;
     for (int j = 0; j < 16; ++j) c.v[j] = cb[j];
     const int64_t nwords = (numel + 7) >> 3;
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(nwords, 256, 256 * 32)), dim3(256), 0, stream,
-                       packed, absmax_q, absmax_scale, absmax_mean, numel, c, out);
+                       packed, absmax_q, absmax_scale, absmax_mean, absmax_plain, numel, c, out);
     return hipGetLastError();
 }
 

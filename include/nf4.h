@@ -145,6 +145,19 @@ typedef struct nf4_weight {
 int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream);
 
 /*
+ * Single-level dequantization to BF16 -- section 3.1, eq. (2), for a weight quantized without
+ * the second level (the "no DQ" rows of section 5.1.2's comparison):
+ *   out[i] = bf16_RNE(fp32(codebook[code_i] * absmax[i / block]))
+ *   packed:   device uint8 [ceil(numel/2)] from nf4_quantize; 16-byte aligned.
+ *   absmax:   device float32 [ceil(numel/block)] from nf4_quantize.
+ *   numel:    >= 0 (0 is a no-op); block must be 64.
+ *   codebook: HOST float[16], the table passed to nf4_quantize (same checks).
+ *   out_bf16: device uint16 [numel], 16-byte aligned.
+ */
+int nf4_dequant_single(const uint8_t *packed, const float *absmax, int64_t numel, int32_t block,
+                       const float codebook[16], uint16_t *out_bf16, void *stream);
+
+/*
  * QLoRA linear forward -- section 3.5 eq. (5) with the LoRA scalar s of eq. (3) (section 4):
  *   T = X L1;  Y = X deq(W)^T + s T L2
  *   X: [M, K] bf16; L1: [K, r] bf16; L2: [r, N] bf16; Y: [M, N] bf16 (N = w->rows, K = w->cols).

@@ -259,6 +259,26 @@ def test_alt_codebook_quantize_dq_dequant_bit_exact(kind):
     assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(-1), oracle.dequant_weight(q, cb).reshape(-1))
 
 
+@pytest.mark.parametrize("dist", ["normal", "heavy_tail"])
+@pytest.mark.parametrize("kind", ["nf4", "int4", "fp4"])
+@pytest.mark.parametrize("dq", [True, False])
+def test_quant_error_statistics_match_oracle(dist, kind, dq):
+    """The quantization-error workload (bench.py --qerror) on a 1024 x 1024 weight: statistics from
+    the library's quantize / double quant / dequant against the oracle's."""
+    import bench
+    _say(f"quant error: {dist} {kind} dq={dq}")
+    cb = nf4.nf4_build_codebook() if kind == "nf4" else _alt_cb(kind)
+    W = (synth.normal_f32(141, (1024, 1024), 0.02) if dist == "normal"
+         else synth.heavy_tail_f32(141, 142, (1024, 1024), 0.02, 0.2, 0.01))
+    got = bench.qerror_gpu(torch, nf4, torch.from_numpy(W).to(DEV), cb, dq)
+    ref = oracle.quant_error(W, cb, dq)
+    assert np.array_equal(got["occupancy"], ref["occupancy"])
+    assert got["max_abs"] == ref["max_abs"]
+    assert abs(got["mse"] - ref["mse"]) <= 1e-12 * ref["mse"]
+    assert abs(got["entropy_bits"] - ref["entropy_bits"]) <= 1e-12
+    assert abs(got["bits_per_param"] - ref["bits_per_param"]) <= 32.0 / W.size   # + the stored mean
+
+
 ALT_SHAPES = [
     (1, 3000, 8192, 64),       # one-token decode layout
     (4, 520, 2048, 128),       # 4x4-MFMA decode layout
