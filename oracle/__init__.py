@@ -16,7 +16,9 @@ Quantized LLMs" study notes, gitcode.csdn.net/6a0046f754b52172bc72e356, unless n
 * ``quantize``      -- section 3.1 (flatten, blocks of B, one constant per block), eq. (1) in its
                        absmax form, section 3.2 step 3 (absmax normalisation to [-1, 1]).  Any
                        ascending 16-entry table; equal neighbours allowed (the lower index wins).
-* ``double_quant``  -- section 3.3 (mean-centred 8-bit float constants, block 256).
+* ``double_quant``  -- section 3.3 (mean-centred 8-bit float constants, block 256); with
+                       ``fmt="int8"`` eq. (1) at 8 bits on the same centred constants (the
+                       integer alternative to the pages' 8-bit float; a reading).
 * ``dequant``       -- section 3.5, eq. (6), with eq. (2) at each level; output in BF16.
 * ``forward``       -- section 3.5 eq. (5) with the scalar s of eq. (3) (section 4, LoRA).
 * ``backward``      -- section 3.5: gradients for the adapters only, through the BF16 weight.
@@ -86,6 +88,9 @@ def _load():
                 "oracle_block_scales": (ctypes.c_int, [P, P, f32, i64, i32, P]),
                 "oracle_dequant": (ctypes.c_int, [P, P, P, f32, i64, i32, i32, P, P]),
                 "oracle_dequant_plain": (ctypes.c_int, [P, P, i64, i32, P, P]),
+                "oracle_double_quant_int8": (ctypes.c_int, [P, i64, i32, P, P, P]),
+                "oracle_block_scales_int8": (ctypes.c_int, [P, P, f32, i64, i32, P]),
+                "oracle_dequant_int8dq": (ctypes.c_int, [P, P, P, f32, i64, i32, i32, P, P]),
                 "oracle_unpack": (None, [P, i64, P]),
             }
             for name, (res, args) in sig.items():
@@ -198,40 +203,47 @@ def grouped_sum(v, group: int = 256) -> float:
     return _load().oracle_grouped_sum(_p(v), v.size, group)
 
 
-def double_quant(absmax, dq_block: int = DQ_BLOCK):
-    """Level-2 quantization of the block constants.
+DQ_FORMATS = ("e4m3", "int8")
+
+
+def double_quant(absmax, dq_block: int = DQ_BLOCK, fmt: str = "e4m3"):
+    """Level-2 quantization of the block constants: section 3.3's 8-bit float (E4M3), or with
+    ``fmt="int8"`` eq. (1)'s 8-bit integers on the same centred constants.
 
     Returns (codes uint8 [nb], scales float32 [ceil(nb/dq_block)], mean float32)."""
+    assert fmt in DQ_FORMATS
     a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
     nb = a.size
     codes = np.zeros(nb, dtype=np.uint8)
     scales = np.zeros((nb + dq_block - 1) // dq_block, dtype=np.float32)
     mean = np.zeros(1, dtype=np.float32)
-    rc = _load().oracle_double_quant(_p(a), nb, dq_block, _p(codes), _p(scales), _p(mean))
+    fn = _load().oracle_double_quant if fmt == "e4m3" else _load().oracle_double_quant_int8
+    rc = fn(_p(a), nb, dq_block, _p(codes), _p(scales), _p(mean))
     if rc != 0:
         raise ValueError("oracle_double_quant failed (%d)" % rc)
     return codes, scales, np.float32(mean[0])
 
 
-def block_scales(codes, scales, mean, dq_block: int = DQ_BLOCK) -> np.ndarray:
+def block_scales(codes, scales, mean, dq_block: int = DQ_BLOCK, fmt: str = "e4m3") -> np.ndarray:
     """The rebuilt first-level constants a' (inner dequant of eq. 6)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     out = np.empty(codes.size, dtype=np.float32)
-    _load().oracle_block_scales(_p(codes), _p(scales), float(mean), codes.size, dq_block, _p(out))
+    fn = _load().oracle_block_scales if fmt == "e4m3" else _load().oracle_block_scales_int8
+    fn(_p(codes), _p(scales), float(mean), codes.size, dq_block, _p(out))
     return out
 
 
 def dequant(packed, codes, scales, mean, numel: int, cb=None, block: int = BLOCK,
-            dq_block: int = DQ_BLOCK) -> np.ndarray:
+            dq_block: int = DQ_BLOCK, fmt: str = "e4m3") -> np.ndarray:
     """Eq. (6): bf16 bit patterns [numel] of the double-dequantized weight."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     cb = codebook() if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
     out = np.empty(numel, dtype=np.uint16)
-    rc = _load().oracle_dequant(_p(packed), _p(codes), _p(scales), float(mean), numel, block,
-                                dq_block, _p(cb), _p(out))
+    fn = _load().oracle_dequant if fmt == "e4m3" else _load().oracle_dequant_int8dq
+    rc = fn(_p(packed), _p(codes), _p(scales), float(mean), numel, block, dq_block, _p(cb), _p(out))
     if rc != 0:
         raise ValueError("oracle_dequant failed (%d)" % rc)
     return out
@@ -254,19 +266,20 @@ def unpack(packed, numel: int) -> np.ndarray:
     return out
 
 
-def quantize_dq(W, cb=None):
+def quantize_dq(W, cb=None, fmt: str = "e4m3"):
     """Quantize + double-quantize a weight; returns a dict of the stored pieces."""
     W = np.asarray(W, dtype=np.float32)
     packed, absmax = quantize(W, cb)
-    codes, scales, mean = double_quant(absmax)
+    codes, scales, mean = double_quant(absmax, fmt=fmt)
     return {"packed": packed, "absmax": absmax, "codes": codes, "scales": scales, "mean": mean,
-            "shape": W.shape}
+            "shape": W.shape, "fmt": fmt}
 
 
 def dequant_weight(q, cb=None) -> np.ndarray:
     """bf16 bits of the weight described by ``quantize_dq``'s dict, reshaped."""
     n = int(np.prod(q["shape"]))
-    return dequant(q["packed"], q["codes"], q["scales"], q["mean"], n, cb).reshape(q["shape"])
+    return dequant(q["packed"], q["codes"], q["scales"], q["mean"], n, cb,
+                   fmt=q.get("fmt", "e4m3")).reshape(q["shape"])
 
 
 def bits_per_parameter(dq: bool, block: int = BLOCK, dq_block: int = DQ_BLOCK) -> float:
@@ -276,7 +289,7 @@ def bits_per_parameter(dq: bool, block: int = BLOCK, dq_block: int = DQ_BLOCK) -
     return 4.0 + (8.0 / block + 32.0 / (block * dq_block) if dq else 32.0 / block)
 
 
-def quant_error(W, cb=None, dq: bool = True) -> dict:
+def quant_error(W, cb=None, dq: bool = True, fmt: str = "e4m3") -> dict:
     """Quantization error of ``W`` under table ``cb`` (the comparison of section 5.1.2, on
     synthetic weights): the weight is quantized, double-quantized when ``dq``, dequantized to
     bf16 (eq. 6, or eq. 2 at one level without DQ), and compared with W in float64.
@@ -288,8 +301,8 @@ def quant_error(W, cb=None, dq: bool = True) -> dict:
     n = W.size
     packed, absmax = quantize(W, cb)
     if dq:
-        codes, scales, mean = double_quant(absmax)
-        deq = dequant(packed, codes, scales, mean, n, cb)
+        codes, scales, mean = double_quant(absmax, fmt=fmt)
+        deq = dequant(packed, codes, scales, mean, n, cb, fmt=fmt)
     else:
         deq = dequant_plain(packed, absmax, n, cb)
     err = bf16_to_f32(deq).astype(np.float64) - W.astype(np.float64)

@@ -261,6 +261,64 @@ static inline int nibble(const uint8_t *packed, int64_t i) {
     return (packed[i >> 1] >> ((i & 1) ? 4 : 0)) & 0xF;
 }
 
+/* ------------------------------------------------------------------------------------------
+ * Double quantization with 8-bit integer codes: eq. (1) of section 3.1 applied to the centred
+ * constants, in place of section 3.3's 8-bit float.  Same structure as above (mean, 256-blocks,
+ * the stored multiplier s undoes the scaling): per block A = max |y|, s = fp32(A / 127),
+ * code = rint(fp32(y / s)) (ties to even) clamped to [-127, 127], stored as its two's complement
+ * byte; s == 0 gives code 0.  Decode: a' = fmaf((float)code, s, mu).
+ * ------------------------------------------------------------------------------------------ */
+int oracle_double_quant_int8(const float *absmax, int64_t nb, int32_t dq_block,
+                             uint8_t *codes, float *scales, float *mean_out) {
+    if (nb <= 0 || dq_block <= 0) return -1;
+    double *d = (double *)malloc((size_t)nb * sizeof(double));
+    for (int64_t i = 0; i < nb; ++i) d[i] = (double)absmax[i];
+    const double S = oracle_grouped_sum(d, nb, 256);
+    free(d);
+    const float mu = (float)(S / (double)nb);
+    *mean_out = mu;
+    const int64_t ng = (nb + dq_block - 1) / dq_block;
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t i0 = g * dq_block;
+        const int64_t i1 = (i0 + dq_block < nb) ? i0 + dq_block : nb;
+        float A = 0.0f;
+        for (int64_t i = i0; i < i1; ++i) { float y = absmax[i] - mu; float m = fabsf(y); if (m > A) A = m; }
+        const float s = A / 127.0f;
+        scales[g] = s;
+        for (int64_t i = i0; i < i1; ++i) {
+            if (s == 0.0f) { codes[i] = 0x00; continue; }
+            float y = absmax[i] - mu;
+            float t = rintf(y / s);
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            codes[i] = (uint8_t)(int8_t)t;
+        }
+    }
+    return 0;
+}
+
+static float int8_decode(uint8_t c) { return (float)(int8_t)c; }
+
+int oracle_block_scales_int8(const uint8_t *codes, const float *scales, float mu, int64_t nb,
+                             int32_t dq_block, float *out) {
+    if (dq_block <= 0) return -1;
+    for (int64_t b = 0; b < nb; ++b)
+        out[b] = fmaf(int8_decode(codes[b]), scales[b / dq_block], mu);
+    return 0;
+}
+
+int oracle_dequant_int8dq(const uint8_t *packed, const uint8_t *codes, const float *scales, float mu,
+                          int64_t numel, int32_t block, int32_t dq_block, const float cb[16],
+                          uint16_t *out) {
+    if (block <= 0 || dq_block <= 0) return -1;
+    for (int64_t i = 0; i < numel; ++i) {
+        const int64_t b = i / block;
+        const float a = fmaf(int8_decode(codes[b]), scales[b / dq_block], mu);
+        out[i] = oracle_bf16_rne(cb[nibble(packed, i)] * a);
+    }
+    return 0;
+}
+
 int oracle_block_scales(const uint8_t *codes, const float *scales, float mu, int64_t nb,
                         int32_t dq_block, float *out) {
     if (dq_block <= 0) return -1;

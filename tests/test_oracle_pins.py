@@ -428,6 +428,36 @@ def test_quant_error_nf4_beats_int4_and_fp4_on_normal_weights():
     assert plain["mse"] <= res["nf4"]["mse"] < 1.01 * plain["mse"]
 
 
+def test_double_quant_int8_is_eq1_on_the_centred_constants():
+    """Integer second level: eq. (1) at 8 bits, round(127 y / max|y|) per 256-block, y = a - mean."""
+    a = np.abs(synth.normal_f32(81, (5000,), 0.05)).astype(np.float32)
+    c, sc, m = oracle.double_quant(a, fmt="int8")
+    _, _, m_e4 = oracle.double_quant(a)
+    assert np.float32(m).view(np.uint32) == np.float32(m_e4).view(np.uint32)   # same mean
+    codes = c.view(np.int8).astype(np.int64)
+    y = (a - np.float32(m)).astype(np.float32)
+    rebuilt = oracle.block_scales(c, sc, m, fmt="int8").astype(np.float64)
+    for j in range(sc.size):
+        blk = slice(256 * j, min(256 * (j + 1), a.size))
+        yj = [Fraction(float(v)) for v in y[blk]]
+        A = max(abs(v) for v in yj)
+        assert abs(Fraction(float(sc[j])) * 127 - A) <= A * Fraction(1, 1 << 23)     # s = A / 127
+        for code, v in zip(codes[blk], yj):
+            assert abs(code - 127 * v / A) <= Fraction(1, 2) + Fraction(1, 1 << 20)
+        k = int(np.argmax(np.abs(y[blk])))
+        assert abs(codes[blk][k]) == 127
+        # the rebuilt constant is within half a step of the original (plus float rounding)
+        err = np.abs(rebuilt[blk] - a[blk].astype(np.float64))
+        assert np.all(err <= float(sc[j]) * (0.5 + 1e-6) + 4 * np.spacing(np.float32(a.max())))
+
+
+def test_double_quant_int8_constant_tensor():
+    a = np.full(700, 0.0375, np.float32)
+    c, sc, m = oracle.double_quant(a, fmt="int8")
+    assert np.all(c == 0) and np.all(sc == 0.0) and m == np.float32(0.0375)
+    assert np.all(oracle.block_scales(c, sc, m, fmt="int8") == np.float32(0.0375))
+
+
 def test_double_quant_constant_and_single_block():
     a = np.full(1000, 0.0371, dtype=np.float32)
     codes, scales, mean = oracle.double_quant(a)
