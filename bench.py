@@ -42,10 +42,10 @@ METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 # taken on: if the hashed sources differ, traffic is reported as null.
 FETCH_SCALE = 1048576.0 / 524301.3
 WRITE_SCALE = 1048576.0 / 1048576.0
-GEMM_TRAFFIC_KIB = {0: (149911.9, 33288.2), 1: (149902.3, 32859.9)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
+GEMM_TRAFFIC_KIB = {0: (149911.9, 33602.0), 1: (149902.3, 32858.1)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
 GEMM_TRAFFIC_SOURCES = {
     "csrc/gemm_bf16.hip": "f2b507d49931aee86104f099c1c36f664584e15eefe0fadcf2dd578ebd1ba616",
-    "csrc/common.h": "3975181d65e4c262f2112e4e2d21fc7735ca999cfcefb5d48a6ef191879916d6",
+    "csrc/common.h": "b0791e84149734c02f8e8b602dc28b879014ef9e27605c11332a13f253f9c97a",
     "csrc/dqtile.h": "490babcb3e32389b8d42f9bf9415f7648bda55abef16a44443e6c8e438a25496",
 }
 
@@ -181,14 +181,14 @@ def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
     return out
 
 
-def qerror_gpu(torch, nf4, W, cb, dq=True):
+def qerror_gpu(torch, nf4, W, cb, dq=True, dq_format="e4m3"):
     """Quantization error of the float32 device weight W [rows, cols] under the 16-entry table cb,
     from the library's own quantize / double quant / dequant (eq. 6, or eq. 2 at one level without
     DQ): mse and max_abs of (deq - W) in float64, the element count per code, its entropy in bits,
     and the stored bits per weight (codes, block constants and, with DQ, the mean)."""
     n = W.numel()
     if dq:
-        w = nf4.NF4Weight.from_float(W, cb)
+        w = nf4.NF4Weight.from_float(W, cb, dq_format=dq_format)
         packed = w.packed
         deq = nf4.nf4_dequant(w).reshape(-1)
         stored = packed.numel() + w.absmax_q.numel() + 4 * w.absmax_scale.numel() + 4 * w.absmax_mean.numel()
@@ -206,8 +206,9 @@ def qerror_gpu(torch, nf4, W, cb, dq=True):
 
 
 def bench_qerror(torch, nf4, synth, dev):
-    """NF4 against Int4 and FP4, with and without DQ, on a 4096 x 4096 weight drawn N(0, 0.02)
-    and with 1 % of entries from N(0, 0.2) (heavy tail); times quantize + dequant per weight."""
+    """NF4 against Int4 and FP4, with DQ (8-bit float or 8-bit integer second level) and without,
+    on a 4096 x 4096 weight drawn N(0, 0.02) and with 1 % of entries from N(0, 0.2) (heavy tail);
+    times quantize + dequant per weight."""
     import numpy as np
     tables = {"nf4": nf4.nf4_build_codebook(), "int4": nf4.nf4_build_int4_codebook(),
               "fp4": nf4.nf4_build_fp4_codebook()}
@@ -218,19 +219,21 @@ def bench_qerror(torch, nf4, synth, dev):
         W = torch.from_numpy(Wh).to(dev)
         var = float((W.double() ** 2).mean())
         for cname, cb in tables.items():
-            for dq in (True, False):
-                st = qerror_gpu(torch, nf4, W, cb, dq)
+            for dqname in ("e4m3", "int8", "none"):
+                dq = dqname != "none"
+                fmt = dqname if dq else "e4m3"
+                st = qerror_gpu(torch, nf4, W, cb, dq, fmt)
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 for _ in range(5):
                     if dq:
-                        nf4.nf4_dequant(nf4.NF4Weight.from_float(W, cb))
+                        nf4.nf4_dequant(nf4.NF4Weight.from_float(W, cb, dq_format=fmt))
                     else:
                         pk, am = nf4.nf4_quantize(W.reshape(-1), cb)
                         nf4.nf4_dequant_single(pk, am, W.numel(), cb)
                 torch.cuda.synchronize()
                 ms = (time.perf_counter() - t0) * 1e3 / 5
-                rows.append({"weights": dname, "type": cname, "dq": dq, "mse": st["mse"],
+                rows.append({"weights": dname, "type": cname, "dq": dqname, "mse": st["mse"],
                              "snr_db": round(10 * np.log10(var / st["mse"]), 3),
                              "max_abs": st["max_abs"], "entropy_bits": round(st["entropy_bits"], 4),
                              "bits_per_param": round(st["bits_per_param"], 4),

@@ -7,8 +7,8 @@ not built, importing the binding raises; there is no fallback path.
 
 Names follow the C ABI:
   nf4_build_codebook, nf4_build_int4_codebook, nf4_build_fp4_codebook, nf4_quantize,
-  nf4_double_quant, nf4_dequant, nf4_dequant_single, qlora_linear_fwd, qlora_linear_bwd,
-  qlora_swiglu_fwd, qlora_swiglu_bwd.
+  nf4_double_quant, nf4_double_quant_int8, nf4_dequant, nf4_dequant_single, qlora_linear_fwd,
+  qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd.
 """
 from __future__ import annotations
 
@@ -30,7 +30,8 @@ DQ_BLOCK = 256
 EXPORTS = (
     "nf4_status_string", "nf4_last_error", "nf4_version", "nf4_build_codebook",
     "nf4_build_int4_codebook", "nf4_build_fp4_codebook", "nf4_quantize",
-    "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_dequant", "nf4_dequant_single",
+    "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_double_quant_int8", "nf4_dequant",
+    "nf4_dequant_single",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
@@ -53,6 +54,7 @@ class _WeightDesc(ctypes.Structure):
         ("block", ctypes.c_int32),
         ("dq_block", ctypes.c_int32),
         ("codebook", ctypes.c_float * 16),
+        ("dq_format", ctypes.c_int32),
     ]
 
 
@@ -80,6 +82,7 @@ def _load():
         "nf4_quantize": (i, [P, i64, i32, P, P, P, P]),
         "nf4_double_quant_workspace_size": (sz, [i64, i32]),
         "nf4_double_quant": (i, [P, i64, i32, P, P, P, P, sz, P]),
+        "nf4_double_quant_int8": (i, [P, i64, i32, P, P, P, P, sz, P]),
         "nf4_dequant": (i, [W, P, P]),
         "nf4_dequant_single": (i, [P, P, i64, i32, P, P, P]),
         "qlora_linear_workspace_size": (sz, [i64, i64, i64, i32]),
@@ -189,8 +192,13 @@ def nf4_quantize(W, codebook=None, block: int = BLOCK):
     return packed, absmax
 
 
-def nf4_double_quant(absmax, dq_block: int = DQ_BLOCK, workspace=None):
-    """Level-2 quantization: returns (absmax_q uint8, absmax_scale float32, absmax_mean float32[1])."""
+#: second-level code formats (nf4_weight.dq_format)
+DQ_FORMATS = {"e4m3": 0, "int8": 1}
+
+
+def nf4_double_quant(absmax, dq_block: int = DQ_BLOCK, workspace=None, fmt: str = "e4m3"):
+    """Level-2 quantization: returns (absmax_q uint8, absmax_scale float32, absmax_mean float32[1]).
+    fmt "e4m3" (nf4_double_quant) or "int8" (nf4_double_quant_int8)."""
     torch = _torch()
     _need(absmax, torch.float32, "absmax")
     nb = absmax.numel()
@@ -199,8 +207,9 @@ def nf4_double_quant(absmax, dq_block: int = DQ_BLOCK, workspace=None):
     mean = torch.empty(1, dtype=torch.float32, device=absmax.device)
     wsb = lib.nf4_double_quant_workspace_size(nb, dq_block)
     ws = _workspace(wsb, absmax.device, workspace)
-    _check(lib.nf4_double_quant(_ptr(absmax), nb, dq_block, _ptr(q), _ptr(sc), _ptr(mean), _ptr(ws),
-                                wsb, _stream(absmax.device)), "nf4_double_quant")
+    fn = {"e4m3": lib.nf4_double_quant, "int8": lib.nf4_double_quant_int8}[fmt]
+    _check(fn(_ptr(absmax), nb, dq_block, _ptr(q), _ptr(sc), _ptr(mean), _ptr(ws), wsb,
+              _stream(absmax.device)), "nf4_double_quant(%s)" % fmt)
     return q, sc, mean
 
 
@@ -216,6 +225,7 @@ class NF4Weight:
     codebook: np.ndarray
     block: int = BLOCK
     dq_block: int = DQ_BLOCK
+    dq_format: str = "e4m3"
 
     def descriptor(self) -> _WeightDesc:
         d = _WeightDesc()
@@ -225,6 +235,7 @@ class NF4Weight:
         d.absmax_mean = self.absmax_mean.data_ptr()
         d.rows, d.cols = int(self.rows), int(self.cols)
         d.block, d.dq_block = int(self.block), int(self.dq_block)
+        d.dq_format = DQ_FORMATS[self.dq_format]
         for j in range(16):
             d.codebook[j] = float(self.codebook[j])
         return d
@@ -234,12 +245,12 @@ class NF4Weight:
         return self.packed.device
 
     @classmethod
-    def from_float(cls, W, codebook=None):
+    def from_float(cls, W, codebook=None, dq_format: str = "e4m3"):
         """Quantize + double-quantize a float32 [rows, cols] device tensor."""
         cb = nf4_build_codebook() if codebook is None else np.ascontiguousarray(codebook, dtype=np.float32)
         packed, absmax = nf4_quantize(W.contiguous(), cb)
-        q, sc, mean = nf4_double_quant(absmax)
-        return cls(packed, q, sc, mean, W.shape[0], W.shape[1], cb)
+        q, sc, mean = nf4_double_quant(absmax, fmt=dq_format)
+        return cls(packed, q, sc, mean, W.shape[0], W.shape[1], cb, dq_format=dq_format)
 
 
 def nf4_dequant(w: NF4Weight):

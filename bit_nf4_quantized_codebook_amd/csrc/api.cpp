@@ -105,6 +105,8 @@ int check_weight(const nf4_weight *w) {
     if (w->rows <= 0 || w->cols <= 0) return fail(NF4_ERR_SHAPE, "weight rows and cols must be > 0");
     if (w->block != 64) return fail(NF4_ERR_UNSUPPORTED, "block must be 64");
     if (w->dq_block != 256) return fail(NF4_ERR_UNSUPPORTED, "dq_block must be 256");
+    if (w->dq_format != NF4_DQ_E4M3 && w->dq_format != NF4_DQ_INT8)
+        return fail(NF4_ERR_ARG, "dq_format must be NF4_DQ_E4M3 or NF4_DQ_INT8");
     if (!aligned16(w->packed)) return fail(NF4_ERR_ALIGN, "packed weight must be 16-byte aligned");
     int zc;
     return check_codebook(w->codebook, &zc);
@@ -119,6 +121,7 @@ nf4k::WeightView view_of(const nf4_weight *w) {
     v.rows = w->rows;
     v.cols = w->cols;
     for (int j = 0; j < 16; ++j) v.cb[j] = w->codebook[j];
+    v.dq_int8 = w->dq_format == NF4_DQ_INT8 ? 1u : 0u;
     return v;
 }
 
@@ -329,9 +332,10 @@ size_t nf4_double_quant_workspace_size(int64_t nblocks, int32_t dq_block) {
     return nf4k::double_quant_ws(nblocks);
 }
 
-int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
-                     float *absmax_scale, float *absmax_mean, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+namespace {
+int double_quant_impl(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                      float *absmax_scale, float *absmax_mean, void *workspace, size_t workspace_bytes,
+                      bool int8, void *stream) {
     if (nblocks <= 0) return fail(NF4_ERR_SHAPE, "nblocks must be >= 1");
     if (dq_block != 256) return fail(NF4_ERR_UNSUPPORTED, "dq_block must be 256");
     if (!absmax || !absmax_q || !absmax_scale || !absmax_mean || !workspace)
@@ -341,9 +345,24 @@ int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uin
     if (workspace_bytes < nf4k::double_quant_ws(nblocks))
         return fail(NF4_ERR_WORKSPACE, "double quant workspace too small");
     NF4_CHECK_HIP(nf4k::launch_double_quant(absmax, nblocks, absmax_q, absmax_scale, absmax_mean,
-                                            workspace, reinterpret_cast<hipStream_t>(stream)),
+                                            workspace, int8, reinterpret_cast<hipStream_t>(stream)),
                   "double quant");
     return NF4_OK;
+}
+}  // namespace
+
+int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                     float *absmax_scale, float *absmax_mean, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    return double_quant_impl(absmax, nblocks, dq_block, absmax_q, absmax_scale, absmax_mean, workspace,
+                             workspace_bytes, false, stream);
+}
+
+int nf4_double_quant_int8(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                          float *absmax_scale, float *absmax_mean, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return double_quant_impl(absmax, nblocks, dq_block, absmax_q, absmax_scale, absmax_mean, workspace,
+                             workspace_bytes, true, stream);
 }
 
 int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
@@ -359,7 +378,7 @@ int nf4_dequant(const nf4_weight *w, uint16_t *out_bf16, void *stream) {
                       "dequant");
     else
         NF4_CHECK_HIP(nf4k::launch_dequant(w->packed, w->absmax_q, w->absmax_scale, w->absmax_mean, nullptr,
-                                           numel, w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
+                                           (uint32_t)w->dq_format, numel, w->codebook, out_bf16, reinterpret_cast<hipStream_t>(stream)),
                       "dequant");
     return NF4_OK;
 }
@@ -376,7 +395,7 @@ int nf4_dequant_single(const uint8_t *packed, const float *absmax, int64_t numel
     if (!packed || !absmax || !out_bf16) return fail(NF4_ERR_NULL, "packed, absmax and out_bf16 must be non-NULL");
     if (!aligned16(packed) || !aligned16(out_bf16))
         return fail(NF4_ERR_ALIGN, "packed and out_bf16 must be 16-byte aligned");
-    NF4_CHECK_HIP(nf4k::launch_dequant(packed, nullptr, nullptr, nullptr, absmax, numel, codebook, out_bf16,
+    NF4_CHECK_HIP(nf4k::launch_dequant(packed, nullptr, nullptr, nullptr, absmax, 0u, numel, codebook, out_bf16,
                                        reinterpret_cast<hipStream_t>(stream)),
                   "single-level dequant");
     return NF4_OK;

@@ -61,9 +61,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float t) {
     return sign | code;
 }
 
-// Rebuilt first-level block constant (eq. 6 inner dequant): one rounding.
-__device__ __forceinline__ float block_scale(uint32_t code, float s2, float mean) {
-    return __builtin_fmaf(e4m3_to_f32(code), s2, mean);
+// Rebuilt first-level block constant (eq. 6 inner dequant): one rounding.  The 8-bit code is
+// OCP E4M3 (the 8-bit float of section 3.3) or, when int8 is set, a two's complement integer
+// (eq. (1) at 8 bits applied to the centred constants).
+__device__ __forceinline__ float block_scale(uint32_t code, float s2, float mean, bool int8) {
+    const float v = int8 ? (float)((int32_t)(code << 24) >> 24) : e4m3_to_f32(code);
+    return __builtin_fmaf(v, s2, mean);
 }
 
 }  // namespace nf4k

@@ -56,6 +56,7 @@ struct GemmArgs {
     const uint8_t *c2;       // E4M3 block constants
     const float *c1;         // 256-block multipliers
     const float *mean;       // [1]
+    uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
     const uint16_t *Ae;      // dT [M, r] bf16 (extension A)
     const uint16_t *Be;      // L1 [Nout, r] (natural layout)
     uint16_t *C;             // [M, Nout] bf16
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     const int ext_steps = (g.r + TK - 1) / TK;
 
     const float mean = g.mean[0];
+
+    const bool dq_i8 = g.dq_int8 != 0;
     const int64_t wblk_per_row = g.wcols >> 6;
     const int64_t wrow_bytes = g.wcols >> 1;
 
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     Lut lut;
     auto write_B = [&](int step, const WStage &ws, uint8_t *Bst, int part) {
         if (part == 0) {
-            float a = block_scale(ws.c2, __uint_as_float(ws.c1), mean);
+            float a = block_scale(ws.c2, __uint_as_float(ws.c1), mean, dq_i8);
             if ((int64_t)step * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
             lut = make_lut(g.cb, a);
         }
@@ -383,7 +386,7 @@ hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint
                              bool accumulate, hipStream_t stream) {
     GemmArgs a;
     a.A = dY;
-    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.Ae = dT; a.Be = L1; a.C = dX;
     a.M = M; a.Nout = w.cols; a.Kred = w.rows;
     a.wrows = w.rows; a.wcols = w.cols;

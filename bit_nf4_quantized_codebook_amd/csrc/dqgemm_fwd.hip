@@ -55,6 +55,7 @@ struct FwdArgs {
     const uint8_t *c2;       // [N*K/64]
     const float *c1;         // [ceil(N*K/64 / 256)]
     const float *mean;       // [1]
+    uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
     const uint16_t *sT;      // [M, r]
     const uint16_t *L2;      // [r, N]
     uint16_t *Y;             // [M, N]
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
     const int main_steps = (int)(g.K / TK);
     const int ext_steps = (g.r + TK - 1) / TK;
     const float mean = g.mean[0];
+    const bool dq_i8 = g.dq_int8 != 0;
     const int64_t nblk_row = g.K >> 6;
     const int64_t row_bytes_w = g.K >> 1;
 
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
         for (int j = 0; j < 2; ++j) {
             const uint32_t code = GROUPED ? (G.c2w[j] >> (8 * phase)) & 0xFFu : R.c2[j];
             const uint32_t mult = GROUPED ? G.c1[j] : R.c1[j];
-            L[j] = make_lut(g.cb, block_scale(code, __uint_as_float(mult), mean));
+            L[j] = make_lut(g.cb, block_scale(code, __uint_as_float(mult), mean, dq_i8));
         }
     };
     auto dequant_B = [&](const WRegs &R, const Lut *L, int s, bf16x8 *B) {
@@ -382,7 +384,7 @@ hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint1
                              hipStream_t stream) {
     FwdArgs a;
     a.X = X;
-    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.sT = sT; a.L2 = L2; a.Y = Y;
     a.M = M; a.N = w.rows; a.K = w.cols;
     a.r = r;

@@ -237,6 +237,7 @@ struct RowsArgs {
     const uint8_t *c2;
     const float *c1;
     const float *mean;
+    uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
     const uint16_t *L2;      // [r, N]
     const float *Tp;         // [nkc, M, r]
     uint16_t *Y;             // [M, N]
@@ -323,7 +324,9 @@ __device__ __forceinline__ f32x4 mfma4x4(uint32_t a0, uint32_t a1, uint32_t b0, 
 //   (B = the four rows' decoded pairs, A = X of four tokens over the same 4 columns).
 //   v_dot2_f32_bf16 issues at about a quarter of the VALU rate, so beyond one token the
 //   products go to the matrix cores.  The cross-wave sums run per batch of ITER row steps.
-template <int MM, int BR, int U, int NWMAX, bool MF>
+// I8: the second-level codes are int8 (else E4M3); a template parameter so that the E4M3 kernel
+// carries no per-block select (it cost 2-3 % here).
+template <int MM, int BR, int U, int NWMAX, bool MF, bool I8>
 __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
     // ring of 2 U register slots, loads U row steps ahead: step i sits in slot i % 2U, and the
     // load of step i + U lands in a slot whose step is already consumed, so no value moves
@@ -431,6 +434,7 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
         tp_chunk_load(rT, a.nkc, E, p - pc * EM, pc, p < npair, tv[f]);
     }
     const float mean = a.mean[0];                 // (a load pending inside the loop would drain the ring)
+    constexpr bool dq_i8 = I8;
     __builtin_amdgcn_sched_barrier(0);            // the weight rows go out last
     u32x4 ring[RING];
 #pragma unroll
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
             constexpr uint32_t sel = 0x0C0C0000u | ((4u + (bi & 3)) << 8);
             pr[bi] = *reinterpret_cast<const uint32_t *>(tabc + __builtin_amdgcn_perm(w[bi >> 2], lb, sel));
         });
-        return block_scale(c2b[qi], c1s[(int)(((q0 + qi) >> 8) - c1lo)], mean);
+        return block_scale(c2b[qi], c1s[(int)(((q0 + qi) >> 8) - c1lo)], mean, dq_i8);
     };
     const int nit = (nsteps + ITER - 1) / ITER;
     if constexpr (!MF) {
@@ -644,13 +648,21 @@ hipError_t launch_t_parts(const uint16_t *X, const uint16_t *L1, int32_t r, int6
     }
 }
 
+template <int MM, bool I8>
+void launch_rows_fmt(const RowsArgs &a, int threads, int grid, hipStream_t stream) {
+    if constexpr (MM == 1)
+        hipLaunchKernelGGL((gemv_rows_kernel<1, 4, 2, MAX_WAVES, false, I8>), dim3(grid), dim3(threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemv_rows_kernel<MM, 4, 2, MAX_WAVES, true, I8>), dim3(grid), dim3(threads), 0, stream, a);
+}
+
 template <int MM>
 hipError_t launch_rows(const RowsArgs &a, int threads, int grid, hipStream_t stream) {
     timing_before(stream, 2);
-    if constexpr (MM == 1)
-        hipLaunchKernelGGL((gemv_rows_kernel<1, 4, 2, MAX_WAVES, false>), dim3(grid), dim3(threads), 0, stream, a);
+    if (a.dq_int8)
+        launch_rows_fmt<MM, true>(a, threads, grid, stream);
     else
-        hipLaunchKernelGGL((gemv_rows_kernel<MM, 4, 2, MAX_WAVES, true>), dim3(grid), dim3(threads), 0, stream, a);
+        launch_rows_fmt<MM, false>(a, threads, grid, stream);
     const hipError_t err = hipGetLastError();
     timing_after(stream);
     return err;
@@ -702,7 +714,7 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
     if (err != hipSuccess) return err;
     RowsArgs a;
     a.X = X;
-    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.L2 = L2; a.Tp = Tp; a.Y = Y; a.T_out = T_out;
     a.M = M; a.N = w.rows; a.K = w.cols;
     a.r = r; a.nkc = g.nkc; a.KW = p.KW; a.S = p.S; a.RS = p.RS; a.R = p.R;

@@ -52,6 +52,7 @@ struct GemvArgs {
     const uint8_t *c2;
     const float *c1;
     const float *mean;
+    uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
     const uint16_t *sT;      // [M, r]  (s * X L1)
     const uint16_t *L2;      // [r, N]
     uint16_t *Y;             // [M, N]
@@ -60,7 +61,9 @@ struct GemvArgs {
     Codebook cb;
 };
 
-template <int MROWS>
+// I8: the second-level codes are int8 (else E4M3), fixed at compile time so that the E4M3
+// kernel carries no per-block select.
+template <int MROWS, bool I8>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     // X window: [MROWS rows][XWIN cols], planar within each 8-column group, double buffered.
     // Lanes whose token row is >= MROWS feed zeros to the MFMA without touching LDS.
@@ -74,6 +77,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     const int64_t n = n0 + ln;                      // this lane's W row
     const int64_t wrow_bytes = g.K >> 1, nblk = g.K >> 6;
     const float mean = g.mean[0];
+    constexpr bool dq_i8 = I8;
 
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.packed + n0 * wrow_bytes, (g.N - n0) * wrow_bytes);
     const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.N * nblk);
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     auto macro_step = [&](int ms, const WStage &st, const uint8_t *Xw) {
         const int kin = (ms * MACRO) % XWIN;             // column offset inside the window
         const int64_t blk = (int64_t)ms * 4 + lg;
-        float a = block_scale(st.c2, __uint_as_float(st.c1), mean);
+        float a = block_scale(st.c2, __uint_as_float(st.c1), mean, dq_i8);
         if (ms >= nmacro || blk >= nblk) a = 0.0f;        // past K: contributes nothing
         const Lut t = make_lut(g.cb, a);
         const uint32_t wd[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
@@ -205,13 +209,16 @@ hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const ui
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream) {
     GemvArgs a;
     a.X = X;
-    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.sT = sT; a.L2 = L2; a.Y = Y;
     a.M = M; a.N = w.rows; a.K = w.cols; a.r = r;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
     const int grid = (int)((w.rows + ROWS_PER_WG - 1) / ROWS_PER_WG);
     timing_before(stream, 2);
-    hipLaunchKernelGGL(gemv_kernel<16>, dim3(grid), dim3(256), 0, stream, a);
+    if (a.dq_int8)
+        hipLaunchKernelGGL((gemv_kernel<16, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemv_kernel<16, false>), dim3(grid), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;

@@ -15,17 +15,19 @@ struct WeightView {
     const float *mean;
     int64_t rows, cols;
     float cb[16];
+    uint32_t dq_int8;     // second-level codes: 0 = E4M3, 1 = int8
 };
 
 hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], uint32_t zero_code,
                            uint8_t *packed, float *absmax, hipStream_t stream);
 size_t double_quant_ws(int64_t nb);
+// int8: second-level codes by eq. (1) at 8 bits (scale max|y| / 127) instead of E4M3
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, float *scales,
-                               float *mean, void *ws, hipStream_t stream);
+                               float *mean, void *ws, bool int8, hipStream_t stream);
 // absmax_plain != NULL: one-level dequantization (eq. 2) with those float32 block constants
 hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const float *absmax_scale,
-                          const float *absmax_mean, const float *absmax_plain, int64_t numel,
-                          const float cb[16], uint16_t *out, hipStream_t stream);
+                          const float *absmax_mean, const float *absmax_plain, uint32_t dq_int8,
+                          int64_t numel, const float cb[16], uint16_t *out, hipStream_t stream);
 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,

@@ -109,12 +109,13 @@ __global__ __launch_bounds__(64) void group_sum_kernel(const Tin *__restrict__ i
     }
 }
 
-// Phase 2: per 256-block of constants, centre by the mean, scale by max|y|/448, encode E4M3.
+// Phase 2: per 256-block of constants, centre by the mean, scale by max|y|/448 and encode E4M3
+// (section 3.3), or with int8 set scale by max|y|/127 and round to an integer (eq. (1) at 8 bits).
 __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__ absmax, int64_t nb,
                                                        const double *__restrict__ total,
                                                        uint8_t *__restrict__ codes,
                                                        float *__restrict__ scales,
-                                                       float *__restrict__ mean_out) {
+                                                       float *__restrict__ mean_out, uint32_t int8) {
     const int lane = threadIdx.x;
     const float mu = (float)(total[0] / (double)nb);
     const int64_t ng = (nb + 255) >> 8;
@@ -129,15 +130,20 @@ __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        const float s = m / 448.0f;
+        const float s = int8 ? m / 127.0f : m / 448.0f;
         uint32_t word = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t c = 0;
             if (s != 0.0f) {
                 float t = y[k] / s;
-                t = fminf(fmaxf(t, -448.0f), 448.0f);
-                c = f32_to_e4m3(t);
+                if (int8) {
+                    t = fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+                    c = (uint32_t)(int32_t)t & 0xFFu;
+                } else {
+                    t = fminf(fmaxf(t, -448.0f), 448.0f);
+                    c = f32_to_e4m3(t);
+                }
             }
             word |= c << (8 * k);
         }
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
                                                       const float *__restrict__ absmax_scale,
                                                       const float *__restrict__ absmax_mean,
                                                       const float *__restrict__ absmax_plain,
-                                                      int64_t numel, Codebook cbk,
+                                                      int64_t numel, Codebook cbk, uint32_t dq_int8,
                                                       uint16_t *__restrict__ out) {
     __shared__ float cb[16];
     if (threadIdx.x < 16) cb[threadIdx.x] = cbk.v[threadIdx.x];
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
          w += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e0 = w << 3;
         const int64_t b = e0 >> 6;
-        const float a = plain ? absmax_plain[b] : block_scale(absmax_q[b], absmax_scale[b >> 8], mean);
+        const float a = plain ? absmax_plain[b] : block_scale(absmax_q[b], absmax_scale[b >> 8], mean, dq_int8 != 0);
         uint32_t word;
         if (e0 + 8 <= numel) {
             word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(packed) + w);
@@ -235,7 +241,7 @@ size_t double_quant_ws(int64_t nb) {
 }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, float *scales,
-                               float *mean, void *ws, hipStream_t stream) {
+                               float *mean, void *ws, bool int8, hipStream_t stream) {
     double *buf = reinterpret_cast<double *>(ws);
     double *level = buf;
     // level 0: floats -> doubles
@@ -256,19 +262,19 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, 
     }
     const int64_t ng = (nb + 255) / 256;
     hipLaunchKernelGGL(dq_encode_kernel, dim3(grid_for(ng, 1, 256 * 32)), dim3(64), 0, stream,
-                       absmax, nb, level, codes, scales, mean);
+                       absmax, nb, level, codes, scales, mean, int8 ? 1u : 0u);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const float *absmax_scale,
-                          const float *absmax_mean, const float *absmax_plain, int64_t numel,
-                          const float cb[16], uint16_t *out, hipStream_t stream) {
+                          const float *absmax_mean, const float *absmax_plain, uint32_t dq_int8,
+                          int64_t numel, const float cb[16], uint16_t *out, hipStream_t stream) {
     if (numel == 0) return hipSuccess;
     Codebook c;
     for (int j = 0; j < 16; ++j) c.v[j] = cb[j];
     const int64_t nwords = (numel + 7) >> 3;
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(nwords, 256, 256 * 32)), dim3(256), 0, stream,
-                       packed, absmax_q, absmax_scale, absmax_mean, absmax_plain, numel, c, out);
+                       packed, absmax_q, absmax_scale, absmax_mean, absmax_plain, numel, c, dq_int8, out);
     return hipGetLastError();
 }
 

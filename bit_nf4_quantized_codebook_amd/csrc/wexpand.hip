@@ -26,6 +26,7 @@ struct ExpandArgs {
     const uint8_t *c2;
     const float *c1;
     const float *mean;
+    uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
     uint16_t *out;
     int64_t N, K;
     Codebook cb;
@@ -44,10 +45,11 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
     }
     const int64_t nwords = (g.N * g.K) >> 3;
     const float mean = g.mean[0];
+    const bool dq_i8 = g.dq_int8 != 0;
     for (int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x; wi < nwords; wi += (int64_t)g.nexp * 256) {
         const int64_t b = wi >> 3;
         const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g.packed) + wi);
-        const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean));
+        const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean, dq_i8));
         __builtin_nontemporal_store(dequant8(t, w), reinterpret_cast<u32x4 *>(g.out) + wi);
     }
 }
@@ -70,13 +72,14 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
     const int64_t kb = blockIdx.x / ntn;
     const int64_t n0 = (blockIdx.x % ntn) * 64;
     const float mean = g.mean[0];
+    const bool dq_i8 = g.dq_int8 != 0;
     {
         const int nl = tid >> 2, q = tid & 3;
         const int64_t n = n0 + nl;
         uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (n < g.N) {
             const int64_t b = n * nbk + kb;
-            const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean));
+            const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean, dq_i8));
             const uint2 w = *reinterpret_cast<const uint2 *>(g.packed + b * 32 + q * 8);
             const u32x4 lo = dequant8(t, w.x), hi = dequant8(t, w.y);
             v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
                                 hipStream_t stream) {
     ExpandArgs a;
-    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean;
+    a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.out = out; a.N = w.rows; a.K = w.cols;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
     a.nred = 0;

@@ -121,12 +121,30 @@ int nf4_double_quant(const float *absmax, int64_t nblocks, int32_t dq_block, uin
                      size_t workspace_bytes, void *stream);
 
 /*
+ * The same second level with 8-bit integer codes instead of the 8-bit float: eq. (1) of
+ * section 3.1 at 8 bits, applied to the mean-centred constants (a reading: the pages name the
+ * second level's format only as an 8-bit float; Int8 is the integer alternative of eq. (1)).
+ * Arguments, mean and workspace exactly as nf4_double_quant, except:
+ *   absmax_q:     two's complement codes, rint(fp32(y / scale_j)) clamped to [-127, 127]
+ *                 (ties to even); all 0 when scale_j == 0.
+ *   absmax_scale: scale_j = fp32(max_j |absmax - mean| / 127).
+ * A weight encoded this way is described with dq_format = NF4_DQ_INT8.
+ */
+int nf4_double_quant_int8(const float *absmax, int64_t nblocks, int32_t dq_block, uint8_t *absmax_q,
+                          float *absmax_scale, float *absmax_mean, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Second-level code formats (nf4_weight.dq_format). */
+enum { NF4_DQ_E4M3 = 0, NF4_DQ_INT8 = 1 };
+
+/*
  * One frozen NF4 weight in double-quantized form (section 3.5, eq. (5) and eq. (6)).
- * All pointers are device pointers produced by nf4_quantize + nf4_double_quant.
+ * All pointers are device pointers produced by nf4_quantize + nf4_double_quant (or
+ * nf4_double_quant_int8, with dq_format = NF4_DQ_INT8).
  */
 typedef struct nf4_weight {
     const uint8_t *packed;        /* [rows*cols/2] 4-bit codes */
-    const uint8_t *absmax_q;      /* [rows*cols/block] E4M3 codes of the block constants */
+    const uint8_t *absmax_q;      /* [rows*cols/block] 8-bit codes of the block constants */
     const float *absmax_scale;    /* [ceil(nblocks/dq_block)] second-level multipliers */
     const float *absmax_mean;     /* [1] the mean removed before the second level */
     int64_t rows;                 /* N_out */
@@ -134,11 +152,14 @@ typedef struct nf4_weight {
     int32_t block;                /* 64 */
     int32_t dq_block;             /* 256 */
     float codebook[16];           /* the codebook used by nf4_quantize (host copy) */
+    int32_t dq_format;            /* NF4_DQ_E4M3 (nf4_double_quant) or NF4_DQ_INT8
+                                     (nf4_double_quant_int8); zero-initialised means E4M3 */
 } nf4_weight;
 
 /*
  * Double dequantization to BF16 -- section 3.5, eq. (6), with eq. (2) at each level:
- *   a'_b = fmaf(E4M3(absmax_q[b]), absmax_scale[b / dq_block], mean)   (one rounding)
+ *   a'_b = fmaf(E4M3(absmax_q[b]), absmax_scale[b / dq_block], mean)   (one rounding;
+ *          the code read as a signed integer when dq_format is NF4_DQ_INT8)
  *   out[i] = bf16_RNE(fp32(codebook[code_i] * a'_{i / block}))
  *   out_bf16: device uint16 [rows*cols], 16-byte aligned.  rows*cols must be even.
  */

@@ -97,6 +97,10 @@ def test_double_quant_argument_errors():
     assert lib.nf4_double_quant(fake, 1000, 128, fake, fake, fake, fake, ws, None) == EUNSUP
     assert lib.nf4_double_quant(fake, 1000, 256, None, fake, fake, fake, ws, None) == ENULL
     assert lib.nf4_double_quant(fake, 1000, 256, fake, fake, fake, fake, ws - 1, None) == EWS
+    for fn in (lib.nf4_double_quant, lib.nf4_double_quant_int8):       # same checks, either format
+        assert fn(fake, 0, 256, fake, fake, fake, fake, ws, None) == ESHAPE
+        assert fn(fake, 1000, 128, fake, fake, fake, fake, ws, None) == EUNSUP
+        assert fn(fake, 1000, 256, fake, fake, fake, fake, ws - 1, None) == EWS
     # workspace grows with the number of summation levels
     assert lib.nf4_double_quant_workspace_size(3670016, 256) >= 8 * (14336 + 56 + 1)
 
@@ -109,6 +113,14 @@ def _desc(rows=256, cols=256, block=64, dq_block=256, ptr=0x100000, cb=None):
     for j in range(16):
         d.codebook[j] = float(cb[j])
     return d
+
+
+def test_weight_dq_format_is_checked():
+    out = ctypes.c_void_p(0x200000)
+    d = _desc()
+    d.dq_format = 7
+    assert lib.nf4_dequant(ctypes.byref(d), out, None) == EARG
+    assert b"dq_format" in lib.nf4_last_error()
 
 
 def test_linear_argument_errors():

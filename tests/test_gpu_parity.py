@@ -259,9 +259,59 @@ def test_alt_codebook_quantize_dq_dequant_bit_exact(kind):
     assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(-1), oracle.dequant_weight(q, cb).reshape(-1))
 
 
+# ---- the integer second level (eq. (1) at 8 bits on the centred constants) ----
+
+@pytest.mark.parametrize("case", ["normal", "heavy_tail", "constant", "ragged"])
+def test_int8_double_quant_dequant_bit_exact(case):
+    _say(f"int8 double quant: {case}")
+    if case == "normal":
+        W = synth.normal_f32(151, (520, 384), 0.02)
+    elif case == "heavy_tail":
+        W = synth.heavy_tail_f32(152, 153, (1024, 1024), 0.02, 0.2, 0.01)
+    elif case == "constant":
+        W = np.tile(np.float32([0.03, -0.01] * 32), (64, 1))        # every block's absmax 0.03
+    else:
+        W = synth.normal_f32(154, (777, 64), 0.05)                  # 777 blocks: ragged 256-groups
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB, dq_format="int8")
+    q = oracle.quantize_dq(W, CB, fmt="int8")
+    assert np.array_equal(w.packed.cpu().numpy(), q["packed"])
+    assert np.array_equal(w.absmax_q.cpu().numpy(), q["codes"])
+    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), q["scales"].view(np.uint32))
+    assert w.absmax_mean.cpu().numpy()[0] == q["mean"]
+    assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(-1), oracle.dequant_weight(q, CB).reshape(-1))
+    if case == "constant":
+        assert np.all(q["codes"] == 0)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 3000, 8192, 64), (4, 520, 2048, 128), (12, 2000, 4096, 32),
+                                     (300, 520, 384, 16), (1100, 264, 640, 24)])
+def test_int8_double_quant_linear_parity(M, N, K, r):
+    _say(f"int8 DQ linear: M={M} N={N} K={K} r={r}")
+    s = 16.0 / r
+    seed = 950 + M + N
+    W = synth.normal_f32(seed, (N, K), 0.02)
+    X = synth.to_bf16_bits(synth.normal_f32(seed + 1, (M, K), 1.0))
+    L1 = synth.to_bf16_bits(synth.normal_f32(seed + 2, (K, r), 1.0 / r))
+    L2 = synth.to_bf16_bits(synth.normal_f32(seed + 3, (r, N), 0.01))
+    dY = synth.to_bf16_bits(synth.normal_f32(seed + 4, (M, N), 1.0))
+    w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB, dq_format="int8")
+    Wq = oracle.dequant_weight(oracle.quantize_dq(W, CB, fmt="int8"), CB)
+    assert np.array_equal(h16(nf4.nf4_dequant(w)), Wq)
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    Yr, _ = oracle.forward(X, Wq, L1, L2, s)
+    g = oracle.backward(dY, X, Wq, L1, L2, s)
+    check_tol("Y", f32(Y), Yr)
+    check_tol("dX", f32(dX), g["dX"])
+    check_tol("dL1", f32(dL1), g["dL1"])
+    check_tol("dL2", f32(dL2), g["dL2"])
+
+
 @pytest.mark.parametrize("dist", ["normal", "heavy_tail"])
 @pytest.mark.parametrize("kind", ["nf4", "int4", "fp4"])
-@pytest.mark.parametrize("dq", [True, False])
+@pytest.mark.parametrize("dq", ["e4m3", "int8", "none"])
 def test_quant_error_statistics_match_oracle(dist, kind, dq):
     """The quantization-error workload (bench.py --qerror) on a 1024 x 1024 weight: statistics from
     the library's quantize / double quant / dequant against the oracle's."""
@@ -270,8 +320,9 @@ def test_quant_error_statistics_match_oracle(dist, kind, dq):
     cb = nf4.nf4_build_codebook() if kind == "nf4" else _alt_cb(kind)
     W = (synth.normal_f32(141, (1024, 1024), 0.02) if dist == "normal"
          else synth.heavy_tail_f32(141, 142, (1024, 1024), 0.02, 0.2, 0.01))
-    got = bench.qerror_gpu(torch, nf4, torch.from_numpy(W).to(DEV), cb, dq)
-    ref = oracle.quant_error(W, cb, dq)
+    fmt = "e4m3" if dq == "none" else dq
+    got = bench.qerror_gpu(torch, nf4, torch.from_numpy(W).to(DEV), cb, dq != "none", fmt)
+    ref = oracle.quant_error(W, cb, dq != "none", fmt)
     assert np.array_equal(got["occupancy"], ref["occupancy"])
     assert got["max_abs"] == ref["max_abs"]
     assert abs(got["mse"] - ref["mse"]) <= 1e-12 * ref["mse"]
