@@ -42,10 +42,10 @@ METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 # taken on: if the hashed sources differ, traffic is reported as null.
 FETCH_SCALE = 1048576.0 / 524301.3
 WRITE_SCALE = 1048576.0 / 1048576.0
-GEMM_TRAFFIC_KIB = {0: (149911.9, 33602.0), 1: (149902.3, 32858.1)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
+GEMM_TRAFFIC_KIB = {0: (149915.8, 33529.9), 1: (149909.9, 32862.4)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
 GEMM_TRAFFIC_SOURCES = {
-    "csrc/gemm_bf16.hip": "f2b507d49931aee86104f099c1c36f664584e15eefe0fadcf2dd578ebd1ba616",
-    "csrc/common.h": "b0791e84149734c02f8e8b602dc28b879014ef9e27605c11332a13f253f9c97a",
+    "csrc/gemm_bf16.hip": "1efce92c46f83bf98ef80465078923ed6336e976b9315cec913625890053b4c0",
+    "csrc/common.h": "1cf2a1ddbbf0b49703ce638ad570d618aa6e5700ecdf039bf1c982405beaf8f7",
     "csrc/dqtile.h": "490babcb3e32389b8d42f9bf9415f7648bda55abef16a44443e6c8e438a25496",
 }
 
@@ -243,6 +243,58 @@ def bench_qerror(torch, nf4, synth, dev):
     return rows
 
 
+def bench_gated(torch, nf4, synth, dev, reps=10):
+    """Gated MLP at the LLaMA-7B MLP shape (4096 tokens, gate and up 11008 x 4096, r = 64): the
+    fused forward (one product, the glue in its epilogue) against two linear forwards and the glue,
+    and the fused backward (dX as one product over both weights) against the linears' backward."""
+    wl = synth.WORKLOADS["llama7b_mlp"]
+    gate, up = wl.linears[0], wl.linears[1]
+    M, F, K, r = wl.M, gate.N, gate.K, wl.r
+    ws = [nf4.NF4Weight.from_float(torch.from_numpy(synth.weight_f32(wl, lin)).to(dev)) for lin in (gate, up)]
+    ad = [tuple(torch.from_numpy(synth.to_bf16_bits(a).view("int16")).to(dev).view(torch.bfloat16)
+                for a in synth.lora_f32(wl, lin)) for lin in (gate, up)]
+    X = torch.from_numpy(synth.to_bf16_bits(synth.x_f32(wl, M=M, K=K)).view("int16")).to(dev).view(torch.bfloat16)
+    s = wl.scale
+    wsb = max(nf4.lib.qlora_gated_workspace_size(M, F, K, r), nf4.lib.qlora_linear_workspace_size(M, F, K, r))
+    wbuf = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def fused():
+        nf4.qlora_gated_fwd(ws[0], ws[1], X, ad[0][0], ad[0][1], ad[1][0], ad[1][1], s, workspace=wbuf,
+                            fuse=True)
+
+    def separate():
+        G, _ = nf4.qlora_linear_fwd(ws[0], X, ad[0][0], ad[0][1], s, workspace=wbuf)
+        U, _ = nf4.qlora_linear_fwd(ws[1], X, ad[1][0], ad[1][1], s, workspace=wbuf)
+        nf4.qlora_swiglu_fwd(G, U)
+
+    G, U, _, Tg, Tu = nf4.qlora_gated_fwd(ws[0], ws[1], X, ad[0][0], ad[0][1], ad[1][0], ad[1][1], s, workspace=wbuf)
+    dH = torch.randn_like(G)
+    dX = torch.empty_like(X)
+
+    def bwd(fuse):
+        return lambda: nf4.qlora_gated_bwd(ws[0], ws[1], dH, X, G, U, ad[0][0], ad[0][1], ad[1][0], ad[1][1],
+                                           Tg, Tu, s, dX=dX, workspace=wbuf, fuse=fuse)
+
+    out = {"workload": f"gated MLP forward and backward, M={M} F={F} K={K} r={r}"}
+    flops = 2 * (2 * M * F * K + 2 * M * K * r + 2 * M * r * F)
+    for name, fn in (("fwd_fused", fused), ("fwd_separate", separate), ("bwd_fused", bwd(True)),
+                     ("bwd_separate", bwd(False))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4)}
+        if name.startswith("fwd"):
+            out[name]["TFLOP/s"] = round(flops / ms / 1e9, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +307,8 @@ def main():
     ap.add_argument("--qerror", action="store_true",
                     help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
                          "normal and heavy-tail 4096 x 4096 weights (one JSON line)")
+    ap.add_argument("--gated", action="store_true",
+                    help="time the gated MLP forward (gate + up + SwiGLU) fused against separate calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of exactly 1 GiB, 5 times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -286,6 +340,9 @@ def main():
         return
     if args.gemv_only:
         print(json.dumps({"gemv": bench_gemv(torch, nf4, synth, dev)}), flush=True)
+        return
+    if args.gated:
+        print(json.dumps(bench_gated(torch, nf4, synth, dev)), flush=True)
         return
     if args.qerror:
         print(json.dumps({"workload": "qerror: 4-bit types on synthetic 4096x4096 weights",

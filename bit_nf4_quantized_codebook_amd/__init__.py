@@ -8,7 +8,7 @@ not built, importing the binding raises; there is no fallback path.
 Names follow the C ABI:
   nf4_build_codebook, nf4_build_int4_codebook, nf4_build_fp4_codebook, nf4_quantize,
   nf4_double_quant, nf4_double_quant_int8, nf4_dequant, nf4_dequant_single, qlora_linear_fwd,
-  qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd.
+  qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd, qlora_gated_fwd, qlora_gated_bwd.
 """
 from __future__ import annotations
 
@@ -33,7 +33,8 @@ EXPORTS = (
     "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_double_quant_int8", "nf4_dequant",
     "nf4_dequant_single",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_swiglu_fwd", "qlora_swiglu_bwd", "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
+    "qlora_swiglu_fwd", "qlora_swiglu_bwd", "qlora_gated_workspace_size", "qlora_gated_fwd", "qlora_gated_bwd",
+    "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
 
 
@@ -90,6 +91,11 @@ def _load():
         "qlora_linear_bwd": (i, [W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P,
                                  ctypes.c_uint32, P, sz, P]),
         "qlora_swiglu_fwd": (i, [P, P, P, i64, P]),
+        "qlora_gated_workspace_size": (sz, [i64, i64, i64, i32]),
+        "qlora_gated_bwd": (i, [W, W, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P, P, P,
+                                ctypes.c_uint32, P, sz, P]),
+        "qlora_gated_fwd": (i, [W, W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P, P, P,
+                                ctypes.c_uint32, P, sz, P]),
         "qlora_swiglu_bwd": (i, [P, P, P, P, P, i64, P]),
         "nf4_set_gemm_timing_events": (i, [P, P, P, i32]),
         "nf4_gemm_timing_count": (i32, []),
@@ -340,6 +346,56 @@ def qlora_swiglu_fwd(g, u, h=None):
         h = torch.empty_like(g)
     _check(lib.qlora_swiglu_fwd(_ptr(g), _ptr(u), _ptr(h), g.numel(), _stream(g.device)), "qlora_swiglu_fwd")
     return h
+
+
+QLORA_GATED_FUSE = 2   # include/nf4.h (QLORA_DX_ACCUMULATE is 1)
+
+
+def qlora_gated_fwd(w_gate: NF4Weight, w_up: NF4Weight, X, L1_gate, L2_gate, L1_up, L2_up, scale: float,
+                    keep_T: bool = True, workspace=None, fuse: bool = False):
+    """Gated MLP forward (gate and up linears + SwiGLU): returns (G, U, H, T_gate, T_up).
+    fuse: one GEMM for both products with the glue in its epilogue (QLORA_GATED_FUSE)."""
+    torch = _torch()
+    M, K = X.shape
+    F, r = w_gate.rows, L1_gate.shape[1]
+    dev = X.device
+    G = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    U = torch.empty_like(G)
+    H = torch.empty_like(G)
+    Tg = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if keep_T else None
+    Tu = torch.empty((M, r), dtype=torch.bfloat16, device=dev) if keep_T else None
+    wsb = lib.qlora_gated_workspace_size(M, F, K, r)
+    ws = _workspace(wsb, dev, workspace)
+    dg, du = w_gate.descriptor(), w_up.descriptor()
+    _check(lib.qlora_gated_fwd(ctypes.byref(dg), ctypes.byref(du), _ptr(X), _ptr(L1_gate), _ptr(L2_gate),
+                               _ptr(L1_up), _ptr(L2_up), float(scale), M, r, _ptr(G), _ptr(U), _ptr(H),
+                               _ptr(Tg) if keep_T else None, _ptr(Tu) if keep_T else None,
+                               QLORA_GATED_FUSE if fuse else 0, _ptr(ws), wsb, _stream(dev)), "qlora_gated_fwd")
+    return G, U, H, Tg, Tu
+
+
+def qlora_gated_bwd(w_gate: NF4Weight, w_up: NF4Weight, dH, X, G, U, L1_gate, L2_gate, L1_up, L2_up,
+                    T_gate, T_up, scale: float, need_dX: bool = True, dX=None, accumulate: bool = False,
+                    workspace=None, fuse: bool = False):
+    """Gated MLP backward: returns (dX, dL1_gate, dL2_gate, dL1_up, dL2_up).
+    fuse: dX as one GEMM over both weights (QLORA_GATED_FUSE)."""
+    torch = _torch()
+    M, K = X.shape
+    F, r = w_gate.rows, L1_gate.shape[1]
+    dev = X.device
+    if need_dX and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    grads = [torch.empty(shp, dtype=torch.bfloat16, device=dev) for shp in ((K, r), (r, F), (K, r), (r, F))]
+    wsb = lib.qlora_gated_workspace_size(M, F, K, r)
+    ws = _workspace(wsb, dev, workspace)
+    flags = (QLORA_GATED_FUSE if fuse else 0) | (1 if accumulate else 0)
+    dg, du = w_gate.descriptor(), w_up.descriptor()
+    p = lambda t: _ptr(t) if t is not None else None  # noqa: E731
+    _check(lib.qlora_gated_bwd(ctypes.byref(dg), ctypes.byref(du), _ptr(dH), _ptr(X), _ptr(G), _ptr(U),
+                               _ptr(L1_gate), _ptr(L2_gate), _ptr(L1_up), _ptr(L2_up), p(T_gate), p(T_up),
+                               float(scale), M, r, p(dX if need_dX else None), *(_ptr(t) for t in grads), flags,
+                               _ptr(ws), wsb, _stream(dev)), "qlora_gated_bwd")
+    return (dX if need_dX else None), grads[0], grads[1], grads[2], grads[3]
 
 
 def qlora_swiglu_bwd(dh, g, u):

@@ -521,6 +521,185 @@ int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t 
     return NF4_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Gated MLP forward: gate and up in one product, the glue in its epilogue
+// ---------------------------------------------------------------------------------------------
+namespace {
+struct GatedPlan {
+    bool fused;
+    Plan lin;            // the linear layer's plan for [2F, K] (fused) or [F, K]
+    size_t off_sTu, total;
+};
+// fused from the expansion threshold on, when the 32-row interleave covers whole groups
+bool gated_fused(int64_t M, int64_t F, int64_t K) { return M >= kExpandMinM && F % 32 == 0 && use_expand(M, 2 * F, K); }
+GatedPlan make_gated_plan(int64_t M, int64_t F, int64_t K, int32_t r) {
+    GatedPlan g;
+    g.fused = gated_fused(M, F, K);
+    g.lin = make_plan(M, g.fused ? 2 * F : F, K, r);
+    g.off_sTu = g.lin.total;
+    g.total = g.lin.total + round256((size_t)M * r * 2);
+    return g;
+}
+}  // namespace
+
+namespace {
+// backward: dG and dU after the linear layer's own plan (which the composed path hands to
+// qlora_linear_bwd); the fused path also keeps the up weight's transposed expansion, dT and T
+struct GatedBwdPlan {
+    bool fused;
+    Plan lin;
+    size_t off_dG, off_dU, off_WdTu, off_dTu, off_Tu, total;
+};
+GatedBwdPlan make_gated_bwd_plan(int64_t M, int64_t F, int64_t K, int32_t r) {
+    GatedBwdPlan g;
+    g.fused = use_expand(M, F, K);
+    g.lin = make_plan(M, F, K, r);
+    size_t off = g.lin.total;
+    g.off_dG = off;   off += round256((size_t)M * F * 2);
+    g.off_dU = off;   off += round256((size_t)M * F * 2);
+    g.off_WdTu = g.off_dTu = g.off_Tu = off;
+    if (g.fused) {
+        g.off_WdTu = off;  off += round256((size_t)F * K * 2);
+        g.off_dTu = off;   off += round256((size_t)M * r * 2);
+        g.off_Tu = off;    off += round256((size_t)M * r * 2);
+    }
+    g.total = off;
+    return g;
+}
+}  // namespace
+
+size_t qlora_gated_workspace_size(int64_t M, int64_t F, int64_t K, int32_t r) {
+    if (M <= 0 || F <= 0 || K <= 0 || r <= 0) return 0;
+    const size_t f = make_gated_plan(M, F, K, r).total, b = make_gated_bwd_plan(M, F, K, r).total;
+    return f > b ? f : b;
+}
+
+int qlora_gated_fwd(const nf4_weight *w_gate, const nf4_weight *w_up, const uint16_t *X, const uint16_t *L1_gate,
+                    const uint16_t *L2_gate, const uint16_t *L1_up, const uint16_t *L2_up, float scale, int64_t M,
+                    int32_t r, uint16_t *G, uint16_t *U, uint16_t *H, uint16_t *T_gate_out, uint16_t *T_up_out,
+                    uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+    if (flags & ~QLORA_GATED_FUSE) return fail(NF4_ERR_ARG, "unknown flags");
+    int rc = check_linear_args(w_gate, M, r, scale);
+    if (rc) return rc;
+    rc = check_linear_args(w_up, M, r, scale);
+    if (rc) return rc;
+    if (w_gate->rows != w_up->rows || w_gate->cols != w_up->cols)
+        return fail(NF4_ERR_SHAPE, "gate and up weights must have the same shape");
+    if (!X || !L1_gate || !L2_gate || !L1_up || !L2_up || !G || !U || !H)
+        return fail(NF4_ERR_NULL, "X, the adapters, G, U and H must be non-NULL");
+    if (!aligned16(X) || !aligned16(L1_gate) || !aligned16(L2_gate) || !aligned16(L1_up) || !aligned16(L2_up) ||
+        !aligned16(G) || !aligned16(U) || !aligned16(H) || (T_gate_out && !aligned16(T_gate_out)) ||
+        (T_up_out && !aligned16(T_up_out)))
+        return fail(NF4_ERR_ALIGN, "activations and adapters must be 16-byte aligned");
+    const int64_t F = w_gate->rows, K = w_gate->cols;
+    const GatedPlan p = make_gated_plan(M, F, K, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "gated workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!p.fused || !(flags & QLORA_GATED_FUSE)) {
+        // the two linears and the glue, each as its own call
+        rc = qlora_linear_fwd(w_gate, X, L1_gate, L2_gate, scale, M, r, G, T_gate_out, workspace, p.lin.total, stream);
+        if (rc) return rc;
+        rc = qlora_linear_fwd(w_up, X, L1_up, L2_up, scale, M, r, U, T_up_out, workspace, p.lin.total, stream);
+        if (rc) return rc;
+        return qlora_swiglu_fwd(G, U, H, M * F, stream);
+    }
+    // each adapter's T partials, then the expansion of its weight into its rows of the combined
+    // weight (the same launch sums the partials), then one product for both
+    uint16_t *Wgu = ws_at<uint16_t>(workspace, p.lin.off_Wd);
+    uint16_t *sTg = ws_at<uint16_t>(workspace, p.lin.off_sT);
+    uint16_t *sTu = ws_at<uint16_t>(workspace, p.off_sTu);
+    hipError_t e;
+    const nf4k::Reduction red_g = T_partials(X, L1_gate, M, K, r, scale, T_gate_out, sTg, p.lin, workspace, s, &e);
+    NF4_CHECK_HIP(e, "T_gate = X L1_gate");
+    NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w_gate), /*transposed=*/false, Wgu, &red_g, s, /*slot=*/0),
+                  "gate expansion + T_gate reduce");
+    const nf4k::Reduction red_u = T_partials(X, L1_up, M, K, r, scale, T_up_out, sTu, p.lin, workspace, s, &e);
+    NF4_CHECK_HIP(e, "T_up = X L1_up");
+    NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w_up), /*transposed=*/false, Wgu, &red_u, s, /*slot=*/1),
+                  "up expansion + T_up reduce");
+    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_gated(X, Wgu, sTg, L2_gate, sTu, L2_up, r, M, F, K, G, U, H, s),
+                  "gated bf16 GEMM");
+    return NF4_OK;
+}
+
+int qlora_gated_bwd(const nf4_weight *w_gate, const nf4_weight *w_up, const uint16_t *dH, const uint16_t *X,
+                    const uint16_t *G, const uint16_t *U, const uint16_t *L1_gate, const uint16_t *L2_gate,
+                    const uint16_t *L1_up, const uint16_t *L2_up, const uint16_t *T_gate, const uint16_t *T_up,
+                    float scale, int64_t M, int32_t r, uint16_t *dX, uint16_t *dL1_gate, uint16_t *dL2_gate,
+                    uint16_t *dL1_up, uint16_t *dL2_up, uint32_t flags, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    if (flags & ~(QLORA_GATED_FUSE | QLORA_DX_ACCUMULATE)) return fail(NF4_ERR_ARG, "unknown flags");
+    int rc = check_linear_args(w_gate, M, r, scale);
+    if (rc) return rc;
+    rc = check_linear_args(w_up, M, r, scale);
+    if (rc) return rc;
+    if (w_gate->rows != w_up->rows || w_gate->cols != w_up->cols)
+        return fail(NF4_ERR_SHAPE, "gate and up weights must have the same shape");
+    if (!dH || !X || !G || !U || !L1_gate || !L2_gate || !L1_up || !L2_up || !dL1_gate || !dL2_gate || !dL1_up ||
+        !dL2_up)
+        return fail(NF4_ERR_NULL, "dH, X, G, U, the adapters and their gradients must be non-NULL");
+    for (const void *q : {(const void *)dH, (const void *)X, (const void *)G, (const void *)U, (const void *)L1_gate,
+                          (const void *)L2_gate, (const void *)L1_up, (const void *)L2_up, (const void *)T_gate,
+                          (const void *)T_up, (const void *)dX, (const void *)dL1_gate, (const void *)dL2_gate,
+                          (const void *)dL1_up, (const void *)dL2_up})
+        if (q && !aligned16(q)) return fail(NF4_ERR_ALIGN, "activations, adapters and gradients must be 16-byte aligned");
+    const int64_t F = w_gate->rows, K = w_gate->cols;
+    const GatedBwdPlan p = make_gated_bwd_plan(M, F, K, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "gated workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint16_t *dG = ws_at<uint16_t>(workspace, p.off_dG), *dU = ws_at<uint16_t>(workspace, p.off_dU);
+    rc = qlora_swiglu_bwd(dH, G, U, dG, dU, M * F, stream);
+    if (rc) return rc;
+    const uint32_t acc = flags & QLORA_DX_ACCUMULATE;
+    if (!p.fused || !(flags & QLORA_GATED_FUSE) || !dX) {
+        // the two linears' backward as their own calls, the second adding into dX
+        rc = qlora_linear_bwd(w_gate, dG, X, L1_gate, L2_gate, T_gate, scale, M, r, dX, dL1_gate, dL2_gate, acc,
+                              workspace, p.lin.total, stream);
+        if (rc) return rc;
+        return qlora_linear_bwd(w_up, dU, X, L1_up, L2_up, T_up, scale, M, r, dX, dL1_up, dL2_up,
+                                dX ? QLORA_DX_ACCUMULATE : 0u, workspace, p.lin.total, stream);
+    }
+    // per adapter: dT (summed by the weight's transposed expansion), then dL2 and dL1; then one
+    // product for dX over both
+    const Plan &lp = p.lin;
+    float *P = ws_at<float>(workspace, lp.off_P);
+    struct Side {
+        const nf4_weight *w;
+        const uint16_t *dA, *L1, *L2, *T;
+        uint16_t *Tb, *dT, *WdT, *dL1, *dL2;
+    } sides[2] = {
+        {w_gate, dG, L1_gate, L2_gate, T_gate, ws_at<uint16_t>(workspace, lp.off_T), ws_at<uint16_t>(workspace, lp.off_dT),
+         ws_at<uint16_t>(workspace, lp.off_Wd), dL1_gate, dL2_gate},
+        {w_up, dU, L1_up, L2_up, T_up, ws_at<uint16_t>(workspace, p.off_Tu), ws_at<uint16_t>(workspace, p.off_dTu),
+         ws_at<uint16_t>(workspace, p.off_WdTu), dL1_up, dL2_up},
+    };
+    for (const Side &sd : sides) {
+        const uint16_t *Tuse = sd.T;
+        if (!Tuse) {
+            rc = compute_T(X, sd.L1, M, K, r, 1.0f, sd.Tb, nullptr, lp, workspace, s);
+            if (rc) return rc;
+            Tuse = sd.Tb;
+        }
+        NF4_CHECK_HIP(nf4k::launch_skinny_nt(sd.dA, sd.L2, /*b_rows_k=*/false, P, M, r, F, lp.ksdT, s), "dT = dA L2^T");
+        const nf4k::Reduction red_dT{P, lp.ksdT, M * r, scale, sd.dT, 0.0f, nullptr};
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(sd.w), /*transposed=*/true, sd.WdT, &red_dT, s),
+                      "weight expansion + dT reduce");
+        float *P1 = P + (size_t)lp.msL2 * r * F;
+        const nf4k::TnProduct tn_dL2{Tuse, sd.dA, P, r, F, lp.msL2};
+        const nf4k::TnProduct tn_dL1{X, sd.dT, P1, K, r, lp.msL1};
+        NF4_CHECK_HIP(nf4k::launch_skinny_tn(tn_dL2, &tn_dL1, M, s), "dL2 = T^T dA, dL1 = X^T dT");
+        const nf4k::Reduction red_dL2{P, lp.msL2, (int64_t)r * F, scale, sd.dL2, 0.0f, nullptr};
+        const nf4k::Reduction red_dL1{P1, lp.msL1, K * (int64_t)r, 1.0f, sd.dL1, 0.0f, nullptr};
+        NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
+    }
+    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd_dual(dG, sides[0].WdT, sides[0].dT, L1_gate, dU, sides[1].WdT, sides[1].dT,
+                                                  L1_up, r, M, F, K, dX, acc != 0, s),
+                  "two-segment bf16 GEMM (bwd)");
+    return NF4_OK;
+}
+
 int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, uint16_t *dg,
                      uint16_t *du, int64_t n, void *stream) {
     if (n < 0) return fail(NF4_ERR_SHAPE, "n must be >= 0");

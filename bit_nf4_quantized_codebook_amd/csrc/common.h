@@ -69,4 +69,12 @@ __device__ __forceinline__ float block_scale(uint32_t code, float s2, float mean
     return __builtin_fmaf(v, s2, mean);
 }
 
+// SwiGLU glue of the gated MLP (not a step of the method), fp32: h = silu(g) u, silu(g) = g sig(g).
+// One definition for the glue kernels and the gated GEMM's epilogue, so both give the same bits.
+// sig uses the hardware reciprocal (v_rcp_f32, about 1 ulp) rather than a division: the results
+// are rounded to bf16, and in the GEMM epilogue the division's dozen instructions per element
+// were exposed.
+__device__ __forceinline__ float swiglu_sig(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float swiglu_h(float g, float u) { return g * swiglu_sig(g) * u; }
+
 }  // namespace nf4k

@@ -15,6 +15,16 @@
 // global memory to LDS (buffer_load ... lds: no registers, no ds_write), two 32 KB stages each,
 // 128-byte rows whose 16-byte chunks are XOR-swizzled by (row / 2) so the fragment reads are
 // bank-conflict free.  The LoRA product is appended as r/64 more reduction steps.
+//
+// Gated MLP forward (gate and up in one product, the SwiGLU glue in the epilogue): B is the
+// combined weight [2F, K] whose 64-row groups hold 32 gate rows then 32 up rows, so in every
+// wave the 32-column MFMA tiles j = 0, 2 hold gate outputs and j = 1, 3 the up outputs of the
+// same columns.  The LoRA steps use s T_gate for the gate tiles and s T_up for the up tiles (two
+// A tiles), and the epilogue writes G, U and H = silu(G) U.
+//
+// Gated MLP backward (dX of gate and up as one product): the reduction runs over two segments,
+// [dG | dU] . [deq(W_gate) ; deq(W_up)], each operand of a segment its own buffer, and the LoRA
+// steps over [dT_gate | dT_up] . [L1_gate ; L1_up]^T.
 
 #include "common.h"
 #include "dqtile.h"
@@ -36,14 +46,21 @@ struct GemmArgs {
     const uint16_t *B;    // [Nout, Kred]
     const uint16_t *Ae;   // [M, r]
     const uint16_t *Be;   // forward: L2 [r, Nout]; backward: L1 [Nout, r]
-    uint16_t *C;          // [M, Nout]
+    uint16_t *C;          // [M, Nout]   (gated: H [M, Nout / 2])
     int64_t M, Nout, Kred;
     int32_t r;
     uint32_t accumulate;
+    // gated forward: Ae2 = s T_up [M, r], Be2 = L2_up [r, Nout / 2] (Ae, Be: gate's), G and U out
+    // two-segment backward: A2 = dU, B2 = deq(W_up)^T, Ae2 = dT_up, Be2 = L1_up (A, B, Ae, Be: gate's);
+    // Kred is one segment's length
+    const uint16_t *Ae2;
+    const uint16_t *Be2;
+    uint16_t *G, *U;      // [M, Nout / 2]
+    const uint16_t *A2, *B2;
 };
 
-template <bool BWD>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
+template <bool BWD, bool GATED, bool DUAL>
+__device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // one LDS object per stage: a fragment read of one stage provably never aliases the
     // direct-to-LDS loads in flight into the other
     __shared__ __align__(16) uint8_t As0[STAGE];
@@ -63,12 +80,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     tile_coords(ntm, ntn, tm, tn);
     const int64_t m0 = (int64_t)tm * TM;
     const int64_t n0 = (int64_t)tn * TN;
-    const int main_steps = (int)((g.Kred + TK - 1) / TK);
+    const int seg_steps = (int)((g.Kred + TK - 1) / TK);
+    const int main_steps = DUAL ? 2 * seg_steps : seg_steps;
     const int ext_steps = (g.r + TK - 1) / TK;
 
     // tile-relative descriptors: rows past M (or Nout) read zeros
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + m0 * g.Kred, (g.M - m0) * g.Kred * 2);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + n0 * g.Kred, (g.Nout - n0) * g.Kred * 2);
+    const __amdgpu_buffer_rsrc_t rA2 = make_rsrc(DUAL ? g.A2 + m0 * g.Kred : g.A, DUAL ? (g.M - m0) * g.Kred * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rB2 = make_rsrc(DUAL ? g.B2 + n0 * g.Kred : g.B, DUAL ? (g.Nout - n0) * g.Kred * 2 : 0);
 
     // ---- loads: instruction q of wave w writes stage rows 8u .. 8u+7 (u = 8w + q); lane l
     // takes row 8u + l/8 and physical chunk l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
@@ -100,6 +120,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
             const uint32_t v = ((q & 1) ? v1 : v0) + (uint32_t)q * row8_off;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + q * 1024), 16, v, 0, 0, 0);
         }
+    };
+
+    // operand A or B of a main-loop step.  Two segments: steps past the first read the second
+    // operand pair, picked by a select of the (uniform) descriptor, no branch inside the pinned
+    // schedule.
+    auto load2 = [&](bool isA, int step, uint8_t *st, int q0 = 0, int q1 = 8) {
+        __amdgpu_buffer_rsrc_t r = isA ? rA : rB;
+        if (DUAL) {
+            const bool second = step >= seg_steps;
+            r = second ? (isA ? rA2 : rB2) : r;
+            step -= second ? seg_steps : 0;
+        }
+        load(r, step, st, q0, q1);
     };
 
     f32x16 acc[4][4];
@@ -163,8 +196,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
             Frags &cur = (s & 1) ? f1 : f0;
             Frags &nxt = (s & 1) ? f0 : f1;
             if (s == 0) {
-                load(rA, step + 1, An, 4, 8);
-                load(rB, step + 1, Bn, 4, 8);
+                load2(true, step + 1, An, 4, 8);
+                load2(false, step + 1, Bn, 4, 8);
             }
             read(Ac, Bc, s + 1, nxt);
             mma(cur);
@@ -175,17 +208,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8));
         __syncthreads();
         read(An, Bn, 0, f0);
-        load(rA, step + 2, Ac, 0, 4);
-        load(rB, step + 2, Bc, 0, 4);
+        load2(true, step + 2, Ac, 0, 4);
+        load2(false, step + 2, Bc, 0, 4);
         mma(f1);
         interleave(8);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    load(rA, 0, As0);
-    load(rB, 0, Bs0);
-    load(rA, 1, As1, 0, 4);
-    load(rB, 1, Bs1, 0, 4);
+    load2(true, 0, As0);
+    load2(false, 0, Bs0);
+    load2(true, 1, As1, 0, 4);
+    load2(false, 1, Bs1, 0, 4);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     read(As0, Bs0, 0, f0);
@@ -211,20 +244,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
     //   backward: Be = L1 [Nout, r]: rows n, columns j -> swizzled layout in Bs0, row reads
     if (ext_steps > 0) {
         const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
+        const int64_t be_cols = GATED ? g.Nout / 2 : g.Nout;     // row length of L2
         const __amdgpu_buffer_rsrc_t rBe = BWD ? make_rsrc(g.Be + n0 * g.r, (g.Nout - n0) * (int64_t)g.r * 2)
-                                               : make_rsrc(g.Be, (int64_t)g.r * g.Nout * 2);
+                                               : make_rsrc(g.Be, (int64_t)g.r * be_cols * 2);
+        const __amdgpu_buffer_rsrc_t rAe2 = make_rsrc(GATED ? g.Ae2 + m0 * g.r : g.Ae,
+                                                      GATED ? (g.M - m0) * (int64_t)g.r * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rBe2 = make_rsrc(GATED ? g.Be2 : g.Be, GATED ? (int64_t)g.r * be_cols * 2 : 0);
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
-        for (int e = 0; e < ext_steps; ++e) {
-            const int j0 = e * TK;
+        // two segments: the up adapter's steps follow the gate's
+        const __amdgpu_buffer_rsrc_t rAeU = make_rsrc(DUAL ? g.Ae2 + m0 * g.r : g.Ae,
+                                                      DUAL ? (g.M - m0) * (int64_t)g.r * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rBeU = make_rsrc(DUAL ? g.Be2 + n0 * g.r : g.Be,
+                                                      DUAL ? (g.Nout - n0) * (int64_t)g.r * 2 : 0);
+        for (int e = 0; e < (DUAL ? 2 : 1) * ext_steps; ++e) {
+            const bool up = DUAL && e >= ext_steps;
+            const int j0 = (up ? e - ext_steps : e) * TK;
+            const __amdgpu_buffer_rsrc_t ra = up ? rAeU : rAe;
+            const __amdgpu_buffer_rsrc_t rb = up ? rBeU : rBe;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int row = 8 * (8 * wave + q) + (lane_e >> 3);
                 const int jj = j0 + a_col[q & 1];
                 const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0x80000000u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe, (lds_void *)((lds_u8 *)As0 + wave * 8192 + q * 1024),
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)((lds_u8 *)As0 + wave * 8192 + q * 1024),
                                                          16, off, 0, 0, 0);
+                if (GATED)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe2, (lds_void *)((lds_u8 *)As1 + wave * 8192 + q * 1024),
+                                                             16, off, 0, 0, 0);
                 if (BWD)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rBe, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
                                                              16, off, 0, 0, 0);
             }
             if (!BWD) {
@@ -234,7 +282,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
                     const int jr = (tid >> 5) + 8 * q, ch = tid & 31;
                     const int64_t col = n0 + ch * 8;
                     const bool ok = j0 + jr < g.r && col < g.Nout;
-                    const u32x4 v = bload16(rBe, ok ? (uint32_t)(((int64_t)(j0 + jr) * g.Nout + col) * 2) : 0x80000000u);
+                    u32x4 v;
+                    if (GATED) {
+                        // combined column col: 32-column group col / 32 of type (col / 32) % 2
+                        // (gate, up), F column (col / 64) 32 + col % 32
+                        const int64_t fcol = (col >> 6) * 32 + (col & 31);
+                        const uint32_t off = (uint32_t)(((int64_t)(j0 + jr) * be_cols + fcol) * 2);
+                        const bool up = (col >> 5) & 1;
+                        const u32x4 vg = bload16(rBe, (ok & !up) ? off : 0x80000000u);
+                        const u32x4 vu = bload16(rBe2, (ok & up) ? off : 0x80000000u);
+                        v = u32x4{vg.x | vu.x, vg.y | vu.y, vg.z | vu.z, vg.w | vu.w};
+                    } else {
+                        v = bload16(rBe, ok ? (uint32_t)(((int64_t)(j0 + jr) * g.Nout + col) * 2) : 0x80000000u);
+                    }
                     uint8_t *Bh = (ch < 16) ? Bs0 : Bs1;
                     *reinterpret_cast<u32x4 *>(Bh + jr * EXT_ROWB + (ch & 15) * 16) = v;
                 }
@@ -265,7 +325,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
                         f.b[j] = __builtin_bit_cast(bf16x8, v);
                     }
                 }
-                mma(f);
+                if (GATED) {
+                    // up tiles (odd j) take s T_up from As1
+                    bf16x8 a2[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a2[i] = *reinterpret_cast<const bf16x8 *>(As1 + lds_off[s] + (wm * 128 + 32 * i) * 128);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((j & 1) ? a2[i] : f.a[i], f.b[j],
+                                                                                acc[i][j], 0, 0, 0);
+                } else {
+                    mma(f);
+                }
             }
             __syncthreads();
         }
@@ -273,7 +347,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
 
     // ---- epilogue: fp32 -> bf16.  Lane (r32, hh) of tile (i, j) holds column
     // wn*128 + 32 j + r32 and rows wm*128 + 32 i + 8 (v/4) + 4 hh + v%4 ----
-    if (!g.accumulate) {
+    if (GATED) {
+        // tiles (i, 2 jp) and (i, 2 jp + 1) hold gate and up of F column (n0 + wn*128)/2 + 32 jp + r32;
+        // g and u are rounded to bf16 (the stored G and U) before the glue, as in the glue kernel
+        const int64_t F = g.Nout >> 1;
+        const uint32_t row_bytes = (uint32_t)(F * 2);
+        const int64_t cbase = (n0 + wn * 128) / 2;
+        const __amdgpu_buffer_rsrc_t rG = make_rsrc(g.G + m0 * F, (g.M - m0) * F * 2);
+        const __amdgpu_buffer_rsrc_t rU = make_rsrc(g.U + m0 * F, (g.M - m0) * F * 2);
+        const __amdgpu_buffer_rsrc_t rH = make_rsrc(g.C + m0 * F, (g.M - m0) * F * 2);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((cbase + r32_e) * 2);
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+            if (cbase + 32 * jp + r32_e >= F) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    const uint32_t gb = f32_to_bf16(acc[i][2 * jp][v]), ub = f32_to_bf16(acc[i][2 * jp + 1][v]);
+                    const uint32_t hb = f32_to_bf16(swiglu_h(bf16_to_f32(gb), bf16_to_f32(ub)));
+                    const uint32_t off = lane_off + jp * 64;
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)gb, rG, off, rows * row_bytes, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ub, rU, off, rows * row_bytes, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb, rH, off, rows * row_bytes, 0);
+                }
+            }
+        }
+    } else if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
         const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
         const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((n0 + wn * 128 + r32_e) * 2);
@@ -314,6 +415,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 template <bool BWD>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
+    gemm_body<BWD, false, false>(g);
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_gated_kernel(GemmArgs g) {
+    gemm_body<false, true, false>(g);
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(GemmArgs g) {
+    gemm_body<true, false, true>(g);
+}
+
+template <bool BWD>
 hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
@@ -328,16 +442,43 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream) {
-    GemmArgs a;
+    GemmArgs a{};
     a.A = X; a.B = Wd; a.Ae = sT; a.Be = L2; a.C = Y;
     a.M = M; a.Nout = N; a.Kred = K; a.r = r; a.accumulate = 0;
     return launch_impl<false>(a, stream);
 }
 
+hipError_t launch_gemm_bf16_gated(const uint16_t *X, const uint16_t *Wgu, const uint16_t *sTg, const uint16_t *L2g,
+                                  const uint16_t *sTu, const uint16_t *L2u, int32_t r, int64_t M, int64_t F,
+                                  int64_t K, uint16_t *G, uint16_t *U, uint16_t *H, hipStream_t stream) {
+    GemmArgs a{};
+    a.A = X; a.B = Wgu; a.Ae = sTg; a.Be = L2g; a.C = H;
+    a.M = M; a.Nout = 2 * F; a.Kred = K; a.r = r; a.accumulate = 0;
+    a.Ae2 = sTu; a.Be2 = L2u; a.G = G; a.U = U;
+    const int ntm = (int)((M + TM - 1) / TM);
+    const int ntn = (int)((a.Nout + TN - 1) / TN);
+    hipLaunchKernelGGL(gemm_bf16_gated_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,
+                                    const uint16_t *dU, const uint16_t *WdTu, const uint16_t *dTu, const uint16_t *L1u,
+                                    int32_t r, int64_t M, int64_t F, int64_t K, uint16_t *dX, bool accumulate,
+                                    hipStream_t stream) {
+    GemmArgs a{};
+    a.A = dG; a.B = WdTg; a.Ae = dTg; a.Be = L1g; a.C = dX;
+    a.A2 = dU; a.B2 = WdTu; a.Ae2 = dTu; a.Be2 = L1u;
+    a.M = M; a.Nout = K; a.Kred = F; a.r = r; a.accumulate = accumulate ? 1u : 0u;
+    const int ntm = (int)((M + TM - 1) / TM);
+    const int ntn = (int)((K + TN - 1) / TN);
+    hipLaunchKernelGGL(gemm_bf16_dual_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
                                 hipStream_t stream) {
-    GemmArgs a;
+    GemmArgs a{};
     a.A = dY; a.B = WdT; a.Ae = dT; a.Be = L1; a.C = dX;
     a.M = M; a.Nout = K; a.Kred = N; a.r = r; a.accumulate = accumulate ? 1u : 0u;
     return launch_impl<true>(a, stream);

@@ -52,10 +52,23 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
 // large token counts: the weight is expanded to bf16 once per call (rows [N, K] for the forward,
 // transposed [K, N] for the backward), then a K-extended bf16 GEMM
 // red (optional): a partials reduction carried by extra workgroups of the same launch
+// slot (rows only): -1 plain; 0 / 1 puts the rows in 32-row slot 0 / 1 of 64-row groups of out (the
+// gate / up interleave of the gated MLP's combined weight)
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
-                                hipStream_t stream);
+                                hipStream_t stream, int slot = -1);
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
+// gated MLP forward: C = [X | sT_gate | sT_up] . [Wgu ; ...]^T over the combined weight Wgu [2F, K]
+// (gate and up rows interleaved in 32-row groups); writes G, U and H = silu(G) U, each [M, F]
+hipError_t launch_gemm_bf16_gated(const uint16_t *X, const uint16_t *Wgu, const uint16_t *sTg, const uint16_t *L2g,
+                                  const uint16_t *sTu, const uint16_t *L2u, int32_t r, int64_t M, int64_t F,
+                                  int64_t K, uint16_t *G, uint16_t *U, uint16_t *H, hipStream_t stream);
+// gated MLP backward: dX = [dG | dU] . [deq(W_gate) ; deq(W_up)] + [dT_gate | dT_up] . [L1_gate ; L1_up]^T,
+// one product whose reduction runs over the two segments (WdT_*: [K, F] transposed expansions)
+hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,
+                                    const uint16_t *dU, const uint16_t *WdTu, const uint16_t *dTu, const uint16_t *L1u,
+                                    int32_t r, int64_t M, int64_t F, int64_t K, uint16_t *dX, bool accumulate,
+                                    hipStream_t stream);
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
                                 hipStream_t stream);

@@ -9,7 +9,7 @@ namespace nf4k {
 
 namespace {
 
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigm(float x) { return swiglu_sig(x); }
 
 __device__ __forceinline__ void unpack8(const u32x4 &v, float f[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -34,14 +34,14 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t *__restr
         unpack8(reinterpret_cast<const u32x4 *>(g)[i], fg);
         unpack8(reinterpret_cast<const u32x4 *>(u)[i], fu);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) fh[k] = fg[k] * sigm(fg[k]) * fu[k];
+        for (int k = 0; k < 8; ++k) fh[k] = swiglu_h(fg[k], fu[k]);
         reinterpret_cast<u32x4 *>(h)[i] = pack8(fh);
     }
     // scalar tail
     const int64_t t = (nv << 3) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t < n && t < (nv << 3) + 8) {
         const float x = bf16_to_f32(g[t]), y = bf16_to_f32(u[t]);
-        h[t] = (uint16_t)f32_to_bf16(x * sigm(x) * y);
+        h[t] = (uint16_t)f32_to_bf16(swiglu_h(x, y));
     }
 }
 

@@ -32,6 +32,7 @@ struct ExpandArgs {
     Codebook cb;
     RedProb red;
     uint32_t nexp, nred;
+    int32_t slot;            // row layout: -1 plain; 0 / 1: rows to 32-row slot 0 / 1 of 64-row groups
 };
 
 // Row layout: 8 lanes per block, one packed dword (8 weights) each, so a wave reads 256
@@ -50,7 +51,14 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
         const int64_t b = wi >> 3;
         const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g.packed) + wi);
         const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean, dq_i8));
-        __builtin_nontemporal_store(dequant8(t, w), reinterpret_cast<u32x4 *>(g.out) + wi);
+        int64_t owi = wi;
+        if (g.slot >= 0) {
+            // gated MLP: gate rows (slot 0) and up rows (slot 1) alternate in groups of 32, so one
+            // 32 x 32 MFMA tile of the GEMM holds gate and the next up for the same outputs
+            const uint32_t kw = (uint32_t)(g.K >> 3), row = (uint32_t)wi / kw, cw = (uint32_t)wi - row * kw;
+            owi = (int64_t)(((row >> 5) << 6) + ((uint32_t)g.slot << 5) + (row & 31u)) * kw + cw;
+        }
+        __builtin_nontemporal_store(dequant8(t, w), reinterpret_cast<u32x4 *>(g.out) + owi);
     }
 }
 
@@ -110,8 +118,9 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
 }  // namespace
 
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
-                                hipStream_t stream) {
+                                hipStream_t stream, int slot) {
     ExpandArgs a;
+    a.slot = transposed ? -1 : slot;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.out = out; a.N = w.rows; a.K = w.cols;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];

@@ -175,3 +175,31 @@ def test_workspace_sizes_cover_all_configs():
         # at least T, sT, dT and the transposed adapters
         assert ws >= 2 * (3 * M * r + r * K + N * r)
         assert ws < 1 << 31
+
+
+def test_flag_bits_are_distinct_and_match_the_binding():
+    text = open(HEADER).read()
+    vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (QLORA_\w+) (\d+)u", text)}
+    assert vals["QLORA_GATED_FUSE"] & vals["QLORA_DX_ACCUMULATE"] == 0
+    assert nf4.QLORA_GATED_FUSE == vals["QLORA_GATED_FUSE"]
+
+
+def test_gated_argument_errors():
+    d = _desc()
+    fake = ctypes.c_void_p(0x100000)
+    ws = lib.qlora_gated_workspace_size(64, 256, 256, 8)
+    assert ws > 0
+    # unknown flag bits
+    assert lib.qlora_gated_fwd(ctypes.byref(d), ctypes.byref(d), fake, fake, fake, fake, fake, 1.0, 64, 8,
+                               fake, fake, fake, None, None, 4, fake, ws, None) == EARG
+    assert lib.qlora_gated_bwd(ctypes.byref(d), ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                               None, None, 1.0, 64, 8, fake, fake, fake, fake, fake, 4, fake, ws, None) == EARG
+    # shapes of gate and up must agree
+    d2 = _desc(rows=512)
+    assert lib.qlora_gated_fwd(ctypes.byref(d), ctypes.byref(d2), fake, fake, fake, fake, fake, 1.0, 64, 8,
+                               fake, fake, fake, None, None, 0, fake, ws, None) == ESHAPE
+    # workspace too small (the size query covers the larger, backward plan; 256 bytes fits neither)
+    assert lib.qlora_gated_fwd(ctypes.byref(d), ctypes.byref(d), fake, fake, fake, fake, fake, 1.0, 64, 8,
+                               fake, fake, fake, None, None, 0, fake, 256, None) == EWS
+    assert lib.qlora_gated_bwd(ctypes.byref(d), ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                               None, None, 1.0, 64, 8, fake, fake, fake, fake, fake, 0, fake, 256, None) == EWS

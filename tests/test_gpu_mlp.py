@@ -155,3 +155,98 @@ def test_llama65b_heavy_tail_layer():
     to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     _check_fwd(lin.name, layer, X, to64(Y), s, rows)
     _check_bwd(lin.name, layer, dY, X, to64(dX), to64(dL1), to64(dL2), s, rows)
+
+
+# ------------------------------------------------------------------------------------------
+# Gated forward: gate and up as one product with the glue in its epilogue
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,F,K,r", [
+    (1024, 2048, 1024, 64),    # one fused product, whole tiles
+    (1100, 544, 640, 32),      # ragged tokens; the combined 1088 columns end in a part tile
+    (2048, 1056, 512, 128),    # r = 128: two LoRA steps per adapter
+    (300, 512, 384, 16),       # below the fused range: the two linears and the glue as calls
+])
+def test_gated_fwd_matches_separate_calls_and_oracle(M, F, K, r):
+    _say(f"gated fwd M={M} F={F} K={K} r={r}")
+    s = 16.0 / r
+    sd = 700 + M + F
+    Wg = synth.normal_f32(sd, (F, K), 0.02)
+    Wu = synth.normal_f32(sd + 1, (F, K), 0.02)
+    X = synth.to_bf16_bits(synth.normal_f32(sd + 2, (M, K), 1.0))
+    ad = [synth.to_bf16_bits(synth.normal_f32(sd + 3 + i, shp, std))
+          for i, (shp, std) in enumerate((((K, r), 1.0 / r), ((r, F), 0.01), ((K, r), 1.0 / r), ((r, F), 0.01)))]
+    wg = nf4.NF4Weight.from_float(torch.from_numpy(Wg).to(DEV), CB)
+    wu = nf4.NF4Weight.from_float(torch.from_numpy(Wu).to(DEV), CB)
+    Xd = d16(X)
+    L1g, L2g, L1u, L2u = (d16(a) for a in ad)
+    G, U, H, Tg, Tu = nf4.qlora_gated_fwd(wg, wu, Xd, L1g, L2g, L1u, L2u, s, fuse=True)
+    G0, U0, H0, Tg0, Tu0 = nf4.qlora_gated_fwd(wg, wu, Xd, L1g, L2g, L1u, L2u, s)
+    Gs, Tgs = nf4.qlora_linear_fwd(wg, Xd, L1g, L2g, s)
+    Us, Tus = nf4.qlora_linear_fwd(wu, Xd, L1u, L2u, s)
+    Hs = nf4.qlora_swiglu_fwd(Gs, Us)
+    torch.cuda.synchronize()
+    # the same bits as the separate calls, fused or not
+    for g_, u_, h_, tg_, tu_ in ((G, U, H, Tg, Tu), (G0, U0, H0, Tg0, Tu0)):
+        assert torch.equal(g_, Gs) and torch.equal(u_, Us) and torch.equal(h_, Hs)
+        assert torch.equal(tg_, Tgs) and torch.equal(tu_, Tus)
+    # and within tolerance of the oracle
+    Wgq = oracle.dequant_weight(oracle.quantize_dq(Wg, CB), CB)
+    Wuq = oracle.dequant_weight(oracle.quantize_dq(Wu, CB), CB)
+    Gr, _ = oracle.forward(X, Wgq, ad[0], ad[1], s)
+    Ur, _ = oracle.forward(X, Wuq, ad[2], ad[3], s)
+    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    check_tol("G", to64(G), Gr)
+    check_tol("U", to64(U), Ur)
+    check_tol("H", to64(H), oracle.swiglu_fwd(h16(G), h16(U)))
+
+
+@pytest.mark.parametrize("M,F,K,r", [
+    (1024, 2048, 1024, 64),    # dX as one product over both weights
+    (1100, 544, 640, 32),      # ragged tokens and reduction segments (544 = 8.5 steps of 64)
+    (2048, 1056, 512, 128),    # two LoRA steps per adapter
+    (300, 512, 384, 16),       # below the fused range: the linears' backward as calls
+])
+def test_gated_bwd_fused_and_composed(M, F, K, r):
+    _say(f"gated bwd M={M} F={F} K={K} r={r}")
+    s = 16.0 / r
+    sd = 800 + M + F
+    Wg = synth.normal_f32(sd, (F, K), 0.02)
+    Wu = synth.normal_f32(sd + 1, (F, K), 0.02)
+    X = synth.to_bf16_bits(synth.normal_f32(sd + 2, (M, K), 1.0))
+    dH = synth.to_bf16_bits(synth.normal_f32(sd + 3, (M, F), 1.0))
+    ad = [synth.to_bf16_bits(synth.normal_f32(sd + 4 + i, shp, std))
+          for i, (shp, std) in enumerate((((K, r), 1.0 / r), ((r, F), 0.01), ((K, r), 1.0 / r), ((r, F), 0.01)))]
+    wg = nf4.NF4Weight.from_float(torch.from_numpy(Wg).to(DEV), CB)
+    wu = nf4.NF4Weight.from_float(torch.from_numpy(Wu).to(DEV), CB)
+    Xd, dHd = d16(X), d16(dH)
+    L1g, L2g, L1u, L2u = (d16(a) for a in ad)
+    G, U, H, Tg, Tu = nf4.qlora_gated_fwd(wg, wu, Xd, L1g, L2g, L1u, L2u, s)
+    args = (wg, wu, dHd, Xd, G, U, L1g, L2g, L1u, L2u)
+    comp = nf4.qlora_gated_bwd(*args, Tg, Tu, s)
+    fused = nf4.qlora_gated_bwd(*args, Tg, Tu, s, fuse=True)
+    recomputed = nf4.qlora_gated_bwd(*args, None, None, s, fuse=True)
+    base = d16(synth.to_bf16_bits(synth.normal_f32(sd + 9, (M, K), 1.0)))
+    acc = base.clone()
+    nf4.qlora_gated_bwd(*args, Tg, Tu, s, dX=acc, accumulate=True, fuse=True)
+    torch.cuda.synchronize()
+    # adapter gradients: the same launches on every path; T recomputed gives the same bits
+    for k in range(1, 5):
+        assert torch.equal(comp[k], fused[k]) and torch.equal(fused[k], recomputed[k])
+    assert torch.equal(fused[0], recomputed[0])
+    # against the oracle, fed the glue's backward of the GPU's own G and U (rounded to bf16)
+    rg, ru = oracle.swiglu_bwd(dH, h16(G), h16(U))
+    dGb, dUb = oracle.bf16_rne(rg.astype(np.float32)), oracle.bf16_rne(ru.astype(np.float32))
+    Wgq = oracle.dequant_weight(oracle.quantize_dq(Wg, CB), CB)
+    Wuq = oracle.dequant_weight(oracle.quantize_dq(Wu, CB), CB)
+    gg = oracle.backward(dGb, X, Wgq, ad[0], ad[1], s)
+    gu = oracle.backward(dUb, X, Wuq, ad[2], ad[3], s)
+    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    dX_ref = gg["dX"] + gu["dX"]
+    check_tol("dX fused", to64(fused[0]), dX_ref)
+    check_tol("dX composed", to64(comp[0]), dX_ref)
+    check_tol("dX += (fused)", to64(acc), dX_ref + to64(base))
+    check_tol("dL1_gate", to64(fused[1]), gg["dL1"])
+    check_tol("dL2_gate", to64(fused[2]), gg["dL2"])
+    check_tol("dL1_up", to64(fused[3]), gu["dL1"])
+    check_tol("dL2_up", to64(fused[4]), gu["dL2"])
