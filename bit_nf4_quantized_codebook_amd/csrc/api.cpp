@@ -140,7 +140,7 @@ bool use_expand(int64_t M, int64_t N, int64_t K) { return M >= kExpandMinM && N 
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
-    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, off_Wd, total;
+    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, off_Wd, off_L2T, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -162,9 +162,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     const size_t ptn = (size_t)p.msL2 * r * N + (size_t)p.msL1 * K * r;
     pmax = pmax > ptn ? pmax : ptn;
     p.off_P = off;   off += round256(pmax * 4);
-    p.off_Yp = p.off_Tp = p.off_Wd = off;
+    p.off_Yp = p.off_Tp = p.off_Wd = p.off_L2T = off;
     if (use_expand(M, N, K)) {
-        p.off_Wd = off;  off += round256((size_t)N * K * 2);
+        p.off_Wd = off;   off += round256((size_t)N * K * 2);
+        p.off_L2T = off;  off += round256((size_t)N * r * 2);   // L2 transposed for the GEMM
     }
     if (nf4k::gemv_fits(M, N, K, r)) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
@@ -429,13 +430,15 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
     if (M > kGemvMaxM && use_expand(M, N, K)) {
         // T's partials, then one launch that expands the weight and sums them, then the GEMM
+        // T's partials; one launch expands the weight, sums them and transposes L2; the GEMM
         uint16_t *Wd = ws_at<uint16_t>(workspace, p.off_Wd);
+        uint16_t *L2T = ws_at<uint16_t>(workspace, p.off_L2T);
         hipError_t e;
         const nf4k::Reduction red = T_partials(X, L1, M, K, r, scale, T_out, sT, p, workspace, s, &e);
         NF4_CHECK_HIP(e, "T = X L1");
-        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s),
-                      "weight expansion + T reduce");
-        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s, -1, L2, L2T, r, N),
+                      "weight expansion + T reduce + L2 transpose");
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2T, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
         return NF4_OK;
     }
     rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);

@@ -1,6 +1,6 @@
 // K-extended bf16 MFMA GEMM of the QLoRA linear layer at large token counts (gfx950):
 //   C = [A | Ae] . [B | Be]^T         (optionally C += ...)
-//   forward : A = X [M, K],  B = deq(W) [N, K],  Ae = sT [M, r],  Be^T = L2 [r, N]
+//   forward : A = X [M, K],  B = deq(W) [N, K],  Ae = sT [M, r],  Be = L2^T [N, r]
 //   backward: A = dY [M, N], B = deq(W)^T [K, N], Ae = dT [M, r], Be = L1 [K, r]
 // B is the frozen weight after the double dequantization to bf16, written by a separate pass
 // (row-major for the forward, transposed for the backward), so both products read B with the
@@ -45,7 +45,7 @@ struct GemmArgs {
     const uint16_t *A;    // [M, Kred]
     const uint16_t *B;    // [Nout, Kred]
     const uint16_t *Ae;   // [M, r]
-    const uint16_t *Be;   // forward: L2 [r, Nout]; backward: L1 [Nout, r]
+    const uint16_t *Be;   // forward: L2^T [Nout, r] (gated: L2 [r, Nout / 2]); backward: L1 [Nout, r]
     uint16_t *C;          // [M, Nout]   (gated: H [M, Nout / 2])
     int64_t M, Nout, Kred;
     int32_t r;
@@ -239,14 +239,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
     // ---- LoRA extension: r/64 more steps (zero padded past r) ----
     //   A tile: Ae rows m0.., columns j (same swizzled layout, straight to LDS), in As0
-    //   forward : Be^T = L2 [r, Nout]: rows j, columns n -> two halves [64 j][128 + 16] in
-    //             Bs0 / Bs1, transposing fragment reads
-    //   backward: Be = L1 [Nout, r]: rows n, columns j -> swizzled layout in Bs0, row reads
+    //   forward and backward: Be = L2^T or L1 [Nout, r]: rows n, columns j -> swizzled layout in
+    //             Bs0, straight to LDS, row reads (L2 is transposed by the expansion launch)
+    //   gated forward: L2_gate / L2_up [r, F]: rows j, columns n -> two halves [64 j][128 + 16]
+    //             in Bs0 / Bs1 through registers, transposing fragment reads
     if (ext_steps > 0) {
         const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
         const int64_t be_cols = GATED ? g.Nout / 2 : g.Nout;     // row length of L2
-        const __amdgpu_buffer_rsrc_t rBe = BWD ? make_rsrc(g.Be + n0 * g.r, (g.Nout - n0) * (int64_t)g.r * 2)
-                                               : make_rsrc(g.Be, (int64_t)g.r * be_cols * 2);
+        // rows layout [Nout, r] (L1, or the forward's L2 transposed); the gated forward reads L2 [r, F]
+        const __amdgpu_buffer_rsrc_t rBe = !GATED ? make_rsrc(g.Be + n0 * g.r, (g.Nout - n0) * (int64_t)g.r * 2)
+                                                  : make_rsrc(g.Be, (int64_t)g.r * be_cols * 2);
         const __amdgpu_buffer_rsrc_t rAe2 = make_rsrc(GATED ? g.Ae2 + m0 * g.r : g.Ae,
                                                       GATED ? (g.M - m0) * (int64_t)g.r * 2 : 0);
         const __amdgpu_buffer_rsrc_t rBe2 = make_rsrc(GATED ? g.Be2 : g.Be, GATED ? (int64_t)g.r * be_cols * 2 : 0);
@@ -271,11 +273,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                 if (GATED)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe2, (lds_void *)((lds_u8 *)As1 + wave * 8192 + q * 1024),
                                                              16, off, 0, 0, 0);
-                if (BWD)
+                if (!GATED)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
                                                              16, off, 0, 0, 0);
             }
-            if (!BWD) {
+            if (GATED) {
                 // L2 rows j0 .. j0+63, columns n0 .. n0+255: 16-byte chunks through registers
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -309,7 +311,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                     f.a[i] = *reinterpret_cast<const bf16x8 *>(As0 + lds_off[s] + (wm * 128 + 32 * i) * 128);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if (BWD) {
+                    if (!GATED) {
                         f.b[j] = *reinterpret_cast<const bf16x8 *>(Bs0 + lds_off[s] + (wn * 128 + 32 * j) * 128);
                     } else {
                         // 16-lane group (hh, half): lane i reads rows 16 s + 8 hh + i/4 (+4),
@@ -440,10 +442,10 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
+hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream) {
     GemmArgs a{};
-    a.A = X; a.B = Wd; a.Ae = sT; a.Be = L2; a.C = Y;
+    a.A = X; a.B = Wd; a.Ae = sT; a.Be = L2T; a.C = Y;
     a.M = M; a.Nout = N; a.Kred = K; a.r = r; a.accumulate = 0;
     return launch_impl<false>(a, stream);
 }

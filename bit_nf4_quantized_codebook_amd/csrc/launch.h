@@ -54,9 +54,13 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
 // red (optional): a partials reduction carried by extra workgroups of the same launch
 // slot (rows only): -1 plain; 0 / 1 puts the rows in 32-row slot 0 / 1 of 64-row groups of out (the
 // gate / up interleave of the gated MLP's combined weight)
+// tr_in (optional, rows layout only): extra workgroups also transpose tr_in [tr_r, tr_n] into
+// tr_out [tr_n, tr_r] (the forward GEMM's L2, so its LoRA step loads like the backward's L1)
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
-                                hipStream_t stream, int slot = -1);
-hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2,
+                                hipStream_t stream, int slot = -1, const uint16_t *tr_in = nullptr,
+                                uint16_t *tr_out = nullptr, int32_t tr_r = 0, int64_t tr_n = 0);
+// L2T: the adapter's L2 transposed, [N, r]
+hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
 // gated MLP forward: C = [X | sT_gate | sT_up] . [Wgu ; ...]^T over the combined weight Wgu [2F, K]
 // (gate and up rows interleaved in 32-row groups); writes G, U and H = silu(G) U, each [M, F]

@@ -20,7 +20,9 @@ namespace nf4k {
 namespace {
 
 // nexp workgroups expand the weight; nred more (optional) sum a set of split-reduction partials
-// that the caller needs at the same point of the stream
+// that the caller needs at the same point of the stream, and (rows layout) ntr more transpose a
+// small matrix; these short jobs take the lowest workgroup indices, so they run alongside the
+// expansion rather than after it
 struct ExpandArgs {
     const uint8_t *packed;
     const uint8_t *c2;
@@ -33,21 +35,64 @@ struct ExpandArgs {
     RedProb red;
     uint32_t nexp, nred;
     int32_t slot;            // row layout: -1 plain; 0 / 1: rows to 32-row slot 0 / 1 of 64-row groups
+    // ntr more (optional, rows layout): transpose tr_in [tr_r, tr_n] into tr_out [tr_n, tr_r] (bf16)
+    const uint16_t *tr_in;
+    uint16_t *tr_out;
+    int32_t tr_r;
+    int64_t tr_n;
+    uint32_t ntr;
 };
+
+// One 64 x 64 tile of the small transpose per workgroup (L2 [r, N] -> [N, r] for the GEMM's LoRA
+// step, so that it loads like the backward's L1).  Thread t loads two 16-byte pieces of row t / 4
+// of the tile (columns 16 (t % 4) ..), and stores two 16-byte pieces of output row t / 4; r and
+// N are multiples of 8, so no piece straddles an edge.
+__device__ __forceinline__ void transpose_block(const ExpandArgs &g, int64_t blk) {
+    __shared__ uint16_t tt[64][64 + 8];
+    const int64_t ncb = (g.tr_n + 63) / 64;
+    const int64_t j0 = (blk / ncb) * 64, n0 = (blk % ncb) * 64;
+    const int t = threadIdx.x, row = t >> 2, c0 = (t & 3) * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t j = j0 + row, n = n0 + c0 + 8 * h;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j < g.tr_r && n < g.tr_n) v = *reinterpret_cast<const u32x4 *>(g.tr_in + j * g.tr_n + n);
+        *reinterpret_cast<u32x4 *>(&tt[row][c0 + 8 * h]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t n = n0 + row, j = j0 + c0 + 8 * h;
+        if (n < g.tr_n && j < g.tr_r) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[k] = (uint32_t)tt[c0 + 8 * h + 2 * k][row] | ((uint32_t)tt[c0 + 8 * h + 2 * k + 1][row] << 16);
+            *reinterpret_cast<u32x4 *>(g.tr_out + n * g.tr_r + j) = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+}
 
 // Row layout: 8 lanes per block, one packed dword (8 weights) each, so a wave reads 256
 // contiguous packed bytes and writes 1 KB of contiguous bf16 per store.  The 8 lanes of a block
 // each build its table (the kernel is bound by HBM, not VALU).  Blocks run over the row-major
 // flattening, so this needs only N*K % 64 == 0.
+// Workgroups: the ntr transpose tiles and the nred reduction workgroups first (short jobs that
+// then overlap the expansion instead of trailing it), the nexp expansion workgroups after them.
 __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
-    if (blockIdx.x >= g.nexp) {
-        reduce_partials_block(g.red, blockIdx.x - g.nexp, g.nred);
+    if (blockIdx.x < g.ntr) {
+        transpose_block(g, blockIdx.x);
         return;
     }
+    if (blockIdx.x < g.ntr + g.nred) {
+        reduce_partials_block(g.red, blockIdx.x - g.ntr, g.nred);
+        return;
+    }
+    const int64_t eb = blockIdx.x - g.ntr - g.nred;
     const int64_t nwords = (g.N * g.K) >> 3;
     const float mean = g.mean[0];
     const bool dq_i8 = g.dq_int8 != 0;
-    for (int64_t wi = (int64_t)blockIdx.x * 256 + threadIdx.x; wi < nwords; wi += (int64_t)g.nexp * 256) {
+    for (int64_t wi = eb * 256 + threadIdx.x; wi < nwords; wi += (int64_t)g.nexp * 256) {
         const int64_t b = wi >> 3;
         const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(g.packed) + wi);
         const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean, dq_i8));
@@ -70,15 +115,17 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
 constexpr int TROW = 64 + 8;   // LDS row (k) length in bf16, padded
 __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
     __shared__ uint16_t tile[64 * TROW];
-    if (blockIdx.x >= g.nexp) {
-        reduce_partials_block(g.red, blockIdx.x - g.nexp, g.nred);
+    // the reduction workgroups first, so that they overlap the expansion instead of trailing it
+    if (blockIdx.x < g.nred) {
+        reduce_partials_block(g.red, blockIdx.x, g.nred);
         return;
     }
+    const int64_t tb = blockIdx.x - g.nred;
     const int tid = threadIdx.x;
     const int64_t nbk = g.K >> 6;
     const int64_t ntn = (g.N + 63) >> 6;
-    const int64_t kb = blockIdx.x / ntn;
-    const int64_t n0 = (blockIdx.x % ntn) * 64;
+    const int64_t kb = tb / ntn;
+    const int64_t n0 = (tb % ntn) * 64;
     const float mean = g.mean[0];
     const bool dq_i8 = g.dq_int8 != 0;
     {
@@ -118,9 +165,12 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
 }  // namespace
 
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
-                                hipStream_t stream, int slot) {
+                                hipStream_t stream, int slot, const uint16_t *tr_in, uint16_t *tr_out,
+                                int32_t tr_r, int64_t tr_n) {
     ExpandArgs a;
     a.slot = transposed ? -1 : slot;
+    a.tr_in = tr_in; a.tr_out = tr_out; a.tr_r = tr_r; a.tr_n = tr_n;
+    a.ntr = (!transposed && tr_in) ? (uint32_t)(((tr_r + 63) / 64) * ((tr_n + 63) / 64)) : 0u;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.out = out; a.N = w.rows; a.K = w.cols;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
@@ -132,7 +182,7 @@ hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *
         if (grid > 256 * 64) grid = 256 * 64;
         if (grid < 1) grid = 1;
         a.nexp = (uint32_t)grid;
-        hipLaunchKernelGGL(expand_rows_kernel, dim3(a.nexp + a.nred), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(expand_rows_kernel, dim3(a.nexp + a.nred + a.ntr), dim3(256), 0, stream, a);
     } else {
         a.nexp = (uint32_t)(((w.rows + 63) / 64) * (w.cols / 64));
         hipLaunchKernelGGL(expand_transposed_kernel, dim3(a.nexp + a.nred), dim3(256), 0, stream, a);
