@@ -166,6 +166,7 @@ def test_llama65b_heavy_tail_layer():
     (1100, 544, 640, 32),      # ragged tokens; the combined 1088 columns end in a part tile
     (2048, 1056, 512, 128),    # r = 128: two LoRA steps per adapter
     (300, 512, 384, 16),       # below the fused range: the two linears and the glue as calls
+    (1024, 520, 256, 8),       # F not a multiple of 32: the fuse flag falls back to the calls
 ])
 def test_gated_fwd_matches_separate_calls_and_oracle(M, F, K, r):
     _say(f"gated fwd M={M} F={F} K={K} r={r}")
@@ -206,6 +207,7 @@ def test_gated_fwd_matches_separate_calls_and_oracle(M, F, K, r):
     (1100, 544, 640, 32),      # ragged tokens and reduction segments (544 = 8.5 steps of 64)
     (2048, 1056, 512, 128),    # two LoRA steps per adapter
     (300, 512, 384, 16),       # below the fused range: the linears' backward as calls
+    (1024, 520, 256, 8),       # ragged segments (520 = 8.1 steps of 64), one LoRA step each
 ])
 def test_gated_bwd_fused_and_composed(M, F, K, r):
     _say(f"gated bwd M={M} F={F} K={K} r={r}")
@@ -234,6 +236,9 @@ def test_gated_bwd_fused_and_composed(M, F, K, r):
     for k in range(1, 5):
         assert torch.equal(comp[k], fused[k]) and torch.equal(fused[k], recomputed[k])
     assert torch.equal(fused[0], recomputed[0])
+    no_dx = nf4.qlora_gated_bwd(*args, Tg, Tu, s, need_dX=False, fuse=True)
+    torch.cuda.synchronize()
+    assert no_dx[0] is None and all(torch.equal(no_dx[k], fused[k]) for k in range(1, 5))
     # against the oracle, fed the glue's backward of the GPU's own G and U (rounded to bf16)
     rg, ru = oracle.swiglu_bwd(dH, h16(G), h16(U))
     dGb, dUb = oracle.bf16_rne(rg.astype(np.float32)), oracle.bf16_rne(ru.astype(np.float32))
