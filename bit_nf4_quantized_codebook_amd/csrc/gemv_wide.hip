@@ -1,4 +1,5 @@
-// Small-batch forward (4 < M <= 16 tokens) of the QLoRA linear layer (gfx950):
+// Small-batch forward (9 to 16 tokens, and smaller token counts on shapes the row kernel of
+// the decode GEMV does not take) of the QLoRA linear layer (gfx950):
 //   Y = X deq(W)^T + s T L2,   T = X L1 computed beforehand (s T passed in, bf16 [M, r])
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),

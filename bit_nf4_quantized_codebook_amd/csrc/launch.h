@@ -32,7 +32,8 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              hipStream_t stream);
-// 4 < M <= 16 tokens: sT = s X L1 (bf16 [M, r]) computed beforehand
+// up to 16 tokens (9-16, or fewer on shapes the row kernel does not take): sT = s X L1 (bf16
+// [M, r]) computed beforehand
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
 // decode-size forward (M <= 8): two launches; Tp is fp32 scratch of the size gemv_plan gives (Yp unused)
