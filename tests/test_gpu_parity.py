@@ -177,6 +177,8 @@ SHAPES = [
     (5, 512, 8192, 16),
     (4, 520, 2048, 128),       # 4x4-MFMA decode layout with r = 128, four row streams
     (1, 1000, 4096, 128),      # one-token decode layout with r = 128
+    (9, 1000, 2048, 16),       # the first token count past the row kernel: the 16x16x32 GEMV
+    (1023, 264, 640, 24),      # the last token count of the fused dequant GEMMs, ragged
     # from 1024 tokens on: bf16 expansion of the weight + K-extended bf16 GEMM
     (1024, 520, 384, 16),      # ragged N (the backward's reduction), odd number of K steps
     (1100, 264, 640, 24),      # ragged M and N
@@ -285,8 +287,10 @@ def test_int8_double_quant_dequant_bit_exact(case):
 
 @pytest.mark.parametrize("M,N,K,r", [(1, 3000, 8192, 64), (4, 520, 2048, 128), (12, 2000, 4096, 32),
                                      (300, 520, 384, 16), (1100, 264, 640, 24)])
-def test_int8_double_quant_linear_parity(M, N, K, r):
-    _say(f"int8 DQ linear: M={M} N={N} K={K} r={r}")
+@pytest.mark.parametrize("table", ["nf4", "fp4"])
+def test_int8_double_quant_linear_parity(M, N, K, r, table):
+    _say(f"int8 DQ linear: {table} M={M} N={N} K={K} r={r}")
+    CB = globals()["CB"] if table == "nf4" else _alt_cb("fp4")
     s = 16.0 / r
     seed = 950 + M + N
     W = synth.normal_f32(seed, (N, K), 0.02)
