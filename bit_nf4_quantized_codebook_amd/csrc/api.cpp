@@ -429,7 +429,6 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
     }
     uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT);
     if (M > kGemvMaxM && use_expand(M, N, K)) {
-        // T's partials, then one launch that expands the weight and sums them, then the GEMM
         // T's partials; one launch expands the weight, sums them and transposes L2; the GEMM
         uint16_t *Wd = ws_at<uint16_t>(workspace, p.off_Wd);
         uint16_t *L2T = ws_at<uint16_t>(workspace, p.off_L2T);
