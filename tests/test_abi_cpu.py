@@ -146,6 +146,11 @@ def test_linear_argument_errors():
     assert fwd(_desc(), wsb=wsb - 1) == EWS
     assert fwd(_desc(), ws=None) == EWS
     assert fwd(_desc(ptr=0x100008)) == EALIGN
+    # 32-bit buffer offsets: each operand under 2 GiB (packed weight, X [M, K], Y [M, N])
+    assert fwd(_desc(rows=65536, cols=65536)) == EUNSUP
+    assert fwd(_desc(rows=65536, cols=65472)) == EWS          # just under: reaches the workspace check
+    assert fwd(_desc(), M=1 << 22) == EUNSUP                  # X: 2^22 x 256 bf16 = 2 GiB
+    assert fwd(_desc(rows=65536), M=1 << 14) == EUNSUP        # Y: 2^14 x 65536 bf16 = 2 GiB
     # backward: unknown flags, NULL gradient outputs
     d = _desc()
     assert lib.qlora_linear_bwd(ctypes.byref(d), fake, fake, fake, fake, None, 2.0, M, r, fake, fake,
