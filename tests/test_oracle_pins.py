@@ -366,6 +366,42 @@ def test_grouped_sum_small_is_sequential_and_exact_cases():
     assert oracle.grouped_sum(w) == tot
 
 
+def test_grouped_sum_three_levels_closed_form():
+    """The order past two levels, on values whose float64 sum depends on it.
+
+    131072 values form 512 groups of 256, then 2 groups, then 1: three levels.  Value 0 is 2^53
+    and each later 256-group holds a single 1.0, the rest zero.
+      level 1: group 0 sums to 2^53, groups 1 .. 511 to 1.0 each (exact);
+      level 2: the first 256 sums are 2^53 followed by 255 ones; each one is added to 2^53 on its
+               own, and 2^53 + 1 lies half-way between 2^53 and 2^53 + 2, so ties-to-even keeps
+               2^53 every time.  The second 256 sums add up to 256 exactly;
+      level 3: 2^53 + 256, exact.
+    A plain sequential sum, and a sequential sum of the 256-group sums (two levels), both keep
+    2^53; the exact sum is 2^53 + 511.  Each of these readings therefore gives a different value."""
+    v = np.zeros(131072)
+    v[0] = 2.0 ** 53
+    v[256::256] = 1.0
+    assert oracle.grouped_sum(v) == 2.0 ** 53 + 256
+    assert math.fsum(v) == 2.0 ** 53 + 511
+    seq = 0.0
+    for x in v[v != 0]:
+        seq += float(x)
+    assert seq == 2.0 ** 53
+
+
+@pytest.mark.parametrize("nb", [262144, 3670016])
+def test_double_quant_mean_is_the_exact_mean_to_one_ulp(nb):
+    """The stored mean against the exactly rounded sum (math.fsum) over n, on non-integer block
+    constants at the 7B-projection and decode-weight block counts (three summation levels at the
+    larger).  The float64 sum's rounding error is far below float32's, so the two agree within
+    one unit in the last place of the float32 mean."""
+    a = (synth.uniform(36 + nb % 7, nb) * 0.08 + 0.011).astype(np.float32)
+    _, _, mean = oracle.double_quant(a)
+    exact = np.float32(math.fsum(a.astype(np.float64)) / nb)
+    assert abs(int(np.float32(mean).view(np.int32)) - int(exact.view(np.int32))) <= 1
+    assert a.size == nb and not np.all(a == np.floor(a))
+
+
 def test_memory_accounting_golden():
     g = GOLDEN["constant_overhead_bits"]
     gb = GOLDEN["block_sizes"]
