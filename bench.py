@@ -8,13 +8,18 @@ already resident in HBM.  The default workload is the LLaMA-7B attention project
 alpha = 16).  The headline value is algorithmic TFLOP/s (2MNK per dense product, LoRA at rank r).
 
 Also reported on the same JSON line:
-  roofline     the dominant kernel (the fused dequant-GEMM), timed live with HIP events recorded
-               by the library around each of its launches in the timed region
+  roofline     the dominant kernel (the larger of the two bf16 GEMM launches), timed live with
+               HIP events recorded by the library around each of its launches in the timed
+               region; step_frac is the whole step's fraction of the bf16 peak
   cpu_baseline the CPU oracle on a bounded sample of the same workload
   gemv         decode-size forward (W 28672x8192, M = 1, 4, 16) in GB/s, weights rotated over
                three replicas so the 256 MB last-level cache cannot hold them
+  c3           the LLaMA-7B SwiGLU MLP (gate/up 11008x4096, down 4096x11008, 4096 tokens, r = 64):
+               forward + backward TFLOP/s, every GEMM launch timed, the dominant one as roofline
+  c4           the LLaMA-65B-shaped MLP (22016x8192 / 8192x22016, 2048 tokens, heavy-tailed
+               weights): the same, plus quantize + double quant of its three weights in GB/s
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv] [--no-mlp]
 """
 from __future__ import annotations
 
@@ -57,9 +62,12 @@ def gemm_traffic_bytes(kind):
         return None
     pkg = os.path.join(ROOT, "bit_nf4_quantized_codebook_amd")
     for rel, digest in GEMM_TRAFFIC_SOURCES.items():
-        with open(os.path.join(pkg, rel), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != digest:
-                return None
+        try:
+            with open(os.path.join(pkg, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
     fetch, write = GEMM_TRAFFIC_KIB[kind]
     return int(round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024))
 
@@ -138,6 +146,15 @@ def cpu_baseline(synth, wl, lin, budget_s=10.0, sample_tokens=512):
         t_total += time.perf_counter() - t0
         reps += 1
     threads = 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
@@ -145,6 +162,7 @@ def cpu_baseline(synth, wl, lin, budget_s=10.0, sample_tokens=512):
         "value": round((fwd + bwd) * reps / t_total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"{reps} oracle fwd+bwd passes over {sample_tokens} of the {wl.M} tokens "
                    f"({lin.N}x{lin.K} weight double-dequantized by the oracle each pass, float64 "
@@ -179,6 +197,173 @@ def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
         del st
         torch.cuda.empty_cache()
     return out
+
+
+# GEMM launches of one MLP step, in launch order: (name, kind recorded by the library)
+MLP_LAUNCHES = (("gate fwd", 0), ("up fwd", 0), ("down fwd", 0), ("down bwd (dH)", 1),
+                ("gate+up bwd (dX over both weights)", 4))
+
+
+def mlp_launch_flops(M, F, K, r):
+    """Algorithmic flops of each GEMM launch of one MLP step (MLP_LAUNCHES order); F = hidden size
+    of the MLP (gate/up rows, down's reduction), K = model width."""
+    fwd_gu = 2 * M * F * K + 2 * M * r * F
+    return (fwd_gu, fwd_gu, 2 * M * K * F + 2 * M * r * K, 2 * M * K * F + 2 * M * r * F,
+            2 * (2 * M * F * K) + 2 * (2 * M * r * K))
+
+
+def mlp_flops(M, F, K, r):
+    """Algorithmic flops of one MLP forward + backward: three linears, LoRA at rank r (the glue's
+    elementwise work is not counted)."""
+    gu = linear_flops(M, F, K, r)
+    dn = linear_flops(M, K, F, r)
+    return 2 * sum(gu) + sum(dn)
+
+
+def make_mlp(torch, nf4, synth, wl, dev):
+    """The three QLoRA linears of a SwiGLU MLP workload, their adapters, X, dY and the buffers of one
+    step; the weights are quantized on the GPU from the seeded float32 draws."""
+    import numpy as np
+    cb = nf4.nf4_build_codebook()
+    gate, up, down = wl.linears
+    M, r, F, K = wl.M, wl.r, gate.N, gate.K
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)  # noqa: E731
+    st = {"M": M, "r": r, "F": F, "K": K, "s": wl.scale, "w": [], "L1": [], "L2": []}
+    for lin in wl.linears:
+        W = torch.from_numpy(synth.weight_f32(wl, lin)).to(dev)
+        st["w"].append(nf4.NF4Weight.from_float(W, cb))
+        del W
+        l1, l2 = synth.lora_f32(wl, lin)
+        st["L1"].append(bf(l1))
+        st["L2"].append(bf(l2))
+    st["X"] = bf(synth.x_f32(wl, M=M, K=K))
+    st["dY"] = bf(synth.dy_f32(wl, M, down.N))
+    e = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    st.update(Y=e(M, K), Td=e(M, r), dH=e(M, F), dX=e(M, K), dL1d=e(F, r), dL2d=e(r, K))
+    wsb = max(nf4.lib.qlora_gated_workspace_size(M, F, K, r), nf4.qlora_linear_workspace_size(M, K, F, r))
+    st["ws"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    return st
+
+
+def step_mlp(nf4, st):
+    """One forward + backward of the MLP: gate and up (two linears, then the glue), down; down's
+    backward, the glue's backward and both linears' backward with dX as one product over the two
+    weights (the library's faster form of each)."""
+    wg, wu, wd = st["w"]
+    (L1g, L1u, L1d), (L2g, L2u, L2d) = st["L1"], st["L2"]
+    s, ws = st["s"], st["ws"]
+    G, U, H, Tg, Tu = nf4.qlora_gated_fwd(wg, wu, st["X"], L1g, L2g, L1u, L2u, s, workspace=ws)
+    nf4.qlora_linear_fwd(wd, H, L1d, L2d, s, Y=st["Y"], T=st["Td"], workspace=ws)
+    nf4.qlora_linear_bwd(wd, st["dY"], H, L1d, L2d, st["Td"], s, dX=st["dH"], dL1=st["dL1d"], dL2=st["dL2d"],
+                         workspace=ws)
+    nf4.qlora_gated_bwd(wg, wu, st["dH"], st["X"], G, U, L1g, L2g, L1u, L2u, Tg, Tu, s, dX=st["dX"],
+                        workspace=ws, fuse=True)
+
+
+def bench_mlp(torch, nf4, synth, dev, wl, steps=10, warmup=3):
+    """Forward + backward TFLOP/s of a SwiGLU MLP workload (three QLoRA linears and the glue), with
+    every GEMM launch of one step in four timed with HIP events on its stream."""
+    st = make_mlp(torch, nf4, synth, wl, dev)
+    M, F, K, r = st["M"], st["F"], st["K"], st["r"]
+    for _ in range(warmup):
+        step_mlp(nf4, st)
+    torch.cuda.synchronize()
+    nl = len(MLP_LAUNCHES)
+    nsampled = (steps + TIMING_EVERY - 1) // TIMING_EVERY
+    timer = nf4.GemmTimer(nl * nsampled)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cnt = 0
+    e0.record()
+    for i in range(steps):
+        sampled = i % TIMING_EVERY == 0
+        if sampled:
+            timer.arm_at(cnt, nl)
+        step_mlp(nf4, st)
+        if sampled:
+            cnt += timer.disarm()
+    e1.record()
+    torch.cuda.synchronize()
+    durs = timer.durations_ms(cnt)
+    timer.close()
+    if cnt != nl * nsampled or any(k != MLP_LAUNCHES[i % nl][1] for i, (k, _) in enumerate(durs)):
+        raise RuntimeError(f"unexpected GEMM launch sequence: {[k for k, _ in durs]}")
+    ms = e0.elapsed_time(e1) / steps
+    flops = mlp_flops(M, F, K, r)
+    lf = mlp_launch_flops(M, F, K, r)
+    kernels = {}
+    for i, (name, _) in enumerate(MLP_LAUNCHES):
+        us = sum(d for j, (_, d) in enumerate(durs) if j % nl == i) / nsampled * 1e3
+        kernels[name] = {"us": round(us, 2), "TFLOP/s": round(lf[i] / us / 1e6, 1),
+                         "frac": round(lf[i] / us / 1e6 / BF16_PEAK_TFLOPS, 4), "flops": lf[i]}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    value = flops / (ms * 1e-3) / 1e12
+    del st
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{wl.name}: {wl.notes}; gate/up W {F}x{K}, down W {K}x{F}, NF4 (block 64, double-quant "
+                    f"block 256), {M} tokens, LoRA r={r} alpha={wl.alpha:g} on all three, forward + backward",
+        "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4), "steps": steps,
+        "flops_per_step": flops, "step_frac": round(value / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": kernels[dom]["frac"], "traffic": None,
+                     "kernel": dom, "avg_launch_us": kernels[dom]["us"], "launches_timed": nsampled},
+        "gemm_launches": kernels,
+    }
+
+
+def quantize_bytes(numel):
+    """Algorithmic HBM bytes of quantize + double quant of one float32 weight: W read (4 B), codes
+    (0.5 B) and block constants (4/64 B) written; the constants read back (4/64 B), their 8-bit codes
+    (1/64 B), second-level scales and the mean written."""
+    nb = numel // 64
+    return 4 * numel + numel // 2 + 4 * nb + 4 * nb + nb + 4 * ((nb + 255) // 256) + 4
+
+
+def bench_quantize(torch, nf4, synth, dev, wl, reps=5):
+    """Quantize + double-quantize every weight of a workload from float32 in HBM, GB/s."""
+    import ctypes
+    import numpy as np
+    cb = nf4.nf4_build_codebook()
+    cbp = ctypes.c_void_p(cb.ctypes.data)
+    bufs = []
+    for lin in wl.linears:
+        n = lin.N * lin.K
+        nb = n // 64
+        wsb = nf4.lib.nf4_double_quant_workspace_size(nb, 256)
+        bufs.append({
+            "W": torch.from_numpy(synth.weight_f32(wl, lin)).to(dev).reshape(-1), "n": n, "nb": nb,
+            "packed": torch.empty(n // 2, dtype=torch.uint8, device=dev),
+            "absmax": torch.empty(nb, dtype=torch.float32, device=dev),
+            "q": torch.empty(nb, dtype=torch.uint8, device=dev),
+            "sc": torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev),
+            "mean": torch.empty(1, dtype=torch.float32, device=dev),
+            "ws": torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev), "wsb": wsb})
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def run():
+        for b in bufs:
+            nf4._check(nf4.lib.nf4_quantize(p(b["W"]), b["n"], 64, cbp, p(b["packed"]), p(b["absmax"]), stream),
+                       "nf4_quantize")
+            nf4._check(nf4.lib.nf4_double_quant(p(b["absmax"]), b["nb"], 256, p(b["q"]), p(b["sc"]), p(b["mean"]),
+                                                p(b["ws"]), b["wsb"], stream), "nf4_double_quant")
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = sum(quantize_bytes(b["n"]) for b in bufs)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"workload": f"quantize + double quant of the {len(wl.linears)} float32 weights of {wl.name} "
+                        f"({' + '.join(f'{l.N}x{l.K}' for l in wl.linears)})",
+            "us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+            "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def qerror_gpu(torch, nf4, W, cb, dq=True, dq_format="e4m3"):
@@ -303,6 +488,7 @@ def main():
     ap.add_argument("--workload", default="llama7b_attn")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the two MLP workloads (c3, c4 keys)")
     ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
     ap.add_argument("--qerror", action="store_true",
                     help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
@@ -350,7 +536,13 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     if wl.swiglu:
-        raise SystemExit("MLP workloads are measured by their own script path; use llama7b_attn")
+        # an MLP workload on its own line (the default run carries both MLP workloads as extra keys)
+        line = bench_mlp(torch, nf4, synth, dev, wl, steps=args.steps, warmup=args.warmup)
+        if wl.name == "llama65b_mlp":
+            line["quantize"] = bench_quantize(torch, nf4, synth, dev, wl)
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "dtype": "bf16", "data": "synthetic", **line}),
+              flush=True)
+        return
     lin = wl.linears[0]
     M, N, K, r = wl.M, lin.N, lin.K, wl.r
     print(f"[bench] workload {wl.name}: M={M} N={N} K={K} r={r}", file=sys.stderr, flush=True)
@@ -406,18 +598,29 @@ def main():
         "avg_launch_us": round(means[dom] * 1e3, 2),
         "flops_per_launch": flops_launch,
         "launches_timed": len(per_kind[dom]),
+        "step_frac": round(value / BF16_PEAK_TFLOPS, 4),
         "other_gemm_avg_us": {("bwd" if k == 1 else "fwd"): round(v * 1e3, 2) for k, v in means.items()},
     }
     print(f"[bench] dominant kernel: {roofline['kernel']} {roofline['avg_launch_us']} us, "
           f"{roofline['achieved']} TFLOP/s ({roofline['frac'] * 100:.1f}% of peak)", file=sys.stderr,
           flush=True)
 
+    del st
+    torch.cuda.empty_cache()
     gemv = None
     if not args.no_gemv:
-        del st
-        torch.cuda.empty_cache()
         gemv = bench_gemv(torch, nf4, synth, dev)
         print(f"[bench] gemv {gemv}", file=sys.stderr, flush=True)
+
+    mlp = {}
+    if not args.no_mlp:
+        for key, name in (("c3", "llama7b_mlp"), ("c4", "llama65b_mlp")):
+            mlp[key] = bench_mlp(torch, nf4, synth, dev, synth.WORKLOADS[name])
+            print(f"[bench] {key} {name}: {mlp[key]['value']} TFLOP/s, {mlp[key]['ms_per_step']} ms/step; "
+                  f"dominant {mlp[key]['roofline']['kernel']} {mlp[key]['roofline']['avg_launch_us']} us",
+                  file=sys.stderr, flush=True)
+        mlp["c4"]["quantize"] = bench_quantize(torch, nf4, synth, dev, synth.WORKLOADS["llama65b_mlp"])
+        print(f"[bench] c4 quantize {mlp['c4']['quantize']}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -447,6 +650,7 @@ def main():
     if gemv is not None:
         line["gemv"] = {"workload": "W 28672x8192 NF4 forward with LoRA r=64, weights rotated over 3 replicas",
                         **gemv}
+    line.update(mlp)
     print(json.dumps(line), flush=True)
 
 

@@ -459,8 +459,11 @@ hipError_t launch_gemm_bf16_gated(const uint16_t *X, const uint16_t *Wgu, const 
     a.Ae2 = sTu; a.Be2 = L2u; a.G = G; a.U = U;
     const int ntm = (int)((M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
+    timing_before(stream, 3);
     hipLaunchKernelGGL(gemm_bf16_gated_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    timing_after(stream);
+    return e;
 }
 
 hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,
@@ -473,8 +476,11 @@ hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, c
     a.M = M; a.Nout = K; a.Kred = F; a.r = r; a.accumulate = accumulate ? 1u : 0u;
     const int ntm = (int)((M + TM - 1) / TM);
     const int ntn = (int)((K + TN - 1) / TN);
+    timing_before(stream, 4);
     hipLaunchKernelGGL(gemm_bf16_dual_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    timing_after(stream);
+    return e;
 }
 
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,

@@ -348,10 +348,26 @@ def backward(dY, X, Wdq, L1, L2, s: float):
 
 
 def forward_rows(X, Wdq, L1, L2, s: float, rows):
-    """Forward for a subset of token rows only (full-size spot checks)."""
+    """Forward for a subset of token rows only (full-size spot checks): each output row depends
+    on its own token row alone."""
     X = _f64(np.asarray(X)[rows])
     Y, T = forward(X, Wdq, L1, L2, s)
     return Y, T
+
+
+def backward_rows(dY, X, Wdq, L1, L2, s: float, rows=None):
+    """``backward`` for full-size spot checks: the adapter gradients dL1 and dL2 sum over every
+    token, so they take all rows; dX row i depends on dY row i alone (through dT row i), so it is
+    evaluated on ``rows`` only (all rows when None).  Same formulas and order as ``backward``."""
+    dY, X, L1, L2 = _f64(dY), _f64(X), _f64(L1), _f64(L2)
+    s = float(s)
+    T = X @ L1
+    dT = s * (dY @ L2.T)
+    dL2 = s * (T.T @ dY)
+    dL1 = X.T @ dT
+    sel = slice(None) if rows is None else rows
+    dX = dY[sel] @ _f64(Wdq) + dT[sel] @ L1.T
+    return {"dX": dX, "dL1": dL1, "dL2": dL2, "dT": dT, "T": T}
 
 
 # ------------------------------------------------------------------------------------------

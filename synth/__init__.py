@@ -24,6 +24,7 @@ _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 _CHUNK = 1 << 22
+_THREADS = max(1, min(16, (__import__('os').cpu_count() or 1)))
 
 
 def _splitmix64(seed: int, start: int, count: int) -> np.ndarray:
@@ -36,12 +37,27 @@ def _splitmix64(seed: int, start: int, count: int) -> np.ndarray:
     return z ^ (z >> np.uint64(31))
 
 
+def _chunks(n: int, chunk: int, fn) -> None:
+    """Run fn(c0, c) over [0, n) in pieces of ``chunk``; pieces are independent (every element is
+    a function of its index), so they run on a thread pool (numpy releases the GIL)."""
+    starts = list(range(0, n, chunk))
+    if len(starts) <= 1:
+        for c0 in starts:
+            fn(c0, min(chunk, n - c0))
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(_THREADS, len(starts))) as ex:
+        list(ex.map(lambda c0: fn(c0, min(chunk, n - c0)), starts))
+
+
+def _uniform_into(out: np.ndarray, seed: int, start: int, c0: int, c: int) -> None:
+    out[c0:c0 + c] = (_splitmix64(seed, start + c0, c) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
 def uniform(seed: int, n: int, start: int = 0) -> np.ndarray:
     """``n`` doubles in [0, 1) from stream ``seed``."""
     out = np.empty(n, dtype=np.float64)
-    for c0 in range(0, n, _CHUNK):
-        c = min(_CHUNK, n - c0)
-        out[c0:c0 + c] = (_splitmix64(seed, start + c0, c) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    _chunks(n, _CHUNK, lambda c0, c: _uniform_into(out, seed, start, c0, c))
     return out
 
 
@@ -49,10 +65,10 @@ def normal(seed: int, n: int) -> np.ndarray:
     """``n`` standard normal doubles (Box-Muller over word pairs 2j, 2j+1)."""
     out = np.empty(n, dtype=np.float64)
     pairs = (n + 1) // 2
-    step = _CHUNK // 2
-    for p0 in range(0, pairs, step):
-        p = min(step, pairs - p0)
-        u = uniform(seed, 2 * p, start=2 * p0)
+
+    def piece(p0: int, p: int) -> None:
+        u = np.empty(2 * p, dtype=np.float64)
+        _uniform_into(u, seed, 2 * p0, 0, 2 * p)
         r = np.sqrt(-2.0 * np.log1p(-u[0::2]))   # 1 - u1 lies in (0, 1]
         th = (2.0 * math.pi) * u[1::2]
         z = np.empty(2 * p, dtype=np.float64)
@@ -61,6 +77,8 @@ def normal(seed: int, n: int) -> np.ndarray:
         lo = 2 * p0
         hi = min(n, lo + 2 * p)
         out[lo:hi] = z[:hi - lo]
+
+    _chunks(pairs, _CHUNK // 2, piece)
     return out
 
 

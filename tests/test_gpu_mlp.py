@@ -1,12 +1,14 @@
-"""GPU parity of the MLP workloads: the LLaMA-7B MLP chain and the heavy-tailed 65B MLP layer.
+"""GPU parity of the MLP workloads: the LLaMA-7B MLP chain and the heavy-tailed LLaMA-65B-shaped
+MLP chain, plus the gated forms (gate and up as one product).
 
-The chain is gate and up (QLoRA linears) -> SwiGLU -> down (QLoRA linear), forward and backward,
+A chain is gate and up (QLoRA linears) -> SwiGLU -> down (QLoRA linear), forward and backward,
 run through the C ABI exactly as a caller would, with dX of gate and up accumulated into one
 buffer.  Each stage is checked against the float64 oracle on the GPU's own bf16 inputs to that
 stage (so an error cannot hide behind the next stage's rounding): token rows are sampled for the
-[M, N] outputs, the adapter gradients are checked in full.  Tolerances: rel-Frobenius <= 5e-3 and
-max-abs <= 2e-2 * max|ref|.  The 65B layer adds a bit-exact check of quantize, double quant and
-dequant on a heavy-tailed weight (1 % of the entries from a ten times wider normal).
+[M, N] outputs (oracle.forward_rows / oracle.backward_rows), the adapter gradients are checked in
+full.  Tolerances: rel-Frobenius <= 5e-3 and max-abs <= 2e-2 * max|ref|.  The 65B chain adds a
+bit-exact check of quantize, double quant and dequant of its three heavy-tailed weights (1 % of
+the entries from a ten times wider normal).
 """
 import numpy as np
 import pytest
@@ -50,17 +52,41 @@ def check_tol(name, got, ref):
 
 
 class Layer:
-    """One QLoRA linear of a workload: device NF4 weight + adapters, and the oracle's bf16 deq(W)."""
+    """One QLoRA linear of a workload: device NF4 weight + adapters, and the oracle's pieces
+    (quantized storage and the bf16 deq(W))."""
 
-    def __init__(self, wl, lin):
-        W = synth.weight_f32(wl, lin)
+    def __init__(self, wl, lin, W, q, Wd):
         l1, l2 = synth.lora_f32(wl, lin)
         self.L1, self.L2 = synth.to_bf16_bits(l1), synth.to_bf16_bits(l2)
         self.w = nf4.NF4Weight.from_float(torch.from_numpy(W).to(DEV), CB)
-        self.q = oracle.quantize_dq(W, CB)
-        self.Wd = oracle.dequant_weight(self.q, CB)        # bf16 bits [N, K]
+        self.q, self.Wd = q, Wd                            # Wd: bf16 bits [N, K]
         self.dL1d, self.dL2d = d16(self.L1), d16(self.L2)
-        self.N, self.K = lin.N, lin.K
+        self.N, self.K, self.name = lin.N, lin.K, lin.name
+
+    def check_storage(self):
+        """Packed codes, second-level codes and scales, the mean and deq(W): bit for bit."""
+        w = self.w
+        assert np.array_equal(w.packed.cpu().numpy(), self.q["packed"]), self.name
+        assert np.array_equal(w.absmax_q.cpu().numpy(), self.q["codes"]), self.name
+        assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), self.q["scales"].view(np.uint32))
+        assert np.array_equal(w.absmax_mean.cpu().numpy().view(np.uint32),
+                              np.asarray([self.q["mean"]], np.float32).view(np.uint32)), self.name
+        assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(self.Wd.shape), self.Wd), self.name
+
+
+def _layers(wl):
+    """The workload's linears; the oracle's quantization of the three weights runs on a thread
+    pool (its C code releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def prep(lin):
+        W = synth.weight_f32(wl, lin)
+        q = oracle.quantize_dq(W, CB)
+        return lin, W, q, oracle.dequant_weight(q, CB)
+
+    with ThreadPoolExecutor(len(wl.linears)) as ex:
+        preps = list(ex.map(prep, wl.linears))
+    return [Layer(wl, *p) for p in preps]
 
 
 def _rows(M, n=32, seed=11):
@@ -68,30 +94,36 @@ def _rows(M, n=32, seed=11):
     return np.unique(np.concatenate([r, [0, M - 1]]))
 
 
+def to64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
 def _check_fwd(name, layer, Xbits, Ygpu, s, rows):
-    Yr, _ = oracle.forward(Xbits[rows], layer.Wd, layer.L1, layer.L2, s)
-    check_tol(f"{name} Y[rows]", Ygpu[rows].astype(np.float64), Yr)
+    Yr, _ = oracle.forward_rows(Xbits, layer.Wd, layer.L1, layer.L2, s, rows)
+    check_tol(f"{name} Y[rows]", Ygpu[rows], Yr)
 
 
 def _check_bwd(name, layer, dYbits, Xbits, dXgpu, dL1gpu, dL2gpu, s, rows):
-    """dX on sampled rows, dL1 and dL2 in full (they reduce over every token)."""
-    X, dY = f64(Xbits), f64(dYbits)
-    L1, L2 = f64(layer.L1), f64(layer.L2)
-    T = X @ L1
-    dT = s * (dY @ L2.T)
-    check_tol(f"{name} dL2", dL2gpu, s * (T.T @ dY))
-    check_tol(f"{name} dL1", dL1gpu, X.T @ dT)
+    """dL1 and dL2 in full (they reduce over every token), dX on sampled rows; returns the oracle's
+    gradients (dX on those rows)."""
+    g = oracle.backward_rows(dYbits, Xbits, layer.Wd, layer.L1, layer.L2, s, rows)
+    check_tol(f"{name} dL2", dL2gpu, g["dL2"])
+    check_tol(f"{name} dL1", dL1gpu, g["dL1"])
     if dXgpu is not None:
-        dXr = dY[rows] @ f64(layer.Wd) + dT[rows] @ L1.T
-        check_tol(f"{name} dX[rows]", dXgpu[rows], dXr)
+        check_tol(f"{name} dX[rows]", dXgpu[rows], g["dX"])
+    return g
 
 
-def test_llama7b_mlp_chain():
-    """C3: gate, up (11008 x 4096), SwiGLU, down (4096 x 11008); 4096 tokens, r = 64."""
-    wl = synth.WORKLOADS["llama7b_mlp"]
+def _mlp_chain(wl, check_storage):
+    """gate and up (QLoRA linears) -> SwiGLU -> down (QLoRA linear), forward and backward, with dX
+    of gate and up accumulated into one buffer; every stage checked against the oracle on the
+    GPU's own bf16 inputs to that stage."""
     M, s = wl.M, wl.scale
-    gate, up, down = (Layer(wl, lin) for lin in wl.linears)
-    _say(f"{wl.name}: M={M}, gate/up {gate.N}x{gate.K}, down {down.N}x{down.K}")
+    gate, up, down = _layers(wl)
+    _say(f"{wl.name}: M={M}, gate/up {gate.N}x{gate.K}, down {down.N}x{down.K}, r={wl.r}")
+    if check_storage:
+        for layer in (gate, up, down):
+            layer.check_storage()
     X = synth.to_bf16_bits(synth.x_f32(wl, M=M, K=gate.K))
     dY = synth.to_bf16_bits(synth.dy_f32(wl, M, down.N))
     Xd, dYd = d16(X), d16(dY)
@@ -109,7 +141,6 @@ def test_llama7b_mlp_chain():
 
     rows = _rows(M)
     Gb, Ub, Hb, dHb, dGb, dUb = (h16(t) for t in (G, U, H, dH, dG, dU))
-    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     _check_fwd("gate", gate, X, to64(G), s, rows)
     _check_fwd("up", up, X, to64(U), s, rows)
     check_tol("swiglu h[rows]", to64(H)[rows], oracle.swiglu_fwd(Gb[rows], Ub[rows]))
@@ -119,42 +150,21 @@ def test_llama7b_mlp_chain():
     check_tol("swiglu dg[rows]", to64(dG)[rows], rg)
     check_tol("swiglu du[rows]", to64(dU)[rows], ru)
     # gate and up adapters in full; dX = both branches summed
-    _check_bwd("gate", gate, dGb, X, None, to64(dL1_gate), to64(dL2_gate), s, rows)
-    _check_bwd("up", up, dUb, X, None, to64(dL1_up), to64(dL2_up), s, rows)
-    dX_ref = 0.0
-    for layer, dYb in ((gate, dGb), (up, dUb)):
-        dYl = f64(dYb)
-        dT = s * (dYl[rows] @ f64(layer.L2).T)
-        dX_ref = dX_ref + dYl[rows] @ f64(layer.Wd) + dT @ f64(layer.L1).T
-    check_tol("dX[rows] (gate + up)", to64(dX)[rows], dX_ref)
+    gg = _check_bwd("gate", gate, dGb, X, None, to64(dL1_gate), to64(dL2_gate), s, rows)
+    gu = _check_bwd("up", up, dUb, X, None, to64(dL1_up), to64(dL2_up), s, rows)
+    check_tol("dX[rows] (gate + up)", to64(dX)[rows], gg["dX"] + gu["dX"])
 
 
-def test_llama65b_heavy_tail_layer():
-    """C4 gate (22016 x 8192, 1 % heavy-tailed entries): storage bit-exact, then one layer's
-    forward and backward on 2048 tokens."""
-    wl = synth.WORKLOADS["llama65b_mlp"]
-    lin = wl.linears[0]
-    M, s = wl.M, wl.scale
-    _say(f"{wl.name} {lin.name}: {lin.N}x{lin.K}, M={M}")
-    layer = Layer(wl, lin)
-    w = layer.w
-    assert np.array_equal(w.packed.cpu().numpy(), layer.q["packed"])
-    assert np.array_equal(w.absmax_q.cpu().numpy(), layer.q["codes"])
-    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), layer.q["scales"].view(np.uint32))
-    assert np.array_equal(w.absmax_mean.cpu().numpy().view(np.uint32),
-                          np.asarray([layer.q["mean"]], np.float32).view(np.uint32))
-    assert np.array_equal(h16(nf4.nf4_dequant(w)).reshape(layer.Wd.shape), layer.Wd)
+def test_llama7b_mlp_chain():
+    """LLaMA-7B MLP: gate, up (11008 x 4096), SwiGLU, down (4096 x 11008); 4096 tokens, r = 64."""
+    _mlp_chain(synth.WORKLOADS["llama7b_mlp"], check_storage=False)
 
-    X = synth.to_bf16_bits(synth.x_f32(wl, M=M, K=lin.K))
-    dY = synth.to_bf16_bits(synth.dy_f32(wl, M, lin.N))
-    Xd, dYd = d16(X), d16(dY)
-    Y, T = nf4.qlora_linear_fwd(w, Xd, layer.dL1d, layer.dL2d, s)
-    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, layer.dL1d, layer.dL2d, T, s)
-    torch.cuda.synchronize()
-    rows = _rows(M)
-    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    _check_fwd(lin.name, layer, X, to64(Y), s, rows)
-    _check_bwd(lin.name, layer, dY, X, to64(dX), to64(dL1), to64(dL2), s, rows)
+
+def test_llama65b_mlp_chain():
+    """LLaMA-65B-shaped MLP with 1 % heavy-tailed weight entries: gate, up (22016 x 8192), SwiGLU,
+    down (8192 x 22016, the longest reduction on the expanded-weight GEMMs); 2048 tokens, r = 64.
+    The storage of all three weights (codes, constants, mean, deq(W)) is checked bit for bit."""
+    _mlp_chain(synth.WORKLOADS["llama65b_mlp"], check_storage=True)
 
 
 # ------------------------------------------------------------------------------------------
@@ -196,7 +206,6 @@ def test_gated_fwd_matches_separate_calls_and_oracle(M, F, K, r):
     Wuq = oracle.dequant_weight(oracle.quantize_dq(Wu, CB), CB)
     Gr, _ = oracle.forward(X, Wgq, ad[0], ad[1], s)
     Ur, _ = oracle.forward(X, Wuq, ad[2], ad[3], s)
-    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     check_tol("G", to64(G), Gr)
     check_tol("U", to64(U), Ur)
     check_tol("H", to64(H), oracle.swiglu_fwd(h16(G), h16(U)))
@@ -246,7 +255,6 @@ def test_gated_bwd_fused_and_composed(M, F, K, r):
     Wuq = oracle.dequant_weight(oracle.quantize_dq(Wu, CB), CB)
     gg = oracle.backward(dGb, X, Wgq, ad[0], ad[1], s)
     gu = oracle.backward(dUb, X, Wuq, ad[2], ad[3], s)
-    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     dX_ref = gg["dX"] + gu["dX"]
     check_tol("dX fused", to64(fused[0]), dX_ref)
     check_tol("dX composed", to64(comp[0]), dX_ref)

@@ -642,6 +642,24 @@ def test_backward_matches_torch_autograd():
         assert np.allclose(g[name], t.grad.numpy(), rtol=1e-12, atol=1e-13), name
 
 
+def test_backward_rows_matches_autograd_on_a_row_subset():
+    """The full-size spot-check form: adapter gradients over every token, dX on chosen rows only,
+    against torch float64 autograd of the whole layer."""
+    wl, Wd, L1, L2, X, dY = _tiny()
+    s = wl.scale
+    rows = np.array([0, 3, 7])
+    g = oracle.backward_rows(dY, X, Wd, L1, L2, s, rows)
+    x = _t64(X).requires_grad_(True)
+    l1 = _t64(L1).requires_grad_(True)
+    l2 = _t64(L2).requires_grad_(True)
+    y = x @ _t64(Wd).T + s * (x @ l1) @ l2
+    (y * _t64(dY)).sum().backward()
+    assert np.allclose(g["dX"], x.grad.numpy()[rows], rtol=1e-12, atol=1e-13)
+    assert np.allclose(g["dL1"], l1.grad.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(g["dL2"], l2.grad.numpy(), rtol=1e-12, atol=1e-13)
+    assert g["dX"].shape == (rows.size, X.shape[1])
+
+
 def test_backward_finite_differences():
     wl, Wd, L1, L2, X, dY = _tiny()
     s = wl.scale
