@@ -240,7 +240,7 @@ void timing_after(hipStream_t stream) {
 }
 }  // namespace nf4k
 
-extern "C" {
+// Entry points: their declarations in nf4.h give them C linkage.
 
 int nf4_set_gemm_timing_events(void **begin, void **end, int32_t *kinds, int32_t n) {
     if (n < 0) return fail(NF4_ERR_ARG, "n must be >= 0");
@@ -341,8 +341,8 @@ int double_quant_impl(const float *absmax, int64_t nblocks, int32_t dq_block, ui
     if (dq_block != 256) return fail(NF4_ERR_UNSUPPORTED, "dq_block must be 256");
     if (!absmax || !absmax_q || !absmax_scale || !absmax_mean || !workspace)
         return fail(NF4_ERR_NULL, "double quant pointers must be non-NULL");
-    if (!aligned16(absmax_q) || !aligned16(workspace))
-        return fail(NF4_ERR_ALIGN, "absmax_q and workspace must be 16-byte aligned");
+    if (!aligned16(absmax) || !aligned16(absmax_q) || !aligned16(workspace))
+        return fail(NF4_ERR_ALIGN, "absmax, absmax_q and workspace must be 16-byte aligned");
     if (workspace_bytes < nf4k::double_quant_ws(nblocks))
         return fail(NF4_ERR_WORKSPACE, "double quant workspace too small");
     NF4_CHECK_HIP(nf4k::launch_double_quant(absmax, nblocks, absmax_q, absmax_scale, absmax_mean,
@@ -714,4 +714,3 @@ int qlora_swiglu_bwd(const uint16_t *dh, const uint16_t *g, const uint16_t *u, u
     return NF4_OK;
 }
 
-}  // extern "C"

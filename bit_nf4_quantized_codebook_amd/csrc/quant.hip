@@ -12,9 +12,12 @@
 namespace nf4k {
 
 // ------------------------------------------------------------------------------------------
-// Level 1: one 64-block per group of 8 lanes; each lane owns 8 consecutive elements.
-// Code = number of decision thresholds strictly below n, where thr[j] is the largest float
-// not above the midpoint of codewords j and j+1 (so ties go to the lower index).
+// Level 1.  A wave takes 8 consecutive 64-blocks (512 floats) per iteration with two fully
+// contiguous 1 KB loads: lane l reads elements 256 q + 4 l .. +3 (q = 0, 1), so block 4 q + l / 16
+// is held by 16 lanes, 4 elements each, and its absmax is a 16-lane max.  Code = number of
+// decision thresholds strictly below n, where thr[j] is the largest float not above the midpoint
+// of codewords j and j+1 (so ties go to the lower index).  Each lane writes its 4 codes as 2 bytes
+// (128 contiguous bytes per wave and q).
 // ------------------------------------------------------------------------------------------
 struct Thresholds {
     float t[15];
@@ -31,82 +34,136 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
                                                        Thresholds th, uint32_t zero_code,
                                                        uint8_t *__restrict__ packed,
                                                        float *__restrict__ absmax) {
-    const int lane8 = threadIdx.x & 7;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
     const int64_t nblocks = (numel + 63) >> 6;
-    const int64_t groups_per_grid = (int64_t)gridDim.x * (blockDim.x >> 3);
-    for (int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 3) + (threadIdx.x >> 3); b < nblocks;
-         b += groups_per_grid) {
-        const int64_t e0 = (b << 6) + lane8 * 8;
-        float x[8];
-        const bool full_block = ((b + 1) << 6) <= numel;
-        if (full_block) {
-            typedef float f4 __attribute__((ext_vector_type(4)));
-            const f4 *p = reinterpret_cast<const f4 *>(W + e0);
-            f4 v0 = __builtin_nontemporal_load(p);
-            f4 v1 = __builtin_nontemporal_load(p + 1);
-            x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-            x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-        } else {
+    const int64_t nchunks = (numel + 511) >> 9;                      // 512-element wave chunks
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t nbytes = (numel + 1) >> 1;
+    for (int64_t ch = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); ch < nchunks; ch += waves) {
+        const int64_t base = ch << 9;
+        const bool full = base + 512 <= numel;
+        float x[2][4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = (e0 + i < numel) ? W[e0 + i] : 0.0f;
+        for (int q = 0; q < 2; ++q) {
+            const int64_t e0 = base + 256 * q + 4 * lane;
+            if (full) {
+                const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(W + e0));
+                x[q][0] = v.x; x[q][1] = v.y; x[q][2] = v.z; x[q][3] = v.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[q][i] = (e0 + i < numel) ? W[e0 + i] : 0.0f;
+            }
         }
-        float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-        a = fmaxf(a, __shfl_xor(a, 1, 8));
-        a = fmaxf(a, __shfl_xor(a, 2, 8));
-        a = fmaxf(a, __shfl_xor(a, 4, 8));
-        uint32_t word = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t c = zero_code;
-            if (a != 0.0f) c = nearest_code(x[i] / a, th);
-            if (e0 + i >= numel) c = zero_code;
-            word |= c << (4 * i);
-        }
-        if (lane8 == 0) absmax[b] = a;
-        if (full_block) {
-            reinterpret_cast<uint32_t *>(packed)[e0 >> 3] = word;
-        } else {
-            const int64_t nbytes = (numel + 1) >> 1;
+        for (int q = 0; q < 2; ++q) {
+            const int64_t e0 = base + 256 * q + 4 * lane;
+            const int64_t b = e0 >> 6;
+            float a = fmaxf(fmaxf(fabsf(x[q][0]), fabsf(x[q][1])), fmaxf(fabsf(x[q][2]), fabsf(x[q][3])));
+            a = fmaxf(a, __shfl_xor(a, 1, 16));
+            a = fmaxf(a, __shfl_xor(a, 2, 16));
+            a = fmaxf(a, __shfl_xor(a, 4, 16));
+            a = fmaxf(a, __shfl_xor(a, 8, 16));
+            uint32_t word = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t byte = (e0 >> 1) + i;
-                if (byte < nbytes) packed[byte] = (uint8_t)(word >> (8 * i));
+                uint32_t c = zero_code;
+                if (a != 0.0f) c = nearest_code(x[q][i] / a, th);
+                if (e0 + i >= numel) c = zero_code;
+                word |= c << (4 * i);
+            }
+            if ((lane & 15) == 0 && b < nblocks) absmax[b] = a;
+            const int64_t byte = e0 >> 1;
+            if (full) {
+                *reinterpret_cast<uint16_t *>(packed + byte) = (uint16_t)word;
+            } else {
+                if (byte < nbytes) packed[byte] = (uint8_t)word;
+                if (byte + 1 < nbytes) packed[byte + 1] = (uint8_t)(word >> 8);
             }
         }
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Double quantization, phase 1: float64 sums of groups of 256 consecutive values, each summed
-// sequentially in ascending order.  One wave per 64 groups: the wave stages its groups through
-// LDS with coalesced loads, then each lane runs the sequential sum of one group.
+// Double quantization, phase 1: the float64 sum behind the mean, taken as a 256-ary tree (groups
+// of 256 consecutive values, each summed sequentially in ascending order, level after level).
+// group_sum_kernel: one level, 64 groups per workgroup.  Its four waves stage the groups in LDS
+// with coalesced 16-byte loads (rows padded to 257 elements, so that lane i reading element k of
+// row i hits bank (i + k) mod 64), then one wave runs the 64 sequential sums, a group per lane.
 // ------------------------------------------------------------------------------------------
 template <typename Tin>
-__global__ __launch_bounds__(64) void group_sum_kernel(const Tin *__restrict__ in, int64_t n,
-                                                       double *__restrict__ out) {
-    __shared__ Tin tile[64][257];
-    const int lane = threadIdx.x;
-    const int64_t g0 = (int64_t)blockIdx.x * 64;
-    const int64_t ngroups = (n + 255) >> 8;
-    for (int g = 0; g < 64; ++g) {
-        const int64_t base = (g0 + g) << 8;
+__global__ __launch_bounds__(256) void group_sum_kernel(const Tin *__restrict__ in, int64_t n,
+                                                        double *__restrict__ out) {
+    constexpr int ROW = 257;
+    constexpr int PER16 = 16 / (int)sizeof(Tin);            // elements per 16-byte load
+    __shared__ Tin tile[64 * ROW];
+    const int tid = threadIdx.x;
+    const int64_t e0 = (int64_t)blockIdx.x * (64 * 256);     // first element of the workgroup
+    typedef Tin v16 __attribute__((ext_vector_type(PER16)));
+    constexpr int LOADS = 64 * 256 / (256 * PER16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t idx = base + i * 64 + lane;
-            tile[g][i * 64 + lane] = (idx < n) ? in[idx] : (Tin)0;
+    for (int q = 0; q < LOADS; ++q) {
+        const int e = (q * 256 + tid) * PER16;                // element within the workgroup's run
+        Tin v[PER16];
+        if (e0 + e + PER16 <= n) {
+            const v16 x = *reinterpret_cast<const v16 *>(in + e0 + e);
+#pragma unroll
+            for (int k = 0; k < PER16; ++k) v[k] = x[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < PER16; ++k) v[k] = (e0 + e + k < n) ? in[e0 + e + k] : (Tin)0;
         }
+#pragma unroll
+        for (int k = 0; k < PER16; ++k) tile[((e + k) >> 8) * ROW + ((e + k) & 255)] = v[k];
     }
     __syncthreads();
-    const int64_t g = g0 + lane;
-    if (g < ngroups) {
-        const int64_t base = g << 8;
-        const int cnt = (int)((n - base) < 256 ? (n - base) : 256);
-        double s = 0.0;
-        for (int i = 0; i < cnt; ++i) s += (double)tile[lane][i];
-        out[g] = s;
+    if (tid >= 64) return;
+    const int64_t g = (int64_t)blockIdx.x * 64 + tid;
+    const int64_t base = g << 8;
+    if (base >= n) return;
+    const int cnt = (int)((n - base) < 256 ? (n - base) : 256);
+    const Tin *row = tile + tid * ROW;
+    double s = 0.0;
+    if (cnt == 256) {
+#pragma unroll 16
+        for (int i = 0; i < 256; ++i) s += (double)row[i];
+    } else {
+        for (int i = 0; i < cnt; ++i) s += (double)row[i];
     }
+    out[g] = s;
+}
+
+// The last levels in one workgroup: up to TAIL_MAX float64 values are staged in LDS (one pad slot
+// per 256, so lanes summing neighbouring groups fall on different banks), then each level's
+// groups are summed sequentially, a group per lane, until one value is left.
+constexpr int TAIL_MAX = 16384;
+__global__ __launch_bounds__(1024) void group_sum_tail_kernel(const double *__restrict__ in, int64_t n,
+                                                              double *__restrict__ total) {
+    __shared__ double v[TAIL_MAX + TAIL_MAX / 256];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < (int)n; e += 1024) v[e + (e >> 8)] = in[e];
+    __syncthreads();
+    int len = (int)n;
+    while (len > 1) {
+        const int ng = (len + 255) >> 8;
+        double s = 0.0;
+        if (tid < ng) {
+            // group tid: values 256 tid .. , stored from 257 tid (one pad slot per 256 before it)
+            const double *g = v + 257 * tid;
+            const int cnt = (len - 256 * tid) < 256 ? (len - 256 * tid) : 256;
+            if (cnt == 256) {
+#pragma unroll 16
+                for (int i = 0; i < 256; ++i) s += g[i];
+            } else {
+                for (int i = 0; i < cnt; ++i) s += g[i];
+            }
+        }
+        __syncthreads();
+        if (tid < ng) v[tid + (tid >> 8)] = s;       // value tid of the next level
+        __syncthreads();
+        len = ng;
+    }
+    if (tid == 0) total[0] = v[0];
 }
 
 // Phase 2: per 256-block of constants, centre by the mean, scale by max|y|/448 and encode E4M3
@@ -222,47 +279,57 @@ hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], u
     if (numel == 0) return hipSuccess;
     Thresholds th;
     for (int j = 0; j < 15; ++j) th.t[j] = thr[j];
-    const int64_t nblocks = (numel + 63) >> 6;
-    const int grid = grid_for(nblocks, 32, 256 * 64);
+    const int64_t nchunks = (numel + 511) >> 9;
+    const int grid = grid_for(nchunks, 4, 256 * 32);
     hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(256), 0, stream, W, numel, th, zero_code,
                        packed, absmax);
     return hipGetLastError();
 }
 
+// Level arrays of the tree sum, back to back, each padded to an even length so that every array
+// starts 16-byte aligned (its kernel reads it with 16-byte loads); the total follows the last one.
+static int64_t padded(int64_t len) { return (len + 1) & ~(int64_t)1; }
+
 size_t double_quant_ws(int64_t nb) {
-    // one float64 per 256-group at each level, levels laid out back to back
+    // one float64 per 256-group at each level
     int64_t len = (nb + 255) / 256;
-    size_t total = (size_t)len;
+    size_t total = (size_t)padded(len);
     while (len > 1) {
         len = (len + 255) / 256;
-        total += (size_t)len;
+        total += (size_t)padded(len);
     }
-    return (total + 1) * sizeof(double);
+    return (total + 2) * sizeof(double);
 }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, float *scales,
                                float *mean, void *ws, bool int8, hipStream_t stream) {
     double *buf = reinterpret_cast<double *>(ws);
     double *level = buf;
-    // level 0: floats -> doubles
+    // level 1: floats -> float64 group sums
     int64_t len = (nb + 255) / 256;
-    hipLaunchKernelGGL(group_sum_kernel<float>, dim3(grid_for(len, 64, 1 << 30)), dim3(64), 0,
+    hipLaunchKernelGGL(group_sum_kernel<float>, dim3(grid_for(len, 64, 1 << 30)), dim3(256), 0,
                        stream, absmax, nb, level);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    while (len > 1) {
-        double *next = level + len;
+    // middle levels while more than one workgroup's LDS holds
+    while (len > TAIL_MAX) {
+        double *next = level + padded(len);
         const int64_t nlen = (len + 255) / 256;
-        hipLaunchKernelGGL(group_sum_kernel<double>, dim3(grid_for(nlen, 64, 1 << 30)), dim3(64), 0,
+        hipLaunchKernelGGL(group_sum_kernel<double>, dim3(grid_for(nlen, 64, 1 << 30)), dim3(256), 0,
                            stream, level, len, next);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         level = next;
         len = nlen;
     }
+    // the remaining levels, and the total after the level arrays
+    double *total = level + padded(len);
+    hipLaunchKernelGGL(group_sum_tail_kernel, dim3(1), dim3(1024), 0, stream, level, len, total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int64_t ng = (nb + 255) / 256;
     hipLaunchKernelGGL(dq_encode_kernel, dim3(grid_for(ng, 1, 256 * 32)), dim3(64), 0, stream,
-                       absmax, nb, level, codes, scales, mean, int8 ? 1u : 0u);
+                       absmax, nb, total, codes, scales, mean, int8 ? 1u : 0u);
     return hipGetLastError();
 }
 

@@ -104,13 +104,14 @@ int nf4_quantize(const float *W, int64_t numel, int32_t block, const float codeb
 /*
  * Level-2 (double) quantization of the block constants -- section 3.3: the constants are
  * centred by their mean and quantized to an 8-bit float in blocks of 256.
- *   absmax:       device float32 [nblocks] (from nf4_quantize).
+ *   absmax:       device float32 [nblocks] (from nf4_quantize), 16-byte aligned.
  *   dq_block:     must be 256, else NF4_ERR_UNSUPPORTED.
  *   absmax_q:     device uint8 [nblocks], OCP FP8 E4M3 codes of (absmax - mean) / scale.
  *   absmax_scale: device float32 [ceil(nblocks/256)], scale_j = fp32(max_j |absmax - mean| / 448),
  *                 the multiplier that undoes the scaling (the inverse of eq. (1)'s constant).
- *   absmax_mean:  device float32 [1], mean = fp32(S / nblocks) where S is the float64 sum taken in
- *                 groups of 256 consecutive values, each summed in ascending order, level by level.
+ *   absmax_mean:  device float32 [1], mean = fp32(S / nblocks) where S is the float64 sum taken as
+ *                 a 256-ary tree: groups of 256 consecutive values, each summed in ascending order,
+ *                 then the group sums the same way, level by level, until one value is left.
  *   workspace:    device, >= nf4_double_quant_workspace_size(nblocks, dq_block) bytes.
  * Codes: E4M3 round-to-nearest-even of clamp(fp32(y / scale_j), -448, 448), sign kept; all 0x00
  * when scale_j == 0.

@@ -101,6 +101,7 @@ def test_double_quant_argument_errors():
         assert fn(fake, 0, 256, fake, fake, fake, fake, ws, None) == ESHAPE
         assert fn(fake, 1000, 128, fake, fake, fake, fake, ws, None) == EUNSUP
         assert fn(fake, 1000, 256, fake, fake, fake, fake, ws - 1, None) == EWS
+    assert lib.nf4_double_quant(ctypes.c_void_p(0x100004), 1000, 256, fake, fake, fake, fake, ws, None) == EALIGN
     # workspace grows with the number of summation levels
     assert lib.nf4_double_quant_workspace_size(3670016, 256) >= 8 * (14336 + 56 + 1)
 

@@ -124,7 +124,7 @@ def test_gemv_weight_dequant_bit_exact_full_size():
     assert np.array_equal(got, oracle.dequant_weight(q, CB).reshape(-1))
 
 
-@pytest.mark.parametrize("nb", [1, 255, 257, 1000, 65537, 300000])
+@pytest.mark.parametrize("nb", [1, 255, 257, 1000, 65537, 300000, 4194305])
 def test_double_quant_ragged_bit_exact(nb):
     _say(f"double quant nb={nb}")
     a = np.abs(synth.normal_f32(110 + nb % 97, (nb,), 0.05)).astype(np.float32)
