@@ -8,7 +8,7 @@ not built, importing the binding raises; there is no fallback path.
 Names follow the C ABI:
   nf4_build_codebook, nf4_build_int4_codebook, nf4_build_fp4_codebook, nf4_quantize,
   nf4_double_quant, nf4_double_quant_int8, nf4_dequant, nf4_dequant_single, qlora_linear_fwd,
-  qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd, qlora_gated_fwd, qlora_gated_bwd.
+  qlora_linear_fwd_static, qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd, qlora_gated_fwd, qlora_gated_bwd.
 """
 from __future__ import annotations
 
@@ -32,7 +32,7 @@ EXPORTS = (
     "nf4_build_int4_codebook", "nf4_build_fp4_codebook", "nf4_quantize",
     "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_double_quant_int8", "nf4_dequant",
     "nf4_dequant_single",
-    "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_fwd_static", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "qlora_gated_workspace_size", "qlora_gated_fwd", "qlora_gated_bwd",
     "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
@@ -88,6 +88,7 @@ def _load():
         "nf4_dequant_single": (i, [P, P, i64, i32, P, P, P]),
         "qlora_linear_workspace_size": (sz, [i64, i64, i64, i32]),
         "qlora_linear_fwd": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P, sz, P]),
+        "qlora_linear_fwd_static": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P]),
         "qlora_linear_bwd": (i, [W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P,
                                  ctypes.c_uint32, P, sz, P]),
         "qlora_swiglu_fwd": (i, [P, P, P, i64, P]),
@@ -306,6 +307,28 @@ def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True,
     d = w.descriptor()
     _check(lib.qlora_linear_fwd(ctypes.byref(d), _ptr(X), _ptr(L1), _ptr(L2), float(scale), M, r,
                                 _ptr(Y), _ptr(T), _ptr(ws), wsb, _stream(X.device)), "qlora_linear_fwd")
+    return Y, T
+
+
+#: bytes of the static scratch behind qlora_linear_fwd_static (include/nf4.h)
+QLORA_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def qlora_linear_fwd_static(w: NF4Weight, X, L1, L2, scale: float, Y, T=None):
+    """qlora_linear_fwd without a workspace: the library's static device scratch stands in for it
+    and the call allocates nothing (Y, and T when wanted, are the caller's).  Returns (Y, T)."""
+    torch = _torch()
+    for t, n in ((X, "X"), (L1, "L1"), (L2, "L2"), (Y, "Y")):
+        _need(t, torch.bfloat16, n)
+    if T is not None:
+        _need(T, torch.bfloat16, "T")
+    M, r = X.shape[0], L1.shape[1]
+    if X.shape[1] != w.cols or L1.shape[0] != w.cols or tuple(L2.shape) != (r, w.rows) or \
+            tuple(Y.shape) != (M, w.rows) or (T is not None and tuple(T.shape) != (M, r)):
+        raise ValueError("shape mismatch")
+    d = w.descriptor()
+    _check(lib.qlora_linear_fwd_static(ctypes.byref(d), _ptr(X), _ptr(L1), _ptr(L2), float(scale), M, r, _ptr(Y),
+                                       _ptr(T), _stream(X.device)), "qlora_linear_fwd_static")
     return Y, T
 
 

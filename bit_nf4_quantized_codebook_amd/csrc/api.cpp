@@ -6,9 +6,20 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nf4.h"
 #include "launch.h"
+
+// ---------------------------------------------------------------------------------------------
+// Static scratch of the forward entry point that allocates nothing (qlora_linear_fwd_static).
+// Each GPU the library runs on holds its own copy from module load until the process ends.  In
+// host code the name is a host-side stand-in, not a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device (static_scratch below).  Every call
+// on one GPU shares the array.
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = QLORA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -171,6 +182,32 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
+    }
+    p.total = off;
+    return p;
+}
+
+// The forward's part of the workspace alone, packed from offset 0: s*T and T's partials (fused or
+// expanded paths), the bf16 expansion and L2 transposed (from kExpandMinM tokens), or the decode
+// GEMV's partials.  The split counts are make_plan's, so the kernels see the same launches.
+Plan make_fwd_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
+    Plan p = make_plan(M, N, K, r);
+    size_t off = 0;
+    p.off_T = p.off_dT = 0;                      // backward only
+    if (nf4k::gemv_fits(M, N, K, r)) {
+        const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
+        p.off_sT = p.off_P = p.off_Wd = p.off_L2T = 0;
+        p.off_Yp = off;  off += round256(g.yp_floats * 4);
+        p.off_Tp = off;  off += round256(g.tp_floats * 4);
+        p.total = off;
+        return p;
+    }
+    p.off_sT = off;  off += round256((size_t)M * r * 2);
+    p.off_P = off;   off += round256((size_t)p.ksT * M * r * 4);
+    p.off_Yp = p.off_Tp = p.off_Wd = p.off_L2T = off;
+    if (use_expand(M, N, K)) {
+        p.off_Wd = off;   off += round256((size_t)N * K * 2);
+        p.off_L2T = off;  off += round256((size_t)N * r * 2);
     }
     p.total = off;
     return p;
@@ -407,20 +444,23 @@ size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
     return make_plan(M, N, K, r).total;
 }
 
-int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
-                     float scale, int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+namespace {
+int check_fwd_args(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2, float scale,
+                   int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out) {
     int rc = check_linear_args(w, M, r, scale);
     if (rc) return rc;
     if (!X || !L1 || !L2 || !Y) return fail(NF4_ERR_NULL, "X, L1, L2 and Y must be non-NULL");
     if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) ||
         (T_out && !aligned16(T_out)))
         return fail(NF4_ERR_ALIGN, "activations and adapters must be 16-byte aligned");
+    return NF4_OK;
+}
+
+// The forward's launches on a workspace laid out by plan p (make_plan or make_fwd_plan).
+int linear_fwd_run(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2, float scale,
+                   int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out, const Plan &p, void *workspace,
+                   hipStream_t s) {
     const int64_t N = w->rows, K = w->cols;
-    const Plan p = make_plan(M, N, K, r);
-    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
-    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (nf4k::gemv_fits(M, N, K, r)) {
         NF4_CHECK_HIP(nf4k::launch_gemv_fwd(view_of(w), X, L1, L2, scale, r, M, Y, T_out,
                                             ws_at<float>(workspace, p.off_Yp), ws_at<float>(workspace, p.off_Tp), s),
@@ -440,7 +480,7 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
         NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2T, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
         return NF4_OK;
     }
-    rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
+    int rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
     if (M <= kGemvMaxM) {
         NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
@@ -448,6 +488,54 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
         NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
     }
     return NF4_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void **out) {
+    int dev = -1;
+    NF4_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(NF4_ERR_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        NF4_CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(NF4_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NF4_OK;
+}
+}  // namespace
+
+int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                     float scale, int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    int rc = check_fwd_args(w, X, L1, L2, scale, M, r, Y, T_out);
+    if (rc) return rc;
+    const Plan p = make_plan(M, w->rows, w->cols, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "linear workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return linear_fwd_run(w, X, L1, L2, scale, M, r, Y, T_out, p, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_fwd_static(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                            float scale, int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out, void *stream) {
+    int rc = check_fwd_args(w, X, L1, L2, scale, M, r, Y, T_out);
+    if (rc) return rc;
+    const Plan p = make_fwd_plan(M, w->rows, w->cols, r);
+    if (p.total > kStaticScratchBytes) {
+        std::snprintf(g_last_error, sizeof g_last_error,
+                      "this shape needs %zu bytes of scratch; the static scratch holds %zu bytes "
+                      "(use qlora_linear_fwd with a workspace)", p.total, kStaticScratchBytes);
+        return NF4_ERR_WORKSPACE;
+    }
+    void *ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    return linear_fwd_run(w, X, L1, L2, scale, M, r, Y, T_out, p, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X, const uint16_t *L1,

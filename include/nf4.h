@@ -194,6 +194,25 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
                      uint16_t *T_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The forward above for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and results, bit for bit, with the
+ * workspace taken from a static device array of QLORA_STATIC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on each GPU it runs on until the process ends.  The caller still passes the
+ * inputs and outputs; the call allocates nothing and calls no allocating routine.
+ *   Arguments, limits and results as qlora_linear_fwd.  Shapes whose forward needs more scratch
+ *   than the array holds return NF4_ERR_WORKSPACE (nf4_last_error() gives the size needed): this
+ *   covers decode and mid-size token counts for weights of up to tens of thousands of rows, and
+ *   from 1024 tokens (where the weight is expanded to bf16) weights of up to about 30 M elements.
+ *   Every call on one GPU uses the same array: calls that overlap on one GPU (concurrent streams,
+ *   threads) race and give undefined results.  The first call on a device looks the array's
+ *   address up (hipGetSymbolAddress) with that device current.
+ */
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int qlora_linear_fwd_static(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
+                            const uint16_t *L2, float scale, int64_t M, int32_t r, uint16_t *Y,
+                            uint16_t *T_out, void *stream);
+
+/*
  * QLoRA linear backward -- section 3.5: only the adapters get gradients (dE/dL1, dE/dL2) and
  * the gradient flows to X through the BF16-dequantized frozen weight; W is never written.
  *   dT  = s dY L2^T          dL2 = s T^T dY  (T = X L1)

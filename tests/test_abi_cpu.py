@@ -162,6 +162,25 @@ def test_linear_argument_errors():
                                 fake, 0, fake, wsb - 1, None) == EWS
 
 
+def test_static_forward_argument_errors():
+    """The forward without a workspace checks its arguments like qlora_linear_fwd and rejects a
+    shape whose forward needs more than the static scratch, all before any HIP call."""
+    fake = ctypes.c_void_p(0x100000)
+    st = lambda d, **kw: lib.qlora_linear_fwd_static(ctypes.byref(d), kw.get("X", fake), fake, fake,  # noqa: E731
+                                                     2.0, kw.get("M", 8), kw.get("r", 8), fake, None, None)
+    assert lib.qlora_linear_fwd_static(None, fake, fake, fake, 2.0, 8, 8, fake, None, None) == ENULL
+    assert st(_desc(), M=0) == ESHAPE
+    assert st(_desc(), r=12) == EUNSUP
+    assert st(_desc(), X=None) == ENULL
+    assert st(_desc(), X=ctypes.c_void_p(0x100002)) == EALIGN
+    # from 1024 tokens an 8192 x 8192 weight is expanded to bf16 (128 MiB): beyond the 64 MiB scratch
+    assert st(_desc(rows=8192, cols=8192), M=4096, r=64) == EWS
+    assert b"static scratch" in lib.nf4_last_error()
+    assert nf4.QLORA_STATIC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert "#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+
+
 def test_dequant_and_swiglu_argument_errors():
     fake = ctypes.c_void_p(0x100000)
     d = _desc()
