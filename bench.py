@@ -18,6 +18,8 @@ Also reported on the same JSON line:
                forward + backward TFLOP/s, every GEMM launch timed, the dominant one as roofline
   c4           the LLaMA-65B-shaped MLP (22016x8192 / 8192x22016, 2048 tokens, heavy-tailed
                weights): the same, plus quantize + double quant of its three weights in GB/s
+  qkv          the LLaMA-7B q, k, v projections (three 4096x4096 linears sharing X) as one product
+               against three linear calls (forward)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv] [--no-mlp]
 """
@@ -199,17 +201,17 @@ def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
     return out
 
 
-# GEMM launches of one MLP step, in launch order: (name, kind recorded by the library)
-MLP_LAUNCHES = (("gate fwd", 0), ("up fwd", 0), ("down fwd", 0), ("down bwd (dH)", 1),
-                ("gate+up bwd (dX over both weights)", 4))
-
-
-def mlp_launch_flops(M, F, K, r):
-    """Algorithmic flops of each GEMM launch of one MLP step (MLP_LAUNCHES order); F = hidden size
-    of the MLP (gate/up rows, down's reduction), K = model width."""
+def mlp_launches(M, F, K, r):
+    """GEMM launches of one MLP step in launch order: (name, kind recorded by the library,
+    algorithmic flops).  F = hidden size of the MLP (gate/up rows, down's reduction), K = model
+    width.  From 1024 tokens with F a multiple of 256, gate and up run as one product."""
     fwd_gu = 2 * M * F * K + 2 * M * r * F
-    return (fwd_gu, fwd_gu, 2 * M * K * F + 2 * M * r * K, 2 * M * K * F + 2 * M * r * F,
-            2 * (2 * M * F * K) + 2 * (2 * M * r * K))
+    if M >= 1024 and F % 256 == 0:
+        first = [("gate+up fwd (one product over both weights)", 0, 2 * fwd_gu)]
+    else:
+        first = [("gate fwd", 0, fwd_gu), ("up fwd", 0, fwd_gu)]
+    return first + [("down fwd", 0, 2 * M * K * F + 2 * M * r * K), ("down bwd (dH)", 1, 2 * M * K * F + 2 * M * r * F),
+                    ("gate+up bwd (dX over both weights)", 4, 2 * (2 * M * F * K) + 2 * (2 * M * r * K))]
 
 
 def mlp_flops(M, F, K, r):
@@ -268,7 +270,8 @@ def bench_mlp(torch, nf4, synth, dev, wl, steps=10, warmup=3):
     for _ in range(warmup):
         step_mlp(nf4, st)
     torch.cuda.synchronize()
-    nl = len(MLP_LAUNCHES)
+    launches = mlp_launches(M, F, K, r)
+    nl = len(launches)
     nsampled = (steps + TIMING_EVERY - 1) // TIMING_EVERY
     timer = nf4.GemmTimer(nl * nsampled)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -285,16 +288,15 @@ def bench_mlp(torch, nf4, synth, dev, wl, steps=10, warmup=3):
     torch.cuda.synchronize()
     durs = timer.durations_ms(cnt)
     timer.close()
-    if cnt != nl * nsampled or any(k != MLP_LAUNCHES[i % nl][1] for i, (k, _) in enumerate(durs)):
+    if cnt != nl * nsampled or any(k != launches[i % nl][1] for i, (k, _) in enumerate(durs)):
         raise RuntimeError(f"unexpected GEMM launch sequence: {[k for k, _ in durs]}")
     ms = e0.elapsed_time(e1) / steps
     flops = mlp_flops(M, F, K, r)
-    lf = mlp_launch_flops(M, F, K, r)
     kernels = {}
-    for i, (name, _) in enumerate(MLP_LAUNCHES):
+    for i, (name, _, lf) in enumerate(launches):
         us = sum(d for j, (_, d) in enumerate(durs) if j % nl == i) / nsampled * 1e3
-        kernels[name] = {"us": round(us, 2), "TFLOP/s": round(lf[i] / us / 1e6, 1),
-                         "frac": round(lf[i] / us / 1e6 / BF16_PEAK_TFLOPS, 4), "flops": lf[i]}
+        kernels[name] = {"us": round(us, 2), "TFLOP/s": round(lf / us / 1e6, 1),
+                         "frac": round(lf / us / 1e6 / BF16_PEAK_TFLOPS, 4), "flops": lf}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     value = flops / (ms * 1e-3) / 1e12
     del st
@@ -430,8 +432,9 @@ def bench_qerror(torch, nf4, synth, dev):
 
 def bench_gated(torch, nf4, synth, dev, reps=10):
     """Gated MLP at the LLaMA-7B MLP shape (4096 tokens, gate and up 11008 x 4096, r = 64): the
-    fused forward (one product, the glue in its epilogue) against two linear forwards and the glue,
-    and the fused backward (dX as one product over both weights) against the linears' backward."""
+    gated forward (gate and up as one product over both weights, then the glue) against two linear
+    forwards and the glue, and the fused backward (dX as one product over both weights) against the
+    linears' backward."""
     wl = synth.WORKLOADS["llama7b_mlp"]
     gate, up = wl.linears[0], wl.linears[1]
     M, F, K, r = wl.M, gate.N, gate.K, wl.r
@@ -443,9 +446,8 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
     wsb = max(nf4.lib.qlora_gated_workspace_size(M, F, K, r), nf4.lib.qlora_linear_workspace_size(M, F, K, r))
     wbuf = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
-    def fused():
-        nf4.qlora_gated_fwd(ws[0], ws[1], X, ad[0][0], ad[0][1], ad[1][0], ad[1][1], s, workspace=wbuf,
-                            fuse=True)
+    def gated():
+        nf4.qlora_gated_fwd(ws[0], ws[1], X, ad[0][0], ad[0][1], ad[1][0], ad[1][1], s, workspace=wbuf)
 
     def separate():
         G, _ = nf4.qlora_linear_fwd(ws[0], X, ad[0][0], ad[0][1], s, workspace=wbuf)
@@ -462,7 +464,7 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
 
     out = {"workload": f"gated MLP forward and backward, M={M} F={F} K={K} r={r}"}
     flops = 2 * (2 * M * F * K + 2 * M * K * r + 2 * M * r * F)
-    for name, fn in (("fwd_fused", fused), ("fwd_separate", separate), ("bwd_fused", bwd(True)),
+    for name, fn in (("fwd_gated", gated), ("fwd_separate", separate), ("bwd_fused", bwd(True)),
                      ("bwd_separate", bwd(False))):
         for _ in range(2):
             fn()
@@ -480,6 +482,50 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
     return out
 
 
+def bench_qkv(torch, nf4, synth, dev, reps=10):
+    """The q, k and v projections of the LLaMA-7B attention block (three 4096 x 4096 QLoRA linears
+    sharing X, 4096 tokens, r = 64): qlora_multi_fwd (one product over the concatenated weights)
+    against three qlora_linear_fwd calls."""
+    import numpy as np
+    wl = synth.WORKLOADS["llama7b_attn"]
+    base = wl.linears[0]
+    lins = [synth.Linear(n, base.N, base.K, 1000 + i, 3000 + i, 4000 + i) for i, n in enumerate(("q", "k", "v"))]
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)  # noqa: E731
+    ws = [nf4.NF4Weight.from_float(torch.from_numpy(synth.weight_f32(wl, l)).to(dev)) for l in lins]
+    ad = [tuple(bf(a) for a in synth.lora_f32(wl, l)) for l in lins]
+    X = bf(synth.x_f32(wl, M=wl.M, K=base.K))
+    M, N, K, r, s = wl.M, base.N, base.K, wl.r, wl.scale
+    wsb = max(nf4.qlora_multi_workspace_size([N] * 3, K, M, r), nf4.qlora_linear_workspace_size(M, N, K, r))
+    wbuf = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    Ts = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+
+    def multi():
+        nf4.qlora_multi_fwd(ws, X, [a[0] for a in ad], [a[1] for a in ad], s, workspace=wbuf)
+
+    def separate():
+        for w, a, Y, T in zip(ws, ad, Ys, Ts):
+            nf4.qlora_linear_fwd(w, X, a[0], a[1], s, Y=Y, T=T, workspace=wbuf)
+
+    flops = 3 * (2 * M * N * K + 2 * M * K * r + 2 * M * r * N)
+    out = {"workload": f"q, k, v projections: 3 x W {N}x{K} NF4 sharing X, {M} tokens, LoRA r={r}, forward"}
+    for name, fn in (("one_product", multi), ("three_calls", separate)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1)}
+    del ws, wbuf
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,7 +540,9 @@ def main():
                     help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
                          "normal and heavy-tail 4096 x 4096 weights (one JSON line)")
     ap.add_argument("--gated", action="store_true",
-                    help="time the gated MLP forward (gate + up + SwiGLU) fused against separate calls")
+                    help="time the gated MLP forward and backward against separate calls")
+    ap.add_argument("--qkv", action="store_true",
+                    help="time the q/k/v projections as one product against three linear calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of exactly 1 GiB, 5 times (the reference kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -529,6 +577,9 @@ def main():
         return
     if args.gated:
         print(json.dumps(bench_gated(torch, nf4, synth, dev)), flush=True)
+        return
+    if args.qkv:
+        print(json.dumps(bench_qkv(torch, nf4, synth, dev)), flush=True)
         return
     if args.qerror:
         print(json.dumps({"workload": "qerror: 4-bit types on synthetic 4096x4096 weights",
@@ -621,6 +672,8 @@ def main():
                   file=sys.stderr, flush=True)
         mlp["c4"]["quantize"] = bench_quantize(torch, nf4, synth, dev, synth.WORKLOADS["llama65b_mlp"])
         print(f"[bench] c4 quantize {mlp['c4']['quantize']}", file=sys.stderr, flush=True)
+        mlp["qkv"] = bench_qkv(torch, nf4, synth, dev)
+        print(f"[bench] qkv {mlp['qkv']}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -8,7 +8,8 @@ not built, importing the binding raises; there is no fallback path.
 Names follow the C ABI:
   nf4_build_codebook, nf4_build_int4_codebook, nf4_build_fp4_codebook, nf4_quantize,
   nf4_double_quant, nf4_double_quant_int8, nf4_dequant, nf4_dequant_single, qlora_linear_fwd,
-  qlora_linear_fwd_static, qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd, qlora_gated_fwd, qlora_gated_bwd.
+  qlora_linear_fwd_static, qlora_linear_bwd, qlora_swiglu_fwd, qlora_swiglu_bwd, qlora_gated_fwd, qlora_gated_bwd,
+  qlora_multi_fwd.
 """
 from __future__ import annotations
 
@@ -34,6 +35,7 @@ EXPORTS = (
     "nf4_dequant_single",
     "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_fwd_static", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "qlora_gated_workspace_size", "qlora_gated_fwd", "qlora_gated_bwd",
+    "qlora_multi_workspace_size", "qlora_multi_fwd",
     "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
 )
 
@@ -98,6 +100,8 @@ def _load():
         "qlora_gated_fwd": (i, [W, W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P, P, P,
                                 ctypes.c_uint32, P, sz, P]),
         "qlora_swiglu_bwd": (i, [P, P, P, P, P, i64, P]),
+        "qlora_multi_workspace_size": (sz, [i32, P, i64, i64, i32]),
+        "qlora_multi_fwd": (i, [i32, P, P, P, P, ctypes.c_float, i64, i32, P, P, P, sz, P]),
         "nf4_set_gemm_timing_events": (i, [P, P, P, i32]),
         "nf4_gemm_timing_count": (i32, []),
     }
@@ -419,6 +423,44 @@ def qlora_gated_bwd(w_gate: NF4Weight, w_up: NF4Weight, dH, X, G, U, L1_gate, L2
                                float(scale), M, r, p(dX if need_dX else None), *(_ptr(t) for t in grads), flags,
                                _ptr(ws), wsb, _stream(dev)), "qlora_gated_bwd")
     return (dX if need_dX else None), grads[0], grads[1], grads[2], grads[3]
+
+
+def qlora_multi_workspace_size(Ns, K: int, M: int, r: int) -> int:
+    arr = (ctypes.c_int64 * len(Ns))(*[int(n) for n in Ns])
+    return int(lib.qlora_multi_workspace_size(len(Ns), ctypes.cast(arr, ctypes.c_void_p), K, M, r))
+
+
+def qlora_multi_fwd(ws, X, L1s, L2s, scale: float, keep_T: bool = True, workspace=None):
+    """Forward of up to three linears sharing X (e.g. the q, k and v projections), each with its own
+    adapter: returns ([Y_i], [T_i or None]).  From 1024 tokens one bf16 GEMM over the concatenated
+    weights; the results equal qlora_linear_fwd's bit for bit."""
+    torch = _torch()
+    n = len(ws)
+    if not (1 <= n <= 3) or len(L1s) != n or len(L2s) != n:
+        raise ValueError("one to three weights, each with L1 and L2")
+    _need(X, torch.bfloat16, "X")
+    M, K = X.shape
+    r = L1s[0].shape[1]
+    for w, L1, L2 in zip(ws, L1s, L2s):
+        _need(L1, torch.bfloat16, "L1")
+        _need(L2, torch.bfloat16, "L2")
+        if w.cols != K or tuple(L1.shape) != (K, r) or tuple(L2.shape) != (r, w.rows):
+            raise ValueError("shape mismatch")
+    Ys = [torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device) for w in ws]
+    Ts = [torch.empty((M, r), dtype=torch.bfloat16, device=X.device) for _ in ws] if keep_T else [None] * n
+    wsb = qlora_multi_workspace_size([w.rows for w in ws], K, M, r)
+    wsp = _workspace(wsb, X.device, workspace)
+    descs = [w.descriptor() for w in ws]
+    P = ctypes.c_void_p
+    dptr = (P * n)(*[ctypes.addressof(d) for d in descs])
+    l1p = (P * n)(*[t.data_ptr() for t in L1s])
+    l2p = (P * n)(*[t.data_ptr() for t in L2s])
+    yp = (P * n)(*[t.data_ptr() for t in Ys])
+    tp = (P * n)(*[t.data_ptr() for t in Ts]) if keep_T else None
+    _check(lib.qlora_multi_fwd(n, ctypes.cast(dptr, P), _ptr(X), ctypes.cast(l1p, P), ctypes.cast(l2p, P),
+                               float(scale), M, r, ctypes.cast(yp, P), ctypes.cast(tp, P) if keep_T else None,
+                               _ptr(wsp), wsb, _stream(X.device)), "qlora_multi_fwd")
+    return Ys, Ts
 
 
 def qlora_swiglu_bwd(dh, g, u):

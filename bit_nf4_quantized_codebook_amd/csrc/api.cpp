@@ -146,8 +146,15 @@ constexpr int64_t kGemvMaxM = 16;     // token counts served by a weight-streami
 // inside the GEMM repeats the work once per 256-row tile of tokens and its VALU work does not hide
 // under the MFMAs on gfx950.
 constexpr int64_t kExpandMinM = 1024;
-// the bf16 copy of the weight is addressed with 32-bit byte offsets
-bool use_expand(int64_t M, int64_t N, int64_t K) { return M >= kExpandMinM && N * K * 2 < ((int64_t)1 << 31); }
+// The bf16 copy of the weight may exceed 2 GiB: the expansion kernels write it through 64-bit
+// pointers, and each GEMM tile bases its buffer descriptor at its own first row and reads 256 rows
+// of at most 2^20 elements from there (the 2 GiB operand limits on X and dY bound the reduction
+// length once M >= kExpandMinM), so every offset stays far below 2^31.
+bool use_expand(int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    (void)K;
+    return M >= kExpandMinM;
+}
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
@@ -160,6 +167,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     Plan p;
     const int64_t mt = (M + kTile - 1) / kTile, rt = (r + kTile - 1) / kTile;
     p.ksT = nf4k::choose_split(mt * rt, (K + kTile - 1) / kTile);
+    if (M <= kGemvMaxM) {
+        // one tile of T: four reduction steps per workgroup (one batch of loads), up to 64
+        const int64_t ks4 = ((K + kTile - 1) / kTile + 3) / 4;
+        if (ks4 > p.ksT) p.ksT = (int)(ks4 < 64 ? ks4 : 64);
+    }
     p.ksdT = nf4k::choose_split(mt * rt, (N + kTile - 1) / kTile);
     p.msL2 = nf4k::choose_split(rt * ((N + kTile - 1) / kTile), mt);
     p.msL1 = nf4k::choose_split(((K + kTile - 1) / kTile) * rt, mt);
@@ -475,7 +487,7 @@ int linear_fwd_run(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, c
         hipError_t e;
         const nf4k::Reduction red = T_partials(X, L1, M, K, r, scale, T_out, sT, p, workspace, s, &e);
         NF4_CHECK_HIP(e, "T = X L1");
-        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s, -1, L2, L2T, r, N),
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s, L2, L2T, r, N),
                       "weight expansion + T reduce + L2 transpose");
         NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2T, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
         return NF4_OK;
@@ -536,6 +548,117 @@ int qlora_linear_fwd_static(const nf4_weight *w, const uint16_t *X, const uint16
     rc = static_scratch(&ws);
     if (rc) return rc;
     return linear_fwd_run(w, X, L1, L2, scale, M, r, Y, T_out, p, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Up to three linears sharing their input (the q, k and v projections of an attention block),
+// forward as one product over their weights concatenated along N
+// ---------------------------------------------------------------------------------------------
+namespace {
+constexpr int kMultiMax = 3;
+constexpr int64_t kGemmTileN = 256;
+
+struct MultiPlan {
+    bool fused;
+    Plan lin;                    // the linear layer's plan for [sum N, K] (fused) or the largest N
+    size_t off_sT[kMultiMax];    // s T of each adapter (fused)
+    size_t total;
+};
+
+bool multi_fusable(int32_t n, const int64_t *N, int64_t K, int64_t M) {
+    if (n < 2 || M < kExpandMinM) return false;
+    int64_t tot = 0;
+    for (int i = 0; i < n; ++i) {
+        if (i + 1 < n && N[i] % kGemmTileN) return false;   // no product tile spans two weights
+        tot += N[i];
+    }
+    return use_expand(M, tot, K);
+}
+
+MultiPlan make_multi_plan(int32_t n, const int64_t *N, int64_t K, int64_t M, int32_t r) {
+    MultiPlan p{};
+    p.fused = multi_fusable(n, N, K, M);
+    int64_t tot = 0, nmax = 0;
+    for (int i = 0; i < n; ++i) {
+        tot += N[i];
+        nmax = N[i] > nmax ? N[i] : nmax;
+    }
+    size_t total = 0;
+    for (int i = 0; i < n; ++i) {   // the separate calls run on the front of the workspace
+        const size_t t = make_plan(M, N[i], K, r).total;
+        total = t > total ? t : total;
+    }
+    if (p.fused) {
+        p.lin = make_plan(M, tot, K, r);
+        size_t off = p.lin.total;
+        p.off_sT[0] = p.lin.off_sT;
+        for (int i = 1; i < n; ++i) {
+            p.off_sT[i] = off;
+            off += round256((size_t)M * r * 2);
+        }
+        total = off > total ? off : total;
+    } else {
+        p.lin = make_plan(M, nmax, K, r);
+    }
+    p.total = total;
+    return p;
+}
+}  // namespace
+
+size_t qlora_multi_workspace_size(int32_t n, const int64_t *N, int64_t K, int64_t M, int32_t r) {
+    if (n < 1 || n > kMultiMax || !N || K <= 0 || M <= 0 || r <= 0) return 0;
+    for (int i = 0; i < n; ++i)
+        if (N[i] <= 0) return 0;
+    return make_multi_plan(n, N, K, M, r).total;
+}
+
+int qlora_multi_fwd(int32_t n, const nf4_weight *const *w, const uint16_t *X, const uint16_t *const *L1,
+                    const uint16_t *const *L2, float scale, int64_t M, int32_t r, uint16_t *const *Y,
+                    uint16_t *const *T_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (n < 1 || n > kMultiMax) return fail(NF4_ERR_ARG, "n must be 1, 2 or 3");
+    if (!w || !L1 || !L2 || !Y) return fail(NF4_ERR_NULL, "w, L1, L2 and Y must be non-NULL arrays");
+    int64_t N[kMultiMax];
+    for (int i = 0; i < n; ++i) {
+        int rc = check_fwd_args(w[i], X, L1[i], L2[i], scale, M, r, Y[i], T_out ? T_out[i] : nullptr);
+        if (rc) return rc;
+        if (w[i]->cols != w[0]->cols) return fail(NF4_ERR_SHAPE, "the weights must have the same cols (K)");
+        N[i] = w[i]->rows;
+    }
+    const int64_t K = w[0]->cols;
+    const MultiPlan p = make_multi_plan(n, N, K, M, r);
+    if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "multi workspace too small");
+    if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!p.fused) {
+        for (int i = 0; i < n; ++i) {
+            const Plan pi = make_plan(M, N[i], K, r);
+            int rc = linear_fwd_run(w[i], X, L1[i], L2[i], scale, M, r, Y[i], T_out ? T_out[i] : nullptr, pi,
+                                    workspace, s);
+            if (rc) return rc;
+        }
+        return NF4_OK;
+    }
+    // each adapter's T partials, then the expansion of its weight into its rows of the combined
+    // weight (the same launch sums the partials and transposes its L2 into its rows of L2^T);
+    // then one product for all
+    uint16_t *Wd = ws_at<uint16_t>(workspace, p.lin.off_Wd);
+    uint16_t *L2T = ws_at<uint16_t>(workspace, p.lin.off_L2T);
+    nf4k::FwdSegment seg[kMultiMax];
+    int64_t row0 = 0;
+    for (int i = 0; i < n; ++i) {
+        uint16_t *sT = ws_at<uint16_t>(workspace, p.off_sT[i]);
+        hipError_t e;
+        const nf4k::Reduction red =
+            T_partials(X, L1[i], M, K, r, scale, T_out ? T_out[i] : nullptr, sT, p.lin, workspace, s, &e);
+        NF4_CHECK_HIP(e, "T = X L1");
+        NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w[i]), /*transposed=*/false, Wd + row0 * K, &red, s, L2[i],
+                                                 L2T + row0 * r, r, N[i]),
+                      "weight expansion + T reduce + L2 transpose");
+        seg[i] = nf4k::FwdSegment{N[i], sT, L2T + row0 * r, Y[i]};
+        row0 += N[i];
+    }
+    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd_seg(X, Wd, seg, n, r, M, K, s), "bf16 GEMM (fwd, concatenated weights)");
+    return NF4_OK;
 }
 
 int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X, const uint16_t *L1,
@@ -615,24 +738,6 @@ int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t 
 // Gated MLP forward: gate and up in one product, the glue in its epilogue
 // ---------------------------------------------------------------------------------------------
 namespace {
-struct GatedPlan {
-    bool fused;
-    Plan lin;            // the linear layer's plan for [2F, K] (fused) or [F, K]
-    size_t off_sTu, total;
-};
-// fused from the expansion threshold on, when the 32-row interleave covers whole groups
-bool gated_fused(int64_t M, int64_t F, int64_t K) { return M >= kExpandMinM && F % 32 == 0 && use_expand(M, 2 * F, K); }
-GatedPlan make_gated_plan(int64_t M, int64_t F, int64_t K, int32_t r) {
-    GatedPlan g;
-    g.fused = gated_fused(M, F, K);
-    g.lin = make_plan(M, g.fused ? 2 * F : F, K, r);
-    g.off_sTu = g.lin.total;
-    g.total = g.lin.total + round256((size_t)M * r * 2);
-    return g;
-}
-}  // namespace
-
-namespace {
 // backward: dG and dU after the linear layer's own plan (which the composed path hands to
 // qlora_linear_bwd); the fused path also keeps the up weight's transposed expansion, dT and T
 struct GatedBwdPlan {
@@ -660,7 +765,8 @@ GatedBwdPlan make_gated_bwd_plan(int64_t M, int64_t F, int64_t K, int32_t r) {
 
 size_t qlora_gated_workspace_size(int64_t M, int64_t F, int64_t K, int32_t r) {
     if (M <= 0 || F <= 0 || K <= 0 || r <= 0) return 0;
-    const size_t f = make_gated_plan(M, F, K, r).total, b = make_gated_bwd_plan(M, F, K, r).total;
+    const int64_t N2[2] = {F, F};
+    const size_t f = make_multi_plan(2, N2, K, M, r).total, b = make_gated_bwd_plan(M, F, K, r).total;
     return f > b ? f : b;
 }
 
@@ -682,35 +788,18 @@ int qlora_gated_fwd(const nf4_weight *w_gate, const nf4_weight *w_up, const uint
         (T_up_out && !aligned16(T_up_out)))
         return fail(NF4_ERR_ALIGN, "activations and adapters must be 16-byte aligned");
     const int64_t F = w_gate->rows, K = w_gate->cols;
-    const GatedPlan p = make_gated_plan(M, F, K, r);
+    const int64_t N2[2] = {F, F};
+    const MultiPlan p = make_multi_plan(2, N2, K, M, r);
     if (!workspace || workspace_bytes < p.total) return fail(NF4_ERR_WORKSPACE, "gated workspace too small");
     if (!aligned16(workspace)) return fail(NF4_ERR_ALIGN, "workspace must be 16-byte aligned");
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (!p.fused || !(flags & QLORA_GATED_FUSE)) {
-        // the two linears and the glue, each as its own call
-        rc = qlora_linear_fwd(w_gate, X, L1_gate, L2_gate, scale, M, r, G, T_gate_out, workspace, p.lin.total, stream);
-        if (rc) return rc;
-        rc = qlora_linear_fwd(w_up, X, L1_up, L2_up, scale, M, r, U, T_up_out, workspace, p.lin.total, stream);
-        if (rc) return rc;
-        return qlora_swiglu_fwd(G, U, H, M * F, stream);
-    }
-    // each adapter's T partials, then the expansion of its weight into its rows of the combined
-    // weight (the same launch sums the partials), then one product for both
-    uint16_t *Wgu = ws_at<uint16_t>(workspace, p.lin.off_Wd);
-    uint16_t *sTg = ws_at<uint16_t>(workspace, p.lin.off_sT);
-    uint16_t *sTu = ws_at<uint16_t>(workspace, p.off_sTu);
-    hipError_t e;
-    const nf4k::Reduction red_g = T_partials(X, L1_gate, M, K, r, scale, T_gate_out, sTg, p.lin, workspace, s, &e);
-    NF4_CHECK_HIP(e, "T_gate = X L1_gate");
-    NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w_gate), /*transposed=*/false, Wgu, &red_g, s, /*slot=*/0),
-                  "gate expansion + T_gate reduce");
-    const nf4k::Reduction red_u = T_partials(X, L1_up, M, K, r, scale, T_up_out, sTu, p.lin, workspace, s, &e);
-    NF4_CHECK_HIP(e, "T_up = X L1_up");
-    NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w_up), /*transposed=*/false, Wgu, &red_u, s, /*slot=*/1),
-                  "up expansion + T_up reduce");
-    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_gated(X, Wgu, sTg, L2_gate, sTu, L2_up, r, M, F, K, G, U, H, s),
-                  "gated bf16 GEMM");
-    return NF4_OK;
+    // gate and up as the linears sharing X (one product over both weights from 1024 tokens), then
+    // the glue
+    const nf4_weight *w2[2] = {w_gate, w_up};
+    const uint16_t *l1[2] = {L1_gate, L1_up}, *l2[2] = {L2_gate, L2_up};
+    uint16_t *y[2] = {G, U}, *t[2] = {T_gate_out, T_up_out};
+    rc = qlora_multi_fwd(2, w2, X, l1, l2, scale, M, r, y, t, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return qlora_swiglu_fwd(G, U, H, M * F, stream);
 }
 
 int qlora_gated_bwd(const nf4_weight *w_gate, const nf4_weight *w_up, const uint16_t *dH, const uint16_t *X,

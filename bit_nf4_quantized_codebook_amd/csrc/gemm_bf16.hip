@@ -16,11 +16,9 @@
 // 128-byte rows whose 16-byte chunks are XOR-swizzled by (row / 2) so the fragment reads are
 // bank-conflict free.  The LoRA product is appended as r/64 more reduction steps.
 //
-// Gated MLP forward (gate and up in one product, the SwiGLU glue in the epilogue): B is the
-// combined weight [2F, K] whose 64-row groups hold 32 gate rows then 32 up rows, so in every
-// wave the 32-column MFMA tiles j = 0, 2 hold gate outputs and j = 1, 3 the up outputs of the
-// same columns.  The LoRA steps use s T_gate for the gate tiles and s T_up for the up tiles (two
-// A tiles), and the epilogue writes G, U and H = silu(G) U.
+// Linears sharing X (the q, k and v projections): B holds their expanded weights one after the
+// other along N; each output tile belongs to one of them and takes that one's s T, L2^T and output
+// buffer in the LoRA steps and the epilogue.
 //
 // Gated MLP backward (dX of gate and up as one product): the reduction runs over two segments,
 // [dG | dU] . [deq(W_gate) ; deq(W_up)], each operand of a segment its own buffer, and the LoRA
@@ -39,27 +37,33 @@ constexpr int TN = 256;
 constexpr int TK = 64;
 constexpr int NTHREADS = 256;
 constexpr int STAGE = TM * TK * 2;          // 32 KB per operand stage
-constexpr int EXT_ROWB = (TN / 2 + 16) * 2; // forward LoRA B tile: two halves [64 j][128 n + 16]
 
 struct GemmArgs {
     const uint16_t *A;    // [M, Kred]
     const uint16_t *B;    // [Nout, Kred]
     const uint16_t *Ae;   // [M, r]
-    const uint16_t *Be;   // forward: L2^T [Nout, r] (gated: L2 [r, Nout / 2]); backward: L1 [Nout, r]
-    uint16_t *C;          // [M, Nout]   (gated: H [M, Nout / 2])
+    const uint16_t *Be;   // forward: L2^T [Nout, r]; backward: L1 [Nout, r]
+    uint16_t *C;          // [M, Nout]
     int64_t M, Nout, Kred;
     int32_t r;
     uint32_t accumulate;
-    // gated forward: Ae2 = s T_up [M, r], Be2 = L2_up [r, Nout / 2] (Ae, Be: gate's), G and U out
     // two-segment backward: A2 = dU, B2 = deq(W_up)^T, Ae2 = dT_up, Be2 = L1_up (A, B, Ae, Be: gate's);
     // Kred is one segment's length
     const uint16_t *Ae2;
     const uint16_t *Be2;
-    uint16_t *G, *U;      // [M, Nout / 2]
     const uint16_t *A2, *B2;
+    // forward of up to three linears sharing X (their weights concatenated along N, each segment
+    // a whole number of 256-column tiles): segment i covers columns seg_start[i] .. seg_start[i+1]
+    // and has its own s T (seg_Ae [M, r]), L2^T (seg_Be [N_i, r]) and output (seg_C [M, N_i]).
+    // A plain forward is one segment.
+    int32_t nseg;
+    int64_t seg_start[4];
+    const uint16_t *seg_Ae[3];
+    const uint16_t *seg_Be[3];
+    uint16_t *seg_C[3];
 };
 
-template <bool BWD, bool GATED, bool DUAL>
+template <bool BWD, bool DUAL>
 __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // one LDS object per stage: a fragment read of one stage provably never aliases the
     // direct-to-LDS loads in flight into the other
@@ -237,21 +241,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int r32_e = lane_e & 31, hh_e = lane_e >> 5;
 
+    // The tile's output segment (forward): its adapter, its output buffer, and the tile's first
+    // column within that buffer.  Uniform per workgroup.
+    // (scalar: the segment index goes through readfirstlane, and the kernel-argument arrays are
+    // indexed by it, so nothing here takes vector registers, which the main loop has used up)
+    const uint16_t *Ae_t = g.Ae, *Be_t = g.Be;
+    uint16_t *C_t = g.C;
+    int64_t cN = g.Nout, cn0 = n0;
+    if (!BWD && !DUAL) {
+        const int sg = __builtin_amdgcn_readfirstlane(
+            (g.nseg > 2 && n0 >= g.seg_start[2]) ? 2 : ((g.nseg > 1 && n0 >= g.seg_start[1]) ? 1 : 0));
+        Ae_t = g.seg_Ae[sg];
+        Be_t = g.seg_Be[sg];
+        C_t = g.seg_C[sg];
+        cN = g.seg_start[sg + 1] - g.seg_start[sg];
+        cn0 = n0 - g.seg_start[sg];
+    }
+
     // ---- LoRA extension: r/64 more steps (zero padded past r) ----
     //   A tile: Ae rows m0.., columns j (same swizzled layout, straight to LDS), in As0
-    //   forward and backward: Be = L2^T or L1 [Nout, r]: rows n, columns j -> swizzled layout in
-    //             Bs0, straight to LDS, row reads (L2 is transposed by the expansion launch)
-    //   gated forward: L2_gate / L2_up [r, F]: rows j, columns n -> two halves [64 j][128 + 16]
-    //             in Bs0 / Bs1 through registers, transposing fragment reads
+    //   B tile: Be = L2^T (forward; transposed by the expansion launch) or L1 (backward) [Nout, r]:
+    //           rows n, columns j -> swizzled layout in Bs0, straight to LDS, row reads
     if (ext_steps > 0) {
-        const __amdgpu_buffer_rsrc_t rAe = make_rsrc(g.Ae + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
-        const int64_t be_cols = GATED ? g.Nout / 2 : g.Nout;     // row length of L2
-        // rows layout [Nout, r] (L1, or the forward's L2 transposed); the gated forward reads L2 [r, F]
-        const __amdgpu_buffer_rsrc_t rBe = !GATED ? make_rsrc(g.Be + n0 * g.r, (g.Nout - n0) * (int64_t)g.r * 2)
-                                                  : make_rsrc(g.Be, (int64_t)g.r * be_cols * 2);
-        const __amdgpu_buffer_rsrc_t rAe2 = make_rsrc(GATED ? g.Ae2 + m0 * g.r : g.Ae,
-                                                      GATED ? (g.M - m0) * (int64_t)g.r * 2 : 0);
-        const __amdgpu_buffer_rsrc_t rBe2 = make_rsrc(GATED ? g.Be2 : g.Be, GATED ? (int64_t)g.r * be_cols * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rAe = make_rsrc(Ae_t + m0 * g.r, (g.M - m0) * (int64_t)g.r * 2);
+        const __amdgpu_buffer_rsrc_t rBe = make_rsrc(Be_t + cn0 * g.r, (cN - cn0) * (int64_t)g.r * 2);
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
         // two segments: the up adapter's steps follow the gate's
         const __amdgpu_buffer_rsrc_t rAeU = make_rsrc(DUAL ? g.Ae2 + m0 * g.r : g.Ae,
@@ -270,36 +283,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                 const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0x80000000u;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)((lds_u8 *)As0 + wave * 8192 + q * 1024),
                                                          16, off, 0, 0, 0);
-                if (GATED)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAe2, (lds_void *)((lds_u8 *)As1 + wave * 8192 + q * 1024),
-                                                             16, off, 0, 0, 0);
-                if (!GATED)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
-                                                             16, off, 0, 0, 0);
-            }
-            if (GATED) {
-                // L2 rows j0 .. j0+63, columns n0 .. n0+255: 16-byte chunks through registers
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int jr = (tid >> 5) + 8 * q, ch = tid & 31;
-                    const int64_t col = n0 + ch * 8;
-                    const bool ok = j0 + jr < g.r && col < g.Nout;
-                    u32x4 v;
-                    if (GATED) {
-                        // combined column col: 32-column group col / 32 of type (col / 32) % 2
-                        // (gate, up), F column (col / 64) 32 + col % 32
-                        const int64_t fcol = (col >> 6) * 32 + (col & 31);
-                        const uint32_t off = (uint32_t)(((int64_t)(j0 + jr) * be_cols + fcol) * 2);
-                        const bool up = (col >> 5) & 1;
-                        const u32x4 vg = bload16(rBe, (ok & !up) ? off : 0x80000000u);
-                        const u32x4 vu = bload16(rBe2, (ok & up) ? off : 0x80000000u);
-                        v = u32x4{vg.x | vu.x, vg.y | vu.y, vg.z | vu.z, vg.w | vu.w};
-                    } else {
-                        v = bload16(rBe, ok ? (uint32_t)(((int64_t)(j0 + jr) * g.Nout + col) * 2) : 0x80000000u);
-                    }
-                    uint8_t *Bh = (ch < 16) ? Bs0 : Bs1;
-                    *reinterpret_cast<u32x4 *>(Bh + jr * EXT_ROWB + (ch & 15) * 16) = v;
-                }
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)((lds_u8 *)Bs0 + wave * 8192 + q * 1024),
+                                                         16, off, 0, 0, 0);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -310,38 +295,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                 for (int i = 0; i < 4; ++i)
                     f.a[i] = *reinterpret_cast<const bf16x8 *>(As0 + lds_off[s] + (wm * 128 + 32 * i) * 128);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (!GATED) {
-                        f.b[j] = *reinterpret_cast<const bf16x8 *>(Bs0 + lds_off[s] + (wn * 128 + 32 * j) * 128);
-                    } else {
-                        // 16-lane group (hh, half): lane i reads rows 16 s + 8 hh + i/4 (+4),
-                        // columns c0 + 4 (i%4) .. +3; after the transpose lane i holds column c0 + i
-                        const int i16 = lane_e & 15, half = (lane_e >> 4) & 1;
-                        const uint8_t *Bh = wn ? Bs1 : Bs0;
-                        const int c0 = 32 * j + 16 * half;
-                        const int rowb = 16 * s + 8 * hh_e + (i16 >> 2);
-                        const uint8_t *base = Bh + (c0 + 4 * (i16 & 3)) * 2;
-                        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * EXT_ROWB));
-                        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + (rowb + 4) * EXT_ROWB));
-                        const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        f.b[j] = __builtin_bit_cast(bf16x8, v);
-                    }
-                }
-                if (GATED) {
-                    // up tiles (odd j) take s T_up from As1
-                    bf16x8 a2[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        a2[i] = *reinterpret_cast<const bf16x8 *>(As1 + lds_off[s] + (wm * 128 + 32 * i) * 128);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((j & 1) ? a2[i] : f.a[i], f.b[j],
-                                                                                acc[i][j], 0, 0, 0);
-                } else {
-                    mma(f);
-                }
+                for (int j = 0; j < 4; ++j)
+                    f.b[j] = *reinterpret_cast<const bf16x8 *>(Bs0 + lds_off[s] + (wn * 128 + 32 * j) * 128);
+                mma(f);
             }
             __syncthreads();
         }
@@ -349,40 +305,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
     // ---- epilogue: fp32 -> bf16.  Lane (r32, hh) of tile (i, j) holds column
     // wn*128 + 32 j + r32 and rows wm*128 + 32 i + 8 (v/4) + 4 hh + v%4 ----
-    if (GATED) {
-        // tiles (i, 2 jp) and (i, 2 jp + 1) hold gate and up of F column (n0 + wn*128)/2 + 32 jp + r32;
-        // g and u are rounded to bf16 (the stored G and U) before the glue, as in the glue kernel
-        const int64_t F = g.Nout >> 1;
-        const uint32_t row_bytes = (uint32_t)(F * 2);
-        const int64_t cbase = (n0 + wn * 128) / 2;
-        const __amdgpu_buffer_rsrc_t rG = make_rsrc(g.G + m0 * F, (g.M - m0) * F * 2);
-        const __amdgpu_buffer_rsrc_t rU = make_rsrc(g.U + m0 * F, (g.M - m0) * F * 2);
-        const __amdgpu_buffer_rsrc_t rH = make_rsrc(g.C + m0 * F, (g.M - m0) * F * 2);
-        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((cbase + r32_e) * 2);
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-            if (cbase + 32 * jp + r32_e >= F) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
-                    const uint32_t gb = f32_to_bf16(acc[i][2 * jp][v]), ub = f32_to_bf16(acc[i][2 * jp + 1][v]);
-                    const uint32_t hb = f32_to_bf16(swiglu_h(bf16_to_f32(gb), bf16_to_f32(ub)));
-                    const uint32_t off = lane_off + jp * 64;
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)gb, rG, off, rows * row_bytes, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ub, rU, off, rows * row_bytes, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb, rH, off, rows * row_bytes, 0);
-                }
-            }
-        }
-    } else if (!g.accumulate) {
-        const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
-        const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
-        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((n0 + wn * 128 + r32_e) * 2);
+    if (!g.accumulate) {
+        const __amdgpu_buffer_rsrc_t rC = make_rsrc(C_t + m0 * cN, (g.M - m0) * cN * 2);
+        const uint32_t row_bytes = (uint32_t)(cN * 2);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((cn0 + wn * 128 + r32_e) * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (n0 + wn * 128 + j * 32 + r32_e >= g.Nout) continue;
+            if (cn0 + wn * 128 + j * 32 + r32_e >= cN) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -418,15 +347,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
 template <bool BWD>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmArgs g) {
-    gemm_body<BWD, false, false>(g);
-}
-
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_gated_kernel(GemmArgs g) {
-    gemm_body<false, true, false>(g);
+    gemm_body<BWD, false>(g);
 }
 
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(GemmArgs g) {
-    gemm_body<true, false, true>(g);
+    gemm_body<true, true>(g);
 }
 
 template <bool BWD>
@@ -444,26 +369,28 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream) {
-    GemmArgs a{};
-    a.A = X; a.B = Wd; a.Ae = sT; a.Be = L2T; a.C = Y;
-    a.M = M; a.Nout = N; a.Kred = K; a.r = r; a.accumulate = 0;
-    return launch_impl<false>(a, stream);
+    const FwdSegment seg{N, sT, L2T, Y};
+    return launch_gemm_bf16_fwd_seg(X, Wd, &seg, 1, r, M, K, stream);
 }
 
-hipError_t launch_gemm_bf16_gated(const uint16_t *X, const uint16_t *Wgu, const uint16_t *sTg, const uint16_t *L2g,
-                                  const uint16_t *sTu, const uint16_t *L2u, int32_t r, int64_t M, int64_t F,
-                                  int64_t K, uint16_t *G, uint16_t *U, uint16_t *H, hipStream_t stream) {
+hipError_t launch_gemm_bf16_fwd_seg(const uint16_t *X, const uint16_t *Wd, const FwdSegment *seg, int nseg, int32_t r,
+                                    int64_t M, int64_t K, hipStream_t stream) {
+    if (nseg < 1 || nseg > 3) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.A = X; a.B = Wgu; a.Ae = sTg; a.Be = L2g; a.C = H;
-    a.M = M; a.Nout = 2 * F; a.Kred = K; a.r = r; a.accumulate = 0;
-    a.Ae2 = sTu; a.Be2 = L2u; a.G = G; a.U = U;
-    const int ntm = (int)((M + TM - 1) / TM);
-    const int ntn = (int)((a.Nout + TN - 1) / TN);
-    timing_before(stream, 3);
-    hipLaunchKernelGGL(gemm_bf16_gated_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    timing_after(stream);
-    return e;
+    a.A = X; a.B = Wd;
+    a.nseg = nseg;
+    int64_t n = 0;
+    for (int i = 0; i < nseg; ++i) {
+        // every boundary but the last on a tile edge: a tile never spans two segments
+        if (i + 1 < nseg && seg[i].N % TN) return hipErrorInvalidValue;
+        a.seg_start[i] = n;
+        a.seg_Ae[i] = seg[i].sT; a.seg_Be[i] = seg[i].L2T; a.seg_C[i] = seg[i].Y;
+        n += seg[i].N;
+    }
+    for (int i = nseg; i < 4; ++i) a.seg_start[i] = n;
+    a.Ae = seg[0].sT; a.Be = seg[0].L2T; a.C = seg[0].Y;
+    a.M = M; a.Nout = n; a.Kred = K; a.r = r; a.accumulate = 0;
+    return launch_impl<false>(a, stream);
 }
 
 hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,

@@ -53,21 +53,24 @@ hipError_t launch_gemv_fwd(const WeightView &w, const uint16_t *X, const uint16_
 // large token counts: the weight is expanded to bf16 once per call (rows [N, K] for the forward,
 // transposed [K, N] for the backward), then a K-extended bf16 GEMM
 // red (optional): a partials reduction carried by extra workgroups of the same launch
-// slot (rows only): -1 plain; 0 / 1 puts the rows in 32-row slot 0 / 1 of 64-row groups of out (the
-// gate / up interleave of the gated MLP's combined weight)
 // tr_in (optional, rows layout only): extra workgroups also transpose tr_in [tr_r, tr_n] into
 // tr_out [tr_n, tr_r] (the forward GEMM's L2, so its LoRA step loads like the backward's L1)
 hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *out, const Reduction *red,
-                                hipStream_t stream, int slot = -1, const uint16_t *tr_in = nullptr,
+                                hipStream_t stream, const uint16_t *tr_in = nullptr,
                                 uint16_t *tr_out = nullptr, int32_t tr_r = 0, int64_t tr_n = 0);
 // L2T: the adapter's L2 transposed, [N, r]
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
-// gated MLP forward: C = [X | sT_gate | sT_up] . [Wgu ; ...]^T over the combined weight Wgu [2F, K]
-// (gate and up rows interleaved in 32-row groups); writes G, U and H = silu(G) U, each [M, F]
-hipError_t launch_gemm_bf16_gated(const uint16_t *X, const uint16_t *Wgu, const uint16_t *sTg, const uint16_t *L2g,
-                                  const uint16_t *sTu, const uint16_t *L2u, int32_t r, int64_t M, int64_t F,
-                                  int64_t K, uint16_t *G, uint16_t *U, uint16_t *H, hipStream_t stream);
+// up to three linears sharing X in one product: Wd holds their expanded weights one after the
+// other ([sum N_i, K]); segment i has N_i output columns (a multiple of 256 but for the last),
+// its s T [M, r], L2^T [N_i, r] and output Y_i [M, N_i]
+struct FwdSegment {
+    int64_t N;
+    const uint16_t *sT, *L2T;
+    uint16_t *Y;
+};
+hipError_t launch_gemm_bf16_fwd_seg(const uint16_t *X, const uint16_t *Wd, const FwdSegment *seg, int nseg, int32_t r,
+                                    int64_t M, int64_t K, hipStream_t stream);
 // gated MLP backward: dX = [dG | dU] . [deq(W_gate) ; deq(W_up)] + [dT_gate | dT_up] . [L1_gate ; L1_up]^T,
 // one product whose reduction runs over the two segments (WdT_*: [K, F] transposed expansions)
 hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,

@@ -213,6 +213,27 @@ int qlora_linear_fwd_static(const nf4_weight *w, const uint16_t *X, const uint16
                             uint16_t *T_out, void *stream);
 
 /*
+ * Up to three QLoRA linears that share their input -- the q, k and v projections of an attention
+ * block, each with its own adapter (LoRA on every linear layer: section 4; each linear is
+ * section 3.5 eq. (5)):   Y_i = X deq(W_i)^T + s (X L1_i) L2_i,  i = 0 .. n-1.
+ *   n: 1 to 3.  w, L1, L2, Y: arrays of n entries (HOST arrays of device pointers); T_out: NULL
+ *   or an array of n entries, each NULL or [M, r] (T_i = X L1_i, as qlora_linear_fwd's T_out).
+ *   W_i [N_i, K] with the same K; Y_i [M, N_i]; other shapes and limits as qlora_linear_fwd.
+ *   workspace: >= qlora_multi_workspace_size(n, N, K, M, r) bytes (N: HOST array of the N_i).
+ * From 1024 tokens, when every N_i but the last is a multiple of 256, the weights are expanded
+ * into one combined weight [sum N_i, K] and the n
+ * products run as one bf16 GEMM whose tiles pick their adapter and output by column range;
+ * otherwise the n forwards run as qlora_linear_fwd calls.  Either way Y_i and T_i equal
+ * qlora_linear_fwd's bit for bit.  The backward of each linear is qlora_linear_bwd (with
+ * QLORA_DX_ACCUMULATE for the second and third, to sum their dX).
+ */
+size_t qlora_multi_workspace_size(int32_t n, const int64_t *N, int64_t K, int64_t M, int32_t r);
+int qlora_multi_fwd(int32_t n, const nf4_weight *const *w, const uint16_t *X, const uint16_t *const *L1,
+                    const uint16_t *const *L2, float scale, int64_t M, int32_t r, uint16_t *const *Y,
+                    uint16_t *const *T_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * QLoRA linear backward/*
  * QLoRA linear backward -- section 3.5: only the adapters get gradients (dE/dL1, dE/dL2) and
  * the gradient flows to X through the BF16-dequantized frozen weight; W is never written.
  *   dT  = s dY L2^T          dL2 = s T^T dY  (T = X L1)
@@ -244,13 +265,11 @@ int qlora_swiglu_fwd(const uint16_t *g, const uint16_t *u, uint16_t *h, int64_t 
  *   T_up_out: optional [M, r] (X L1, unscaled), as qlora_linear_fwd's T_out.
  *   workspace: >= qlora_gated_workspace_size(M, F, K, r) bytes (forward and backward).
  *   Limits as qlora_linear_fwd.
- * flags: 0 runs the two linears and the glue as their own calls.  QLORA_GATED_FUSE (from 1024
- * tokens, F a multiple of 32) runs both products as one bf16 GEMM over a combined weight (gate
- * and up rows in alternate 32-row groups) whose epilogue writes G, U and H.  On one MI355X at
- * the LLaMA-7B MLP shape the fused product is about 5 % slower: its tiles finish together, so the
- * glue's arithmetic and the third output are not hidden.  Either way G and U equal
- * qlora_linear_fwd's outputs and H equals qlora_swiglu_fwd(G, U) bit for bit.  Other flag bits:
- * NF4_ERR_ARG.
+ * Gate and up run as qlora_multi_fwd (one bf16 GEMM over both weights from 1024 tokens when F is a
+ * multiple of 256), then the glue; G and U equal qlora_linear_fwd's outputs and H equals
+ * qlora_swiglu_fwd(G, U) bit for bit.  flags: 0 or QLORA_GATED_FUSE, which selects the backward's
+ * fused product and changes nothing here (a forward with the glue in the product's epilogue
+ * measured about 9 % slower than this and was removed).  Other flag bits: NF4_ERR_ARG.
  */
 #define QLORA_GATED_FUSE 2u   /* distinct from QLORA_DX_ACCUMULATE */
 size_t qlora_gated_workspace_size(int64_t M, int64_t F, int64_t K, int32_t r);

@@ -181,6 +181,28 @@ def test_static_forward_argument_errors():
     assert "#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
 
 
+def test_multi_forward_argument_errors():
+    """The forward of linears sharing X: n, the arrays, matching K and the workspace are checked
+    before any HIP call; the workspace covers both the fused plan and each separate call."""
+    fake = ctypes.c_void_p(0x100000)
+    P = ctypes.c_void_p
+    d = [_desc(rows=256, cols=256), _desc(rows=512, cols=256), _desc(rows=256, cols=128)]
+    dp = (P * 3)(*[ctypes.addressof(x) for x in d])
+    arr = (P * 3)(fake, fake, fake)
+    N = (ctypes.c_int64 * 3)(256, 512, 256)
+    wsb = lib.qlora_multi_workspace_size(3, ctypes.cast(N, P), 256, 1024, 16)
+    assert wsb >= lib.qlora_linear_workspace_size(1024, 512, 256, 16)
+    assert wsb >= lib.qlora_linear_workspace_size(1024, 1024, 256, 16)     # the fused plan
+    assert lib.qlora_multi_workspace_size(4, ctypes.cast(N, P), 256, 1024, 16) == 0
+    call = lambda n, **kw: lib.qlora_multi_fwd(n, kw.get("w", ctypes.cast(dp, P)), fake,  # noqa: E731
+                                               ctypes.cast(arr, P), ctypes.cast(arr, P), 2.0, 1024, 16,
+                                               kw.get("Y", ctypes.cast(arr, P)), None, fake, kw.get("wsb", wsb), None)
+    assert call(0) == EARG and call(4) == EARG
+    assert call(2, w=None) == ENULL and call(2, Y=None) == ENULL
+    assert call(3) == ESHAPE                        # the third weight has another K
+    assert call(2, wsb=16) == EWS
+
+
 def test_dequant_and_swiglu_argument_errors():
     fake = ctypes.c_void_p(0x100000)
     d = _desc()

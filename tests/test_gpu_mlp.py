@@ -168,15 +168,15 @@ def test_llama65b_mlp_chain():
 
 
 # ------------------------------------------------------------------------------------------
-# Gated forward: gate and up as one product with the glue in its epilogue
+# Gated forward: gate and up as the linears sharing X (one product over both weights), then the glue
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,F,K,r", [
-    (1024, 2048, 1024, 64),    # one fused product, whole tiles
-    (1100, 544, 640, 32),      # ragged tokens; the combined 1088 columns end in a part tile
-    (2048, 1056, 512, 128),    # r = 128: two LoRA steps per adapter
-    (300, 512, 384, 16),       # below the fused range: the two linears and the glue as calls
-    (1024, 520, 256, 8),       # F not a multiple of 32: the fuse flag falls back to the calls
+    (1024, 2048, 1024, 64),    # one product over both weights, whole tiles
+    (1100, 768, 640, 32),      # ragged tokens, one product
+    (2048, 1280, 512, 128),    # r = 128: two LoRA steps per adapter, one product
+    (300, 512, 384, 16),       # below the expanded-weight range: the two linears as calls
+    (1024, 520, 256, 8),       # F not a multiple of 256: the two linears as calls
 ])
 def test_gated_fwd_matches_separate_calls_and_oracle(M, F, K, r):
     _say(f"gated fwd M={M} F={F} K={K} r={r}")

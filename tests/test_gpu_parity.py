@@ -454,6 +454,59 @@ def test_full_size_attention_projection_sampled():
     assert torch.equal(Y, Y2) and torch.equal(dX, dX2) and torch.equal(dL1, dL12) and torch.equal(dL2, dL22)
 
 
+def test_expanded_weight_past_2_gib_sampled():
+    """From 1024 tokens the weight is expanded to bf16 before the GEMMs; here that copy is 2 GiB
+    (W 32768 x 32768, 1024 tokens, r = 16), past what 32-bit buffer offsets from the base reach.
+
+    W is a seeded 2048-row block repeated 16 times down the rows.  Quantization works per 64-block
+    and the 256-groups of the second level align with the repeats (one repeat holds 2^20 blocks),
+    so codes, constants and deq(W) repeat as well -- the test checks exactly that on the GPU's
+    storage against the oracle's (computed on the whole weight's block constants), which lets the
+    oracle's references be assembled from one 2048-row repeat: outputs by column range, the
+    backward summed over the 16 column ranges of dY."""
+    M, N, K, r, s = 1024, 32768, 32768, 16, 1.0
+    tile = 2048
+    nt = N // tile
+    _say(f"expanded weight past 2 GiB: M={M} N={N} K={K} r={r}")
+    Wt = synth.normal_f32(1600, (tile, K), 0.02)
+    Wdev = torch.from_numpy(Wt).to(DEV).repeat(nt, 1)
+    w = nf4.NF4Weight.from_float(Wdev, CB)
+    del Wdev
+    torch.cuda.synchronize()
+    pt, at = oracle.quantize(Wt, CB)
+    assert np.array_equal(w.packed.cpu().numpy(), np.tile(pt, nt))
+    a_full = np.tile(at, nt)
+    codes, scales, mean = oracle.double_quant(a_full)
+    nbt = at.size
+    assert np.array_equal(codes, np.tile(codes[:nbt], nt)) and np.array_equal(scales, np.tile(scales[:nbt // 256], nt))
+    assert np.array_equal(w.absmax_q.cpu().numpy(), codes)
+    assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    assert w.absmax_mean.cpu().numpy()[0] == mean
+    Wd_t = oracle.dequant(pt, codes[:nbt], scales[:nbt // 256], mean, tile * K, CB).reshape(tile, K)
+    X = synth.to_bf16_bits(synth.normal_f32(1601, (M, K), 1.0))
+    L1 = synth.to_bf16_bits(synth.normal_f32(1602, (K, r), 1.0 / r))
+    L2 = synth.to_bf16_bits(synth.normal_f32(1603, (r, N), 0.01))
+    dY = synth.to_bf16_bits(synth.normal_f32(1604, (M, N), 1.0))
+    Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
+    Y, T = nf4.qlora_linear_fwd(w, Xd, L1d, L2d, s)
+    dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dYd, Xd, L1d, L2d, T, s)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(9).choice(M, 24, replace=False), [0, M - 1]]))
+    Yr = np.empty((rows.size, N))
+    dXr, dL1r, dL2r = 0.0, 0.0, np.empty((r, N))
+    for t in range(nt):
+        c = slice(t * tile, (t + 1) * tile)
+        Yr[:, c], _ = oracle.forward_rows(X, Wd_t, L1, L2[:, c], s, rows)
+        g = oracle.backward_rows(dY[:, c], X, Wd_t, L1, L2[:, c], s, rows)
+        dXr = dXr + g["dX"]
+        dL1r = dL1r + g["dL1"]
+        dL2r[:, c] = g["dL2"]
+    check_tol("Y[rows]", f32(Y)[rows], Yr)
+    check_tol("dX[rows]", f32(dX)[rows], dXr)
+    check_tol("dL1", f32(dL1), dL1r)
+    check_tol("dL2", f32(dL2), dL2r)
+
+
 # ------------------------------------------------------------------------------------------
 # SwiGLU glue
 # ------------------------------------------------------------------------------------------
