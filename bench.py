@@ -482,10 +482,12 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
     return out
 
 
-def bench_qkv(torch, nf4, synth, dev, reps=10):
+def bench_qkv(torch, nf4, synth, dev, reps=10, rounds=3):
     """The q, k and v projections of the LLaMA-7B attention block (three 4096 x 4096 QLoRA linears
-    sharing X, 4096 tokens, r = 64): qlora_multi_fwd (one product over the concatenated weights)
-    against three qlora_linear_fwd calls."""
+    sharing X, r = 64, forward): qlora_multi_fwd (one product over the concatenated weights)
+    against three qlora_linear_fwd calls, at 4096 tokens and at 1024 (where one linear's 64 output
+    tiles leave most CUs idle).  The two forms alternate, first one then the other, over `rounds`
+    rounds of `reps` calls each; the median round is reported."""
     import numpy as np
     wl = synth.WORKLOADS["llama7b_attn"]
     base = wl.linears[0]
@@ -493,35 +495,45 @@ def bench_qkv(torch, nf4, synth, dev, reps=10):
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)  # noqa: E731
     ws = [nf4.NF4Weight.from_float(torch.from_numpy(synth.weight_f32(wl, l)).to(dev)) for l in lins]
     ad = [tuple(bf(a) for a in synth.lora_f32(wl, l)) for l in lins]
-    X = bf(synth.x_f32(wl, M=wl.M, K=base.K))
-    M, N, K, r, s = wl.M, base.N, base.K, wl.r, wl.scale
-    wsb = max(nf4.qlora_multi_workspace_size([N] * 3, K, M, r), nf4.qlora_linear_workspace_size(M, N, K, r))
-    wbuf = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    Ts = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    X_full = bf(synth.x_f32(wl, M=wl.M, K=base.K))
+    N, K, r, s = base.N, base.K, wl.r, wl.scale
+    out = {"workload": f"q, k, v projections: 3 x W {N}x{K} NF4 sharing X, LoRA r={r}, forward"}
+    for M in (wl.M, 1024):
+        X = X_full[:M].contiguous()
+        wsb = max(nf4.qlora_multi_workspace_size([N] * 3, K, M, r), nf4.qlora_linear_workspace_size(M, N, K, r))
+        wbuf = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        Ts = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(3)]
 
-    def multi():
-        nf4.qlora_multi_fwd(ws, X, [a[0] for a in ad], [a[1] for a in ad], s, workspace=wbuf)
+        def multi():
+            nf4.qlora_multi_fwd(ws, X, [a[0] for a in ad], [a[1] for a in ad], s, workspace=wbuf)
 
-    def separate():
-        for w, a, Y, T in zip(ws, ad, Ys, Ts):
-            nf4.qlora_linear_fwd(w, X, a[0], a[1], s, Y=Y, T=T, workspace=wbuf)
+        def separate():
+            for w, a, Y, T in zip(ws, ad, Ys, Ts):
+                nf4.qlora_linear_fwd(w, X, a[0], a[1], s, Y=Y, T=T, workspace=wbuf)
 
-    flops = 3 * (2 * M * N * K + 2 * M * K * r + 2 * M * r * N)
-    out = {"workload": f"q, k, v projections: 3 x W {N}x{K} NF4 sharing X, {M} tokens, LoRA r={r}, forward"}
-    for name, fn in (("one_product", multi), ("three_calls", separate)):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        out[name] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1)}
-    del ws, wbuf
+        flops = 3 * (2 * M * N * K + 2 * M * K * r + 2 * M * r * N)
+        times = {"one_product": [], "three_calls": []}
+        for rnd in range(rounds):
+            order = (("one_product", multi), ("three_calls", separate))
+            for name, fn in (order if rnd % 2 == 0 else order[::-1]):
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1) / reps)
+        res = {}
+        for name, t in times.items():
+            ms = float(np.median(t))
+            res[name] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 1)}
+        out[f"M{M}"] = res
+        del wbuf, Ys, Ts
+    del ws
     torch.cuda.empty_cache()
     return out
 

@@ -43,6 +43,26 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int &tm, int &tn) 
     tn = t % ntn;
 }
 
+// Tile index -> (tm, tn) for the bf16 GEMM: each XCD takes a contiguous run of tile indices (as
+// above), and the run is walked in groups of GM tile rows, column by column within a group, so
+// that the 32 tiles an XCD runs at once form a GM x (32 / GM) block: they share GM tile rows of A
+// and 32 / GM tile columns of B in that XCD's L2.
+template <int GM>
+__device__ __forceinline__ void tile_coords_grouped(int ntm, int ntn, int &tm, int &tn) {
+    const int nt = ntm * ntn;
+    const int bid = blockIdx.x;
+    const int q = nt / 8;
+    int t = bid;
+    if (bid < 8 * q) t = (bid % 8) * q + bid / 8;
+    const int per_group = GM * ntn;
+    const int grp = t / per_group;
+    const int first = grp * GM;
+    const int gsize = min(ntm - first, GM);
+    const int in = t - grp * per_group;
+    tm = first + in % gsize;
+    tn = in / gsize;
+}
+
 // ---- the 16-entry bf16 table of one quantization block, as byte planes ----
 struct Lut {
     uint32_t la0, la1, lb0, lb1;   // low bytes of entries 0-3, 4-7, 8-11, 12-15

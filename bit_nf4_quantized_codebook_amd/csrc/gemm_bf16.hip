@@ -81,7 +81,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     const int ntm = (int)((g.M + TM - 1) / TM);
     const int ntn = (int)((g.Nout + TN - 1) / TN);
     int tm, tn;
-    tile_coords(ntm, ntn, tm, tn);
+    tile_coords_grouped<4>(ntm, ntn, tm, tn);
     const int64_t m0 = (int64_t)tm * TM;
     const int64_t n0 = (int64_t)tn * TN;
     const int seg_steps = (int)((g.Kred + TK - 1) / TK);
