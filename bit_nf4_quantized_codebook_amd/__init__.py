@@ -33,7 +33,7 @@ EXPORTS = (
     "nf4_build_int4_codebook", "nf4_build_fp4_codebook", "nf4_quantize",
     "nf4_double_quant_workspace_size", "nf4_double_quant", "nf4_double_quant_int8", "nf4_dequant",
     "nf4_dequant_single",
-    "qlora_linear_workspace_size", "qlora_linear_fwd", "qlora_linear_fwd_static", "qlora_linear_bwd",
+    "qlora_linear_workspace_size", "qlora_linear_route", "qlora_linear_fwd", "qlora_linear_fwd_static", "qlora_linear_bwd",
     "qlora_swiglu_fwd", "qlora_swiglu_bwd", "qlora_gated_workspace_size", "qlora_gated_fwd", "qlora_gated_bwd",
     "qlora_multi_workspace_size", "qlora_multi_fwd",
     "nf4_set_gemm_timing_events", "nf4_gemm_timing_count",
@@ -89,6 +89,7 @@ def _load():
         "nf4_dequant": (i, [W, P, P]),
         "nf4_dequant_single": (i, [P, P, i64, i32, P, P, P]),
         "qlora_linear_workspace_size": (sz, [i64, i64, i64, i32]),
+        "qlora_linear_route": (i, [i64, i64, i64, i32, P]),
         "qlora_linear_fwd": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P, sz, P]),
         "qlora_linear_fwd_static": (i, [W, P, P, P, ctypes.c_float, i64, i32, P, P, P]),
         "qlora_linear_bwd": (i, [W, P, P, P, P, P, ctypes.c_float, i64, i32, P, P, P,
@@ -293,6 +294,17 @@ def qlora_linear_workspace_size(M: int, N: int, K: int, r: int) -> int:
     return int(lib.qlora_linear_workspace_size(M, N, K, r))
 
 
+_PATHS = {0: None, 1: "gemv", 2: "gemv_wide", 3: "fused", 4: "expanded"}
+
+
+def qlora_linear_route(M: int, N: int, K: int, r: int) -> dict:
+    """How the layer runs this shape: the forward's and backward's path and how many workgroups
+    each output tile's reduction is split over (1: not split)."""
+    info = (ctypes.c_int32 * 4)()
+    _check(lib.qlora_linear_route(M, N, K, r, info), "qlora_linear_route")
+    return {"fwd": _PATHS[info[0]], "fwd_split": int(info[1]), "bwd": _PATHS[info[3]], "bwd_split": int(info[2])}
+
+
 def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True, Y=None,
                      workspace=None, T=None):
     """Y = X deq(W)^T + scale (X L1) L2.  Returns (Y, T) with T = X L1 (or None)."""
@@ -315,7 +327,7 @@ def qlora_linear_fwd(w: NF4Weight, X, L1, L2, scale: float, keep_T: bool = True,
 
 
 #: bytes of the static scratch behind qlora_linear_fwd_static (include/nf4.h)
-QLORA_STATIC_SCRATCH_BYTES = 64 << 20
+QLORA_STATIC_SCRATCH_BYTES = 128 << 20
 
 
 def qlora_linear_fwd_static(w: NF4Weight, X, L1, L2, scale: float, Y, T=None):

@@ -158,8 +158,30 @@ bool use_expand(int64_t M, int64_t N, int64_t K) {
 
 struct Plan {
     int ksT, ksdT, msL2, msL1;
-    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, off_Wd, off_L2T, total;
+    // split of the forward and backward products' reductions over workgroups (1: none)
+    nf4k::SplitPlan kf, kb;
+    size_t off_T, off_sT, off_dT, off_P, off_Yp, off_Tp, off_Wd, off_L2T, off_Pg, total;
 };
+
+constexpr int64_t kGemmTile = 256;   // output tile of the product kernels (both dims)
+constexpr int kSplitQuantum = 4;     // reduction steps per split: a multiple of 4
+
+// the products' splits: forward [M, N] over K, backward [M, K] over N
+void plan_splits(Plan &p, int64_t M, int64_t N, int64_t K) {
+    const int64_t mt = (M + kGemmTile - 1) / kGemmTile;
+    p.kf = p.kb = nf4k::SplitPlan{1, 0};
+    if (M <= kGemvMaxM) return;
+    p.kf = nf4k::gemm_split(mt * ((N + kGemmTile - 1) / kGemmTile), (K + kTile - 1) / kTile, kSplitQuantum);
+    p.kb = nf4k::gemm_split(mt * ((K + kGemmTile - 1) / kGemmTile), (N + kTile - 1) / kTile, kSplitQuantum);
+}
+size_t split_floats(const Plan &p, int64_t M, int64_t N, int64_t K, bool fwd_only) {
+    size_t f = p.kf.ksplit > 1 ? (size_t)p.kf.ksplit * M * N : 0;
+    if (!fwd_only && p.kb.ksplit > 1) {
+        const size_t b = (size_t)p.kb.ksplit * M * K;
+        f = b > f ? b : f;
+    }
+    return f;
+}
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -195,6 +217,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
     }
+    plan_splits(p, M, N, K);
+    p.off_Pg = off;  off += round256(split_floats(p, M, N, K, false) * 4);
     p.total = off;
     return p;
 }
@@ -208,7 +232,7 @@ Plan make_fwd_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
     p.off_T = p.off_dT = 0;                      // backward only
     if (nf4k::gemv_fits(M, N, K, r)) {
         const nf4k::GemvPlan g = nf4k::gemv_plan(M, N, K, r);
-        p.off_sT = p.off_P = p.off_Wd = p.off_L2T = 0;
+        p.off_sT = p.off_P = p.off_Wd = p.off_L2T = p.off_Pg = 0;
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
         p.total = off;
@@ -221,6 +245,7 @@ Plan make_fwd_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
         p.off_Wd = off;   off += round256((size_t)N * K * 2);
         p.off_L2T = off;  off += round256((size_t)N * r * 2);
     }
+    p.off_Pg = off;  off += round256(split_floats(p, M, N, K, true) * 4);
     p.total = off;
     return p;
 }
@@ -456,6 +481,18 @@ size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
     return make_plan(M, N, K, r).total;
 }
 
+int qlora_linear_route(int64_t M, int64_t N, int64_t K, int32_t r, int32_t info[4]) {
+    if (!info) return fail(NF4_ERR_NULL, "info is NULL");
+    if (M <= 0 || N <= 0 || K <= 0 || r <= 0) return fail(NF4_ERR_SHAPE, "M, N, K and r must be >= 1");
+    const Plan p = make_plan(M, N, K, r);
+    const bool gemv = nf4k::gemv_fits(M, N, K, r);
+    info[0] = gemv ? 1 : (M <= kGemvMaxM ? 2 : (use_expand(M, N, K) ? 4 : 3));
+    info[1] = p.kf.ksplit;
+    info[2] = p.kb.ksplit;
+    info[3] = M <= kGemvMaxM ? 0 : (use_expand(M, N, K) ? 4 : 3);
+    return NF4_OK;
+}
+
 namespace {
 int check_fwd_args(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, const uint16_t *L2, float scale,
                    int64_t M, int32_t r, uint16_t *Y, uint16_t *T_out) {
@@ -465,6 +502,20 @@ int check_fwd_args(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, c
     if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) ||
         (T_out && !aligned16(T_out)))
         return fail(NF4_ERR_ALIGN, "activations and adapters must be 16-byte aligned");
+    return NF4_OK;
+}
+
+nf4k::SplitK split_of(const nf4k::SplitPlan &sp, const Plan &p, void *ws) {
+    return nf4k::SplitK{sp.ksplit, sp.per, ws_at<float>(ws, p.off_Pg)};
+}
+// the fixed-order sum of a split product's partials into out (n elements), added to what out
+// holds when accumulating; nothing when the product was not split
+int reduce_split(const nf4k::SplitPlan &sp, const Plan &p, void *ws, int64_t n, uint16_t *out, bool accumulate,
+                 hipStream_t s) {
+    if (sp.ksplit <= 1) return NF4_OK;
+    nf4k::Reduction red{ws_at<float>(ws, p.off_Pg), sp.ksplit, n, 1.0f, out, 0.0f, nullptr};
+    red.accum = accumulate;
+    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red, nullptr, s), "split product reduce");
     return NF4_OK;
 }
 
@@ -489,17 +540,19 @@ int linear_fwd_run(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, c
         NF4_CHECK_HIP(e, "T = X L1");
         NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(w), /*transposed=*/false, Wd, &red, s, L2, L2T, r, N),
                       "weight expansion + T reduce + L2 transpose");
-        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2T, r, M, N, K, Y, s), "bf16 GEMM (fwd)");
-        return NF4_OK;
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd(X, Wd, sT, L2T, r, M, N, K, Y, split_of(p.kf, p, workspace), s),
+                      "bf16 GEMM (fwd)");
+        return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
     }
     int rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
     if (M <= kGemvMaxM) {
         NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
-    } else {
-        NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, s), "fused dequant GEMM (fwd)");
+        return NF4_OK;
     }
-    return NF4_OK;
+    NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, split_of(p.kf, p, workspace), s),
+                  "fused dequant GEMM (fwd)");
+    return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
 }
 
 constexpr int kMaxDevices = 64;
@@ -657,7 +710,23 @@ int qlora_multi_fwd(int32_t n, const nf4_weight *const *w, const uint16_t *X, co
         seg[i] = nf4k::FwdSegment{N[i], sT, L2T + row0 * r, Y[i]};
         row0 += N[i];
     }
-    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd_seg(X, Wd, seg, n, r, M, K, s), "bf16 GEMM (fwd, concatenated weights)");
+    const Plan &pl = p.lin;
+    NF4_CHECK_HIP(nf4k::launch_gemm_bf16_fwd_seg(X, Wd, seg, n, r, M, K, split_of(pl.kf, pl, workspace), s),
+                  "bf16 GEMM (fwd, concatenated weights)");
+    if (pl.kf.ksplit > 1) {
+        // each linear's partials: [M, N_i] blocks at M * (its first column), split k of all of them
+        // at k M sum(N)
+        const float *Pg = ws_at<float>(workspace, pl.off_Pg);
+        nf4k::Reduction red[kMultiMax];
+        int64_t c0 = 0;
+        for (int i = 0; i < n; ++i) {
+            red[i] = nf4k::Reduction{Pg + M * c0, pl.kf.ksplit, M * N[i], 1.0f, Y[i], 0.0f, nullptr};
+            red[i].stride = M * row0;
+            c0 += N[i];
+        }
+        NF4_CHECK_HIP(nf4k::launch_reduce_partials(red[0], n > 1 ? &red[1] : nullptr, s, n > 2 ? &red[2] : nullptr),
+                      "split product reduce");
+    }
     return NF4_OK;
 }
 
@@ -713,15 +782,15 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     const nf4k::Reduction red_dL1{P1, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr};
     NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
     // dX = dY deq(W) + dT L1^T
+    const bool acc = (flags & QLORA_DX_ACCUMULATE) != 0;
     if (expand) {
-        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd(dY, WdT, dT, L1, r, M, N, K, dX,
-                                                 (flags & QLORA_DX_ACCUMULATE) != 0, s),
+        NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd(dY, WdT, dT, L1, r, M, N, K, dX, acc, split_of(p.kb, p, workspace), s),
                       "bf16 GEMM (bwd)");
     } else if (dX) {
-        NF4_CHECK_HIP(nf4k::launch_dqgemm_bwd(view_of(w), dY, dT, L1, r, M, dX,
-                                              (flags & QLORA_DX_ACCUMULATE) != 0, s),
+        NF4_CHECK_HIP(nf4k::launch_dqgemm_bwd(view_of(w), dY, dT, L1, r, M, dX, acc, split_of(p.kb, p, workspace), s),
                       "fused dequant GEMM (bwd)");
     }
+    if (dX) return reduce_split(p.kb, p, workspace, M * K, dX, acc, s);
     return NF4_OK;
 }
 

@@ -25,6 +25,10 @@
 // blocks across each 16-lane group.
 // Register stages of W are fetched two steps ahead; the dequantization of step s+1 is spread
 // over the four MFMA sub-steps of step s.
+//
+// Few output tiles (few tokens): the reduction is split over up to 16 workgroups per tile, each
+// writing a float32 partial tile that a fixed-order reduction sums (and adds to dX when
+// accumulating).
 
 #include "common.h"
 #include "dqtile.h"
@@ -65,6 +69,10 @@ struct GemmArgs {
     int32_t r;
     uint32_t accumulate;
     Codebook cb;
+    // split reduction (ksplit > 1): workgroup b takes tile b % tiles and steps [split per,
+    // (split + 1) per) with split = b / tiles, writing float32 partials P + split M Nout
+    int32_t ksplit, split_per;
+    float *P;
 };
 
 
@@ -87,13 +95,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
 
     const int ntm = (int)((g.M + TM - 1) / TM);
     const int ntn = (int)((g.Nout + TN - 1) / TN);
+    const int ntiles = ntm * ntn;
+    const int split = (int)(blockIdx.x / (uint32_t)ntiles);
     int tm, tn;
-    tile_coords(ntm, ntn, tm, tn);
+    tile_coords(ntm, ntn, (int)blockIdx.x - split * ntiles, tm, tn);
     const int64_t m0 = (int64_t)tm * TM;
     const int64_t o0 = (int64_t)tn * TN;
 
-    const int main_steps = (int)((g.Kred + TK - 1) / TK);
-    const int ext_steps = (g.r + TK - 1) / TK;
+    // this workgroup's steps: kb .. kb + main_steps - 1; the loops below count from 0
+    const int kb = split * g.split_per;
+    const int main_steps = min((int)((g.Kred + TK - 1) / TK) - kb, g.split_per);
+    const int ext_steps = split == g.ksplit - 1 ? (g.r + TK - 1) / TK : 0;
 
     const float mean = g.mean[0];
 
@@ -118,8 +130,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         a_col[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
         a_voff[q] = (uint32_t)((row * g.Kred + a_col[q]) * 2);
     }
-    const int kred32 = (int)g.Kred;
+    // reduction columns up to the end of this workgroup's steps
+    const int kred32 = (int)min(g.Kred, (int64_t)(kb + main_steps) * TK);
     auto load_A = [&](int step, uint8_t *Ad) {
+        step += kb;
         // reduction columns left from this step on; <= 0 past the last step (loads read zeros),
         // < 64 on a ragged last step (its columns past N read zeros)
         const int rem = kred32 - step * TK;
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     };
     auto load_W = [&](int step, WStage &ws) {
         const bool live = step < main_steps;
-        const int64_t n = (int64_t)step * TK + bw_row, blk = (o0 >> 6) + bw_blk;
+        const int64_t n = (int64_t)(kb + step) * TK + bw_row, blk = (o0 >> 6) + bw_blk;
         const uint32_t off = (uint32_t)(n * wrow_bytes + blk * 32);
         const uint32_t b = (uint32_t)(n * wblk_per_row + blk);
         ws.w[0] = bload16(rW, live ? off : 0xFFFFFFF0u);
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     auto write_B = [&](int step, const WStage &ws, uint8_t *Bst, int part) {
         if (part == 0) {
             float a = block_scale(ws.c2, __uint_as_float(ws.c1), mean, dq_i8);
-            if ((int64_t)step * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
+            if ((int64_t)(kb + step) * TK + bw_row >= g.wrows) a = 0.0f;   // ragged reduction
             lut = make_lut(g.cb, a);
         }
         uint8_t *Bd = Bst + bw_row * ROWB_OUT + bw_blk * 128;
@@ -328,7 +342,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     // descriptor: rows past M fall outside it, row offsets are scalars, the column offset is a
     // per-lane constant, so no per-element address arithmetic remains.
     const int colw = (r32 & ~7) | planar_col(r32 & 7);
-    if (!g.accumulate) {
+    if (g.ksplit > 1) {
+        // float32 partial tile (rows past M fall outside the descriptor)
+        const __amdgpu_buffer_rsrc_t rP = make_rsrc(g.P + (int64_t)split * g.M * g.Nout + m0 * g.Nout,
+                                                    (g.M - m0) * g.Nout * 4);
+        const uint32_t prow = (uint32_t)(g.Nout * 4);
+        const uint32_t poff = (uint32_t)((wm * 128 + hh * 4) * prow) + (uint32_t)((o0 + wn * 128 + colw) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (o0 + wn * 128 + j * 32 + colw >= g.Nout) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rP, poff + j * 128,
+                                                          rows * prow, 0);
+                }
+            }
+        }
+    } else if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
         const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
         const uint32_t lane_off = (uint32_t)((wm * 128 + hh * 4) * row_bytes) +
@@ -369,11 +402,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     }
 }
 
-hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_impl(GemmArgs &a, const SplitK &sk, hipStream_t stream) {
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
+    const int64_t steps = (a.Kred + TK - 1) / TK;
+    a.ksplit = sk.ksplit > 1 ? sk.ksplit : 1;
+    a.split_per = (int32_t)(a.ksplit > 1 ? sk.per : steps);
+    a.P = sk.P;
+    if (a.ksplit > 1 && (!sk.P || (int64_t)(a.ksplit - 1) * sk.per >= steps || (int64_t)a.ksplit * sk.per < steps))
+        return hipErrorInvalidValue;
     timing_before(stream, 1);
-    hipLaunchKernelGGL(dqgemm_bwd_kernel, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL(dqgemm_bwd_kernel, dim3(ntm * ntn * a.ksplit), dim3(NTHREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
@@ -383,7 +422,7 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
-                             bool accumulate, hipStream_t stream) {
+                             bool accumulate, const SplitK &sk, hipStream_t stream) {
     GemmArgs a;
     a.A = dY;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
@@ -392,7 +431,7 @@ hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint
     a.wrows = w.rows; a.wcols = w.cols;
     a.r = r; a.accumulate = accumulate ? 1u : 0u;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
-    return launch_impl(a, stream);
+    return launch_impl(a, sk, stream);
 }
 
 }  // namespace nf4k

@@ -25,6 +25,11 @@
 // The LoRA product is appended as r/64 more reduction steps: A' = [X | sT], B' = [deq(W) ; L2].
 // L2 [r, N] is read in its natural layout into LDS and its fragments come from transposing
 // reads (ds_read_b64_tr_b16).
+//
+// Few output tiles (few tokens: one 256-row tile up to 256 of them): the reduction is split over
+// up to 16 workgroups per tile (a multiple of 4 steps each, so the grouped codes stay aligned),
+// each writing a float32 partial tile that a fixed-order reduction sums; the weight is then
+// still decoded once per tile row, by 16 times as many workgroups.
 
 #include "common.h"
 #include "dqtile.h"
@@ -62,6 +67,10 @@ struct FwdArgs {
     int64_t M, N, K;
     int32_t r;
     Codebook cb;
+    // split reduction (ksplit > 1): workgroup b takes tile b % tiles and steps [split per,
+    // (split + 1) per) with split = b / tiles, writing float32 partials P + split M N ([M, N])
+    int32_t ksplit, split_per;
+    float *P;
 };
 
 // packed bytes (and, unless grouped, block code and multiplier) of the two W rows of a lane at
@@ -90,13 +99,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
 
     const int ntm = (int)((g.M + TM - 1) / TM);
     const int ntn = (int)((g.N + TN - 1) / TN);
+    const int ntiles = ntm * ntn;
+    const int split = (int)(blockIdx.x / (uint32_t)ntiles);
     int tm, tn;
-    tile_coords(ntm, ntn, tm, tn);
+    tile_coords(ntm, ntn, (int)blockIdx.x - split * ntiles, tm, tn);
     const int64_t m0 = (int64_t)tm * TM;
     const int64_t n0 = (int64_t)tn * TN;
 
-    const int main_steps = (int)(g.K / TK);
-    const int ext_steps = (g.r + TK - 1) / TK;
+    // this workgroup's steps: kbeg .. kend - 1 (kbeg a multiple of 4); the loops below count
+    // from 0, the loads add kbeg
+    const int kbeg = split * g.split_per;
+    const int kend = min((int)(g.K / TK), kbeg + g.split_per);
+    const int main_steps = kend - kbeg;
+    const int ext_steps = split == g.ksplit - 1 ? (g.r + TK - 1) / TK : 0;
     const float mean = g.mean[0];
     const bool dq_i8 = g.dq_int8 != 0;
     const int64_t nblk_row = g.K >> 6;
@@ -119,7 +134,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
         a_voff[q] = (uint32_t)(((lane >> 3) * g.K + col) * 2);
     }
     const uint32_t a_wave_off = (uint32_t)(64 * wave * g.K * 2);
-    const int last = main_steps - 1;
+    const int last = kend - 1;   // absolute
     // The main loop runs a multiple of 4 steps.  X loads of the padding steps (and of the
     // prefetches past the end) get an offset beyond the buffer, so they land as zeros and the
     // padding steps add nothing; W loads past the end re-read the last block (in bounds, finite).
@@ -130,7 +145,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
         // the whole offset sits in the lane offset (scalar offset 0), so rows past M are out of
         // range for the descriptor's bound check
         const uint32_t oob = step < main_steps ? 0u : 0x80000000u;
-        const uint32_t base = a_wave_off + (uint32_t)min(step, last) * (TK * 2);
+        const uint32_t base = a_wave_off + (uint32_t)min(kbeg + step, last) * (TK * 2);
         const uint32_t v0 = (a_voff[0] + base) | oob, v1 = (a_voff[1] + base) | oob;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
         b_idx[j] = (uint32_t)(n * nblk_row);
     }
     auto load_W = [&](int step, WRegs &R) {
-        const uint32_t st = (uint32_t)min(step, last);
+        const uint32_t st = (uint32_t)min(kbeg + step, last);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             R.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rW, w_voff[j], st * 32, 0);
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
     // grouped: codes of steps 4 grp .. 4 grp + 3 (b_idx is a multiple of 4, so the dword is
     // aligned and the 4 blocks never straddle a 256-block boundary)
     auto load_G = [&](int grp, GRegs &G) {
-        const uint32_t st = (uint32_t)min(4 * grp, last & ~3);
+        const uint32_t st = (uint32_t)min(kbeg + 4 * grp, last & ~3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             G.c2w[j] = __builtin_amdgcn_raw_buffer_load_b32(rC2, b_idx[j], st, 0);
@@ -356,6 +371,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
 
     // ---- epilogue: fp32 -> bf16.  Lane (r32, hh) of tile (i, j) holds column 64 w + 32 j + r32
     // and rows 32 i + 8 (v/4) + 4 hh + v%4; rows past M fall outside the store descriptor ----
+    if (g.ksplit > 1) {
+        // float32 partial tile
+        const __amdgpu_buffer_rsrc_t rP = make_rsrc(g.P + (int64_t)split * g.M * g.N + m0 * g.N, (g.M - m0) * g.N * 4);
+        const uint32_t prow = (uint32_t)(g.N * 4);
+        const uint32_t poff = (uint32_t)(hh * 4) * prow + (uint32_t)((n0 + 64 * wave + r32) * 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (n0 + 64 * wave + 32 * j + r32 >= g.N) continue;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rP, poff + j * 128,
+                                                          rows * prow, 0);
+                }
+            }
+        }
+        return;
+    }
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.Y + m0 * g.N, (g.M - m0) * g.N * 2);
     const uint32_t row_bytes = (uint32_t)(g.N * 2);
     const uint32_t lane_off = (uint32_t)(hh * 4) * row_bytes + (uint32_t)((n0 + 64 * wave + r32) * 2);
@@ -381,7 +416,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_fwd_kernel(FwdArgs g) {
 
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
-                             hipStream_t stream) {
+                             const SplitK &sk, hipStream_t stream) {
     FwdArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
@@ -391,11 +426,19 @@ hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint1
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
     const int ntm = (int)((M + TM - 1) / TM);
     const int ntn = (int)((w.rows + TN - 1) / TN);
+    const int64_t steps = w.cols / TK;
+    a.ksplit = sk.ksplit > 1 ? sk.ksplit : 1;
+    a.split_per = (int32_t)(a.ksplit > 1 ? sk.per : steps);
+    a.P = sk.P;
+    if (a.ksplit > 1 && (!sk.P || sk.per % 4 || (int64_t)(a.ksplit - 1) * sk.per >= steps ||
+                         (int64_t)a.ksplit * sk.per < steps))
+        return hipErrorInvalidValue;
+    const dim3 grid(ntm * ntn * a.ksplit);
     timing_before(stream, 0);
     if (w.cols % 256 == 0)
-        hipLaunchKernelGGL(dqgemm_fwd_kernel<true>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL(dqgemm_fwd_kernel<true>, grid, dim3(NTHREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL(dqgemm_fwd_kernel<false>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+        hipLaunchKernelGGL(dqgemm_fwd_kernel<false>, grid, dim3(NTHREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;

@@ -31,11 +31,11 @@ __device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
-// Tile index -> (tm, tn), keeping each XCD (blockIdx % 8) on a contiguous run of tiles so that
-// the tiles sharing A rows land on the same L2.
-__device__ __forceinline__ void tile_coords(int ntm, int ntn, int &tm, int &tn) {
+// Tile index bid (blockIdx.x, or its tile part when a product's reduction is split) -> (tm, tn),
+// keeping each XCD (bid % 8) on a contiguous run of tiles so that the tiles sharing A rows land on
+// the same L2.
+__device__ __forceinline__ void tile_coords(int ntm, int ntn, int bid, int &tm, int &tn) {
     const int nt = ntm * ntn;
-    const int bid = blockIdx.x;
     const int q = nt / 8;
     int t = bid;
     if (bid < 8 * q) t = (bid % 8) * q + bid / 8;
@@ -48,9 +48,8 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int &tm, int &tn) 
 // that the 32 tiles an XCD runs at once form a GM x (32 / GM) block: they share GM tile rows of A
 // and 32 / GM tile columns of B in that XCD's L2.
 template <int GM>
-__device__ __forceinline__ void tile_coords_grouped(int ntm, int ntn, int &tm, int &tn) {
+__device__ __forceinline__ void tile_coords_grouped(int ntm, int ntn, int bid, int &tm, int &tn) {
     const int nt = ntm * ntn;
-    const int bid = blockIdx.x;
     const int q = nt / 8;
     int t = bid;
     if (bid < 8 * q) t = (bid % 8) * q + bid / 8;

@@ -20,6 +20,9 @@
 // other along N; each output tile belongs to one of them and takes that one's s T, L2^T and output
 // buffer in the LoRA steps and the epilogue.
 //
+// Few output tiles (fewer than half the CUs): the reduction is split over up to 16 workgroups per
+// tile, each writing a float32 partial tile, summed afterwards in a fixed order.
+//
 // Gated MLP backward (dX of gate and up as one product): the reduction runs over two segments,
 // [dG | dU] . [deq(W_gate) ; deq(W_up)], each operand of a segment its own buffer, and the LoRA
 // steps over [dT_gate | dT_up] . [L1_gate ; L1_up]^T.
@@ -61,6 +64,12 @@ struct GemmArgs {
     const uint16_t *seg_Ae[3];
     const uint16_t *seg_Be[3];
     uint16_t *seg_C[3];
+    // split reduction (ksplit > 1): workgroup b takes output tile b % tiles and reduction steps
+    // [split per, (split + 1) per) with split = b / tiles, and writes float32 partials:
+    // P + split * M * Nout + M * seg_start[i], row-major [M, N_i] per segment
+    int32_t ksplit;
+    int32_t split_per;
+    float *P;
 };
 
 template <bool BWD, bool DUAL>
@@ -80,13 +89,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
     const int ntm = (int)((g.M + TM - 1) / TM);
     const int ntn = (int)((g.Nout + TN - 1) / TN);
+    const int ntiles = ntm * ntn;
+    const int split = (int)(blockIdx.x / (uint32_t)ntiles);
     int tm, tn;
-    tile_coords_grouped<4>(ntm, ntn, tm, tn);
+    tile_coords_grouped<4>(ntm, ntn, (int)blockIdx.x - split * ntiles, tm, tn);
     const int64_t m0 = (int64_t)tm * TM;
     const int64_t n0 = (int64_t)tn * TN;
     const int seg_steps = (int)((g.Kred + TK - 1) / TK);
-    const int main_steps = DUAL ? 2 * seg_steps : seg_steps;
-    const int ext_steps = (g.r + TK - 1) / TK;
+    // this workgroup's reduction steps: kb .. kb + main_steps - 1 (all of them unless split)
+    const int kb = split * g.split_per;
+    const int main_steps = DUAL ? 2 * seg_steps : min(seg_steps - kb, g.split_per);
+    const int ext_steps = split == g.ksplit - 1 ? (g.r + TK - 1) / TK : 0;
 
     // tile-relative descriptors: rows past M (or Nout) read zeros
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + m0 * g.Kred, (g.M - m0) * g.Kred * 2);
@@ -107,8 +120,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     }
     const uint32_t wave_off = (uint32_t)(64 * wave * g.Kred * 2);
     const uint32_t row8_off = (uint32_t)(8 * g.Kred * 2);
-    const int kred32 = (int)g.Kred;
-    // Columns at or past Kred (a ragged last step, or the steps past the end) read zeros.  The
+    // reduction columns this workgroup reads: up to Kred, or to the end of its split
+    const int kred32 = DUAL ? (int)g.Kred : (int)min(g.Kred, (int64_t)(kb + main_steps) * TK);
+    // Columns at or past that (a ragged last step, or the steps past the end) read zeros.  The
     // whole offset sits in the lane offset (the scalar offset is 0), so rows past the end of the
     // operand are out of range for the descriptor's bound check.
     auto load = [&](__amdgpu_buffer_rsrc_t r, int step, uint8_t *st, int q0 = 0, int q1 = 8) {
@@ -135,6 +149,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             const bool second = step >= seg_steps;
             r = second ? (isA ? rA2 : rB2) : r;
             step -= second ? seg_steps : 0;
+        } else {
+            step += kb;
         }
         load(r, step, st, q0, q1);
     };
@@ -305,7 +321,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
     // ---- epilogue: fp32 -> bf16.  Lane (r32, hh) of tile (i, j) holds column
     // wn*128 + 32 j + r32 and rows wm*128 + 32 i + 8 (v/4) + 4 hh + v%4 ----
-    if (!g.accumulate) {
+    if (!DUAL && g.ksplit > 1) {
+        // float32 partial tile: rows past M fall outside the descriptor
+        // the segment's partials start at M * (its first column), n0 - cn0
+        float *Pt = g.P + (int64_t)split * g.M * g.Nout + g.M * (n0 - cn0) + m0 * cN;
+        const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pt, (g.M - m0) * cN * 4);
+        const uint32_t row_bytes = (uint32_t)(cN * 4);
+        const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((cn0 + wn * 128 + r32_e) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (cn0 + wn * 128 + j * 32 + r32_e >= cN) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rP, lane_off + j * 128,
+                                                          rows * row_bytes, 0);
+                }
+            }
+        }
+    } else if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(C_t + m0 * cN, (g.M - m0) * cN * 2);
         const uint32_t row_bytes = (uint32_t)(cN * 2);
         const uint32_t lane_off = (uint32_t)((wm * 128 + hh_e * 4) * row_bytes) + (uint32_t)((cn0 + wn * 128 + r32_e) * 2);
@@ -355,11 +391,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(GemmArgs g)
 }
 
 template <bool BWD>
-hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_impl(GemmArgs &a, const SplitK &sk, hipStream_t stream) {
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
+    const int64_t steps = (a.Kred + TK - 1) / TK;
+    a.ksplit = sk.ksplit > 1 ? sk.ksplit : 1;
+    a.split_per = (int32_t)(a.ksplit > 1 ? sk.per : steps);
+    a.P = sk.P;
+    if (a.ksplit > 1 && (!sk.P || (int64_t)(a.ksplit - 1) * sk.per >= steps || (int64_t)a.ksplit * sk.per < steps))
+        return hipErrorInvalidValue;
     timing_before(stream, BWD ? 1 : 0);
-    hipLaunchKernelGGL(gemm_bf16_kernel<BWD>, dim3(ntm * ntn), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL(gemm_bf16_kernel<BWD>, dim3(ntm * ntn * a.ksplit), dim3(NTHREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
@@ -368,13 +410,14 @@ hipError_t launch_impl(const GemmArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
-                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream) {
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, const SplitK &sk,
+                                hipStream_t stream) {
     const FwdSegment seg{N, sT, L2T, Y};
-    return launch_gemm_bf16_fwd_seg(X, Wd, &seg, 1, r, M, K, stream);
+    return launch_gemm_bf16_fwd_seg(X, Wd, &seg, 1, r, M, K, sk, stream);
 }
 
 hipError_t launch_gemm_bf16_fwd_seg(const uint16_t *X, const uint16_t *Wd, const FwdSegment *seg, int nseg, int32_t r,
-                                    int64_t M, int64_t K, hipStream_t stream) {
+                                    int64_t M, int64_t K, const SplitK &sk, hipStream_t stream) {
     if (nseg < 1 || nseg > 3) return hipErrorInvalidValue;
     GemmArgs a{};
     a.A = X; a.B = Wd;
@@ -390,7 +433,7 @@ hipError_t launch_gemm_bf16_fwd_seg(const uint16_t *X, const uint16_t *Wd, const
     for (int i = nseg; i < 4; ++i) a.seg_start[i] = n;
     a.Ae = seg[0].sT; a.Be = seg[0].L2T; a.C = seg[0].Y;
     a.M = M; a.Nout = n; a.Kred = K; a.r = r; a.accumulate = 0;
-    return launch_impl<false>(a, stream);
+    return launch_impl<false>(a, sk, stream);
 }
 
 hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,
@@ -401,6 +444,7 @@ hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, c
     a.A = dG; a.B = WdTg; a.Ae = dTg; a.Be = L1g; a.C = dX;
     a.A2 = dU; a.B2 = WdTu; a.Ae2 = dTu; a.Be2 = L1u;
     a.M = M; a.Nout = K; a.Kred = F; a.r = r; a.accumulate = accumulate ? 1u : 0u;
+    a.ksplit = 1; a.split_per = (int32_t)((F + TK - 1) / TK);
     const int ntm = (int)((M + TM - 1) / TM);
     const int ntn = (int)((K + TN - 1) / TN);
     timing_before(stream, 4);
@@ -412,11 +456,11 @@ hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, c
 
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
-                                hipStream_t stream) {
+                                const SplitK &sk, hipStream_t stream) {
     GemmArgs a{};
     a.A = dY; a.B = WdT; a.Ae = dT; a.Be = L1; a.C = dX;
     a.M = M; a.Nout = K; a.Kred = N; a.r = r; a.accumulate = accumulate ? 1u : 0u;
-    return launch_impl<true>(a, stream);
+    return launch_impl<true>(a, sk, stream);
 }
 
 }  // namespace nf4k

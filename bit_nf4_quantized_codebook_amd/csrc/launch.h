@@ -29,9 +29,29 @@ hipError_t launch_dequant(const uint8_t *packed, const uint8_t *absmax_q, const 
                           const float *absmax_mean, const float *absmax_plain, uint32_t dq_int8,
                           int64_t numel, const float cb[16], uint16_t *out, hipStream_t stream);
 
+// Split of a product's reduction over ksplit workgroups per output tile, for shapes whose output
+// tiles alone would leave CUs idle.  Split k takes reduction steps [k per, (k + 1) per) (per from
+// gemm_split); the last split also runs the LoRA steps.  With ksplit > 1 the kernel writes
+// float32 partials P[k] (row-major [M, Nout]; the forward of several linears keeps each one's
+// columns together, [M, N_i] at M * (its first column)) instead of the bf16 output, and a
+// fixed-order reduction (launch_reduce_partials) sums them.
+struct SplitK {
+    int ksplit;
+    int64_t per;     // reduction steps per split
+    float *P;
+};
+// The split of a product with `tiles` output tiles and `steps` reduction steps: as many splits as
+// keep the launch within one workgroup per CU (at most 16), each a multiple of `quantum` steps
+// (per), none empty.  ksplit = 1 (per = steps) when the tiles fill the chip.
+struct SplitPlan {
+    int ksplit;
+    int64_t per;
+};
+SplitPlan gemm_split(int64_t tiles, int64_t steps, int quantum);
+
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
-                             hipStream_t stream);
+                             const SplitK &sk, hipStream_t stream);
 // up to 16 tokens (9-16, or fewer on shapes the row kernel does not take): sT = s X L1 (bf16
 // [M, r]) computed beforehand
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
@@ -60,7 +80,8 @@ hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *
                                 uint16_t *tr_out = nullptr, int32_t tr_r = 0, int64_t tr_n = 0);
 // L2T: the adapter's L2 transposed, [N, r]
 hipError_t launch_gemm_bf16_fwd(const uint16_t *X, const uint16_t *Wd, const uint16_t *sT, const uint16_t *L2T,
-                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, hipStream_t stream);
+                                int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *Y, const SplitK &sk,
+                                hipStream_t stream);
 // up to three linears sharing X in one product: Wd holds their expanded weights one after the
 // other ([sum N_i, K]); segment i has N_i output columns (a multiple of 256 but for the last),
 // its s T [M, r], L2^T [N_i, r] and output Y_i [M, N_i]
@@ -70,19 +91,20 @@ struct FwdSegment {
     uint16_t *Y;
 };
 hipError_t launch_gemm_bf16_fwd_seg(const uint16_t *X, const uint16_t *Wd, const FwdSegment *seg, int nseg, int32_t r,
-                                    int64_t M, int64_t K, hipStream_t stream);
+                                    int64_t M, int64_t K, const SplitK &sk, hipStream_t stream);
 // gated MLP backward: dX = [dG | dU] . [deq(W_gate) ; deq(W_up)] + [dT_gate | dT_up] . [L1_gate ; L1_up]^T,
 // one product whose reduction runs over the two segments (WdT_*: [K, F] transposed expansions)
 hipError_t launch_gemm_bf16_bwd_dual(const uint16_t *dG, const uint16_t *WdTg, const uint16_t *dTg, const uint16_t *L1g,
                                     const uint16_t *dU, const uint16_t *WdTu, const uint16_t *dTu, const uint16_t *L1u,
                                     int32_t r, int64_t M, int64_t F, int64_t K, uint16_t *dX, bool accumulate,
                                     hipStream_t stream);
+// with sk.ksplit > 1, accumulate is the reduction's (the kernel writes partials)
 hipError_t launch_gemm_bf16_bwd(const uint16_t *dY, const uint16_t *WdT, const uint16_t *dT, const uint16_t *L1,
                                 int32_t r, int64_t M, int64_t N, int64_t K, uint16_t *dX, bool accumulate,
-                                hipStream_t stream);
+                                const SplitK &sk, hipStream_t stream);
 hipError_t launch_dqgemm_bwd(const WeightView &w, const uint16_t *dY, const uint16_t *dT,
                              const uint16_t *L1, int32_t r, int64_t M, uint16_t *dX,
-                             bool accumulate, hipStream_t stream);
+                             bool accumulate, const SplitK &sk, hipStream_t stream);
 
 int choose_split(int64_t tiles, int64_t red_steps);
 // b_rows_k: B given as [Kred, R] (true) or as [R, Kred] (false)
@@ -97,8 +119,9 @@ struct TnProduct {
     int nsplit;
 };
 hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream);
-// out = bf16(s1 * sum of the nsplit partials), out2 (optional) = bf16(s2 * same); one launch for one
-// or two reductions
+// out = bf16(s1 * sum of the nsplit partials), out2 (optional) = bf16(s2 * same); partial k of
+// element i at P[k stride + i] (stride 0: n); accum: out = bf16(s1 * sum + out) (out2 unused).
+// One launch for one to three reductions.
 struct Reduction {
     const float *P;
     int nsplit;
@@ -107,8 +130,11 @@ struct Reduction {
     uint16_t *out;
     float s2;
     uint16_t *out2;
+    int64_t stride = 0;
+    bool accum = false;
 };
-hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream);
+hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream,
+                                  const Reduction *c = nullptr);
 struct RedProb;
 RedProb red_prob(const Reduction &r, uint32_t &nblocks);
 

@@ -226,14 +226,18 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
     }
 }
 
-// One launch serves one or two reductions: blocks [0, nb0) take the first, the rest the second.
+// One launch serves one to three reductions: blocks [0, nb[0]) take the first, the next nb[1] the
+// second, the rest the third.
 struct RedGroup {
-    RedProb p[2];
-    uint32_t nb0, nb1;
+    RedProb p[3];
+    uint32_t nb[3];
 };
 __global__ __launch_bounds__(256) void reduce_partials_kernel(RedGroup grp) {
-    const int second = blockIdx.x >= grp.nb0;
-    reduce_partials_block(grp.p[second], blockIdx.x - (second ? grp.nb0 : 0u), second ? grp.nb1 : grp.nb0);
+    uint32_t b = blockIdx.x;
+    const int i = b < grp.nb[0] ? 0 : (b < grp.nb[0] + grp.nb[1] ? 1 : 2);
+    if (i >= 1) b -= grp.nb[0];
+    if (i == 2) b -= grp.nb[1];
+    reduce_partials_block(grp.p[i], b, grp.nb[i]);
 }
 
 }  // namespace
@@ -275,8 +279,23 @@ TnProb tn_prob(const TnProduct &t, int64_t M, uint32_t &nblocks) {
 RedProb red_prob(const Reduction &r, uint32_t &nblocks) {
     RedProb p;
     p.P = r.P; p.n = r.n; p.out = r.out; p.out2 = r.out2; p.s1 = r.s1; p.s2 = r.s2; p.nsplit = r.nsplit;
+    p.stride = r.stride ? r.stride : r.n;
+    p.accum = r.accum ? 1u : 0u;
     nblocks = reduce_blocks(r.n);
     return p;
+}
+
+SplitPlan gemm_split(int64_t tiles, int64_t steps, int quantum) {
+    int64_t s = tiles > 0 ? 256 / tiles : 1;
+    const int64_t smax = steps / quantum;
+    if (s > smax) s = smax;
+    if (s > 16) s = 16;
+    if (s < 1) s = 1;
+    int64_t per = (steps + s - 1) / s;
+    per = (per + quantum - 1) / quantum * quantum;
+    s = (steps + per - 1) / per;   // rounding per up may leave the last splits empty: drop them
+    if (s <= 1) return SplitPlan{1, steps};
+    return SplitPlan{(int)s, per};
 }
 
 hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream) {
@@ -290,14 +309,22 @@ hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, h
     return hipGetLastError();
 }
 
-hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream) {
+hipError_t launch_reduce_partials(const Reduction &a, const Reduction *b, hipStream_t stream, const Reduction *c) {
     RedGroup g;
-    uint32_t n0 = 0, n1 = 0;
-    g.p[0] = red_prob(a, n0);
-    g.p[1] = b ? red_prob(*b, n1) : g.p[0];
-    g.nb0 = n0;
-    g.nb1 = b ? n1 : n0;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3(n0 + (b ? n1 : 0u)), dim3(256), 0, stream, g);
+    const Reduction *rs[3] = {&a, b, c};
+    uint32_t total = 0;
+    int used = 0;
+    for (int i = 0; i < 3; ++i) {
+        if (!rs[i]) continue;
+        g.p[used] = red_prob(*rs[i], g.nb[used]);
+        total += g.nb[used];
+        ++used;
+    }
+    for (int i = used; i < 3; ++i) {
+        g.p[i] = g.p[0];
+        g.nb[i] = 0;
+    }
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(total), dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 

@@ -1,8 +1,10 @@
 // Fixed-order sum of split-reduction partials, shared by the launches that carry it: its own
-// launch (one or two reductions) and, at large token counts, extra workgroups of the weight
+// launch (one to three reductions) and, at large token counts, extra workgroups of the weight
 // expansion launch.
-//   out[i] = bf16(s1 * sum_k P[k][i]) (k ascending); out2 (optional) = bf16(s2 * the same sum).
-// Four elements per thread (n is a multiple of 4 for every caller: r % 8 == 0).
+//   out[i] = bf16(s1 * sum_k P[k stride + i]) (k ascending); out2 (optional) = bf16(s2 * the same
+//   sum); with accum, out[i] = bf16(s1 * sum + out[i]) (the product added to what out holds).
+// Four elements per thread (n and stride are multiples of 4 for every caller: r % 8 == 0, and the
+// split GEMMs' output widths are multiples of 8).
 #pragma once
 
 #include "common.h"
@@ -11,10 +13,11 @@ namespace nf4k {
 
 struct RedProb {
     const float *P;
-    int64_t n;
+    int64_t n, stride;
     uint16_t *out, *out2;
     float s1, s2;
     int32_t nsplit;
+    uint32_t accum;
 };
 
 // workgroup `blk` of `nblk` workgroups (256 threads) covering one reduction
@@ -23,14 +26,19 @@ __device__ __forceinline__ void reduce_partials_block(const RedProb &pr, int64_t
     const float *__restrict__ P = pr.P;
     uint16_t *__restrict__ out = pr.out;
     uint16_t *__restrict__ out2 = pr.out2;
-    const int64_t n = pr.n;
+    const int64_t n = pr.n, stride = pr.stride;
     const int nsplit = pr.nsplit;
     const float s1 = pr.s1, s2 = pr.s2;
     const int64_t n4 = n >> 2;
     for (int64_t i = blk * 256 + threadIdx.x; i < n4; i += nblk * 256) {
         f32v4 acc = reinterpret_cast<const f32v4 *>(P)[i];
-        for (int k = 1; k < nsplit; ++k) acc += reinterpret_cast<const f32v4 *>(P + (int64_t)k * n)[i];
-        if (out) {
+        for (int k = 1; k < nsplit; ++k) acc += reinterpret_cast<const f32v4 *>(P + (int64_t)k * stride)[i];
+        if (out && pr.accum) {
+            const uint2 old = reinterpret_cast<const uint2 *>(out)[i];
+            const uint2 o = {pack_bf16x2(s1 * acc.x + bf16_to_f32(old.x & 0xFFFFu), s1 * acc.y + bf16_to_f32(old.x >> 16)),
+                             pack_bf16x2(s1 * acc.z + bf16_to_f32(old.y & 0xFFFFu), s1 * acc.w + bf16_to_f32(old.y >> 16))};
+            reinterpret_cast<uint2 *>(out)[i] = o;
+        } else if (out) {
             uint2 o = {pack_bf16x2(s1 * acc.x, s1 * acc.y), pack_bf16x2(s1 * acc.z, s1 * acc.w)};
             reinterpret_cast<uint2 *>(out)[i] = o;
         }

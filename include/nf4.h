@@ -189,6 +189,17 @@ int nf4_dequant_single(const uint8_t *packed, const float *absmax, int64_t numel
  *   workspace: >= qlora_linear_workspace_size(M, N, K, r) bytes.
  */
 size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/*
+ * How the linear layer runs a shape (host, no GPU work): info[0] = the forward's path (1: decode
+ * GEMV, up to 8 tokens; 2: wide GEMV, up to 16; 3: fused dequant GEMM; 4: bf16 expansion of the
+ * weight, then the bf16 GEMM), info[1] = the workgroups each output tile of the forward's product
+ * splits its reduction over (1: not split), info[2] = the same for the backward's dX product,
+ * info[3] = the backward's path (3 or 4; 0 up to 16 tokens, where only the forward is a GEMV).
+ * Split products sum float32 partials in a fixed order, so a split and an unsplit product of the
+ * same values can differ in their last bits.  Returns NF4_OK, or NF4_ERR_SHAPE / NF4_ERR_NULL.
+ */
+int qlora_linear_route(int64_t M, int64_t N, int64_t K, int32_t r, int32_t info[4]);
 int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
                      const uint16_t *L2, float scale, int64_t M, int32_t r, uint16_t *Y,
                      uint16_t *T_out, void *workspace, size_t workspace_bytes, void *stream);
@@ -196,18 +207,19 @@ int qlora_linear_fwd(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
 /*
  * The forward above for callers that cannot allocate (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same kernels and results, bit for bit, with the
- * workspace taken from a static device array of QLORA_STATIC_SCRATCH_BYTES (64 MiB) that the
+ * workspace taken from a static device array of QLORA_STATIC_SCRATCH_BYTES (128 MiB) that the
  * library holds on each GPU it runs on until the process ends.  The caller still passes the
  * inputs and outputs; the call allocates nothing and calls no allocating routine.
  *   Arguments, limits and results as qlora_linear_fwd.  Shapes whose forward needs more scratch
  *   than the array holds return NF4_ERR_WORKSPACE (nf4_last_error() gives the size needed): this
  *   covers decode and mid-size token counts for weights of up to tens of thousands of rows, and
- *   from 1024 tokens (where the weight is expanded to bf16) weights of up to about 30 M elements.
+ *   from 1024 tokens (where the weight is expanded to bf16) weights of up to about 60 M elements,
+ *   fewer where the product's reduction is split (its float32 partials also live there).
  *   Every call on one GPU uses the same array: calls that overlap on one GPU (concurrent streams,
  *   threads) race and give undefined results.  The first call on a device looks the array's
  *   address up (hipGetSymbolAddress) with that device current.
  */
-#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 int qlora_linear_fwd_static(const nf4_weight *w, const uint16_t *X, const uint16_t *L1,
                             const uint16_t *L2, float scale, int64_t M, int32_t r, uint16_t *Y,
                             uint16_t *T_out, void *stream);

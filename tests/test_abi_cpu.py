@@ -173,12 +173,12 @@ def test_static_forward_argument_errors():
     assert st(_desc(), r=12) == EUNSUP
     assert st(_desc(), X=None) == ENULL
     assert st(_desc(), X=ctypes.c_void_p(0x100002)) == EALIGN
-    # from 1024 tokens an 8192 x 8192 weight is expanded to bf16 (128 MiB): beyond the 64 MiB scratch
+    # from 1024 tokens an 8192 x 8192 weight is expanded to bf16 (128 MiB): with the rest, beyond the 128 MiB scratch
     assert st(_desc(rows=8192, cols=8192), M=4096, r=64) == EWS
     assert b"static scratch" in lib.nf4_last_error()
-    assert nf4.QLORA_STATIC_SCRATCH_BYTES == 64 << 20
+    assert nf4.QLORA_STATIC_SCRATCH_BYTES == 128 << 20
     hdr = open(HEADER).read()
-    assert "#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+    assert "#define QLORA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)" in hdr
 
 
 def test_multi_forward_argument_errors():
@@ -222,6 +222,30 @@ def test_workspace_sizes_cover_all_configs():
         # at least T, sT, dT and the transposed adapters
         assert ws >= 2 * (3 * M * r + r * K + N * r)
         assert ws < 1 << 31
+
+
+def test_route_by_token_count_and_tile_count():
+    """qlora_linear_route: the documented path per token count, no split where the output tiles
+    fill the 256 CUs (the 7B training shapes), splits where they do not; bad arguments rejected."""
+    info = (ctypes.c_int32 * 4)()
+    assert lib.qlora_linear_route(8, 256, 256, 8, None) == ENULL
+    assert lib.qlora_linear_route(0, 256, 256, 8, info) == ESHAPE
+    route = nf4.qlora_linear_route
+    assert route(1, 28672, 8192, 64) == {"fwd": "gemv", "fwd_split": 1, "bwd": None, "bwd_split": 1}
+    assert route(16, 28672, 8192, 64)["fwd"] == "gemv_wide"
+    assert route(17, 4096, 4096, 64)["fwd"] == "fused" and route(1023, 4096, 4096, 64)["bwd"] == "fused"
+    assert route(1024, 4096, 4096, 64)["fwd"] == "expanded"
+    # 4096 x 4096 x 4096: 256 output tiles each way, no split; the 7B MLP shapes likewise
+    for M, N, K in [(4096, 4096, 4096), (4096, 11008, 4096), (4096, 4096, 11008), (2048, 22016, 8192)]:
+        rt = route(M, N, K, 64)
+        assert rt["fwd_split"] == 1 and rt["bwd_split"] == 1, (M, N, K, rt)
+    # 32 tokens: 16 tiles, 16 splits of 4 steps each way; 512 tokens: 32 tiles, 8 splits
+    assert route(32, 4096, 4096, 64)["fwd_split"] == 16 and route(32, 4096, 4096, 64)["bwd_split"] == 16
+    assert route(512, 4096, 4096, 64)["fwd_split"] == 8
+    # never more splits than whole groups of 4 reduction steps
+    assert route(100, 4096, 384, 64)["fwd_split"] == 1
+    # the workspace grows by the partials: splits x M x N float32 at least
+    assert lib.qlora_linear_workspace_size(32, 4096, 4096, 64) >= 16 * 32 * 4096 * 4
 
 
 def test_flag_bits_are_distinct_and_match_the_binding():

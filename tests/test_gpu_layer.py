@@ -1,9 +1,11 @@
 """GPU parity of the linears of a whole decoder layer.
 
 * qlora_multi_fwd: up to three linears sharing their input (the q, k and v projections), forward
-  as one bf16 GEMM over the concatenated weights from 1024 tokens.  Its outputs must equal three
-  qlora_linear_fwd calls bit for bit (each output tile runs the same arithmetic) and the oracle
-  within tolerance.
+  as one bf16 GEMM over the concatenated weights from 1024 tokens (every weight but the last a
+  whole number of 256-column tiles).  Its outputs must equal three qlora_linear_fwd calls bit for
+  bit where the joined product splits its reduction as each separate one does (each output tile
+  then runs the same arithmetic; qlora_linear_route gives the splits), and the oracle within
+  tolerance everywhere.
 * A decoder layer's linears in one chain: q/k/v (one product), the output projection o, and the
   gated MLP (gate and up with the glue, then down), forward and backward, every stage checked
   against the float64 oracle on the GPU's own bf16 inputs to that stage.  The attention core
@@ -69,7 +71,7 @@ class Lin:
 @pytest.mark.parametrize("M,Ns,K,r", [
     (1024, (512, 256, 256), 512, 16),      # one product over three weights (GQA-like k, v)
     (1100, (768, 256, 520), 384, 32),      # ragged tokens; the last weight ends in a part tile
-    (2048, (1024, 1024, 1024), 1024, 64),  # equal q, k, v
+    (2048, (1024, 1024, 1024), 1024, 64),  # equal q, k, v; the separate calls split 4 ways, the joined 2
     (1024, (256, 512), 256, 128),          # two weights, two LoRA steps
     (1024, (520, 256, 256), 256, 16),      # a first weight off the tile grid: separate calls
     (300, (512, 256, 256), 512, 16),       # below the expanded-weight range: separate calls
@@ -83,8 +85,16 @@ def test_multi_fwd_matches_separate_calls_and_oracle(M, Ns, K, r):
     Ys, Ts = nf4.qlora_multi_fwd([l.w for l in lins], Xd, [l.L1d for l in lins], [l.L2d for l in lins], s)
     sep = [nf4.qlora_linear_fwd(l.w, Xd, l.L1d, l.L2d, s) for l in lins]
     torch.cuda.synchronize()
+    # the documented condition for one product: 1024 tokens, every weight but the last whole tiles
+    joined = len(Ns) > 1 and M >= 1024 and all(N % 256 == 0 for N in Ns[:-1])
+    ks_joined = nf4.qlora_linear_route(M, sum(Ns), K, r)["fwd_split"]
     for i, (l, (Y1, T1)) in enumerate(zip(lins, sep)):
-        assert torch.equal(Ys[i].view(torch.int16), Y1.view(torch.int16)), i
+        same = not joined or nf4.qlora_linear_route(M, Ns[i], K, r)["fwd_split"] == ks_joined
+        _say(f"  Y{i}: bit for bit against the separate call: {same}")
+        if same:
+            assert torch.equal(Ys[i].view(torch.int16), Y1.view(torch.int16)), i
+        else:
+            check_tol(f"Y{i} vs separate", to64(Ys[i]), to64(Y1))
         assert torch.equal(Ts[i].view(torch.int16), T1.view(torch.int16)), i
         Yr, Tr = oracle.forward(X, l.Wd, l.L1, l.L2, s)
         check_tol(f"Y{i}", to64(Ys[i]), Yr)

@@ -183,12 +183,17 @@ SHAPES = [
     (1024, 520, 384, 16),      # ragged N (the backward's reduction), odd number of K steps
     (1100, 264, 640, 24),      # ragged M and N
     (1040, 1032, 320, 128),    # two LoRA extension steps
+    # few output tiles: the products' reductions split over several workgroups per tile
+    (32, 4096, 4096, 64),      # fused GEMMs, 16 splits of 4 steps each way
+    (200, 1032, 2112, 16),     # fused: K not a multiple of 256, ragged last split both ways
+    (700, 2048, 1024, 32),     # fused, three tile rows: 4 splits forward, 8 backward
+    (1536, 1024, 2048, 64),    # expanded weight + bf16 GEMM: 8 splits forward, 4 backward
 ]
 
 
 @pytest.mark.parametrize("M,N,K,r", SHAPES)
 def test_linear_fwd_bwd_parity(M, N, K, r):
-    _say(f"linear fwd/bwd M={M} N={N} K={K} r={r}")
+    _say(f"linear fwd/bwd M={M} N={N} K={K} r={r} {nf4.qlora_linear_route(M, N, K, r)}")
     s = 16.0 / r
     w, Wd, X, L1, L2, dY = _make_layer(M, N, K, r, seed=200 + M + N)
     Xd, L1d, L2d, dYd = d16(X), d16(L1), d16(L2), d16(dY)
