@@ -19,9 +19,12 @@ Also reported on the same JSON line:
   c4           the LLaMA-65B-shaped MLP (22016x8192 / 8192x22016, 2048 tokens, heavy-tailed
                weights): the same, plus quantize + double quant of its three weights in GB/s
   qkv          the LLaMA-7B q, k, v projections (three 4096x4096 linears sharing X) as one product
-               against three linear calls (forward)
+               against three linear calls (forward), at 4096 and 1024 tokens
+  mid          the 7B attention projection forward + backward at 32, 256, 512 and 1536 tokens (the
+               fused dequant GEMMs and the under-filled expanded GEMM, their reductions split)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv] [--no-mlp]
+                       [--no-mid]
 """
 from __future__ import annotations
 
@@ -49,11 +52,11 @@ METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 # taken on: if the hashed sources differ, traffic is reported as null.
 FETCH_SCALE = 1048576.0 / 524301.3
 WRITE_SCALE = 1048576.0 / 1048576.0
-GEMM_TRAFFIC_KIB = {0: (149908.0, 33971.7), 1: (149904.9, 32958.6)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
+GEMM_TRAFFIC_KIB = {0: (99996.0, 33116.0), 1: (99984.0, 32922.0)}   # kind -> (FETCH_SIZE, WRITE_SIZE)
 GEMM_TRAFFIC_SOURCES = {
-    "csrc/gemm_bf16.hip": "a3a08acecb22e38cf5c2736dd73e000bea69ca9fdd6700dff8b68a222466e5d0",
+    "csrc/gemm_bf16.hip": "8d4c622103c4179b729e2f2b1d8fa91ead1c5985e53e4327c52d5db59c5225d5",
     "csrc/common.h": "1cf2a1ddbbf0b49703ce638ad570d618aa6e5700ecdf039bf1c982405beaf8f7",
-    "csrc/dqtile.h": "490babcb3e32389b8d42f9bf9415f7648bda55abef16a44443e6c8e438a25496",
+    "csrc/dqtile.h": "5e5858351a391c0bf4b3b0eb26d1438c822fbee72afe0766f9790cb36c7179b7",
 }
 
 
@@ -482,6 +485,34 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
     return out
 
 
+def bench_mid(torch, nf4, synth, dev, Ms=(32, 256, 512, 1536), steps=20, warmup=5):
+    """The LLaMA-7B attention projection (W 4096 x 4096, r = 64) forward + backward at token counts
+    between the decode GEMVs and the training shapes: the fused dequant GEMMs (up to 1023 tokens)
+    and the expanded-weight GEMM below a full wave of output tiles, each with its reduction split
+    over several workgroups per tile (qlora_linear_route gives the splits)."""
+    wl = synth.WORKLOADS["llama7b_attn"]
+    lin = wl.linears[0]
+    out = {"workload": f"W {lin.N}x{lin.K} NF4, LoRA r={wl.r}, forward + backward, by token count"}
+    for M in Ms:
+        st = make_linear(torch, nf4, synth, wl, lin, M, dev)
+        for i in range(warmup):
+            step_linear(nf4, st, i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step_linear(nf4, st, i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        fwd, bwd = linear_flops(M, lin.N, lin.K, wl.r)
+        out[f"M{M}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round((fwd + bwd) / ms / 1e9, 1),
+                        "route": nf4.qlora_linear_route(M, lin.N, lin.K, wl.r)}
+        del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_qkv(torch, nf4, synth, dev, reps=10, rounds=3):
     """The q, k and v projections of the LLaMA-7B attention block (three 4096 x 4096 QLoRA linears
     sharing X, r = 64, forward): qlora_multi_fwd (one product over the concatenated weights)
@@ -547,6 +578,8 @@ def main():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true", help="skip the two MLP workloads (c3, c4 keys)")
+    ap.add_argument("--no-mid", action="store_true", help="skip the mid-size token counts (mid key)")
+    ap.add_argument("--mid", action="store_true", help="time only the mid-size token counts")
     ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
     ap.add_argument("--qerror", action="store_true",
                     help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
@@ -592,6 +625,9 @@ def main():
         return
     if args.qkv:
         print(json.dumps(bench_qkv(torch, nf4, synth, dev)), flush=True)
+        return
+    if args.mid:
+        print(json.dumps(bench_mid(torch, nf4, synth, dev)), flush=True)
         return
     if args.qerror:
         print(json.dumps({"workload": "qerror: 4-bit types on synthetic 4096x4096 weights",
@@ -686,6 +722,9 @@ def main():
         print(f"[bench] c4 quantize {mlp['c4']['quantize']}", file=sys.stderr, flush=True)
         mlp["qkv"] = bench_qkv(torch, nf4, synth, dev)
         print(f"[bench] qkv {mlp['qkv']}", file=sys.stderr, flush=True)
+    if not args.no_mid:
+        mlp["mid"] = bench_mid(torch, nf4, synth, dev)
+        print(f"[bench] mid {mlp['mid']}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -99,14 +99,18 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(ExpandArgs g) {
     }
 }
 
-// Transposed layout, one 64 x 64 tile (64 W rows n0.., one block column kb) per workgroup:
-// thread t expands 16 weights of row n0 + t/4 (columns 16 (t%4) ..) into an LDS tile [k][n],
-// then writes 16 consecutive n of one output row k.  In the tile, the 16-column group of n is
-// XOR-ed with k/16, so the 2-byte writes of the four column groups of a wave land on different
-// banks.
-constexpr int TROW = 64 + 8;   // LDS row (k) length in bf16, padded
+// Transposed layout, one tile of 128 W rows (n0 ..) by 256 W columns (4 blocks, k0 ..) per
+// workgroup.  Thread t decodes block q = t % 4 of W rows n0 + 2p and n0 + 2p + 1 (p = t / 4): its
+// 4 threads per row pair read each row's 128 packed bytes as one line.  It writes the bf16 pairs
+// (w[n][k], w[n+1][k]) of its 64 columns into an LDS tile [256 k][64 pairs]; then 16 lanes write
+// each output row k (128 n, 256 bytes) with 16-byte stores.  In the tile, the 16-byte group of 4
+// pairs is XOR-ed with 4 (k / 64): the 4-byte writes of a wave (16 row pairs x 4 blocks at one
+// column offset) then land on 64 different banks, and the 16 lanes reading one row take 16
+// different groups.  N % 8 == 0, so an 8-column output group is wholly inside or outside N.
+constexpr int TT_N = 128;        // W rows per tile (output columns)
+constexpr int TT_K = 256;        // W columns per tile (output rows): 4 blocks
 __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
-    __shared__ uint16_t tile[64 * TROW];
+    __shared__ __align__(16) uint32_t tile[TT_K * (TT_N / 2)];   // 64 KB
     // the reduction workgroups first, so that they overlap the expansion instead of trailing it
     if (blockIdx.x < g.nred) {
         reduce_partials_block(g.red, blockIdx.x, g.nred);
@@ -115,41 +119,51 @@ __global__ __launch_bounds__(256) void expand_transposed_kernel(ExpandArgs g) {
     const int64_t tb = blockIdx.x - g.nred;
     const int tid = threadIdx.x;
     const int64_t nbk = g.K >> 6;
-    const int64_t ntn = (g.N + 63) >> 6;
-    const int64_t kb = tb / ntn;
-    const int64_t n0 = (tb % ntn) * 64;
+    const int64_t ntn = (g.N + TT_N - 1) / TT_N;
+    const int64_t kt = tb / ntn;
+    const int64_t n0 = (tb % ntn) * TT_N;
     const float mean = g.mean[0];
     const bool dq_i8 = g.dq_int8 != 0;
     {
-        const int nl = tid >> 2, q = tid & 3;
-        const int64_t n = n0 + nl;
-        uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (n < g.N) {
-            const int64_t b = n * nbk + kb;
-            const Lut t = make_lut(g.cb, block_scale(g.c2[b], g.c1[b >> 8], mean, dq_i8));
-            const uint2 w = *reinterpret_cast<const uint2 *>(g.packed + b * 32 + q * 8);
-            const u32x4 lo = dequant8(t, w.x), hi = dequant8(t, w.y);
-            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-        }
+        const int p = tid >> 2, q = tid & 3;
+        const int64_t n = n0 + 2 * p;
+        const int64_t kb = kt * 4 + q;
+        if (n < g.N && kb < nbk) {      // N is even: row n + 1 exists too
+            const int64_t ba = n * nbk + kb, bb = ba + nbk;
+            const u32x4 *pa = reinterpret_cast<const u32x4 *>(g.packed + ba * 32);
+            const u32x4 *pb = reinterpret_cast<const u32x4 *>(g.packed + bb * 32);
+            const u32x4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+            const Lut La = make_lut(g.cb, block_scale(g.c2[ba], g.c1[ba >> 8], mean, dq_i8));
+            const Lut Lb = make_lut(g.cb, block_scale(g.c2[bb], g.c1[bb >> 8], mean, dq_i8));
+            const uint32_t wa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const uint32_t wb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const int grp = (p >> 2) ^ (4 * q), sub = p & 3;
+            uint32_t *col = tile + grp * 4 + sub;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) tile[(16 * q + e) * TROW + (nl ^ (16 * q))] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            for (int d = 0; d < 8; ++d) {
+                const u32x4 ea = dequant8(La, wa[d]), eb = dequant8(Lb, wb[d]);
+                const uint32_t ev[4] = {ea.x, ea.y, ea.z, ea.w}, fv[4] = {eb.x, eb.y, eb.z, eb.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kk = 64 * q + 8 * d + 2 * i;
+                    col[kk * (TT_N / 2)] = __builtin_amdgcn_perm(fv[i], ev[i], 0x05040100u);
+                    col[(kk + 1) * (TT_N / 2)] = __builtin_amdgcn_perm(fv[i], ev[i], 0x07060302u);
+                }
+            }
+        }
     }
     __syncthreads();
     {
-        const int kl = tid >> 2, q = tid & 3;
-        const int64_t k = kb * 64 + kl;
-        const int64_t n = n0 + 16 * q;
-        const u32x4 *s = reinterpret_cast<const u32x4 *>(tile + kl * TROW + 16 * (q ^ ((kl >> 4) & 3)));
-        const u32x4 a = s[0], c = s[1];
-        uint16_t *dst = g.out + k * g.N + n;
-        // plain stores: the four 32-byte pieces of a 128-byte row segment combine in L2
-        if (n + 16 <= g.N) {
-            reinterpret_cast<u32x4 *>(dst)[0] = a;
-            reinterpret_cast<u32x4 *>(dst)[1] = c;
-        } else {
-            // N % 8 == 0: the last tile ends on an 8-column boundary
-            if (n < g.N) reinterpret_cast<u32x4 *>(dst)[0] = a;
+        const int c = tid & 15, r16 = tid >> 4;
+        const int64_t n = n0 + 8 * c;
+#pragma unroll 4
+        for (int it = 0; it < TT_K / 16; ++it) {
+            const int kk = r16 + 16 * it;
+            const int64_t k = kt * TT_K + kk;
+            if (k < g.K && n < g.N) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + kk * (TT_N / 2) + ((c ^ (4 * (kk >> 6))) * 4));
+                *reinterpret_cast<u32x4 *>(g.out + k * g.N + n) = v;
+            }
         }
     }
 }
@@ -175,7 +189,7 @@ hipError_t launch_expand_weight(const WeightView &w, bool transposed, uint16_t *
         a.nexp = (uint32_t)grid;
         hipLaunchKernelGGL(expand_rows_kernel, dim3(a.nexp + a.nred + a.ntr), dim3(256), 0, stream, a);
     } else {
-        a.nexp = (uint32_t)(((w.rows + 63) / 64) * (w.cols / 64));
+        a.nexp = (uint32_t)(((w.rows + TT_N - 1) / TT_N) * ((w.cols + TT_K - 1) / TT_K));
         hipLaunchKernelGGL(expand_transposed_kernel, dim3(a.nexp + a.nred), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
