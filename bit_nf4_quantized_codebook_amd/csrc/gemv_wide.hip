@@ -16,7 +16,11 @@
 //     fragments are stored in LDS in the same order (permuted once per window)
 //   - W is fetched four macro steps ahead; X is staged through LDS in windows of 1024 columns,
 //     double buffered (the next window travels through registers while the current one is
-//     consumed), shared by the 4 waves of a block
+//     consumed), shared by the waves of a block
+//   - a block has NW = ceil(N / 16 / 256) waves (4 to 8), so that the grid is about one block
+//     per CU (28672 rows: 256 blocks of 7 waves, where 4-wave blocks made 448, two on most CUs)
+//   - the kernel is bound by the VALU work of the exact decode (about 250 VALU instructions per
+//     wave per 4096 weights), not by HBM
 // Epilogue: 2 more MFMAs add s T L2 (A = s T, B = a strided gather of L2), then bf16 stores.
 
 #include "common.h"
@@ -27,8 +31,7 @@ namespace nf4k {
 
 namespace {
 
-constexpr int NWAVE = 4;
-constexpr int ROWS_PER_WG = 16 * NWAVE;        // 64 W rows
+constexpr int NWAVE_MAX = 8;
 constexpr int XWIN = 1024;                     // X window (columns)
 constexpr int XROW = XWIN + 8;                 // padded LDS row (elements): rows start 4 banks apart
 constexpr int MACRO = 256;                     // columns per macro step (4 blocks)
@@ -64,17 +67,19 @@ struct GemvArgs {
 
 // I8: the second-level codes are int8 (else E4M3), fixed at compile time so that the E4M3
 // kernel carries no per-block select.
-template <int MROWS, bool I8>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+template <int MROWS, bool I8, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     // X window: [MROWS rows][XWIN cols], planar within each 8-column group, double buffered.
     // Lanes whose token row is >= MROWS feed zeros to the MFMA without touching LDS.
     __shared__ __align__(16) uint8_t Xs0[MROWS * XROW * 2];
     __shared__ __align__(16) uint8_t Xs1[MROWS * XROW * 2];
-    constexpr int XCH = MROWS * (XWIN / 8) / 256;        // 16-byte X chunks per thread per window
+    constexpr int NT = NW * 64;
+    constexpr int XCHUNKS = MROWS * (XWIN / 8);           // 16-byte X chunks per window
+    constexpr int XCH = (XCHUNKS + NT - 1) / NT;         // per thread (the last round part-filled)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * ROWS_PER_WG + wave * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * NW) + wave * 16;
     const int64_t n = n0 + ln;                      // this lane's W row
     const int64_t wrow_bytes = g.K >> 1, nblk = g.K >> 6;
     const float mean = g.mean[0];
@@ -92,19 +97,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     auto fetch_x = [&](int win) {
 #pragma unroll
         for (int q = 0; q < XCH; ++q) {
-            const int c = tid + 256 * q;                 // chunk id: row = c / 128, col8 = c % 128
+            const int c = tid + NT * q;                  // chunk id: row = c / 128, col8 = c % 128
             const int row = c >> 7, col8 = c & 127;
             const int64_t k = (int64_t)win * XWIN + col8 * 8;
-            const bool ok = row < g.M && k < g.K;
+            const bool ok = c < XCHUNKS && row < g.M && k < g.K;
             xr[q] = bload16(rX, ok ? (uint32_t)((row * g.K + k) * 2) : 0xFFFFFFF0u);
         }
     };
     auto store_x = [&](uint8_t *dst) {
 #pragma unroll
         for (int q = 0; q < XCH; ++q) {
-            const int c = tid + 256 * q;
+            const int c = tid + NT * q;
             const int row = c >> 7, col8 = c & 127;
-            *reinterpret_cast<u32x4 *>(dst + (row * XROW + col8 * 8) * 2) = to_planar(xr[q]);
+            if (c < XCHUNKS)
+                *reinterpret_cast<u32x4 *>(dst + (row * XROW + col8 * 8) * 2) = to_planar(xr[q]);
         }
     };
 
@@ -204,6 +210,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     }
 }
 
+template <bool I8>
+void launch_i8(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
+    const dim3 gd(grid);
+    switch (nw) {
+        case 1: hipLaunchKernelGGL((gemv_kernel<16, I8, 1>), gd, dim3(64), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<16, I8, 2>), gd, dim3(128), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((gemv_kernel<16, I8, 3>), gd, dim3(192), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((gemv_kernel<16, I8, 4>), gd, dim3(256), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((gemv_kernel<16, I8, 5>), gd, dim3(320), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((gemv_kernel<16, I8, 6>), gd, dim3(384), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((gemv_kernel<16, I8, 7>), gd, dim3(448), 0, stream, a); break;
+        default: hipLaunchKernelGGL((gemv_kernel<16, I8, 8>), gd, dim3(512), 0, stream, a); break;
+    }
+}
+void launch_nw(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
+    if (a.dq_int8) launch_i8<true>(a, nw, grid, stream);
+    else launch_i8<false>(a, nw, grid, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
@@ -214,12 +239,15 @@ hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const ui
     a.sT = sT; a.L2 = L2; a.Y = Y;
     a.M = M; a.N = w.rows; a.K = w.cols; a.r = r;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
-    const int grid = (int)((w.rows + ROWS_PER_WG - 1) / ROWS_PER_WG);
+    // waves per block: about one block per CU, and at least 4 (each block stages the whole X
+    // window for its rows, so fewer waves would read X from L2 more often than W from HBM)
+    const int64_t groups = (w.rows + 15) / 16;
+    int nw = (int)((groups + 255) / 256);
+    nw = nw < 4 ? 4 : (nw > NWAVE_MAX ? NWAVE_MAX : nw);
+    if (groups < nw) nw = (int)groups;
+    const int grid = (int)((groups + nw - 1) / nw);
     timing_before(stream, 2);
-    if (a.dq_int8)
-        hipLaunchKernelGGL((gemv_kernel<16, true>), dim3(grid), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemv_kernel<16, false>), dim3(grid), dim3(256), 0, stream, a);
+    launch_nw(a, nw, grid, stream);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
