@@ -18,24 +18,48 @@ namespace nf4k {
 // decision thresholds strictly below n, where thr[j] is the largest float not above the midpoint
 // of codewords j and j+1 (so ties go to the lower index).  Each lane writes its 4 codes as 2 bytes
 // (128 contiguous bytes per wave and q).
+//
+// n = fp32(x / a) without a division per element: with r = fp32(1 / a) (one IEEE division per
+// block and lane), q0 = fp32(x r) is within an ulp of x / a, the remainder x - a q0 is exact in
+// one fma, and fp32(q0 + (x - a q0) r) is the correctly rounded quotient (Markstein's correction
+// step) as long as that remainder stays in the normal range.  With a in [2^-60, 2^100] it does
+// for every quotient of magnitude 2^-40 or more; below that the result may differ from x / a in
+// its last bits, which decides no code as long as every threshold is at least 2^-39 away from
+// zero (the host checks; otherwise, and for blocks outside that range, the kernel divides).  A
+// CPU run over 4e8 random and boundary cases (all-ones significands, quotients next to the
+// thresholds) found no difference at or above 2^-40.
+// The code is found by binary search over the 15 sorted (non-decreasing) thresholds, one bit per
+// level: 4 compares, the thresholds of the last three levels read from a 16-entry LDS table at the
+// index the bits so far give (all lanes read one of a few words: broadcast, no bank conflicts),
+// instead of 15 compares that each waited on the one condition register.
 // ------------------------------------------------------------------------------------------
 struct Thresholds {
     float t[15];
 };
 
-__device__ __forceinline__ uint32_t nearest_code(float n, const Thresholds &th) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 15; ++j) c += (n > th.t[j]) ? 1u : 0u;
-    return c;
+// v moved by the DPP control CTRL within 16-lane rows (every source lane inside the row)
+template <int CTRL>
+__device__ __forceinline__ float row_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// t7: the middle threshold; ts: the 15 thresholds in LDS
+__device__ __forceinline__ uint32_t nearest_code(float n, float t7, const float *ts) {
+    uint32_t c = n > t7 ? 1u : 0u;                        // c = b3
+    c = 2 * c + (n > ts[8 * c + 3] ? 1u : 0u);            // t[3] or t[11]; c = 2 b3 + b2
+    c = 2 * c + (n > ts[4 * c + 1] ? 1u : 0u);            // t[1], t[5], t[9] or t[13]
+    return 2 * c + (n > ts[2 * c] ? 1u : 0u);             // t[0], t[2], ..., t[14]
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ W, int64_t numel,
-                                                       Thresholds th, uint32_t zero_code,
+                                                       Thresholds th, uint32_t zero_code, uint32_t fast_div,
                                                        uint8_t *__restrict__ packed,
                                                        float *__restrict__ absmax) {
     typedef float f4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
+    __shared__ float ts[16];
+    if (threadIdx.x < 15) ts[threadIdx.x] = th.t[threadIdx.x];
+    __syncthreads();
     const int64_t nblocks = (numel + 63) >> 6;
     const int64_t nchunks = (numel + 511) >> 9;                      // 512-element wave chunks
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -60,17 +84,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
             const int64_t e0 = base + 256 * q + 4 * lane;
             const int64_t b = e0 >> 6;
             float a = fmaxf(fmaxf(fabsf(x[q][0]), fabsf(x[q][1])), fmaxf(fabsf(x[q][2]), fabsf(x[q][3])));
-            a = fmaxf(a, __shfl_xor(a, 1, 16));
-            a = fmaxf(a, __shfl_xor(a, 2, 16));
-            a = fmaxf(a, __shfl_xor(a, 4, 16));
-            a = fmaxf(a, __shfl_xor(a, 8, 16));
+            // max over the block's 16 lanes with DPP row moves (no LDS round trips): lane ^ 1,
+            // lane ^ 2 (quad permutes), then the mirror within each 8 and within the 16
+            a = fmaxf(a, row_move<0xB1>(a));
+            a = fmaxf(a, row_move<0x4E>(a));
+            a = fmaxf(a, row_move<0x141>(a));
+            a = fmaxf(a, row_move<0x140>(a));
+            float n[4];
+            if (fast_div && a >= 0x1p-60f && a <= 0x1p100f) {   // uniform per block
+                const float r = 1.0f / a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float q0 = x[q][i] * r;
+                    n[i] = __builtin_fmaf(__builtin_fmaf(-a, q0, x[q][i]), r, q0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) n[i] = x[q][i] / a;   // a == 0: masked below
+            }
+            // every element is coded (an all-zero block or a padding element as n = 0), then the
+            // zero code is selected for those: no branch per element
             uint32_t word = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint32_t c = zero_code;
-                if (a != 0.0f) c = nearest_code(x[q][i] / a, th);
-                if (e0 + i >= numel) c = zero_code;
-                word |= c << (4 * i);
+                const bool valid = a != 0.0f && e0 + i < numel;
+                const uint32_t c = nearest_code(valid ? n[i] : 0.0f, th.t[7], ts);
+                word |= (valid ? c : zero_code) << (4 * i);
             }
             if ((lane & 15) == 0 && b < nblocks) absmax[b] = a;
             const int64_t byte = e0 >> 1;
@@ -278,11 +317,17 @@ hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], u
                            uint8_t *packed, float *absmax, hipStream_t stream) {
     if (numel == 0) return hipSuccess;
     Thresholds th;
-    for (int j = 0; j < 15; ++j) th.t[j] = thr[j];
+    // the reciprocal form of the division decides every code as the division would when no
+    // threshold lies within 2^-39 of zero (see the kernel)
+    uint32_t fast_div = 1;
+    for (int j = 0; j < 15; ++j) {
+        th.t[j] = thr[j];
+        if (!(std::fabs(thr[j]) >= 0x1p-39f)) fast_div = 0;   // also a NaN threshold
+    }
     const int64_t nchunks = (numel + 511) >> 9;
     const int grid = grid_for(nchunks, 4, 256 * 32);
     hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(256), 0, stream, W, numel, th, zero_code,
-                       packed, absmax);
+                       fast_div, packed, absmax);
     return hipGetLastError();
 }
 
