@@ -580,6 +580,8 @@ def main():
     ap.add_argument("--no-mlp", action="store_true", help="skip the two MLP workloads (c3, c4 keys)")
     ap.add_argument("--no-mid", action="store_true", help="skip the mid-size token counts (mid key)")
     ap.add_argument("--mid", action="store_true", help="time only the mid-size token counts")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time only quantization + double quantization of the 65B-shaped MLP's weights")
     ap.add_argument("--gemv-only", action="store_true", help="time only the decode-size forward")
     ap.add_argument("--qerror", action="store_true",
                     help="quantization error of NF4, Int4 and FP4, with and without DQ, on synthetic "
@@ -628,6 +630,9 @@ def main():
         return
     if args.mid:
         print(json.dumps(bench_mid(torch, nf4, synth, dev)), flush=True)
+        return
+    if args.quantize:
+        print(json.dumps(bench_quantize(torch, nf4, synth, dev, synth.WORKLOADS["llama65b_mlp"])), flush=True)
         return
     if args.qerror:
         print(json.dumps({"workload": "qerror: 4-bit types on synthetic 4096x4096 weights",
