@@ -487,9 +487,10 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
 
 def bench_mid(torch, nf4, synth, dev, Ms=(32, 256, 512, 1536), steps=20, warmup=5):
     """The LLaMA-7B attention projection (W 4096 x 4096, r = 64) forward + backward at token counts
-    between the decode GEMVs and the training shapes: the fused dequant GEMMs (up to 1023 tokens)
-    and the expanded-weight GEMM below a full wave of output tiles, each with its reduction split
-    over several workgroups per tile (qlora_linear_route gives the splits)."""
+    between the decode GEMVs and the training shapes: the wide GEMV forward (up to 32 tokens), the
+    fused dequant GEMMs (the backward, and the forward from 33 tokens) and the expanded-weight GEMM
+    below a full wave of output tiles, each with its reduction split over several workgroups where
+    the output tiles leave CUs idle (qlora_linear_route gives the paths and splits)."""
     wl = synth.WORKLOADS["llama7b_attn"]
     lin = wl.linears[0]
     out = {"workload": f"W {lin.N}x{lin.K} NF4, LoRA r={wl.r}, forward + backward, by token count"}

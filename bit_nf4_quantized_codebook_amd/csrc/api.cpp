@@ -140,7 +140,7 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // Workspace plan of the linear layer (identical for the size query and the calls)
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
-constexpr int64_t kGemvMaxM = 16;     // token counts served by a weight-streaming GEMV
+constexpr int64_t kGemvMaxM = 32;     // token counts whose forward is a weight-streaming GEMV
 // From this many tokens on, the weight is expanded to bf16 once per call and multiplied by a plain
 // bf16 GEMM: the expansion pass costs about 2.5 bytes of HBM traffic per weight, while dequantizing
 // inside the GEMM repeats the work once per 256-row tile of tokens and its VALU work does not hide
@@ -166,12 +166,15 @@ struct Plan {
 constexpr int64_t kGemmTile = 256;   // output tile of the product kernels (both dims)
 constexpr int kSplitQuantum = 4;     // reduction steps per split: a multiple of 4
 
-// the products' splits: forward [M, N] over K, backward [M, K] over N
-void plan_splits(Plan &p, int64_t M, int64_t N, int64_t K) {
+// the products' splits: forward [M, N] over K (the wide GEMV's own rule up to kGemvMaxM tokens,
+// none for the decode GEMV), backward [M, K] over N
+void plan_splits(Plan &p, int64_t M, int64_t N, int64_t K, int32_t r) {
     const int64_t mt = (M + kGemmTile - 1) / kGemmTile;
     p.kf = p.kb = nf4k::SplitPlan{1, 0};
-    if (M <= kGemvMaxM) return;
-    p.kf = nf4k::gemm_split(mt * ((N + kGemmTile - 1) / kGemmTile), (K + kTile - 1) / kTile, kSplitQuantum);
+    if (M > kGemvMaxM)
+        p.kf = nf4k::gemm_split(mt * ((N + kGemmTile - 1) / kGemmTile), (K + kTile - 1) / kTile, kSplitQuantum);
+    else if (!nf4k::gemv_fits(M, N, K, r))
+        p.kf = nf4k::gemv_wide_split(M, N, K);
     p.kb = nf4k::gemm_split(mt * ((K + kGemmTile - 1) / kGemmTile), (N + kTile - 1) / kTile, kSplitQuantum);
 }
 size_t split_floats(const Plan &p, int64_t M, int64_t N, int64_t K, bool fwd_only) {
@@ -217,7 +220,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
         p.off_Yp = off;  off += round256(g.yp_floats * 4);
         p.off_Tp = off;  off += round256(g.tp_floats * 4);
     }
-    plan_splits(p, M, N, K);
+    plan_splits(p, M, N, K, r);
     p.off_Pg = off;  off += round256(split_floats(p, M, N, K, false) * 4);
     p.total = off;
     return p;
@@ -489,7 +492,7 @@ int qlora_linear_route(int64_t M, int64_t N, int64_t K, int32_t r, int32_t info[
     info[0] = gemv ? 1 : (M <= kGemvMaxM ? 2 : (use_expand(M, N, K) ? 4 : 3));
     info[1] = p.kf.ksplit;
     info[2] = p.kb.ksplit;
-    info[3] = M <= kGemvMaxM ? 0 : (use_expand(M, N, K) ? 4 : 3);
+    info[3] = use_expand(M, N, K) ? 4 : 3;
     return NF4_OK;
 }
 
@@ -547,8 +550,9 @@ int linear_fwd_run(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, c
     int rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
     if (M <= kGemvMaxM) {
-        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, s), "dequant GEMV (fwd)");
-        return NF4_OK;
+        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, split_of(p.kf, p, workspace), s),
+                      "dequant GEMV (fwd)");
+        return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
     }
     NF4_CHECK_HIP(nf4k::launch_dqgemm_fwd(view_of(w), X, sT, L2, r, M, Y, split_of(p.kf, p, workspace), s),
                   "fused dequant GEMM (fwd)");

@@ -1,4 +1,4 @@
-// Small-batch forward (9 to 16 tokens, and smaller token counts on shapes the row kernel of
+// Small-batch forward (9 to 32 tokens, and smaller token counts on shapes the row kernel of
 // the decode GEMV does not take) of the QLoRA linear layer (gfx950):
 //   Y = X deq(W)^T + s T L2,   T = X L1 computed beforehand (s T passed in, bf16 [M, r])
 //
@@ -8,7 +8,9 @@
 // This shape streams the 4-bit weight once from HBM; the cost to hide is the dequantization,
 // not the arithmetic.  With up to 16 tokens the 16 rows of v_mfma_f32_16x16x32_bf16 are mostly
 // used, so the products go there (rows past M are zero), and the VALU only turns codes into bf16
-// -- exactly the dequantized weights of eq. (6), so this path matches the large-batch GEMM:
+// -- exactly the dequantized weights of eq. (6), so this path matches the large-batch GEMM.
+// 17 to 32 tokens take two groups of 16: each decoded B fragment feeds one MFMA per group, so
+// the decode, which bounds the kernel, is done once for both:
 //   - a wave owns 16 W rows; per 256-column "macro step" lane (n = l % 16, g = l / 16) owns one
 //     whole quantization block (row n, block 4 step + g): 32 packed bytes, one 16-entry bf16
 //     table (v_perm byte planes), 8 dwords -> 8 MFMAs (one B fragment each)
@@ -18,7 +20,10 @@
 //     double buffered (the next window travels through registers while the current one is
 //     consumed), shared by the waves of a block
 //   - a block has NW = ceil(N / 16 / 256) waves (4 to 8), so that the grid is about one block
-//     per CU (28672 rows: 256 blocks of 7 waves, where 4-wave blocks made 448, two on most CUs)
+//     per CU (28672 rows: 256 blocks of 7 waves, where 4-wave blocks made 448, two on most CUs);
+//     where the rows give fewer blocks than CUs (4096 rows: 64), the reduction is split over
+//     S = 256 / blocks workgroups of whole X windows each, which write float32 partials that a
+//     fixed-order pass sums (the LoRA term rides in the last split)
 //   - the kernel is bound by the VALU work of the exact decode (about 250 VALU instructions per
 //     wave per 4096 weights), not by HBM
 // Epilogue: 2 more MFMAs add s T L2 (A = s T, B = a strided gather of L2), then bf16 stores.
@@ -60,8 +65,10 @@ struct GemvArgs {
     const uint16_t *sT;      // [M, r]  (s * X L1)
     const uint16_t *L2;      // [r, N]
     uint16_t *Y;             // [M, N]
+    float *P;                // [ksplit, M, N] partials (ksplit > 1)
     int64_t M, N, K;
     int32_t r;
+    int32_t ksplit, kper;    // reduction split: macro steps per split (a multiple of 4)
     Codebook cb;
 };
 
@@ -69,8 +76,8 @@ struct GemvArgs {
 // kernel carries no per-block select.
 template <int MROWS, bool I8, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
-    // X window: [MROWS rows][XWIN cols], planar within each 8-column group, double buffered.
-    // Lanes whose token row is >= MROWS feed zeros to the MFMA without touching LDS.
+    // X window: [MROWS rows][XWIN cols], planar within each 8-column group, double buffered;
+    // rows at or past M hold zeros.
     __shared__ __align__(16) uint8_t Xs0[MROWS * XROW * 2];
     __shared__ __align__(16) uint8_t Xs1[MROWS * XROW * 2];
     constexpr int NT = NW * 64;
@@ -79,7 +86,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * NW) + wave * 16;
+    const int nrb = (int)(gridDim.x / g.ksplit);             // row blocks
+    const int split = (int)blockIdx.x / nrb;
+    const int64_t n0 = (int64_t)((int)blockIdx.x - split * nrb) * (16 * NW) + wave * 16;
     const int64_t n = n0 + ln;                      // this lane's W row
     const int64_t wrow_bytes = g.K >> 1, nblk = g.K >> 6;
     const float mean = g.mean[0];
@@ -89,8 +98,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.N * nblk);
     const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(g.c1, ((g.N * nblk + 255) >> 8) * 4);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.X, g.M * g.K * 2);
+    constexpr int G = MROWS / 16;                     // 16-token groups
 
     const int nmacro = (int)((g.K + MACRO - 1) / MACRO);
+    const int ms_begin = split * g.kper;                       // this workgroup's macro steps
+    const int ms_end = min(nmacro, ms_begin + g.kper);
+    const int64_t kend = min(g.K, (int64_t)ms_end * MACRO);
 
     // ---- X windows: global -> registers early, registers -> LDS later ----
     u32x4 xr[XCH];
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
             const int c = tid + NT * q;                  // chunk id: row = c / 128, col8 = c % 128
             const int row = c >> 7, col8 = c & 127;
             const int64_t k = (int64_t)win * XWIN + col8 * 8;
-            const bool ok = c < XCHUNKS && row < g.M && k < g.K;
+            const bool ok = c < XCHUNKS && row < g.M && k < kend;
             xr[q] = bload16(rX, ok ? (uint32_t)((row * g.K + k) * 2) : 0xFFFFFFF0u);
         }
     };
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     };
     auto load_w = [&](int ms, WStage &st) {
         const int64_t blk = (int64_t)ms * 4 + lg;
-        const bool live = ms < nmacro && blk < nblk;
+        const bool live = ms < ms_end && blk < nblk;
         const uint32_t off = (uint32_t)(ln * wrow_bytes + blk * 32);
         st.w[0] = bload16(rW, live ? off : 0xFFFFFFF0u);
         st.w[1] = bload16(rW, live ? off + 16 : 0xFFFFFFF0u);
@@ -130,43 +143,48 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
         st.c1 = bload4(rC1, okr ? (b >> 8) * 4 : 0xFFFFFFF0u);
     };
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto macro_step = [&](int ms, const WStage &st, const uint8_t *Xw) {
         const int kin = (ms * MACRO) % XWIN;             // column offset inside the window
         const int64_t blk = (int64_t)ms * 4 + lg;
         float a = block_scale(st.c2, __uint_as_float(st.c1), mean, dq_i8);
-        if (ms >= nmacro || blk >= nblk) a = 0.0f;        // past K: contributes nothing
+        if (ms >= ms_end || blk >= nblk) a = 0.0f;        // past the split or K: contributes nothing
         const Lut t = make_lut(g.cb, a);
         const uint32_t wd[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
                                 st.w[1].x, st.w[1].y, st.w[1].z, st.w[1].w};
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
             const u32x4 b = dequant8_planar(t, wd[d]);
-            // A: X row ln, columns kin + 64 lg + 8 d .. +7 (planar, same order as b)
-            u32x4 av = {0u, 0u, 0u, 0u};
-            if (ln < MROWS)
-                av = *reinterpret_cast<const u32x4 *>(Xw + (ln * XROW + kin + lg * 64 + d * 8) * 2);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+            // A of group q: X row 16 q + ln, columns kin + 64 lg + 8 d .. +7 (planar, as b)
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                const u32x4 av =
+                    *reinterpret_cast<const u32x4 *>(Xw + ((16 * q + ln) * XROW + kin + lg * 64 + d * 8) * 2);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                 __builtin_bit_cast(bf16x8, b), acc[q], 0, 0, 0);
+            }
         }
     };
 
     // Four macro steps per X window (XWIN / MACRO); W is fetched four macro steps ahead.
     // Window w+1 is fetched at the first macro step of window w, written to the other LDS buffer
     // at its third, and made visible by the barrier that closes window w.
+    // ms_begin and the split length are multiples of 4: a split covers whole windows.
     WStage S0, S1, S2, S3;
-    fetch_x(0);
+    fetch_x(ms_begin / 4);
     store_x(Xs0);
-    load_w(0, S0);
-    load_w(1, S1);
-    load_w(2, S2);
-    load_w(3, S3);
+    load_w(ms_begin, S0);
+    load_w(ms_begin + 1, S1);
+    load_w(ms_begin + 2, S2);
+    load_w(ms_begin + 3, S3);
     __syncthreads();
-    for (int ms = 0; ms < nmacro; ms += 4) {
+    for (int ms = ms_begin; ms < ms_end; ms += 4) {
         const int win = ms / 4;
-        uint8_t *Xcur = (win & 1) ? Xs1 : Xs0;
-        uint8_t *Xnxt = (win & 1) ? Xs0 : Xs1;
-        fetch_x(win + 1);                                // past the end: reads zeros
+        uint8_t *Xcur = ((ms - ms_begin) & 4) ? Xs1 : Xs0;
+        uint8_t *Xnxt = ((ms - ms_begin) & 4) ? Xs0 : Xs1;
+        fetch_x(win + 1);                                // past the split's end: reads zeros
         macro_step(ms, S0, Xcur);
         load_w(ms + 4, S0);
         macro_step(ms + 1, S1, Xcur);
@@ -179,14 +197,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
         __syncthreads();
     }
 
-    // ---- LoRA: acc += (s T) L2 over r in steps of 32 (two MFMAs for r = 64) ----
+    // ---- LoRA (last split): acc += (s T) L2 over r in steps of 32 (two MFMAs for r = 64) ----
     const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.sT, g.M * (int64_t)g.r * 2);
     const __amdgpu_buffer_rsrc_t rL2 = make_rsrc(g.L2, (int64_t)g.r * g.N * 2);
-    for (int j0 = 0; j0 < g.r; j0 += 32) {
-        // A: sT row ln, j = j0 + 8 lg .. +7 (natural order); B: L2[j][n] for the same j
+    const int rlora = split == g.ksplit - 1 ? g.r : 0;
+    for (int j0 = 0; j0 < rlora; j0 += 32) {
+        // A of group q: sT row 16 q + ln, j = j0 + 8 lg .. +7 (natural order); B: L2[j][n] for
+        // the same j
         const int jj = j0 + lg * 8;
-        const bool oka = ln < g.M && jj < g.r;
-        const u32x4 av = bload16(rT, oka ? (uint32_t)((ln * (int64_t)g.r + jj) * 2) : 0xFFFFFFF0u);
         uint32_t bw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -196,56 +214,109 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
             bw[i] = (lo & 0xFFFFu) | (hi << 16);
         }
         const u32x4 bv = {bw[0], bw[1], bw[2], bw[3]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                      __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int64_t row = 16 * q + ln;
+            const bool oka = row < g.M && jj < g.r;
+            const u32x4 av = bload16(rT, oka ? (uint32_t)((row * g.r + jj) * 2) : 0xFFFFFFF0u);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, bv), acc[q], 0, 0, 0);
+        }
     }
 
-    // ---- store: lane holds rows 4 lg + i (tokens), column n ----
+    // ---- store: lane holds rows 16 q + 4 lg + i (tokens) of group q, column n ----
     if (n < g.N) {
+        float *P = g.P + (int64_t)split * g.M * g.N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = lg * 4 + i;
-            if (m < g.M) g.Y[m * g.N + n] = (uint16_t)f32_to_bf16(acc[i]);
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * q + lg * 4 + i;
+                if (m < g.M) {
+                    if (g.ksplit > 1) P[m * g.N + n] = acc[q][i];
+                    else g.Y[m * g.N + n] = (uint16_t)f32_to_bf16(acc[q][i]);
+                }
+            }
         }
     }
 }
 
-template <bool I8>
+// 16 token rows: 1 to 8 waves; 32 rows: 4 to 8 (fewer waves would hold a larger share of the
+// X window in registers)
+template <int MROWS, bool I8>
 void launch_i8(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
     const dim3 gd(grid);
     switch (nw) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<16, I8, 1>), gd, dim3(64), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<16, I8, 2>), gd, dim3(128), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((gemv_kernel<16, I8, 3>), gd, dim3(192), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<16, I8, 4>), gd, dim3(256), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((gemv_kernel<16, I8, 5>), gd, dim3(320), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((gemv_kernel<16, I8, 6>), gd, dim3(384), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL((gemv_kernel<16, I8, 7>), gd, dim3(448), 0, stream, a); break;
-        default: hipLaunchKernelGGL((gemv_kernel<16, I8, 8>), gd, dim3(512), 0, stream, a); break;
+        case 1: if constexpr (MROWS == 16) hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 1>), gd, dim3(64), 0, stream, a); break;
+        case 2: if constexpr (MROWS == 16) hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 2>), gd, dim3(128), 0, stream, a); break;
+        case 3: if constexpr (MROWS == 16) hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 3>), gd, dim3(192), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 4>), gd, dim3(256), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 5>), gd, dim3(320), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 6>), gd, dim3(384), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 7>), gd, dim3(448), 0, stream, a); break;
+        default: hipLaunchKernelGGL((gemv_kernel<MROWS, I8, 8>), gd, dim3(512), 0, stream, a); break;
     }
 }
 void launch_nw(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
-    if (a.dq_int8) launch_i8<true>(a, nw, grid, stream);
-    else launch_i8<false>(a, nw, grid, stream);
+    if (a.M > 16) {
+        if (a.dq_int8) launch_i8<32, true>(a, nw, grid, stream);
+        else launch_i8<32, false>(a, nw, grid, stream);
+    } else {
+        if (a.dq_int8) launch_i8<16, true>(a, nw, grid, stream);
+        else launch_i8<16, false>(a, nw, grid, stream);
+    }
+}
+
+// waves per block: about one block per CU, and at least 4 (each block stages the whole X window
+// for its rows, so fewer waves would read X from L2 more often than W from HBM); 32 token rows
+// keep 4 waves even for fewer row groups (the idle waves store nothing)
+int wide_waves(int64_t M, int64_t N) {
+    const int64_t groups = (N + 15) / 16;
+    int nw = (int)((groups + 255) / 256);
+    nw = nw < 4 ? 4 : (nw > NWAVE_MAX ? NWAVE_MAX : nw);
+    if (groups < nw && M <= 16) nw = (int)groups;
+    return nw;
 }
 
 }  // namespace
 
+// Split the reduction when the row blocks leave CUs idle: S = 256 / blocks workgroups per row
+// block, each over whole 1024-column windows (per = a multiple of 4 macro steps), no split empty.
+SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K) {
+    const int nw = wide_waves(M, N);
+    const int64_t blocks = ((N + 15) / 16 + nw - 1) / nw;
+    const int64_t nmacro = (K + MACRO - 1) / MACRO, nwin = (nmacro + 3) / 4;
+    int64_t s = blocks > 0 ? 256 / blocks : 1;
+    if (s > nwin) s = nwin;
+    if (s > 16) s = 16;
+    if (s <= 1) return SplitPlan{1, nwin * 4};
+    const int64_t wper = (nwin + s - 1) / s;
+    s = (nwin + wper - 1) / wper;
+    return s <= 1 ? SplitPlan{1, nwin * 4} : SplitPlan{(int)s, wper * 4};
+}
+
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
-                                const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream) {
+                                const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, const SplitK &sk,
+                                hipStream_t stream) {
+    if (M < 1 || M > 32) return hipErrorInvalidValue;
     GemvArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
     a.sT = sT; a.L2 = L2; a.Y = Y;
     a.M = M; a.N = w.rows; a.K = w.cols; a.r = r;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
-    // waves per block: about one block per CU, and at least 4 (each block stages the whole X
-    // window for its rows, so fewer waves would read X from L2 more often than W from HBM)
+    const int nw = wide_waves(M, w.rows);
+    if (M > 16 && nw < 4) return hipErrorInvalidValue;
+    const int64_t nmacro = (w.cols + MACRO - 1) / MACRO;
+    a.ksplit = sk.ksplit > 1 ? sk.ksplit : 1;
+    a.kper = (int32_t)(a.ksplit > 1 ? sk.per : (nmacro + 3) / 4 * 4);
+    a.P = sk.P;
+    // every split non-empty and made of whole windows: what the kernel's window loop assumes
+    if (a.ksplit > 1 && (!sk.P || sk.per % 4 || (int64_t)(a.ksplit - 1) * sk.per >= nmacro ||
+                         (int64_t)a.ksplit * sk.per < nmacro))
+        return hipErrorInvalidValue;
     const int64_t groups = (w.rows + 15) / 16;
-    int nw = (int)((groups + 255) / 256);
-    nw = nw < 4 ? 4 : (nw > NWAVE_MAX ? NWAVE_MAX : nw);
-    if (groups < nw) nw = (int)groups;
-    const int grid = (int)((groups + nw - 1) / nw);
+    const int grid = (int)((groups + nw - 1) / nw) * a.ksplit;
     timing_before(stream, 2);
     launch_nw(a, nw, grid, stream);
     hipError_t e = hipGetLastError();

@@ -54,8 +54,13 @@ hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint1
                              const SplitK &sk, hipStream_t stream);
 // up to 16 tokens (9-16, or fewer on shapes the row kernel does not take): sT = s X L1 (bf16
 // [M, r]) computed beforehand
+// small-batch forward (M <= 32); with sk.ksplit > 1 each workgroup takes sk.per macro steps (256
+// columns each, a multiple of 4) of the reduction and writes float32 partials to sk.P ([ksplit][M][N],
+// the LoRA term in the last split), which launch_reduce_partials then sums
+SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
-                                const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, hipStream_t stream);
+                                const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, const SplitK &sk,
+                                hipStream_t stream);
 // decode-size forward (M <= 8): two launches; Tp is fp32 scratch of the size gemv_plan gives (Yp unused)
 struct GemvPlan {
     int nseg, nkc;

@@ -157,7 +157,7 @@ SHAPES = [
     # M, N, K, r
     (8, 256, 256, 8),          # the tiny workload's shape
     (300, 520, 384, 16),       # several tiles, ragged M and N
-    (17, 64, 128, 64),         # M just above the small-M range, single N tile
+    (17, 64, 128, 64),         # 17 tokens: the wide GEMV's two token groups, one row group
     (1, 512, 256, 64),
     (4, 256, 512, 32),
     (16, 1024, 1024, 128),
@@ -184,7 +184,11 @@ SHAPES = [
     (1100, 264, 640, 24),      # ragged M and N
     (1040, 1032, 320, 128),    # two LoRA extension steps
     # few output tiles: the products' reductions split over several workgroups per tile
-    (32, 4096, 4096, 64),      # fused GEMMs, 16 splits of 4 steps each way
+    (32, 4096, 4096, 64),      # wide GEMV forward (two token groups); backward 16 splits
+    (24, 1000, 2048, 16),      # wide GEMV, second token group part-filled, ragged row group
+    (32, 72, 2112, 64),        # wide GEMV, fewer row groups than the block's four waves
+    (33, 2048, 1024, 32),      # the first token count of the fused GEMMs: split both ways
+    (1, 4096, 8192, 16),       # decode GEMV forward; backward dX split over 8 workgroups
     (200, 1032, 2112, 16),     # fused: K not a multiple of 256, ragged last split both ways
     (700, 2048, 1024, 32),     # fused, three tile rows: 4 splits forward, 8 backward
     (1536, 1024, 2048, 64),    # expanded weight + bf16 GEMM: 8 splits forward, 4 backward
