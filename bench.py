@@ -485,7 +485,7 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
     return out
 
 
-def bench_mid(torch, nf4, synth, dev, Ms=(32, 256, 512, 1536), steps=20, warmup=5):
+def bench_mid(torch, nf4, synth, dev, Ms=(1, 16, 32, 256, 512, 1536), steps=20, warmup=5):
     """The LLaMA-7B attention projection (W 4096 x 4096, r = 64) forward + backward at token counts
     between the decode GEMVs and the training shapes: the wide GEMV forward (up to 32 tokens), the
     fused dequant GEMMs (the backward, and the forward from 33 tokens) and the expanded-weight GEMM

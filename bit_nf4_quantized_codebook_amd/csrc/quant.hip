@@ -6,6 +6,9 @@
 // All three are HBM-streaming kernels: one pass over their input, coalesced 16-byte accesses,
 // grid-stride loops sized to fill the 256 CUs.
 
+#include <cmath>
+#include <cstring>
+
 #include "common.h"
 #include "launch.h"
 
@@ -28,14 +31,32 @@ namespace nf4k {
 // zero (the host checks; otherwise, and for blocks outside that range, the kernel divides).  A
 // CPU run over 4e8 random and boundary cases (all-ones significands, quotients next to the
 // thresholds) found no difference at or above 2^-40.
-// The code is found by binary search over the 15 sorted (non-decreasing) thresholds, one bit per
-// level: 4 compares, the thresholds of the last three levels read from a 16-entry LDS table at the
-// index the bits so far give (all lanes read one of a few words: broadcast, no bank conflicts),
-// instead of 15 compares that each waited on the one condition register.
+// The code, the number of thresholds below n, comes from a 256-bucket table over [-1, 1]: bucket
+// i = trunc(fp32(n * 127.5 + 128)) (one fma, a clamp, a conversion) holds the count of thresholds
+// below the bucket and the one threshold inside it (or +inf), so the code is that count plus one
+// compare.  The host builds the table and checks that it decides every code as the count would:
+// each bucket widened by 2^-12 of its width on both sides (far more than the fma's rounding
+// moves n across a bucket edge) holds at most one threshold, and none lies below the first
+// bucket (a NaN quotient takes bucket 0 and code 0, as the count gives).  Codebooks that fail the
+// check (two codewords closer than a bucket, as in a table with two zeros) take a binary search
+// instead, one bit per level: 4 compares, the last three levels' thresholds read from LDS.
 // ------------------------------------------------------------------------------------------
 struct Thresholds {
     float t[15];
 };
+
+constexpr int QT_BUCKETS = 256;
+struct QTable {
+    uint32_t thr[QT_BUCKETS];    // bits of the threshold inside the bucket, +inf if none
+    uint8_t below[QT_BUCKETS];   // thresholds below the bucket
+};
+
+__device__ __forceinline__ uint32_t table_code(float n, const uint2 *tab) {
+    // med3 clamps into [0, 255] (a NaN quotient gives 0); the conversion truncates
+    const uint32_t i = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_fmaf(n, 127.5f, 128.0f), 0.0f, 255.0f);
+    const uint2 e = tab[i];
+    return e.y + (n > __uint_as_float(e.x) ? 1u : 0u);
+}
 
 // v moved by the DPP control CTRL within 16-lane rows (every source lane inside the row)
 template <int CTRL>
@@ -51,14 +72,17 @@ __device__ __forceinline__ uint32_t nearest_code(float n, float t7, const float 
     return 2 * c + (n > ts[2 * c] ? 1u : 0u);             // t[0], t[2], ..., t[14]
 }
 
+template <bool TABLE>
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ W, int64_t numel,
-                                                       Thresholds th, uint32_t zero_code, uint32_t fast_div,
-                                                       uint8_t *__restrict__ packed,
+                                                       Thresholds th, QTable qt, uint32_t zero_code,
+                                                       uint32_t fast_div, uint8_t *__restrict__ packed,
                                                        float *__restrict__ absmax) {
     typedef float f4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
     __shared__ float ts[16];
-    if (threadIdx.x < 15) ts[threadIdx.x] = th.t[threadIdx.x];
+    __shared__ uint2 tab[TABLE ? QT_BUCKETS : 1];
+    if (TABLE) tab[threadIdx.x] = make_uint2(qt.thr[threadIdx.x], qt.below[threadIdx.x]);   // 256 threads
+    else if (threadIdx.x < 15) ts[threadIdx.x] = th.t[threadIdx.x];
     __syncthreads();
     const int64_t nblocks = (numel + 63) >> 6;
     const int64_t nchunks = (numel + 511) >> 9;                      // 512-element wave chunks
@@ -102,14 +126,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
 #pragma unroll
                 for (int i = 0; i < 4; ++i) n[i] = x[q][i] / a;   // a == 0: masked below
             }
-            // every element is coded (an all-zero block or a padding element as n = 0), then the
-            // zero code is selected for those: no branch per element
+            // every element is coded, then the zero code is selected for an all-zero block and
+            // for padding elements past the end: no branch per element
             uint32_t word = 0;
+            if (TABLE) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool valid = a != 0.0f && e0 + i < numel;
-                const uint32_t c = nearest_code(valid ? n[i] : 0.0f, th.t[7], ts);
-                word |= (valid ? c : zero_code) << (4 * i);
+                for (int i = 0; i < 4; ++i) word |= table_code(n[i], tab) << (4 * i);
+                if (!full) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (e0 + i >= numel) word = (word & ~(15u << (4 * i))) | (zero_code << (4 * i));
+                }
+                if (a == 0.0f) word = zero_code * 0x1111u;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool valid = a != 0.0f && e0 + i < numel;
+                    const uint32_t c = nearest_code(valid ? n[i] : 0.0f, th.t[7], ts);
+                    word |= (valid ? c : zero_code) << (4 * i);
+                }
             }
             if ((lane & 15) == 0 && b < nblocks) absmax[b] = a;
             const int64_t byte = e0 >> 1;
@@ -313,6 +348,33 @@ static int grid_for(int64_t items, int per_block, int max_blocks) {
     return (int)g;
 }
 
+// The bucket table of the level-1 kernel; false where a widened bucket holds two thresholds or a
+// threshold lies below the first bucket (the kernel then searches).  Bucket i takes the quotients
+// n whose fp32(n * 127.5 + 128) truncates to i: n in [(i - 128) / 127.5, (i - 127) / 127.5), up to
+// the fma's rounding (2^-17 in units of the bucket), well inside the 2^-12 margin checked here.
+bool build_quant_table(const float thr[15], QTable &q) {
+    for (int i = 0; i < QT_BUCKETS; ++i) {
+        const double lo = ((double)i - 128.0 - 0x1p-12) / 127.5;
+        const double hi = ((double)i - 127.0 + 0x1p-12) / 127.5;
+        int below = 0, inside = 0;
+        float t_in = INFINITY;
+        for (int j = 0; j < 15; ++j) {
+            const double t = (double)thr[j];
+            if (!(t == t)) return false;
+            if (t < lo) {
+                ++below;
+            } else if (t <= hi) {
+                ++inside;
+                t_in = thr[j];
+            }
+        }
+        if (inside > 1 || (i == 0 && below != 0)) return false;
+        std::memcpy(&q.thr[i], &t_in, 4);
+        q.below[i] = (uint8_t)below;
+    }
+    return true;
+}
+
 hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], uint32_t zero_code,
                            uint8_t *packed, float *absmax, hipStream_t stream) {
     if (numel == 0) return hipSuccess;
@@ -324,10 +386,17 @@ hipError_t launch_quantize(const float *W, int64_t numel, const float thr[15], u
         th.t[j] = thr[j];
         if (!(std::fabs(thr[j]) >= 0x1p-39f)) fast_div = 0;   // also a NaN threshold
     }
+    static_assert(sizeof(QTable) + sizeof(Thresholds) + 64 <= 4096, "kernel arguments");
+    QTable qt;
+    const bool table = build_quant_table(thr, qt);
     const int64_t nchunks = (numel + 511) >> 9;
     const int grid = grid_for(nchunks, 4, 256 * 32);
-    hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(256), 0, stream, W, numel, th, zero_code,
-                       fast_div, packed, absmax);
+    if (table)
+        hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(256), 0, stream, W, numel, th, qt, zero_code,
+                           fast_div, packed, absmax);
+    else
+        hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(256), 0, stream, W, numel, th, qt, zero_code,
+                           fast_div, packed, absmax);
     return hipGetLastError();
 }
 
