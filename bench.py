@@ -487,8 +487,8 @@ def bench_gated(torch, nf4, synth, dev, reps=10):
 
 def bench_mid(torch, nf4, synth, dev, Ms=(1, 16, 32, 256, 512, 1536), steps=20, warmup=5):
     """The LLaMA-7B attention projection (W 4096 x 4096, r = 64) forward + backward at token counts
-    between the decode GEMVs and the training shapes: the wide GEMV forward (up to 32 tokens), the
-    fused dequant GEMMs (the backward, and the forward from 33 tokens) and the expanded-weight GEMM
+    between the decode GEMVs and the training shapes: the wide GEMV forward (up to 64 tokens), the
+    fused dequant GEMMs (the backward, and the forward from 65 tokens) and the expanded-weight GEMM
     below a full wave of output tiles, each with its reduction split over several workgroups where
     the output tiles leave CUs idle (qlora_linear_route gives the paths and splits)."""
     wl = synth.WORKLOADS["llama7b_attn"]

@@ -140,7 +140,7 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // Workspace plan of the linear layer (identical for the size query and the calls)
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
-constexpr int64_t kGemvMaxM = 32;     // token counts whose forward is a weight-streaming GEMV
+constexpr int64_t kGemvMaxM = 64;     // token counts whose forward is a weight-streaming GEMV
 // From this many tokens on, the weight is expanded to bf16 once per call and multiplied by a plain
 // bf16 GEMM: the expansion pass costs about 2.5 bytes of HBM traffic per weight, while dequantizing
 // inside the GEMM repeats the work once per 256-row tile of tokens and its VALU work does not hide

@@ -1,4 +1,4 @@
-// Small-batch forward (9 to 32 tokens, and smaller token counts on shapes the row kernel of
+// Small-batch forward (9 to 64 tokens, and smaller token counts on shapes the row kernel of
 // the decode GEMV does not take) of the QLoRA linear layer (gfx950):
 //   Y = X deq(W)^T + s T L2,   T = X L1 computed beforehand (s T passed in, bf16 [M, r])
 //
@@ -9,14 +9,16 @@
 // not the arithmetic.  With up to 16 tokens the 16 rows of v_mfma_f32_16x16x32_bf16 are mostly
 // used, so the products go there (rows past M are zero), and the VALU only turns codes into bf16
 // -- exactly the dequantized weights of eq. (6), so this path matches the large-batch GEMM.
-// 17 to 32 tokens take two groups of 16: each decoded B fragment feeds one MFMA per group, so
-// the decode, which bounds the kernel, is done once for both:
+// 17 to 32 tokens take two groups of 16 and 33 to 64 four (with X windows of 512 columns, so
+// that the two buffers fit in LDS): each decoded B fragment feeds one MFMA per group, so the
+// decode, which bounds the kernel, is done once for all of them:
 //   - a wave owns 16 W rows; per 256-column "macro step" lane (n = l % 16, g = l / 16) owns one
 //     whole quantization block (row n, block 4 step + g): 32 packed bytes, one 16-entry bf16
 //     table (v_perm byte planes), 8 dwords -> 8 MFMAs (one B fragment each)
 //   - codes are expanded in planar order (elements 0,2,4,6 | 1,3,5,7 of each 8), so the X
 //     fragments are stored in LDS in the same order (permuted once per window)
-//   - W is fetched four macro steps ahead; X is staged through LDS in windows of 1024 columns,
+//   - W is fetched four macro steps ahead; X is staged through LDS in windows of 1024 columns
+//     (512 for 64 tokens),
 //     double buffered (the next window travels through registers while the current one is
 //     consumed), shared by the waves of a block
 //   - a block has NW = ceil(N / 16 / 256) waves (4 to 8), so that the grid is about one block
@@ -37,9 +39,10 @@ namespace nf4k {
 namespace {
 
 constexpr int NWAVE_MAX = 8;
-constexpr int XWIN = 1024;                     // X window (columns)
-constexpr int XROW = XWIN + 8;                 // padded LDS row (elements): rows start 4 banks apart
 constexpr int MACRO = 256;                     // columns per macro step (4 blocks)
+// X window (columns) staged per buffer: 1024 for up to 32 token rows, 512 for 64 (so that the two
+// buffers stay within LDS); padded LDS rows (+8 elements) start 4 banks apart
+template <int MROWS> constexpr int xwin() { return MROWS >= 64 ? 512 : 1024; }
 
 __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
@@ -76,12 +79,16 @@ struct GemvArgs {
 // kernel carries no per-block select.
 template <int MROWS, bool I8, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
+    constexpr int XWIN = xwin<MROWS>();
+    constexpr int XROW = XWIN + 8;
+    constexpr int WPW = XWIN / MACRO;                     // macro steps per window: 4 or 2
+    constexpr int C8 = XWIN / 8;                          // 16-byte chunks per window row
     // X window: [MROWS rows][XWIN cols], planar within each 8-column group, double buffered;
-    // rows at or past M hold zeros.
+    // rows at or past the token count hold zeros.
     __shared__ __align__(16) uint8_t Xs0[MROWS * XROW * 2];
     __shared__ __align__(16) uint8_t Xs1[MROWS * XROW * 2];
     constexpr int NT = NW * 64;
-    constexpr int XCHUNKS = MROWS * (XWIN / 8);           // 16-byte X chunks per window
+    constexpr int XCHUNKS = MROWS * C8;                   // 16-byte X chunks per window
     constexpr int XCH = (XCHUNKS + NT - 1) / NT;         // per thread (the last round part-filled)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -110,8 +117,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     auto fetch_x = [&](int win) {
 #pragma unroll
         for (int q = 0; q < XCH; ++q) {
-            const int c = tid + NT * q;                  // chunk id: row = c / 128, col8 = c % 128
-            const int row = c >> 7, col8 = c & 127;
+            const int c = tid + NT * q;                  // chunk id: row = c / C8, col8 = c % C8
+            const int row = c / C8, col8 = c % C8;
             const int64_t k = (int64_t)win * XWIN + col8 * 8;
             const bool ok = c < XCHUNKS && row < g.M && k < kend;
             xr[q] = bload16(rX, ok ? (uint32_t)((row * g.K + k) * 2) : 0xFFFFFFF0u);
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
 #pragma unroll
         for (int q = 0; q < XCH; ++q) {
             const int c = tid + NT * q;
-            const int row = c >> 7, col8 = c & 127;
+            const int row = c / C8, col8 = c % C8;
             if (c < XCHUNKS)
                 *reinterpret_cast<u32x4 *>(dst + (row * XROW + col8 * 8) * 2) = to_planar(xr[q]);
         }
@@ -168,33 +175,29 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
         }
     };
 
-    // Four macro steps per X window (XWIN / MACRO); W is fetched four macro steps ahead.
-    // Window w+1 is fetched at the first macro step of window w, written to the other LDS buffer
-    // at its third, and made visible by the barrier that closes window w.
-    // ms_begin and the split length are multiples of 4: a split covers whole windows.
-    WStage S0, S1, S2, S3;
-    fetch_x(ms_begin / 4);
+    // WPW macro steps per X window; W is fetched four macro steps ahead.  Window w+1 is fetched
+    // at the first macro step of window w, written to the other LDS buffer halfway through it,
+    // and made visible by the barrier that closes window w.  ms_begin and the split length are
+    // multiples of 4 (whole windows); one loop pass is 4 macro steps.
+    WStage S[4];
+    fetch_x(ms_begin / WPW);
     store_x(Xs0);
-    load_w(ms_begin, S0);
-    load_w(ms_begin + 1, S1);
-    load_w(ms_begin + 2, S2);
-    load_w(ms_begin + 3, S3);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) load_w(ms_begin + h, S[h]);
     __syncthreads();
     for (int ms = ms_begin; ms < ms_end; ms += 4) {
-        const int win = ms / 4;
-        uint8_t *Xcur = ((ms - ms_begin) & 4) ? Xs1 : Xs0;
-        uint8_t *Xnxt = ((ms - ms_begin) & 4) ? Xs0 : Xs1;
-        fetch_x(win + 1);                                // past the split's end: reads zeros
-        macro_step(ms, S0, Xcur);
-        load_w(ms + 4, S0);
-        macro_step(ms + 1, S1, Xcur);
-        load_w(ms + 5, S1);
-        store_x(Xnxt);
-        macro_step(ms + 2, S2, Xcur);
-        load_w(ms + 6, S2);
-        macro_step(ms + 3, S3, Xcur);
-        load_w(ms + 7, S3);
-        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int m = ms + h;
+            const bool odd = (((m - ms_begin) / WPW) & 1) != 0;   // window parity
+            uint8_t *Xcur = odd ? Xs1 : Xs0;
+            uint8_t *Xnxt = odd ? Xs0 : Xs1;
+            if (h % WPW == 0) fetch_x(m / WPW + 1);               // past the split's end: zeros
+            macro_step(m, S[h], Xcur);
+            load_w(m + 4, S[h]);
+            if (h % WPW == WPW / 2 - 1) store_x(Xnxt);
+            if (h % WPW == WPW - 1) __syncthreads();
+        }
     }
 
     // ---- LoRA (last split): acc += (s T) L2 over r in steps of 32 (two MFMAs for r = 64) ----
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
         for (int q = 0; q < G; ++q) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = 16 * q + lg * 4 + i;
+                const int64_t m = 16 * q + lg * 4 + i;
                 if (m < g.M) {
                     if (g.ksplit > 1) P[m * g.N + n] = acc[q][i];
                     else g.Y[m * g.N + n] = (uint16_t)f32_to_bf16(acc[q][i]);
@@ -258,7 +261,10 @@ void launch_i8(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
     }
 }
 void launch_nw(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
-    if (a.M > 16) {
+    if (a.M > 32) {
+        if (a.dq_int8) launch_i8<64, true>(a, nw, grid, stream);
+        else launch_i8<64, false>(a, nw, grid, stream);
+    } else if (a.M > 16) {
         if (a.dq_int8) launch_i8<32, true>(a, nw, grid, stream);
         else launch_i8<32, false>(a, nw, grid, stream);
     } else {
@@ -268,8 +274,8 @@ void launch_nw(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
 }
 
 // waves per block: about one block per CU, and at least 4 (each block stages the whole X window
-// for its rows, so fewer waves would read X from L2 more often than W from HBM); 32 token rows
-// keep 4 waves even for fewer row groups (the idle waves store nothing)
+// for its rows, so fewer waves would read X from L2 more often than W from HBM); 32 and 64 token
+// rows keep 4 waves even for fewer row groups (the idle waves store nothing)
 int wide_waves(int64_t M, int64_t N) {
     const int64_t groups = (N + 15) / 16;
     int nw = (int)((groups + 255) / 256);
@@ -277,11 +283,10 @@ int wide_waves(int64_t M, int64_t N) {
     if (groups < nw && M <= 16) nw = (int)groups;
     return nw;
 }
-
 }  // namespace
 
 // Split the reduction when the row blocks leave CUs idle: S = 256 / blocks workgroups per row
-// block, each over whole 1024-column windows (per = a multiple of 4 macro steps), no split empty.
+// block, each over a whole number of 4 macro steps (whole X windows), no split empty.
 SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K) {
     const int nw = wide_waves(M, N);
     const int64_t blocks = ((N + 15) / 16 + nw - 1) / nw;
@@ -298,7 +303,7 @@ SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, const SplitK &sk,
                                 hipStream_t stream) {
-    if (M < 1 || M > 32) return hipErrorInvalidValue;
+    if (M < 1 || M > 64) return hipErrorInvalidValue;
     GemvArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;

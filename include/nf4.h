@@ -192,7 +192,7 @@ size_t qlora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /*
  * How the linear layer runs a shape (host, no GPU work): info[0] = the forward's path (1: decode
- * GEMV, up to 8 tokens; 2: wide GEMV, up to 32; 3: fused dequant GEMM; 4: bf16 expansion of the
+ * GEMV, up to 8 tokens; 2: wide GEMV, up to 64; 3: fused dequant GEMM; 4: bf16 expansion of the
  * weight, then the bf16 GEMM), info[1] = the workgroups each output tile (each block of rows on
  * the wide GEMV) of the forward's product splits its reduction over (1: not split, as always on
  * the decode GEMV), info[2] = the same for the backward's dX product, info[3] = the backward's dX

@@ -239,19 +239,20 @@ def test_route_by_token_count_and_tile_count():
     # 28672 rows make 256 blocks: no split
     assert route(32, 4096, 4096, 64) == {"fwd": "gemv_wide", "fwd_split": 4, "bwd": "fused", "bwd_split": 16}
     assert route(16, 28672, 8192, 64)["fwd_split"] == 1 and route(16, 4096, 11008, 64)["fwd_split"] == 4
-    assert route(33, 4096, 4096, 64)["fwd"] == "fused" and route(1023, 4096, 4096, 64)["bwd"] == "fused"
+    assert route(64, 4096, 4096, 64)["fwd"] == "gemv_wide" and route(65, 4096, 4096, 64)["fwd"] == "fused"
+    assert route(1023, 4096, 4096, 64)["bwd"] == "fused"
     assert route(1024, 4096, 4096, 64)["fwd"] == "expanded"
     # 4096 x 4096 x 4096: 256 output tiles each way, no split; the 7B MLP shapes likewise
     for M, N, K in [(4096, 4096, 4096), (4096, 11008, 4096), (4096, 4096, 11008), (2048, 22016, 8192)]:
         rt = route(M, N, K, 64)
         assert rt["fwd_split"] == 1 and rt["bwd_split"] == 1, (M, N, K, rt)
-    # 64 tokens: 16 tiles, 16 splits of 4 steps each way; 512 tokens: 32 tiles, 8 splits
-    assert route(64, 4096, 4096, 64)["fwd_split"] == 16 and route(64, 4096, 4096, 64)["bwd_split"] == 16
+    # 128 tokens: 16 tiles, 16 splits of 4 steps each way; 512 tokens: 32 tiles, 8 splits
+    assert route(128, 4096, 4096, 64)["fwd_split"] == 16 and route(128, 4096, 4096, 64)["bwd_split"] == 16
     assert route(512, 4096, 4096, 64)["fwd_split"] == 8
     # never more splits than whole groups of 4 reduction steps
     assert route(100, 4096, 384, 64)["fwd_split"] == 1
     # the workspace grows by the partials: splits x M x N float32 at least
-    assert lib.qlora_linear_workspace_size(64, 4096, 4096, 64) >= 16 * 64 * 4096 * 4
+    assert lib.qlora_linear_workspace_size(128, 4096, 4096, 64) >= 16 * 128 * 4096 * 4
 
 
 def test_flag_bits_are_distinct_and_match_the_binding():

@@ -187,7 +187,10 @@ SHAPES = [
     (32, 4096, 4096, 64),      # wide GEMV forward (two token groups); backward 16 splits
     (24, 1000, 2048, 16),      # wide GEMV, second token group part-filled, ragged row group
     (32, 72, 2112, 64),        # wide GEMV, fewer row groups than the block's four waves
-    (33, 2048, 1024, 32),      # the first token count of the fused GEMMs: split both ways
+    (33, 2048, 1024, 32),      # wide GEMV, four token groups (three of them padding)
+    (64, 72, 2112, 64),        # wide GEMV, 64 tokens, fewer row groups than the block's waves
+    (50, 1000, 4096, 16),      # wide GEMV, fourth token group part-filled, reduction split
+    (65, 2048, 1024, 32),      # the first token count of the fused GEMMs: split both ways
     (1, 4096, 8192, 16),       # decode GEMV forward; backward dX split over 8 workgroups
     (200, 1032, 2112, 16),     # fused: K not a multiple of 256, ragged last split both ways
     (700, 2048, 1024, 32),     # fused, three tile rows: 4 splits forward, 8 backward
