@@ -11,6 +11,9 @@
 //
 // Block tile 256 x 256 outputs, reduction step 64 (one quantization block per W row), 4 waves
 // in 2 x 2, each 128 x 128 with v_mfma_f32_32x32x16_bf16 (16 tiles, 256 fp32 accumulators).
+// Up to 64 tokens the tile is 64 x 256 (4 waves side by side, each 64 x 64): a 256-row tile
+// would spend three quarters or more of its MFMA work on padding rows, while the weight's
+// decode, the same per step either way, then bounds the step.
 //
 // A (activations, reduction-contiguous) goes straight from global memory to LDS with
 // buffer_load ... lds (no registers, no ds_write), 32 KB per stage, 16-byte chunks XOR-swizzled
@@ -38,11 +41,9 @@ namespace nf4k {
 
 namespace {
 
-constexpr int TM = 256;          // output rows per block tile
 constexpr int TN = 256;          // output cols per block tile
 constexpr int TK = 64;           // reduction per step (= one quantization block)
 constexpr int NTHREADS = 256;
-constexpr int A_STAGE = TM * TK * 2;                 // 32 KB, swizzled, unpadded
 // s_waitcnt immediate: vmcnt <= 4 (the W loads issued after the A loads may stay in flight),
 // expcnt unchecked, lgkmcnt = 0.  gfx9 layout: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14
 constexpr int kWaitA = 4 | (7 << 4) | (0 << 8);
@@ -76,8 +77,17 @@ struct GemmArgs {
 };
 
 
+// TM: output rows per block tile, 256 (waves 2 x 2) or 64 (waves 1 x 4)
+template <int TM>
 __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     constexpr int B_STAGE = B_STAGE_BYTES;
+    constexpr int A_STAGE = TM * TK * 2;              // 32 or 8 KB, swizzled, unpadded
+    constexpr int WN_WAVES = TM == 256 ? 2 : 4;       // waves along the output columns
+    constexpr int WT_M = TM * WN_WAVES / 4;           // wave tile: WT_M x WT_N
+    constexpr int WT_N = TN / WN_WAVES;
+    constexpr int IM = WT_M / 32, JN = WT_N / 32;     // 32 x 32 MFMA tiles of a wave
+    constexpr int QA = TM / 32;                       // A loads (1 KB each) per wave and step
+    static_assert(TM == 256 || TM == 64, "block tile rows");
     // separate LDS objects, so the compiler sees that the direct-to-LDS A loads never alias the
     // B tile reads and adds no memory-counter waits of its own before them
     // each stage is its own object: a read of stage 0 provably never aliases the loads in flight
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> (WN_WAVES == 2 ? 1 : 2), wn = wave & (WN_WAVES - 1);
     const int r32 = lane & 31, hh = lane >> 5;
 
     const int ntm = (int)((g.M + TM - 1) / TM);
@@ -119,14 +129,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rC2 = make_rsrc(g.c2, g.wrows * wblk_per_row);
     const __amdgpu_buffer_rsrc_t rC1 = make_rsrc(g.c1, ((g.wrows * wblk_per_row + 255) >> 8) * 4);
 
-    // ---- A: direct global -> LDS.  Each wave issues 8 x 1 KB per step: instruction q writes
-    // LDS rows 8u..8u+7 (u = 8*wave + q); lane l -> row 8u + l/8, physical chunk l%8, which holds
-    // logical chunk (l%8) ^ ((row/2) % 8). ----
-    uint32_t a_voff[8];
-    int a_col[8];
+    // ---- A: direct global -> LDS.  Each wave issues QA x 1 KB per step: instruction q writes
+    // LDS rows 8u..8u+7 (u = QA*wave + q); lane l -> row 8u + l/8, physical chunk l%8, which
+    // holds logical chunk (l%8) ^ ((row/2) % 8). ----
+    uint32_t a_voff[QA];
+    int a_col[QA];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = 8 * (8 * wave + q) + (lane >> 3);
+    for (int q = 0; q < QA; ++q) {
+        const int row = 8 * (QA * wave + q) + (lane >> 3);
         a_col[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
         a_voff[q] = (uint32_t)((row * g.Kred + a_col[q]) * 2);
     }
@@ -138,9 +148,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         // < 64 on a ragged last step (its columns past N read zeros)
         const int rem = kred32 - step * TK;
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
-        lds_u8 *dst = (lds_u8 *)Ad + wave * 8192;
+        lds_u8 *dst = (lds_u8 *)Ad + wave * (QA * 1024);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < QA; ++q) {
             uint32_t off = a_voff[q] + (uint32_t)step * TK * 2;
             if (a_col[q] >= rem) off = 0xFFFFFFF0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(dst + q * 1024), 16, off, 0, 0, 0);
@@ -181,24 +191,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[IM][JN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // ---- fragments of sub-step s (16 reduction elements): lane (r32, hh) takes elements
     // 16 s + 8 hh .. +7 of its row (A) / column (B) ----
     auto frag_A = [&](const uint8_t *Ast, int s, int i) -> bf16x8 {
-        const int row = wm * 128 + i * 32 + r32;
+        const int row = wm * WT_M + i * 32 + r32;
         const int c = (2 * s + hh) ^ ((row >> 1) & 7);
         return *reinterpret_cast<const bf16x8 *>(Ast + row * 128 + c * 16);
     };
     // B fragment of the extension step, from its [out col][red] tile (row reads)
     auto frag_rowread = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
-        const int row = wn * 128 + j * 32 + r32;
+        const int row = wn * WT_N + j * 32 + r32;
         return *reinterpret_cast<const bf16x8 *>(Bst + row * ROWB_RED + (s * 16 + hh * 8) * 2);
     };
     // B fragment of a main-loop step, from its [red][out col] tile: 16-lane group (hh, half):
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     // the transpose, lane i holds column col0 + i.
     auto frag_B = [&](const uint8_t *Bst, int s, int j) -> bf16x8 {
         const int i16 = lane & 15, half = (lane >> 4) & 1;
-        const int col0 = wn * 128 + j * 32 + half * 16;
+        const int col0 = wn * WT_N + j * 32 + half * 16;
         const int rowb = s * 16 + hh * 8 + (i16 >> 2);
         const uint8_t *base = Bst + (col0 + 4 * (i16 & 3)) * 2;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + rowb * ROWB_OUT));
@@ -215,19 +225,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         return __builtin_bit_cast(bf16x8, v);
     };
     struct Frags {
-        bf16x8 a[4], b[4];
+        bf16x8 a[IM], b[JN];
     };
     auto load_frags = [&](const uint8_t *Ast, const uint8_t *Bst, int s, Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f.a[i] = frag_A(Ast, s, i);
+        for (int i = 0; i < IM; ++i) f.a[i] = frag_A(Ast, s, i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.b[j] = frag_B(Bst, s, j);
+        for (int j = 0; j < JN; ++j) f.b[j] = frag_B(Bst, s, j);
     };
     auto mma = [&](const Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
     auto mfma_sub = [&](const uint8_t *Ast, const uint8_t *Bst, int s) {
@@ -240,13 +250,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     // of the next step's dequantization (VALU + 2 LDS writes) and the direct-to-LDS A loads.
     // MFMA (32 cycles each) and VALU issue from the same wave co-execute when interleaved.
     auto interleave = [&]() {
+        if constexpr (TM == 256) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // 5 VALU
-            if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            if (k == 9 || k == 13) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-            if (k == 2 || k == 6 || k == 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // 5 VALU
+                if (k < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                if (k == 9 || k == 13) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+                if (k == 2 || k == 6 || k == 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+            }
+        } else {
+            // 4 MFMAs per sub-step: the same quarter of the decode spread over them
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);     // 20 VALU
+                if (k < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 DS reads
+                if (k == 1 || k == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+                if (k == 0 || k == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+            }
         }
     };
 
@@ -311,13 +333,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
             const int j0 = e * TK;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                // A: row (tid/8) + 32 q, reduction chunk tid % 8 (columns past r read zeros)
+                // A (rows < TM): row (tid/8) + 32 q, reduction chunk tid % 8 (columns past r read
+                // zeros); B: output column o0 + row, the same reduction chunk
                 const int row = (tid >> 3) + 32 * q, chunk = tid & 7;
                 const int jj = j0 + chunk * 8;
+                if (q < TM / 32) {
+                    const uint32_t offa = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0xFFFFFFF0u;
+                    const u32x4 va = bload16(rAe, offa);
+                    *reinterpret_cast<u32x4 *>(Ast + row * 128 + (chunk ^ ((row >> 1) & 7)) * 16) = va;
+                }
                 const uint32_t off = jj < g.r ? (uint32_t)((row * (int64_t)g.r + jj) * 2) : 0xFFFFFFF0u;
-                const u32x4 va = bload16(rAe, off);
-                *reinterpret_cast<u32x4 *>(Ast + row * 128 + (chunk ^ ((row >> 1) & 7)) * 16) = va;
-                // B: output column o0 + row, reduction chunk
                 const u32x4 vb = bload16(rBe, off);
                 const int pos = (row & ~7) | ((row & 1) << 2) | ((row & 7) >> 1);
                 *reinterpret_cast<u32x4 *>(Bst + pos * ROWB_RED + chunk * 16) = vb;
@@ -327,9 +352,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
             for (int s = 0; s < 4; ++s) {
                 Frags f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) f.a[i] = frag_A(Ast, s, i);
+                for (int i = 0; i < IM; ++i) f.a[i] = frag_A(Ast, s, i);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) f.b[j] = frag_rowread(Bst, s, j);
+                for (int j = 0; j < JN; ++j) f.b[j] = frag_rowread(Bst, s, j);
                 mma(f);
             }
             __syncthreads();
@@ -347,12 +372,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         const __amdgpu_buffer_rsrc_t rP = make_rsrc(g.P + (int64_t)split * g.M * g.Nout + m0 * g.Nout,
                                                     (g.M - m0) * g.Nout * 4);
         const uint32_t prow = (uint32_t)(g.Nout * 4);
-        const uint32_t poff = (uint32_t)((wm * 128 + hh * 4) * prow) + (uint32_t)((o0 + wn * 128 + colw) * 4);
+        const uint32_t poff = (uint32_t)((wm * WT_M + hh * 4) * prow) + (uint32_t)((o0 + wn * WT_N + colw) * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (o0 + wn * 128 + j * 32 + colw >= g.Nout) continue;
+        for (int j = 0; j < JN; ++j) {
+            if (o0 + wn * WT_N + j * 32 + colw >= g.Nout) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < IM; ++i) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
@@ -364,13 +389,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     } else if (!g.accumulate) {
         const __amdgpu_buffer_rsrc_t rC = make_rsrc(g.C + m0 * g.Nout, (g.M - m0) * g.Nout * 2);
         const uint32_t row_bytes = (uint32_t)(g.Nout * 2);
-        const uint32_t lane_off = (uint32_t)((wm * 128 + hh * 4) * row_bytes) +
-                                  (uint32_t)((o0 + wn * 128 + colw) * 2);
+        const uint32_t lane_off = (uint32_t)((wm * WT_M + hh * 4) * row_bytes) +
+                                  (uint32_t)((o0 + wn * WT_N + colw) * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (o0 + wn * 128 + j * 32 + colw >= g.Nout) continue;
+        for (int j = 0; j < JN; ++j) {
+            if (o0 + wn * WT_N + j * 32 + colw >= g.Nout) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < IM; ++i) {
 #pragma unroll
                 for (int v = 0; v < 16; v += 2) {
                     const uint32_t rows = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
@@ -384,14 +409,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < IM; ++i) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = o0 + wn * 128 + j * 32 + colw;
+            for (int j = 0; j < JN; ++j) {
+                const int64_t col = o0 + wn * WT_N + j * 32 + colw;
                 if (col >= g.Nout) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int64_t row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                    const int64_t row = m0 + wm * WT_M + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
                     if (row < g.M) {
                         uint16_t *p = g.C + row * g.Nout + col;
                         *p = (uint16_t)f32_to_bf16(acc[i][j][v] + bf16_to_f32(*p));
@@ -402,7 +427,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dqgemm_bwd_kernel(GemmArgs g) {
     }
 }
 
+// up to this many tokens the 64-row block tile
+constexpr int64_t kSmallTileM = 64;
+
 hipError_t launch_impl(GemmArgs &a, const SplitK &sk, hipStream_t stream) {
+    const int TM = a.M <= kSmallTileM ? 64 : 256;
     const int ntm = (int)((a.M + TM - 1) / TM);
     const int ntn = (int)((a.Nout + TN - 1) / TN);
     const int64_t steps = (a.Kred + TK - 1) / TK;
@@ -412,7 +441,10 @@ hipError_t launch_impl(GemmArgs &a, const SplitK &sk, hipStream_t stream) {
     if (a.ksplit > 1 && (!sk.P || (int64_t)(a.ksplit - 1) * sk.per >= steps || (int64_t)a.ksplit * sk.per < steps))
         return hipErrorInvalidValue;
     timing_before(stream, 1);
-    hipLaunchKernelGGL(dqgemm_bwd_kernel, dim3(ntm * ntn * a.ksplit), dim3(NTHREADS), 0, stream, a);
+    if (TM == 64)
+        hipLaunchKernelGGL(dqgemm_bwd_kernel<64>, dim3(ntm * ntn * a.ksplit), dim3(NTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(dqgemm_bwd_kernel<256>, dim3(ntm * ntn * a.ksplit), dim3(NTHREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
