@@ -141,6 +141,9 @@ nf4k::WeightView view_of(const nf4_weight *w) {
 // ---------------------------------------------------------------------------------------------
 constexpr int64_t kTile = 64;
 constexpr int64_t kGemvMaxM = 64;     // token counts whose forward is a weight-streaming GEMV
+// Up to this many bytes of T's float32 partials, each wide-GEMV workgroup that needs s T sums them
+// itself (no reduction launch); beyond, their reading costs the GEMV more than the launch
+constexpr size_t kGemvTSumBytes = 128 << 10;
 // From this many tokens on, the weight is expanded to bf16 once per call and multiplied by a plain
 // bf16 GEMM: the expansion pass costs about 2.5 bytes of HBM traffic per weight, while dequantizing
 // inside the GEMM repeats the work once per 256-row tile of tokens and its VALU work does not hide
@@ -547,10 +550,21 @@ int linear_fwd_run(const nf4_weight *w, const uint16_t *X, const uint16_t *L1, c
                       "bf16 GEMM (fwd)");
         return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
     }
+    if (M <= kGemvMaxM && (size_t)p.ksT * M * r * 4 <= kGemvTSumBytes) {
+        // T's partials; the GEMV sums them itself (s T in its LDS, T_out from its first workgroup)
+        hipError_t e;
+        const nf4k::Reduction red = T_partials(X, L1, M, K, r, scale, T_out, nullptr, p, workspace, s, &e);
+        NF4_CHECK_HIP(e, "T = X L1");
+        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, &red, nullptr, L2, r, M, Y,
+                                                 split_of(p.kf, p, workspace), s),
+                      "dequant GEMV (fwd)");
+        return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
+    }
     int rc = compute_T(X, L1, M, K, r, scale, T_out, sT, p, workspace, s);
     if (rc) return rc;
     if (M <= kGemvMaxM) {
-        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, sT, L2, r, M, Y, split_of(p.kf, p, workspace), s),
+        NF4_CHECK_HIP(nf4k::launch_gemv_wide_fwd(view_of(w), X, nullptr, sT, L2, r, M, Y,
+                                                 split_of(p.kf, p, workspace), s),
                       "dequant GEMV (fwd)");
         return reduce_split(p.kf, p, workspace, M * N, Y, false, s);
     }

@@ -1,6 +1,6 @@
 // Small-batch forward (9 to 64 tokens, and smaller token counts on shapes the row kernel of
 // the decode GEMV does not take) of the QLoRA linear layer (gfx950):
-//   Y = X deq(W)^T + s T L2,   T = X L1 computed beforehand (s T passed in, bf16 [M, r])
+//   Y = X deq(W)^T + s T L2,   T = X L1 from float32 partials computed beforehand
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
 // section 3.5 eq. (5) / eq. (6); section 4 eq. (3).
@@ -28,6 +28,11 @@
 //     fixed-order pass sums (the LoRA term rides in the last split)
 //   - the kernel is bound by the VALU work of the exact decode (about 250 VALU instructions per
 //     wave per 4096 weights), not by HBM
+// Prologue: s T into LDS.  Where T's float32 split partials are few (at most 128 KB), each
+// workgroup that needs s T sums them itself in ascending split order (the order of the standalone
+// reduction, so T has the same bits on every path), and workgroup 0 also writes T for the
+// backward: this saves the reduction's own launch.  Otherwise s T comes reduced (bf16) and is
+// copied in.
 // Epilogue: 2 more MFMAs add s T L2 (A = s T, B = a strided gather of L2), then bf16 stores.
 
 #include "common.h"
@@ -39,6 +44,7 @@ namespace nf4k {
 namespace {
 
 constexpr int NWAVE_MAX = 8;
+constexpr int R_MAX = 128;                     // LoRA rank
 constexpr int MACRO = 256;                     // columns per macro step (4 blocks)
 // X window (columns) staged per buffer: 1024 for up to 32 token rows, 512 for 64 (so that the two
 // buffers stay within LDS); padded LDS rows (+8 elements) start 4 banks apart
@@ -65,7 +71,11 @@ struct GemvArgs {
     const float *c1;
     const float *mean;
     uint32_t dq_int8;        // second-level codes are int8 (else E4M3)
-    const uint16_t *sT;      // [M, r]  (s * X L1)
+    const float *Tp;         // T's float32 partials [ksT][M, r], or null: sT given
+    const uint16_t *sT;      // [M, r] s T (bf16), when Tp is null
+    int32_t ksT;
+    float tscale;            // s
+    uint16_t *T_out;         // [M, r] T (optional)
     const uint16_t *L2;      // [r, N]
     uint16_t *Y;             // [M, N]
     float *P;                // [ksplit, M, N] partials (ksplit > 1)
@@ -87,6 +97,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     // rows at or past the token count hold zeros.
     __shared__ __align__(16) uint8_t Xs0[MROWS * XROW * 2];
     __shared__ __align__(16) uint8_t Xs1[MROWS * XROW * 2];
+    __shared__ __align__(16) uint16_t sTs[MROWS * R_MAX];  // s T, bf16 [M][r]
     constexpr int NT = NW * 64;
     constexpr int XCHUNKS = MROWS * C8;                   // 16-byte X chunks per window
     constexpr int XCH = (XCHUNKS + NT - 1) / NT;         // per thread (the last round part-filled)
@@ -184,6 +195,37 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     store_x(Xs0);
 #pragma unroll
     for (int h = 0; h < 4; ++h) load_w(ms_begin + h, S[h]);
+
+    // s T (the last split, which adds the LoRA term) and T (workgroup 0) from T's partials while
+    // the first weight steps stream in
+    if (!g.Tp) {
+        if (split == g.ksplit - 1) {
+            const uint2 *src = reinterpret_cast<const uint2 *>(g.sT);
+            for (int i = tid; i < (int)((g.M * g.r) >> 2); i += NT) reinterpret_cast<uint2 *>(sTs)[i] = src[i];
+        }
+    } else if (split == g.ksplit - 1 || blockIdx.x == 0) {
+        typedef float f32v4 __attribute__((ext_vector_type(4)));
+        const int64_t E = g.M * g.r;
+        const f32v4 *Tp = reinterpret_cast<const f32v4 *>(g.Tp);
+        for (int i = tid; i < (int)(E >> 2); i += NT) {
+            f32v4 acc = Tp[i];
+            for (int k0 = 1; k0 < g.ksT; k0 += 8) {
+                f32v4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (k0 + u < g.ksT) v[u] = Tp[(int64_t)(k0 + u) * (E >> 2) + i];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (k0 + u < g.ksT) acc += v[u];
+            }
+            const float sc = g.tscale;
+            *reinterpret_cast<uint2 *>(sTs + 4 * i) = uint2{pack_bf16x2(sc * acc.x, sc * acc.y),
+                                                            pack_bf16x2(sc * acc.z, sc * acc.w)};
+            if (blockIdx.x == 0 && g.T_out)
+                reinterpret_cast<uint2 *>(g.T_out)[i] = uint2{pack_bf16x2(1.0f * acc.x, 1.0f * acc.y),
+                                                              pack_bf16x2(1.0f * acc.z, 1.0f * acc.w)};
+        }
+    }
     __syncthreads();
     for (int ms = ms_begin; ms < ms_end; ms += 4) {
 #pragma unroll
@@ -201,7 +243,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     }
 
     // ---- LoRA (last split): acc += (s T) L2 over r in steps of 32 (two MFMAs for r = 64) ----
-    const __amdgpu_buffer_rsrc_t rT = make_rsrc(g.sT, g.M * (int64_t)g.r * 2);
     const __amdgpu_buffer_rsrc_t rL2 = make_rsrc(g.L2, (int64_t)g.r * g.N * 2);
     const int rlora = split == g.ksplit - 1 ? g.r : 0;
     for (int j0 = 0; j0 < rlora; j0 += 32) {
@@ -221,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
         for (int q = 0; q < G; ++q) {
             const int64_t row = 16 * q + ln;
             const bool oka = row < g.M && jj < g.r;
-            const u32x4 av = bload16(rT, oka ? (uint32_t)((row * g.r + jj) * 2) : 0xFFFFFFF0u);
+            const u32x4 av = oka ? *reinterpret_cast<const u32x4 *>(sTs + row * g.r + jj) : u32x4{0u, 0u, 0u, 0u};
             acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                              __builtin_bit_cast(bf16x8, bv), acc[q], 0, 0, 0);
         }
@@ -300,14 +341,21 @@ SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K) {
     return s <= 1 ? SplitPlan{1, nwin * 4} : SplitPlan{(int)s, wper * 4};
 }
 
-hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
+hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const Reduction *Tred, const uint16_t *sT,
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, const SplitK &sk,
                                 hipStream_t stream) {
     if (M < 1 || M > 64) return hipErrorInvalidValue;
     GemvArgs a;
     a.X = X;
     a.packed = w.packed; a.c2 = w.c2; a.c1 = w.c1; a.mean = w.mean; a.dq_int8 = w.dq_int8;
-    a.sT = sT; a.L2 = L2; a.Y = Y;
+    a.L2 = L2; a.Y = Y;
+    if (r < 8 || r > R_MAX || r % 8 || (Tred == nullptr) == (sT == nullptr)) return hipErrorInvalidValue;
+    if (Tred) {
+        if (Tred->n != M * r || Tred->nsplit < 1 || Tred->s1 != 1.0f || Tred->stride) return hipErrorInvalidValue;
+        a.Tp = Tred->P; a.ksT = Tred->nsplit; a.tscale = Tred->s2; a.T_out = Tred->out; a.sT = nullptr;
+    } else {
+        a.Tp = nullptr; a.ksT = 0; a.tscale = 0.0f; a.T_out = nullptr; a.sT = sT;
+    }
     a.M = M; a.N = w.rows; a.K = w.cols; a.r = r;
     for (int j = 0; j < 16; ++j) a.cb.v[j] = w.cb[j];
     const int nw = wide_waves(M, w.rows);

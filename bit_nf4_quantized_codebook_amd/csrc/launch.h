@@ -58,7 +58,9 @@ hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint1
 // columns each, a multiple of 4) of the reduction and writes float32 partials to sk.P ([ksplit][M][N],
 // the LoRA term in the last split), which launch_reduce_partials then sums
 SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
+// s T either reduced (sT, bf16 [M, r]) or as T's pending reduction (Tred: its partials, split
+// count, T_out as out and s as s2), which the kernel then sums itself; exactly one is given
+hipError_t launch_gemv_wide_fwd(const WeightView &w, const uint16_t *X, const Reduction *Tred, const uint16_t *sT,
                                 const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y, const SplitK &sk,
                                 hipStream_t stream);
 // decode-size forward (M <= 8): two launches; Tp is fp32 scratch of the size gemv_plan gives (Yp unused)

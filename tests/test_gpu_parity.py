@@ -189,6 +189,7 @@ SHAPES = [
     (32, 72, 2112, 64),        # wide GEMV, fewer row groups than the block's four waves
     (33, 2048, 1024, 32),      # wide GEMV, four token groups (three of them padding)
     (64, 72, 2112, 64),        # wide GEMV, 64 tokens, fewer row groups than the block's waves
+    (64, 4096, 4096, 64),      # wide GEMV, reduction split, s T reduced beforehand (256 KB of T partials)
     (50, 1000, 4096, 16),      # wide GEMV, fourth token group part-filled, reduction split
     (65, 2048, 1024, 32),      # the first token count of the fused GEMMs: split both ways
     (1, 4096, 8192, 16),       # decode GEMV forward; backward dX split over 8 workgroups
