@@ -327,11 +327,15 @@ int wide_waves(int64_t M, int64_t N) {
 }  // namespace
 
 // Split the reduction when the row blocks leave CUs idle: S = 256 / blocks workgroups per row
-// block, each over a whole number of 4 macro steps (whole X windows), no split empty.
+// block, each over a whole number of 4 macro steps (whole X windows), no split empty.  A block
+// with little work (macro steps x 16-token groups under 32, e.g. 16 tokens at K = 4096) is not
+// split: the partials' reduction launch costs more than the idle CUs (measured 1-3 us either way).
 SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K) {
     const int nw = wide_waves(M, N);
     const int64_t blocks = ((N + 15) / 16 + nw - 1) / nw;
     const int64_t nmacro = (K + MACRO - 1) / MACRO, nwin = (nmacro + 3) / 4;
+    const int64_t groups = M > 32 ? 4 : (M > 16 ? 2 : 1);
+    if (nmacro * groups < 32) return SplitPlan{1, nwin * 4};
     int64_t s = blocks > 0 ? 256 / blocks : 1;
     if (s > nwin) s = nwin;
     if (s > 16) s = 16;
