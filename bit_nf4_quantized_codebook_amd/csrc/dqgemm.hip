@@ -1,5 +1,5 @@
-// Fused double-dequantize + bf16 MFMA GEMM for the backward of the QLoRA linear layer at
-// 16 < M < 1024 tokens (gfx950):
+// Fused double-dequantize + bf16 MFMA GEMM for the backward of the QLoRA linear layer below
+// 1024 tokens (gfx950):
 //   dX = dY . deq(W) + dT . L1^T       reduction over N (the W rows), output cols = W cols
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),

@@ -52,9 +52,8 @@ SplitPlan gemm_split(int64_t tiles, int64_t steps, int quantum);
 hipError_t launch_dqgemm_fwd(const WeightView &w, const uint16_t *X, const uint16_t *sT,
                              const uint16_t *L2, int32_t r, int64_t M, uint16_t *Y,
                              const SplitK &sk, hipStream_t stream);
-// up to 16 tokens (9-16, or fewer on shapes the row kernel does not take): sT = s X L1 (bf16
-// [M, r]) computed beforehand
-// small-batch forward (M <= 32); with sk.ksplit > 1 each workgroup takes sk.per macro steps (256
+// small-batch forward (M <= 64: 9 or more tokens, or fewer on shapes the row kernel does not
+// take); with sk.ksplit > 1 each workgroup takes sk.per macro steps (256
 // columns each, a multiple of 4) of the reduction and writes float32 partials to sk.P ([ksplit][M][N],
 // the LoRA term in the last split), which launch_reduce_partials then sums
 SplitPlan gemv_wide_split(int64_t M, int64_t N, int64_t K);
