@@ -5,7 +5,9 @@ One step = one forward + one backward pass (dX, dL1, dL2) of the frozen NF4 line
 LoRA branch over one batch, through the C ABI (qlora_linear_fwd + qlora_linear_bwd), inputs
 already resident in HBM.  The default workload is the LLaMA-7B attention projection
 (W 4096x4096 NF4, block 64, double quantization block 256; 8 x 512 = 4096 tokens; r = 64,
-alpha = 16).  The headline value is algorithmic TFLOP/s (2MNK per dense product, LoRA at rank r).
+alpha = 16).  The headline value is algorithmic TFLOP/s (2MNK per dense product, LoRA at rank r),
+timed over 100 steps after 200 untimed ones (the clocks of sustained load; every other timed
+region below follows at least 150 ms of the same work).
 
 Also reported on the same JSON line:
   roofline     the dominant kernel (the larger of the two bf16 GEMM launches), timed live with
@@ -20,8 +22,9 @@ Also reported on the same JSON line:
                weights): the same, plus quantize + double quant of its three weights in GB/s
   qkv          the LLaMA-7B q, k, v projections (three 4096x4096 linears sharing X) as one product
                against three linear calls (forward), at 4096 and 1024 tokens
-  mid          the 7B attention projection forward + backward at 32, 256, 512 and 1536 tokens (the
-               fused dequant GEMMs and the under-filled expanded GEMM, their reductions split)
+  mid          the 7B attention projection forward + backward at 1, 16, 32, 256, 512 and 1536
+               tokens (the GEMVs, the fused dequant GEMMs and the under-filled expanded GEMM, their
+               reductions split where tiles leave CUs idle)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-gemv] [--no-mlp]
                        [--no-mid]
@@ -40,6 +43,27 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 TIMING_EVERY = 4               # timed steps whose GEMM launches carry HIP events
+# Sustained work before each timed region: the GPU's clocks climb over the first ~10-50 ms of
+# load after an idle spell (the 7B projection step read 0.304-0.310 ms after 5 warm-up steps,
+# 0.275 after 50 and 0.271 after 200), so every timed region follows at least this much.
+WARM_MS = 150.0
+
+
+def warm(torch, fn, min_ms=WARM_MS, min_calls=3):
+    """Call fn(i) until the calls have kept the GPU busy for min_ms (timed with events, in batches
+    that double), at least min_calls times; returns the number of calls."""
+    done, calls, batch = 0.0, 0, 1
+    while done < min_ms or calls < min_calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(batch):
+            fn(calls + i)
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+        calls += batch
+        batch = min(2 * batch, 4096)
+    return calls
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "NF4 dequant-GEMM+LoRA fwd/bwd TFLOP/s (7B shapes); M=1 GEMV GB/s"
 
@@ -182,11 +206,11 @@ def bench_gemv(torch, nf4, synth, dev, reps=60, warmup=10):
     out = {}
     for M in (1, 4, 16):
         st = make_linear(torch, nf4, synth, wl, lin, M, dev, replicas=3)
-        for i in range(warmup):
-            w = st["w"][i % 3]
-            nf4.qlora_linear_fwd(w, st["X"], st["L1"], st["L2"], st["s"], Y=st["Y"], T=st["T"],
+
+        def call(i):
+            nf4.qlora_linear_fwd(st["w"][i % 3], st["X"], st["L1"], st["L2"], st["s"], Y=st["Y"], T=st["T"],
                                  workspace=st["ws"])
-        torch.cuda.synchronize()
+        warm(torch, call, min_calls=warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
@@ -270,9 +294,7 @@ def bench_mlp(torch, nf4, synth, dev, wl, steps=10, warmup=3):
     every GEMM launch of one step in four timed with HIP events on its stream."""
     st = make_mlp(torch, nf4, synth, wl, dev)
     M, F, K, r = st["M"], st["F"], st["K"], st["r"]
-    for _ in range(warmup):
-        step_mlp(nf4, st)
-    torch.cuda.synchronize()
+    warm(torch, lambda i: step_mlp(nf4, st), min_calls=warmup)
     launches = mlp_launches(M, F, K, r)
     nl = len(launches)
     nsampled = (steps + TIMING_EVERY - 1) // TIMING_EVERY
@@ -353,8 +375,7 @@ def bench_quantize(torch, nf4, synth, dev, wl, reps=5):
             nf4._check(nf4.lib.nf4_double_quant(p(b["absmax"]), b["nb"], 256, p(b["q"]), p(b["sc"]), p(b["mean"]),
                                                 p(b["ws"]), b["wsb"], stream), "nf4_double_quant")
 
-    run()
-    torch.cuda.synchronize()
+    warm(torch, lambda i: run())
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -496,9 +517,7 @@ def bench_mid(torch, nf4, synth, dev, Ms=(1, 16, 32, 256, 512, 1536), steps=20, 
     out = {"workload": f"W {lin.N}x{lin.K} NF4, LoRA r={wl.r}, forward + backward, by token count"}
     for M in Ms:
         st = make_linear(torch, nf4, synth, wl, lin, M, dev)
-        for i in range(warmup):
-            step_linear(nf4, st, i)
-        torch.cuda.synchronize()
+        warm(torch, lambda i: step_linear(nf4, st, i), min_calls=warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -549,9 +568,7 @@ def bench_qkv(torch, nf4, synth, dev, reps=10, rounds=3):
         for rnd in range(rounds):
             order = (("one_product", multi), ("three_calls", separate))
             for name, fn in (order if rnd % 2 == 0 else order[::-1]):
-                for _ in range(2):
-                    fn()
-                torch.cuda.synchronize()
+                warm(torch, lambda i: fn(), min_ms=50.0, min_calls=2)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 for _ in range(reps):
@@ -573,8 +590,8 @@ def bench_qkv(torch, nf4, synth, dev, reps=10, rounds=3):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama7b_attn")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
