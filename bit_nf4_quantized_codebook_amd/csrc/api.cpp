@@ -793,12 +793,20 @@ int qlora_linear_bwd(const nf4_weight *w, const uint16_t *dY, const uint16_t *X,
     // dL2 = s T^T dY and dL1 = X^T dT, independent: one launch for both products, one for both
     // reductions (the partials side by side)
     float *P1 = P + (size_t)p.msL2 * r * N;
-    const nf4k::TnProduct tn_dL2{Tuse, dY, P, r, N, p.msL2};
-    const nf4k::TnProduct tn_dL1{X, dT, P1, K, r, p.msL1};
+    // unsplit (below 1024 tokens): the products write dL2 and dL1 themselves, no reduction launch
+    const bool tn_direct = p.msL2 == 1 && p.msL1 == 1;
+    nf4k::TnProduct tn_dL2{Tuse, dY, P, r, N, p.msL2};
+    nf4k::TnProduct tn_dL1{X, dT, P1, K, r, p.msL1};
+    if (tn_direct) {
+        tn_dL2.out = dL2; tn_dL2.scale = scale;
+        tn_dL1.out = dL1; tn_dL1.scale = 1.0f;
+    }
     NF4_CHECK_HIP(nf4k::launch_skinny_tn(tn_dL2, &tn_dL1, M, s), "dL2 = T^T dY, dL1 = X^T dT");
-    const nf4k::Reduction red_dL2{P, p.msL2, (int64_t)r * N, scale, dL2, 0.0f, nullptr};
-    const nf4k::Reduction red_dL1{P1, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr};
-    NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
+    if (!tn_direct) {
+        const nf4k::Reduction red_dL2{P, p.msL2, (int64_t)r * N, scale, dL2, 0.0f, nullptr};
+        const nf4k::Reduction red_dL1{P1, p.msL1, K * (int64_t)r, 1.0f, dL1, 0.0f, nullptr};
+        NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
+    }
     // dX = dY deq(W) + dT L1^T
     const bool acc = (flags & QLORA_DX_ACCUMULATE) != 0;
     if (expand) {
@@ -953,12 +961,19 @@ int qlora_gated_bwd(const nf4_weight *w_gate, const nf4_weight *w_up, const uint
         NF4_CHECK_HIP(nf4k::launch_expand_weight(view_of(sd.w), /*transposed=*/true, sd.WdT, &red_dT, s),
                       "weight expansion + dT reduce");
         float *P1 = P + (size_t)lp.msL2 * r * F;
-        const nf4k::TnProduct tn_dL2{Tuse, sd.dA, P, r, F, lp.msL2};
-        const nf4k::TnProduct tn_dL1{X, sd.dT, P1, K, r, lp.msL1};
+        const bool tn_direct = lp.msL2 == 1 && lp.msL1 == 1;
+        nf4k::TnProduct tn_dL2{Tuse, sd.dA, P, r, F, lp.msL2};
+        nf4k::TnProduct tn_dL1{X, sd.dT, P1, K, r, lp.msL1};
+        if (tn_direct) {
+            tn_dL2.out = sd.dL2; tn_dL2.scale = scale;
+            tn_dL1.out = sd.dL1; tn_dL1.scale = 1.0f;
+        }
         NF4_CHECK_HIP(nf4k::launch_skinny_tn(tn_dL2, &tn_dL1, M, s), "dL2 = T^T dA, dL1 = X^T dT");
-        const nf4k::Reduction red_dL2{P, lp.msL2, (int64_t)r * F, scale, sd.dL2, 0.0f, nullptr};
-        const nf4k::Reduction red_dL1{P1, lp.msL1, K * (int64_t)r, 1.0f, sd.dL1, 0.0f, nullptr};
-        NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
+        if (!tn_direct) {
+            const nf4k::Reduction red_dL2{P, lp.msL2, (int64_t)r * F, scale, sd.dL2, 0.0f, nullptr};
+            const nf4k::Reduction red_dL1{P1, lp.msL1, K * (int64_t)r, 1.0f, sd.dL1, 0.0f, nullptr};
+            NF4_CHECK_HIP(nf4k::launch_reduce_partials(red_dL2, &red_dL1, s), "dL2, dL1 reduce");
+        }
     }
     NF4_CHECK_HIP(nf4k::launch_gemm_bf16_bwd_dual(dG, sides[0].WdT, sides[0].dT, L1_gate, dU, sides[1].WdT, sides[1].dT,
                                                   L1_up, r, M, F, K, dX, acc != 0, s),

@@ -123,6 +123,10 @@ struct TnProduct {
     float *P;
     int64_t Pn, Qn;
     int nsplit;
+    // unsplit (nsplit == 1) with out set: bf16(scale * product) written to out [Pn, Qn] directly,
+    // what the reduction of the one partial would write, and P unused
+    uint16_t *out = nullptr;
+    float scale = 1.0f;
 };
 hipError_t launch_skinny_tn(const TnProduct &a, const TnProduct *b, int64_t M, hipStream_t stream);
 // out = bf16(s1 * sum of the nsplit partials), out2 (optional) = bf16(s2 * same); partial k of

@@ -144,6 +144,8 @@ __global__ __launch_bounds__(256) void skinny_nt_kernel(const uint16_t *__restri
 struct TnProb {
     const uint16_t *U, *V;
     float *P;
+    uint16_t *out;           // unsplit: bf16(scale * product) here instead of P
+    float scale;
     int64_t Pn, Qn, mchunk;
     int32_t tx, ty;
 };
@@ -216,7 +218,13 @@ __global__ __launch_bounds__(256) void skinny_tn_kernel(TnGroup grp) {
         __syncthreads();
     }
     const int64_t col = q0 + wn * 32 + r32;
-    if (col < Qn) {
+    if (col < Qn && pr.out) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = p0 + wm * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+            if (row < Pn) pr.out[row * Qn + col] = (uint16_t)f32_to_bf16(pr.scale * acc[v]);
+        }
+    } else if (col < Qn) {
         float *Pk = P + (int64_t)bz * Pn * Qn;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -269,6 +277,8 @@ TnProb tn_prob(const TnProduct &t, int64_t M, uint32_t &nblocks) {
     const int64_t per = (steps + t.nsplit - 1) / t.nsplit;
     TnProb p;
     p.U = t.U; p.V = t.V; p.P = t.P; p.Pn = t.Pn; p.Qn = t.Qn; p.mchunk = per * ST;
+    p.out = t.nsplit == 1 ? t.out : nullptr;
+    p.scale = t.scale;
     p.tx = (int32_t)((t.Pn + ST - 1) / ST);
     p.ty = (int32_t)((t.Qn + ST - 1) / ST);
     nblocks = (uint32_t)p.tx * (uint32_t)p.ty * (uint32_t)t.nsplit;
