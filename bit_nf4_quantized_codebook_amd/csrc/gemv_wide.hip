@@ -1,6 +1,7 @@
 // Small-batch forward (9 to 64 tokens, and smaller token counts on shapes the row kernel of
 // the decode GEMV does not take) of the QLoRA linear layer (gfx950):
-//   Y = X deq(W)^T + s T L2,   T = X L1 from float32 partials computed beforehand
+//   Y = X deq(W)^T + s T L2,   T = X L1 computed beforehand (its float32 split partials, or
+//   s T already reduced)
 //
 // Page: "QLoRA: Efficient Finetuning of Quantized LLMs" study notes (gitcode.csdn.net),
 // section 3.5 eq. (5) / eq. (6); section 4 eq. (3).
@@ -18,14 +19,14 @@
 //   - codes are expanded in planar order (elements 0,2,4,6 | 1,3,5,7 of each 8), so the X
 //     fragments are stored in LDS in the same order (permuted once per window)
 //   - W is fetched four macro steps ahead; X is staged through LDS in windows of 1024 columns
-//     (512 for 64 tokens),
-//     double buffered (the next window travels through registers while the current one is
-//     consumed), shared by the waves of a block
+//     (512 for 64 tokens), double buffered (the next window travels through registers while the
+//     current one is consumed), shared by the waves of a block
 //   - a block has NW = ceil(N / 16 / 256) waves (4 to 8), so that the grid is about one block
 //     per CU (28672 rows: 256 blocks of 7 waves, where 4-wave blocks made 448, two on most CUs);
-//     where the rows give fewer blocks than CUs (4096 rows: 64), the reduction is split over
-//     S = 256 / blocks workgroups of whole X windows each, which write float32 partials that a
-//     fixed-order pass sums (the LoRA term rides in the last split)
+//     where the rows give fewer blocks than CUs (4096 rows: 64) and each block has enough work,
+//     the reduction is split over S = 256 / blocks workgroups of whole groups of 4 macro steps,
+//     which write float32 partials that a fixed-order pass sums (the LoRA term rides in the last
+//     split)
 //   - the kernel is bound by the VALU work of the exact decode (about 250 VALU instructions per
 //     wave per 4096 weights), not by HBM
 // Prologue: s T into LDS.  Where T's float32 split partials are few (at most 128 KB), each
@@ -285,8 +286,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvArgs g) {
     }
 }
 
-// 16 token rows: 1 to 8 waves; 32 rows: 4 to 8 (fewer waves would hold a larger share of the
-// X window in registers)
+// 16 token rows: 1 to 8 waves; 32 and 64 rows: 4 to 8 (fewer waves would hold a larger share of
+// the X window in registers)
 template <int MROWS, bool I8>
 void launch_i8(const GemvArgs &a, int nw, int grid, hipStream_t stream) {
     const dim3 gd(grid);
