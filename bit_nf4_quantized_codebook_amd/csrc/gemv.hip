@@ -323,7 +323,9 @@ __device__ __forceinline__ f32x4 mfma4x4(uint32_t a0, uint32_t a1, uint32_t b0, 
 //   each 16-byte chunk (32 codes) feeds 8 v_mfma_f32_4x4x4_16b_bf16 per group of 4 tokens
 //   (B = the four rows' decoded pairs, A = X of four tokens over the same 4 columns).
 //   v_dot2_f32_bf16 issues at about a quarter of the VALU rate, so beyond one token the
-//   products go to the matrix cores.  The cross-wave sums run per batch of ITER row steps.
+//   products go to the matrix cores.  With 4 tokens the waves' partials of every row wait in LDS
+//   for the epilogue (as with one token); with 8 they do not fit, and the cross-wave sums run
+//   per batch of ITER row steps.
 // I8: the second-level codes are int8 (else E4M3); a template parameter so that the E4M3 kernel
 // carries no per-block select (it cost 2-3 % here).
 template <int MM, int BR, int U, int NWMAX, bool MF, bool I8>
@@ -338,6 +340,10 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
     constexpr int ROWS_STEP = MF ? 4 : 1;        // rows per row step and lane group
     constexpr int LANES_ROW = MF ? 16 : 64;      // 16-byte chunks of a row per wave and step
     constexpr int BROWS = ITER * ROWS_STEP;      // rows per batch of the cross-wave sums (MF)
+    // 4 tokens: every row's wave partials stay in LDS (part [KW][R][4]) and the epilogue sums
+    // them, as for one token; 8 tokens: the waves' partials of each batch of rows are summed
+    // after the batch (all rows' would not fit)
+    constexpr bool DEFER = MF && MM == 4;
     // staging areas are filled by whole-wave DMA copies (1 KB or 256 bytes per wave and step)
     __shared__ __align__(16) uint32_t tab[TAB_WORDS];
     __shared__ __align__(16) uint32_t c2s[(C2_CAP + 2048) / 4];
@@ -346,7 +352,8 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
     __shared__ __align__(16) uint16_t l2s[R_MAX_LORA * R_MAX];   // [r][R]
     __shared__ uint32_t cbh[16];
     // T's chunk sums in the prologue; afterwards the wave partials of the rows
-    //   MF = false: part [KW][R][MM];  MF = true: part [wave][BROWS][MM] and res [R][MM] at RES_OFF
+    //   MF = false or 4 tokens: part [KW][R][MM];  8 tokens: part [wave][BROWS][MM] and res [R][MM]
+    //   at RES_OFF
     __shared__ float scr[CSUM_CAP];
     float *csum = scr, *part = scr, *res = scr + RES_OFF;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -544,9 +551,14 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) cq = mfma4x4(x[q][2 * t], x[q][2 * t + 1], pr[2 * t], pr[2 * t + 1], cq);
                     const float v = reduce_blocks4(sc * cq);
-                    if (holder) part[(wave * BROWS + ROWS_STEP * rr + jrow) * MM + 4 * q + htok] = v;
+                    if constexpr (DEFER) {
+                        if (holder & (i < nsteps)) part[(kw * a.R + lrow(i)) * MM + 4 * q + htok] = v;
+                    } else {
+                        if (holder) part[(wave * BROWS + ROWS_STEP * rr + jrow) * MM + 4 * q + htok] = v;
+                    }
                 }
             });
+            if constexpr (DEFER) continue;
             // the KW waves of each row meet here: batch `it` of every stream
             lds_barrier();
             for (int e = tid; e < a.S * BROWS * MM; e += nthr) {
@@ -576,7 +588,7 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
                 const int j = 8 * jj + q;
                 lo = __builtin_fmaf(sTs[m * a.r + j], bf16_to_f32(l2s[j * a.R + rl]), lo);
             }
-            if constexpr (MF) {
+            if constexpr (MF && !DEFER) {
                 if (q == 0) lo += res[rl * MM + m];
             } else if (q < a.KW) {
                 for (int k = q; k < a.KW; k += 8) lo += part[(k * a.R + rl) * MM + m];
@@ -611,7 +623,8 @@ RowsPlan rows_plan(int64_t N, int64_t K, int mm) {
     int64_t cap = R_MAX;
     if (cap > C2_CAP / nblk) cap = C2_CAP / nblk;
     if (!mf && cap > PART_CAP / p.KW) cap = PART_CAP / p.KW;
-    if (mf && cap > (CSUM_CAP - RES_OFF) / mm) cap = (CSUM_CAP - RES_OFF) / mm;
+    if (mm == 4 && cap > CSUM_CAP / (4 * p.KW)) cap = CSUM_CAP / (4 * p.KW);   // all rows' partials
+    if (mm == 8 && cap > (CSUM_CAP - RES_OFF) / mm) cap = (CSUM_CAP - RES_OFF) / mm;
     cap = cap / unit * unit;
     if (R > cap) R = cap;
     p.R = (int)R;
@@ -697,6 +710,7 @@ bool gemv_fits(int64_t M, int64_t N, int64_t K, int32_t r) {
     const int64_t nch = (t_parts(M, K, r) + 7) / 8;
     if (p.S < 1 || p.R < 8 || p.R > R_MAX || p.R * (K >> 6) > C2_CAP || nch * mm * r > CSUM_CAP) return false;
     if (mm == 1) return (int64_t)p.KW * p.R <= PART_CAP;
+    if (mm == 4) return (int64_t)p.KW * p.R * 4 <= CSUM_CAP;   // every row's wave partials
     // cross-wave partials of one batch, and the row sums
     return (int64_t)p.S * p.KW * 16 * mm <= RES_OFF && (int64_t)p.R * mm <= CSUM_CAP - RES_OFF;   // 16 rows a batch
 }
