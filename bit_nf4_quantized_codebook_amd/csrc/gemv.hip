@@ -559,16 +559,23 @@ __global__ __launch_bounds__(NWMAX * 64) void gemv_rows_kernel(RowsArgs a) {
                 }
             });
             if constexpr (DEFER) continue;
-            // the KW waves of each row meet here: batch `it` of every stream
+            // the KW waves of each row meet here: batch `it` of every stream, 8 lanes per sum (lane
+            // q adds waves q, q + 8, ..., then a prefix sum over the 8 ends in lane 7)
             lds_barrier();
-            for (int e = tid; e < a.S * BROWS * MM; e += nthr) {
+            const int nsum = a.S * BROWS * MM;
+            for (int i0 = 0; i0 < nsum * 8; i0 += nthr) {     // uniform trip count (DPP below)
+                const int e = (i0 + tid) >> 3, q = tid & 7;
                 const int ss = e / (BROWS * MM), rem = e - ss * (BROWS * MM);
                 const int br = rem / MM, m = rem - br * MM;
                 float t = 0.0f;
-                for (int k = 0; k < a.KW; ++k) t += part[((ss * a.KW + k) * BROWS + br) * MM + m];
+                if (e < nsum)
+                    for (int k = q; k < a.KW; k += 8) t += part[((ss * a.KW + k) * BROWS + br) * MM + m];
+                t += dpp<0x111>(t);
+                t += dpp<0x112>(t);
+                t += dpp<0x114>(t);
                 const int st = it * ITER + br / ROWS_STEP;          // the row's step in its stream
                 const int row = ss * a.RS + ROWS_STEP * st + (br % ROWS_STEP);
-                if (st < nsteps && row < nrows) res[row * MM + m] = t;
+                if (e < nsum && q == 7 && st < nsteps && row < nrows) res[row * MM + m] = t;
             }
             lds_barrier();
         }
