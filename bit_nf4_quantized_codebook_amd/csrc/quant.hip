@@ -218,7 +218,20 @@ __global__ __launch_bounds__(1024) void group_sum_tail_kernel(const double *__re
                                                               double *__restrict__ total) {
     __shared__ double v[TAIL_MAX + TAIL_MAX / 256];
     const int tid = threadIdx.x;
-    for (int e = tid; e < (int)n; e += 1024) v[e + (e >> 8)] = in[e];
+    {
+        // every load in flight before the first LDS store
+        double r[TAIL_MAX / 1024];
+#pragma unroll
+        for (int q = 0; q < TAIL_MAX / 1024; ++q) {
+            const int e = tid + 1024 * q;
+            r[q] = e < (int)n ? in[e] : 0.0;
+        }
+#pragma unroll
+        for (int q = 0; q < TAIL_MAX / 1024; ++q) {
+            const int e = tid + 1024 * q;
+            if (e < (int)n) v[e + (e >> 8)] = r[q];
+        }
+    }
     __syncthreads();
     int len = (int)n;
     while (len > 1) {
@@ -250,20 +263,38 @@ __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__
                                                        uint8_t *__restrict__ codes,
                                                        float *__restrict__ scales,
                                                        float *__restrict__ mean_out, uint32_t int8) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x;
     const float mu = (float)(total[0] / (double)nb);
     const int64_t ng = (nb + 255) >> 8;
-    for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
+    // y = absmax - mean of the group's 4 values of this lane (0 past the end)
+    auto load = [&](int64_t g, float (&y)[4]) {
         const int64_t i0 = (g << 8) + lane * 4;
-        float y[4];
-        float m = 0.0f;
+        if (g < ng && i0 + 3 < nb) {
+            const f4 a = *reinterpret_cast<const f4 *>(absmax + i0);
+            y[0] = a.x - mu; y[1] = a.y - mu; y[2] = a.z - mu; y[3] = a.w - mu;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            y[k] = (i0 + k < nb) ? (absmax[i0 + k] - mu) : 0.0f;
-            m = fmaxf(m, fabsf(y[k]));
+            for (int k = 0; k < 4; ++k) y[k] = (g < ng && i0 + k < nb) ? (absmax[i0 + k] - mu) : 0.0f;
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    };
+    // the next group's loads go out before this group's arithmetic
+    float y[4];
+    load(blockIdx.x, y);
+    for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
+        float yn[4];
+        load(g + gridDim.x, yn);
+        const int64_t i0 = (g << 8) + lane * 4;
+        float m = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+        // max over the wave: within each 16-lane row by DPP moves (lane ^ 1, lane ^ 2, the mirror
+        // within 8, the mirror within 16), then the four rows' maxima
+        m = fmaxf(m, row_move<0xB1>(m));
+        m = fmaxf(m, row_move<0x4E>(m));
+        m = fmaxf(m, row_move<0x141>(m));
+        m = fmaxf(m, row_move<0x140>(m));
+        const int mi = __float_as_int(m);
+        m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 0)), __int_as_float(__builtin_amdgcn_readlane(mi, 16))),
+                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 32)), __int_as_float(__builtin_amdgcn_readlane(mi, 48))));
         const float s = int8 ? m / 127.0f : m / 448.0f;
         uint32_t word = 0;
 #pragma unroll
@@ -290,6 +321,8 @@ __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__
         }
         if (lane == 0) scales[g] = s;
         if (lane == 0 && g == 0) mean_out[0] = mu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = yn[k];
     }
 }
 
