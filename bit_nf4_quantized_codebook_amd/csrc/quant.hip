@@ -479,7 +479,8 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, uint8_t *codes, 
     if (e != hipSuccess) return e;
     const int64_t ng = (nb + 255) / 256;
     // (two groups per wave, a workgroup per group, or four one-group waves per workgroup: each
-    // measured slower, 8.6-9.2 us against 7.9 us at 11008 groups)
+    // measured slower, 8.6-9.2 us against 7.9 us at 11008 groups, when the wave's max still went
+    // through LDS shuffles)
     hipLaunchKernelGGL(dq_encode_kernel, dim3(grid_for(ng, 1, 256 * 32)), dim3(64), 0, stream,
                        absmax, nb, total, codes, scales, mean, int8 ? 1u : 0u);
     return hipGetLastError();
