@@ -176,6 +176,8 @@ SHAPES = [
     (12, 2000, 4096, 32),      # four token groups (tokens 12..15 padding), two row streams
     (5, 512, 8192, 16),
     (4, 520, 2048, 128),       # 4x4-MFMA decode layout with r = 128, four row streams
+    (3, 1000, 4096, 64),       # 4x4-MFMA, 2-4 tokens: two row streams, ragged last workgroup (8 of 16 rows)
+    (7, 1000, 2048, 32),       # 4x4-MFMA, 5-8 tokens: four row streams, each batch's sums in four passes
     (1, 1000, 4096, 128),      # one-token decode layout with r = 128
     (9, 1000, 2048, 16),       # the first token count past the row kernel: the 16x16x32 GEMV
     (1023, 264, 640, 24),      # the last token count of the fused dequant GEMMs, ragged
