@@ -285,7 +285,8 @@ __global__ __launch_bounds__(64) void dq_encode_kernel(const float *__restrict__
         float yn[4];
         load(g + gridDim.x, yn);
         const int64_t i0 = (g << 8) + lane * 4;
-        float m = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+        // from 0: a NaN constant is passed over, as fmaxf does (the lane's value is never NaN)
+        float m = fmaxf(fmaxf(fmaxf(0.0f, fabsf(y[0])), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
         // max over the wave: within each 16-lane row by DPP moves (lane ^ 1, lane ^ 2, the mirror
         // within 8, the mirror within 16), then the four rows' maxima
         m = fmaxf(m, row_move<0xB1>(m));

@@ -137,6 +137,21 @@ def test_double_quant_ragged_bit_exact(nb):
     assert mean.cpu().numpy()[0] == m_ref
 
 
+def test_double_quant_nan_constants_match_oracle():
+    """A NaN block constant (an all-NaN weight block) makes the mean NaN, so every centred
+    constant is NaN: each group's max then passes over them (scale 0, codes 0), as the oracle's
+    does; 8204 groups, so some workgroups encode a second group."""
+    nb = 2_100_000
+    _say(f"double quant with NaN constants nb={nb}")
+    a = np.abs(synth.normal_f32(1234, (nb,), 0.05)).astype(np.float32)
+    a[300:304] = np.float32("nan")
+    q, sc, mean = nf4.nf4_double_quant(torch.from_numpy(a).to(DEV))
+    c_ref, s_ref, m_ref = oracle.double_quant(a)
+    assert np.isnan(m_ref) and np.isnan(mean.cpu().numpy()[0])
+    assert np.array_equal(q.cpu().numpy(), c_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
 # ------------------------------------------------------------------------------------------
 # Linear layer: tolerance against the float64 oracle
 # ------------------------------------------------------------------------------------------
