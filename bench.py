@@ -45,7 +45,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 TIMING_EVERY = 4               # timed steps whose GEMM launches carry HIP events
 # Sustained work before each timed region: the GPU's clocks climb over the first ~10-50 ms of
 # load after an idle spell (the 7B projection step read 0.304-0.310 ms after 5 warm-up steps,
-# 0.275 after 50 and 0.271 after 200), so every timed region follows at least this much.
+# 0.275 after 50 and 0.271 after 200; 2000 steps, the default, read 0.278-0.279 against
+# 0.280-0.281 after 200 on one box), so every timed region follows at least this much.
 WARM_MS = 150.0
 
 
@@ -591,7 +592,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="llama7b_attn")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
