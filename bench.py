@@ -616,7 +616,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the layer would shard "
               "data-parallel with one all-reduce of the LoRA gradients); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
