@@ -1,9 +1,12 @@
-"""Graph capture of the forward that allocates nothing (qlora_linear_fwd_static), the entry point for
-callers that record their work into a HIP graph: captured once per token count, then replayed with
-new inputs written into the captured buffers, with eager work and device synchronisations between
-the replays; every replay's Y and T against the eager forward's bits (qlora_linear_fwd runs the same
-kernels).  The token counts take every forward path: the decode GEMV, the 16-token GEMV, the fused
-dequant GEMM and the bf16 expansion + GEMM."""
+"""Graph capture (torch's CUDAGraph over the library's HIP launches).
+
+The forward that allocates nothing (qlora_linear_fwd_static), the entry point for callers that
+record their work into a graph: captured once per token count, then replayed with new inputs written
+into the captured buffers, with eager work and device synchronisations between the replays; every
+replay's Y and T against the eager forward's bits (qlora_linear_fwd runs the same kernels).  The
+token counts take every forward path: the decode GEMV, the 16-token GEMV, the fused dequant GEMM and
+the bf16 expansion + GEMM.  And a whole forward + backward step through the workspace entry points,
+captured and replayed the same way."""
 import numpy as np
 import pytest
 
@@ -53,3 +56,44 @@ def test_static_forward_graph_replays_match_eager(M):
         torch.cuda.synchronize()
         assert torch.equal(Y.view(torch.int16), Y_ref.view(torch.int16)), (M, rep)
         assert torch.equal(T.view(torch.int16), T_ref.view(torch.int16)), (M, rep)
+
+
+@pytest.mark.parametrize("M", [16, 4096])
+def test_training_step_graph_replays_match_eager(M):
+    """A whole forward + backward step through the workspace entry points captured into one graph
+    (outputs and workspaces come from the graph's memory pool), replayed with new X and dY: Y, T,
+    dX, dL1 and dL2 of every replay bit for bit against eager calls."""
+    N, K, r, s = 4096, 4096, 64, 0.25
+    print(f"graph capture of a training step: M={M} N={N} K={K} r={r} {nf4.qlora_linear_route(M, N, K, r)}",
+          flush=True)
+    cb = nf4.nf4_build_codebook()
+    w = nf4.NF4Weight.from_float(torch.from_numpy(synth.normal_f32(1900, (N, K), 0.02)).to(DEV), cb)
+    L1 = _bf16(synth.normal_f32(1901, (K, r), 1.0 / r))
+    L2 = _bf16(synth.normal_f32(1902, (r, N), 0.01))
+    X = _bf16(synth.normal_f32(1910, (M, K), 1.0))
+    dY = _bf16(synth.normal_f32(1911, (M, N), 1.0))
+
+    def step():
+        Y, T = nf4.qlora_linear_fwd(w, X, L1, L2, s)
+        dX, dL1, dL2 = nf4.qlora_linear_bwd(w, dY, X, L1, L2, T, s)
+        return Y, T, dX, dL1, dL2
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        X.copy_(_bf16(synth.normal_f32(1920 + rep, (M, K), 1.0)))
+        dY.copy_(_bf16(synth.normal_f32(1930 + rep, (M, N), 1.0)))
+        g.replay()
+        torch.cuda.synchronize()
+        refs = step()                                            # eager work between the replays
+        torch.cuda.synchronize()
+        for name, a, b in zip(("Y", "T", "dX", "dL1", "dL2"), outs, refs):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (M, rep, name)
